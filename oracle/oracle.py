@@ -1,0 +1,303 @@
+"""Plain CPU oracle for the CSA2 hierarchical sparse-attention decode step.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+leg of the benchmark import this module; the product path never does, and it
+shares no code, table or helper with the HIP kernels.
+
+The heavy loops live in ``csa2_oracle.c`` (plain C, int64 / fp64, built with
+gcc); this file is the literal orchestration of the method in numpy, one
+function per step of the method, each naming the passage it follows.
+
+Sources (page title, section):
+  [CED]  "DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 2: CSA2 &
+         Hierarchical Sparse Indexing" and "Act 3: FP4 KV & SWA Bounded Replay".
+  [HOW]  "How DeepSeek V4.1 Flash Actually Works", "The three KV-cache
+         optimizations", item 2 "Compress Sparse Attention".
+  [AGAIN] "DeepSeek Has Done It Again...", "Architecture and inference
+         efficiency", bullet "Sparse attention for long context".
+  [IMP]  "Deepseek just did the impossible", "Memory and Compute Optimization".
+Readings fixed where the pages are silent (int8 keys/queries, the score rule,
+tie order, FP4 E2M1 + E8M0 per 32, K = V = latent, 1/sqrt(512)) are listed with
+each function.
+
+Parity status: all functions are pinned by the CPU tests; none is unpinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "csa2_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libcsa2_oracle.so")
+
+__all__ = [
+    "build", "load", "bf16_to_f64", "fp4_quantize", "fp4_dequantize", "fp4_value",
+    "index_scores", "topk", "eligible_count", "window_positions", "index_full",
+    "index_reindex", "select_topk", "attention_positions", "attention",
+    "layer_kind", "layer_pattern", "decode_step",
+]
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into a shared object next to the source."""
+    if force or not os.path.exists(_LIB_PATH) or \
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared",
+                        _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH) or \
+                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build(force=True)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16_to_double.restype = ctypes.c_double
+        lib.oracle_fp4_value.argtypes = [ctypes.c_int, ctypes.c_int]
+        lib.oracle_fp4_value.restype = ctypes.c_double
+        lib.oracle_fp4_quantize.argtypes = [P, I64, ctypes.c_int, P, P]
+        lib.oracle_fp4_quantize.restype = None
+        lib.oracle_fp4_dequantize.argtypes = [P, P, I64, ctypes.c_int, P]
+        lib.oracle_fp4_dequantize.restype = None
+        lib.oracle_index_scores.argtypes = [P, ctypes.c_int, P, I64, P, P, ctypes.c_int, P]
+        lib.oracle_index_scores.restype = None
+        lib.oracle_topk.argtypes = [P, P, I64, I64, P, P]
+        lib.oracle_topk.restype = I64
+        lib.oracle_attention.argtypes = [P, ctypes.c_int, ctypes.c_int, P, I64,
+                                         ctypes.c_double, P, P]
+        lib.oracle_attention.restype = None
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+# --------------------------------------------------------------------------
+# FP4 E2M1 with one E8M0 scale per 32 elements ([CED] "Act 3": FP4 main KV;
+# [HOW] item 2: KV values stored in FP4; block format per OCP MX v1.0).
+# --------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact value of bf16 bit patterns (uint16) as float64."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def fp4_value(nibble: int, scale_byte: int) -> float:
+    return load().oracle_fp4_value(int(nibble), int(scale_byte))
+
+
+def fp4_quantize(x_bf16: np.ndarray):
+    """Rows of D bf16 values (uint16 bit patterns, shape [n, D]) ->
+    (codes [n, D/2] uint8, scales [n, D/32] uint8)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    n, D = x.shape
+    assert D % 32 == 0
+    codes = np.zeros((n, D // 2), dtype=np.uint8)
+    scales = np.zeros((n, D // 32), dtype=np.uint8)
+    if n:
+        load().oracle_fp4_quantize(_ptr(x), n, D, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def fp4_dequantize(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint8)
+    n, half = c.shape
+    D = half * 2
+    assert s.shape == (n, D // 32)
+    out = np.zeros((n, D), dtype=np.float64)
+    if n:
+        load().oracle_fp4_dequantize(_ptr(c), _ptr(s), n, D, _ptr(out))
+    return out
+
+
+# --------------------------------------------------------------------------
+# Index scores and the rank order.
+# --------------------------------------------------------------------------
+
+_SCORE_LIMIT = 1 << 31
+
+
+def index_scores(keys: np.ndarray, rows: np.ndarray, q: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """s(p) = sum_h w_h * max(0, q_h . K[p]) for every listed cache row.
+
+    The pages say an indexing layer scans the context and scores positions
+    ([HOW] item 2; [CED] "Act 2"); the rule itself (int8 keys and queries, one
+    key per token shared by all index heads, per-head weights, ReLU, exact
+    integer sum) is this path's reading.  Returned as int64; every value is
+    asserted to lie in [0, 2^31).
+    """
+    keys = np.ascontiguousarray(keys, dtype=np.int8)
+    dk = keys.shape[1]
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    q = np.ascontiguousarray(q, dtype=np.int8)
+    w = np.ascontiguousarray(w, dtype=np.int8)
+    H = q.shape[0]
+    assert q.shape == (H, dk) and w.shape == (H,)
+    out = np.zeros(rows.shape[0], dtype=np.int64)
+    if rows.shape[0]:
+        assert rows.min() >= 0 and rows.max() < keys.shape[0]
+        load().oracle_index_scores(_ptr(keys), dk, _ptr(rows), rows.shape[0],
+                                   _ptr(q), _ptr(w), H, _ptr(out))
+        assert out.min() >= 0 and out.max() < _SCORE_LIMIT
+    return out
+
+
+def topk(score: np.ndarray, pos: np.ndarray, k: int):
+    """The first min(k, n) candidates under the order  p before p'  iff
+    s(p) > s(p') or (s(p) == s(p') and p < p'), returned ascending by
+    position together with their scores.
+
+    [HOW] item 2 and [AGAIN]: keep the 512 most relevant / up to 512 positions;
+    ties go to the lower position (this path's reading).
+    """
+    s = np.ascontiguousarray(score, dtype=np.int64)
+    p = np.ascontiguousarray(pos, dtype=np.int64)
+    n = s.shape[0]
+    assert p.shape == (n,)
+    keff = max(0, min(int(k), n))
+    out_p = np.zeros(keff, dtype=np.int64)
+    out_s = np.zeros(keff, dtype=np.int64)
+    if keff:
+        got = load().oracle_topk(_ptr(s), _ptr(p), n, keff, _ptr(out_p), _ptr(out_s))
+        assert got == keff
+    return out_p, out_s
+
+
+# --------------------------------------------------------------------------
+# The CSA2 modes.
+# --------------------------------------------------------------------------
+
+def eligible_count(L: int, window: int) -> int:
+    """Positions eligible for global selection: [0, L - W).  The window rows
+    [L - W, L) are attended anyway and are never selected twice ([HOW] item 2:
+    512 selected entries plus a local 128-token window)."""
+    return max(0, int(L) - int(window))
+
+
+def window_positions(L: int, window: int) -> np.ndarray:
+    return np.arange(max(0, int(L) - int(window)), int(L), dtype=np.int64)
+
+
+def index_full(keys, row_off: int, L: int, q, w, window: int, P: int):
+    """Full mode: score every eligible position of the context and keep the
+    first min(P, E) under the rank order as the candidate pool, ascending by
+    position ([CED] "Act 2": the first full-mode indexing layer searches the
+    whole context and builds a candidate pool; [HOW] item 2: up to 16,384
+    candidate positions)."""
+    E = eligible_count(L, window)
+    pos = np.arange(E, dtype=np.int64)
+    s = index_scores(keys, row_off + pos, q, w)
+    return topk(s, pos, min(int(P), E))
+
+
+def index_reindex(keys, row_off: int, cand_pos, q, w) -> np.ndarray:
+    """Reindex mode: re-score only the pool with this layer's own index query
+    and weights and the same index keys ([CED] "Act 2": later layers search
+    only the much smaller pool; [HOW] item 2: later layers search within that
+    shortlist)."""
+    cand_pos = np.asarray(cand_pos, dtype=np.int64)
+    return index_scores(keys, row_off + cand_pos, q, w)
+
+
+def select_topk(score, cand_pos, k: int):
+    """Top-k global positions of a scored candidate list ([HOW] item 2: the 512
+    most relevant entries), ascending by position."""
+    return topk(score, cand_pos, k)
+
+
+def attention_positions(L: int, sel_pos, window: int) -> np.ndarray:
+    """S = selection U window, selection first; the two are disjoint."""
+    sel = np.asarray(sel_pos, dtype=np.int64)
+    win = window_positions(L, window)
+    assert sel.size == 0 or sel.max() < max(0, L - window), "selection overlaps the window"
+    return np.concatenate([sel, win])
+
+
+def attention(q_bf16: np.ndarray, codes: np.ndarray, scales: np.ndarray, sm_scale: float):
+    """Softmax attention of every query head over the given FP4 rows, K = V =
+    the dequantised latent row (MQA).  Returns (out [Hq, D] float64,
+    lse [Hq] float64, natural log).  [HOW] item 2 / [AGAIN]: attention over the
+    selected global positions and the recent window."""
+    v = fp4_dequantize(codes, scales)
+    q = np.ascontiguousarray(q_bf16, dtype=np.uint16)
+    Hq, D = q.shape
+    S = v.shape[0]
+    assert v.shape[1] == D
+    out = np.zeros((Hq, D), dtype=np.float64)
+    lse = np.zeros(Hq, dtype=np.float64)
+    load().oracle_attention(_ptr(q), Hq, D, _ptr(np.ascontiguousarray(v)), S,
+                            float(sm_scale), _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def layer_kind(l: int) -> str:
+    """Layer pattern of the 20-layer decoder: Full once, then Reindex at layer 1
+    and every 4th layer, Reuse otherwise ([CED] "Act 2": Full -> Reindex ->
+    Reuse; [IMP]: Full, Reindex and Reuse sharing modes)."""
+    if l == 0:
+        return "F"
+    if l == 1 or l % 4 == 0:
+        return "R"
+    return "U"
+
+
+def layer_pattern(n_layers: int) -> str:
+    return "".join(layer_kind(l) for l in range(n_layers))
+
+
+def decode_step(pattern: str, keys, row_off: int, L: int, window: int, P: int, k: int,
+                idx_q, idx_w, attn_q, kv_rows, sm_scale: float):
+    """One decode step of one sequence over the layers of ``pattern``.
+
+    idx_q[l], idx_w[l]: int8 index query / weights of F and R layers.
+    attn_q[l]: [Hq, D] bf16 bit patterns.  kv_rows(l, positions) -> bf16 bit
+    patterns [n, D] of layer l's latent rows at those positions (quantised
+    here with the oracle's own FP4 rule).
+    Returns per-layer dicts with pool, selection, out and lse.
+    Reuse takes the most recent layer's selection; Reindex re-scores the most
+    recent Full layer's pool ([CED] "Act 2"; [HOW] item 2: selection reuse).
+    """
+    results = []
+    pool = None
+    sel = None
+    for l, kind in enumerate(pattern):
+        rec = {"kind": kind}
+        if kind == "F":
+            pool_pos, pool_score = index_full(keys, row_off, L, idx_q[l], idx_w[l], window, P)
+            pool = pool_pos
+            sel, _ = select_topk(pool_score, pool_pos, k)
+            rec.update(pool_pos=pool_pos, pool_score=pool_score)
+        elif kind == "R":
+            assert pool is not None, "Reindex needs an earlier Full layer"
+            sc = index_reindex(keys, row_off, pool, idx_q[l], idx_w[l])
+            sel, _ = select_topk(sc, pool, k)
+            rec.update(reindex_score=sc)
+        else:
+            assert sel is not None, "Reuse needs an earlier selection"
+        S = attention_positions(L, sel, window)
+        x = kv_rows(l, S)
+        codes, scales = fp4_quantize(x)
+        out, lse = attention(attn_q[l], codes, scales, sm_scale)
+        rec.update(sel=sel, out=out, lse=lse, S=S)
+        results.append(rec)
+    return results

@@ -1,0 +1,254 @@
+"""Decode-step benchmark of the CSA2 sparse-attention path on one MI355X.
+
+Workload (default): ctx_1m -- one sequence at L = 1,048,576 cached tokens,
+20 decoder layers F R U U R U U U R ... (Full once, Reindex at layer 1 and
+every 4th layer, Reuse otherwise), pool P = 16,384, top-k 512, window 128,
+64 int8 index heads x 64, 64 bf16 query heads x 512, FP4 E2M1 latent KV with
+E8M0 scales per 32 elements.  Synthetic seeded inputs.
+
+A step is the whole hot path: Full index scan + pool, 6 top-k selections,
+5 Reindex passes, 20 sparse-attention layers.  The step is captured once in a
+HIP graph and replayed.  Cold timing (the headline) evicts the 256 MB
+Infinity Cache before every step with an untimed read of a 1 GiB buffer and
+times each step with HIP events on the replay stream; warm timing replays
+back to back.
+
+Output: one JSON line (metric, value = steps/s, roofline of the Full scan's
+scoring kernel, CPU-oracle baseline, ...).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def algorithmic_bytes(wl, L: int) -> dict:
+    """Bytes the method must move per step (every buffer crossing the C ABI
+    once, plus the index keys and KV rows it reads)."""
+    E = max(0, L - wl.window)
+    Peff = min(wl.P, E)
+    keff = min(wl.k, Peff)
+    W = min(wl.window, L)
+    pat = wl.pattern
+    nF, nR = pat.count("F"), pat.count("R")
+    full = 64 * E + 65 * wl.H + 8 * Peff
+    sel = 8 * Peff + 4 * keff
+    rei = 72 * Peff + 65 * wl.H
+    attn = 272 * (keff + W) + 6 * wl.Hq * wl.D + 4 * keff
+    return {"full": nF * full * wl.B, "select": (nF + nR) * sel * wl.B,
+            "reindex": nR * rei * wl.B, "attn": wl.n_layers * attn * wl.B,
+            "scan_kernel": (64 * E + 65 * wl.H) * wl.B}
+
+
+def stale_traffic(profile_path: str, src_path: str):
+    """HBM traffic of the scan kernel from a committed counter summary, or
+    None if the kernel source changed since the counters were taken."""
+    try:
+        rec = json.load(open(profile_path))
+        sha = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
+        if rec.get("source_sha256") != sha:
+            return None
+        return rec.get("traffic_bytes_per_launch")
+    except Exception:
+        return None
+
+
+def cpu_baseline(case, wl, keys, seconds_target: float = 12.0) -> dict:
+    """The oracle timed on the host cores on one full decode step (index scan
+    over all 1,048,576 positions, 6 selections, 5 Reindex, 20 attention
+    layers), repeated while under the time target."""
+    import numpy as np
+    import torch
+
+    import oracle
+    oracle.build(force=False)
+    b = 0
+    L = case.lengths[0]
+    keys = keys.cpu().numpy()
+    idx_q = {l: case.index_q(0, l, b).cpu().numpy() for l, c in enumerate(wl.pattern) if c in "FR"}
+    idx_w = {l: case.index_w(0, l, b).cpu().numpy() for l, c in enumerate(wl.pattern) if c in "FR"}
+    u16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    attn_q = [u16(case.attn_q(0, l, b)) for l in range(wl.n_layers)]
+    cpu_case = type(case)(wl, case.seed, "cpu")
+    kv_rows = lambda l, S: u16(cpu_case.kv_bf16(l, b, S))
+    times = []
+    t_all = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        oracle.decode_step(wl.pattern, keys, 0, L, wl.window, wl.P, wl.k, idx_q, idx_w, attn_q,
+                           kv_rows, wl.sm_scale)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_all + times[-1] > seconds_target or len(times) >= 50:
+            break
+    cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
+    per = statistics.median(times)
+    return {"value": round(1.0 / per, 4), "unit": "decode steps/s", "cores": cores,
+            "kind": "oracle",
+            "sample": "%d full decode step(s) of the same workload (1 sequence, L=%d, 20 layers), "
+                      "median %.2f s/step" % (len(times), L, per)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="ctx_1m")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly (debug)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(got --gpus %d)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from decode_kv_amd import csa2, pipeline
+    from decode_kv_amd import workloads as W
+
+    assert torch.cuda.is_available(), "no GPU"
+    csa2.lib()
+    dev = torch.device("cuda:0")
+    wl = W.WORKLOADS[args.workload]
+    t_setup = time.perf_counter()
+    case = W.Case(wl, args.seed, dev)
+    eng = pipeline.Engine(case, dev)
+    inp = eng.step_inputs(0)
+    torch.cuda.synchronize()
+    print("setup %.1f s" % (time.perf_counter() - t_setup), file=sys.stderr, flush=True)
+    assert not wl.append, "the bench workloads replay an idempotent step"
+
+    stream = torch.cuda.Stream()
+    scan0 = torch.cuda.Event(enable_timing=True)
+    scan1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        scan0.record()
+        scan1.record()
+    torch.cuda.synchronize()
+
+    # eager warm-up (also compiles nothing: kernels are prebuilt)
+    with torch.cuda.stream(stream):
+        for _ in range(2):
+            eng.run_step(inp)
+    torch.cuda.synchronize()
+    ref_out = eng.out.clone()
+
+    graph = None
+    if not args.no_graph:
+        csa2.set_scan_timer(scan0, scan1)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            eng.run_step(inp)
+        csa2.set_scan_timer(None, None)
+        torch.cuda.synchronize()
+
+    def step():
+        if graph is not None:
+            graph.replay()
+        else:
+            csa2.set_scan_timer(scan0, scan1)
+            eng.run_step(inp)
+            csa2.set_scan_timer(None, None)
+
+    scrub = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    scrub_sink = torch.empty((), dtype=torch.int64, device=dev)
+
+    def evict():
+        torch.sum(scrub.view(torch.int64), dim=0, out=scrub_sink)
+
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            evict()
+            step()
+    torch.cuda.synchronize()
+    assert torch.equal(eng.out, ref_out), "graph replay differs from eager step"
+
+    # ---- timed region: K cold steps ---------------------------------------
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    scan_ms = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(K):
+            evict()
+            ev[i][0].record()
+            step()
+            ev[i][1].record()
+            ev[i][1].synchronize()
+            scan_ms.append(scan0.elapsed_time(scan1))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+
+    # warm: back-to-back replays, one event pair around all of them
+    with torch.cuda.stream(stream):
+        w0 = torch.cuda.Event(enable_timing=True)
+        w1 = torch.cuda.Event(enable_timing=True)
+        w0.record()
+        for _ in range(K):
+            step()
+        w1.record()
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / K
+
+    ms = statistics.mean(step_ms)
+    L = case.lengths[0]
+    ab = algorithmic_bytes(wl, L)
+    step_bytes = ab["full"] + ab["select"] + ab["reindex"] + ab["attn"]
+    scan_avg_ms = statistics.mean(scan_ms)
+    scan_gbs = ab["scan_kernel"] / (scan_avg_ms * 1e-3) / 1e9
+    traffic = stale_traffic(os.path.join(ROOT, "profiles", "full_score_ctx_1m_counters.json"),
+                            os.path.join(ROOT, "decode_kv_amd", "csrc", "index_full.hip"))
+    res = {
+        "metric": "decode steps/s at 1M ctx (index+sparse attn) + achieved HBM GB/s vs peak",
+        "value": round(1000.0 / ms, 2),
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8-mfma index, bf16-mfma attention (fp32 accumulate), fp4 kv",
+        "data": "synthetic (seeded SplitMix64): int8 N(0,30) keys + 1,024 planted, N(0,1) bf16 queries and latent rows",
+        "config": {"workload": wl.name, "L": L, "batch": wl.B, "layers": wl.n_layers,
+                   "pattern": wl.pattern, "P": wl.P, "k": wl.k, "window": wl.window,
+                   "index_heads": wl.H, "query_heads": wl.Hq, "latent": wl.D,
+                   "mode": "cold (Infinity Cache evicted before each step)",
+                   "graph": graph is not None},
+        "step_ms_p10_p50_p90": [round(x, 5) for x in statistics.quantiles(step_ms, n=10)[0::4]]
+        if K >= 10 else None,
+        "warm_ms_per_step": round(warm_ms, 5),
+        "algorithmic_MB_per_step": round(step_bytes / 1e6, 3),
+        "step_GBps": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+        "step_frac_of_hbm_peak": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"kernel": "full_score_kernel (Full-mode index scan)", "bound": "hbm",
+                     "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "avg_launch_us": round(scan_avg_ms * 1e3, 3),
+                     "algorithmic_bytes_per_launch": ab["scan_kernel"]},
+        "timed_region_wall_s": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(case, wl, eng.keys)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

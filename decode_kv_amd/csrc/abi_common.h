@@ -1,0 +1,34 @@
+// Host-side status handling shared by the C-ABI entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/csa2.h"
+
+namespace csa2 {
+
+// Record a message as the calling thread's last error and return `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// CSA2_OK, or CSA2_ERR_HIP with the runtime's message recorded.
+int hip_status(hipError_t e, const char* what);
+
+// Status of the most recent launch on this thread.
+inline int launch_status(const char* what) { return hip_status(hipGetLastError(), what); }
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace sizes (bytes) of the ops that need one.
+size_t index_full_ws_bytes(int B, long long total_len, int P);
+size_t sparse_attn_ws_bytes(int B, int Hq, int D, int k, int window);
+int sparse_attn_splits(int B, int Hq, int k, int window);
+
+// Events set by csa2_set_scan_timer (NULL when disabled).
+extern hipEvent_t g_scan_ev_start;
+extern hipEvent_t g_scan_ev_stop;
+
+}  // namespace csa2

@@ -1,0 +1,75 @@
+// Internal device helpers shared by the CSA2 kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace csa2 {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;   // CDNA wavefront
+constexpr int kDk = 64;     // index key / query width (bytes)
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+template <typename T>
+__device__ __forceinline__ T bitcast(const auto& x) {
+    return __builtin_bit_cast(T, x);
+}
+
+// Integer score of one 16-token group against up to 64 index heads, on the
+// int8 matrix cores.  One v_mfma_i32_16x16x64_i8 per block of 16 heads:
+//   A = q rows (M = head, K = key byte), B = key rows (K = key byte, N = token).
+// Lane l supplies row/column (l & 15) and key bytes [16*(l>>4), +16) of both
+// operands, so any hardware ordering of K is the same for A and B and the dot
+// product is exact.  The 16x16 int32 result gives lane l the dot products of
+// token (l & 15) with heads 16*mb + 4*(l>>4) + i, i = 0..3; the epilogue applies
+// ReLU and the head weight, then the four lane groups are summed.
+template <int NB>
+__device__ __forceinline__ int score_group16(const i32x4 (&qa)[NB], const uint32_t (&wr)[NB][4],
+                                             i32x4 keyop) {
+    uint32_t part = 0;
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) {
+        i32x4 acc = {0, 0, 0, 0};
+        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mb], keyop, acc, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            int r = acc[i] > 0 ? acc[i] : 0;          // ReLU, < 2^21
+            part += __umul24(wr[mb][i], (uint32_t)r);  // weight <= 15
+        }
+    }
+    part += __shfl_xor(part, 16);
+    part += __shfl_xor(part, 32);
+    return (int)part;
+}
+
+// Load the q operands and per-lane weights of one sequence's index query.
+//   q: [H][64] int8 of this sequence, w: [H] int8.
+template <int NB>
+__device__ __forceinline__ void load_index_query(const int8_t* __restrict__ q,
+                                                 const int8_t* __restrict__ w, int H,
+                                                 i32x4 (&qa)[NB], uint32_t (&wr)[NB][4]) {
+    const int l = lane_id();
+    const int row = l & 15, grp = l >> 4;
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) {
+        const int h = mb * 16 + row;
+        if (h < H)
+            qa[mb] = *reinterpret_cast<const i32x4*>(q + (size_t)h * kDk + grp * 16);
+        else
+            qa[mb] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int hh = mb * 16 + grp * 4 + i;
+            wr[mb][i] = hh < H ? (uint32_t)(uint8_t)w[hh] : 0u;
+        }
+    }
+}
+
+}  // namespace csa2

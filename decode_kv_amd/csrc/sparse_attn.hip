@@ -1,0 +1,346 @@
+// csa2_sparse_attn_decode: attention of every query head over the selected
+// global positions plus the recent window, reading the FP4 latent cache
+// ("How DeepSeek V4.1 Flash Actually Works", item 2: the 512 most relevant KV
+// entries plus a local 128-token window; "DeepSeek Has Done It Again...": up
+// to 512 global positions alongside the 128 most recent tokens).  MQA with
+// K = V = the dequantised 512-wide latent row.
+//
+// Workgroup = (split, sequence, group of 64 heads); wave w owns 16 heads.
+// Per tile of 32 attended rows:
+//   * gather the FP4 codes and E8M0 scales of the rows, dequantise exactly to
+//     bf16 and stage them in LDS twice: row-major (for q.v) and d-major (for
+//     p.v), so both products read contiguous 16- or 8-byte operands;
+//   * S^T = V q^T on bf16 MFMA (16x16x32), fp32 accumulation;
+//   * online softmax in base 2, per head;
+//   * O += P V on bf16 MFMA, with P split into a bf16 high part and a bf16
+//     residual so the weights carry ~16 significant bits.
+// The k-slots of P's MFMA operand are the rows the S^T result left in each
+// lane, and V's operand is read with the same row order, so P never moves.
+// Splits write (m, l, O) partials; a second kernel merges them with a
+// log-sum-exp combine.
+#include <math.h>
+
+#include "abi_common.h"
+#include "common.h"
+
+namespace csa2 {
+
+constexpr int kAttnThreads = 256;
+constexpr int kAttnRows = 32;
+constexpr int kAttnD = 512;
+constexpr int kHeadsPerWg = 64;
+constexpr int kVjdLd = kAttnD + 8;      // bf16 per row-major row (padded)
+constexpr int kVdjLd = kAttnRows + 8;   // bf16 per d-major row (80 B: 16-B aligned)
+
+// bf16 bits of one E2M1 code (sign + 3 magnitude bits) times 2^(sb - 127);
+// exact, including bf16 subnormal results.  sb <= 252.
+__device__ __forceinline__ uint32_t e2m1_bf16(uint32_t c, int sb) {
+    const uint32_t m = c & 7u;
+    const uint32_t sign = (c & 8u) << 12;
+    const int ex = sb - 1 + (int)(m >> 1);
+    const uint32_t mant = ((m & 1u) && m > 1u) ? 64u : 0u;
+    uint32_t mag;
+    if (m == 0) mag = 0;
+    else if (ex >= 1) mag = ((uint32_t)ex << 7) | mant;
+    else mag = (128u + mant) >> (1 - ex);
+    return sign | mag;
+}
+
+__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, int sb) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = e2m1_bf16((codes >> (8 * i)) & 0xFu, sb);
+        const uint32_t hi = e2m1_bf16((codes >> (8 * i + 4)) & 0xFu, sb);
+        r[i] = lo | (hi << 16);
+    }
+    return r;
+}
+
+__device__ __forceinline__ uint16_t bf16_bits(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+__device__ __forceinline__ float bf16_value(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+}
+
+__global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_fp4,
+    const uint8_t* __restrict__ kv_scale, const long long* __restrict__ row_off,
+    const int* __restrict__ len, const int* __restrict__ sel_pos,
+    const int* __restrict__ sel_len, int Hq, int k, int window, float scale_log2,
+    int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml,
+    float* __restrict__ out, float* __restrict__ lse) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_vjd[kAttnRows * kVjdLd];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vdj[kAttnD * kVdjLd];
+    __shared__ long long s_row[kAttnRows];
+
+    const int split = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
+    const int g = l >> 4, c16 = l & 15;
+    const int h0 = hg * kHeadsPerWg + wave * 16;
+    const bool wave_active = h0 < Hq;
+
+    const int L = max(0, len[b]);
+    const int win = min(window, L);
+    const int nsel = max(0, min(sel_len[b], k));
+    const int S = nsel + win;
+    const int ntile = (S + kAttnRows - 1) / kAttnRows;
+    const int t_begin = (int)((long long)split * ntile / n_splits);
+    const int t_end = (int)((long long)(split + 1) * ntile / n_splits);
+    const long long roff = row_off[b];
+
+    bf16x8 qb[kAttnD / 32];
+    if (wave_active) {
+        const uint16_t* qh = q + ((size_t)b * Hq + h0 + c16) * kAttnD + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < kAttnD / 32; ++ks)
+            qb[ks] = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(qh + 32 * ks));
+    }
+    f32x4 o[kAttnD / 16];
+#pragma unroll
+    for (int nb = 0; nb < kAttnD / 16; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY, l_run = 0.f;
+
+    for (int tile = t_begin; tile < t_end; ++tile) {
+        __syncthreads();  // previous tile's LDS reads are done
+        if (tid < kAttnRows) {
+            const int j = tile * kAttnRows + tid;
+            long long pos = -1;
+            if (j < nsel) pos = sel_pos[(size_t)b * k + j];
+            else if (j < S) pos = L - win + (j - nsel);
+            s_row[tid] = pos >= 0 ? roff + pos : -1;
+        }
+        __syncthreads();
+        {   // dequantise: thread owns rows 8rg..8rg+7 x elements 8dc..8dc+7
+            const int dc = tid >> 2, rg = tid & 3;
+            u32x4 v[8];
+#pragma unroll
+            for (int r = 0; r < 8; ++r) {
+                const int j = 8 * rg + r;
+                const long long row = s_row[j];
+                if (row >= 0) {
+                    const uint32_t codes =
+                        *reinterpret_cast<const uint32_t*>(kv_fp4 + row * (kAttnD / 2) + 4 * dc);
+                    const int sb = kv_scale[row * (kAttnD / 32) + (dc >> 2)];
+                    v[r] = fp4x8_to_bf16x8(codes, sb);
+                } else {
+                    v[r] = u32x4{0u, 0u, 0u, 0u};
+                }
+                *reinterpret_cast<u32x4*>(s_vjd + j * kVjdLd + 8 * dc) = v[r];
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                const int half = (c & 1) * 16;
+                u32x4 t;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const uint32_t a = (v[2 * i][c >> 1] >> half) & 0xFFFFu;
+                    const uint32_t bb = (v[2 * i + 1][c >> 1] >> half) & 0xFFFFu;
+                    t[i] = a | (bb << 16);
+                }
+                *reinterpret_cast<u32x4*>(s_vdj + (8 * dc + c) * kVdjLd + 8 * rg) = t;
+            }
+        }
+        __syncthreads();
+        if (!wave_active) continue;
+
+        // S^T[row][head] = V[row] . q[head]
+        f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kAttnD / 32; ++ks) {
+            const bf16x8 a0 = bitcast<bf16x8>(
+                *reinterpret_cast<const u32x4*>(s_vjd + c16 * kVjdLd + 32 * ks + 8 * g));
+            const bf16x8 a1 = bitcast<bf16x8>(
+                *reinterpret_cast<const u32x4*>(s_vjd + (16 + c16) * kVjdLd + 32 * ks + 8 * g));
+            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[ks], s0, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[ks], s1, 0, 0, 0);
+        }
+        // lane holds head h0 + c16, rows 4g+i (s0) and 16+4g+i (s1)
+        float t[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            t[i] = s_row[4 * g + i] >= 0 ? s0[i] * scale_log2 : -INFINITY;
+            t[4 + i] = s_row[16 + 4 * g + i] >= 0 ? s1[i] * scale_log2 : -INFINITY;
+        }
+        float tmax = t[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, t[i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        const float m_new = fmaxf(m_run, tmax);   // finite: every tile has a valid row
+        const float alpha = exp2f(m_run - m_new);
+        float p[8], psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            p[i] = exp2f(t[i] - m_new);
+            psum += p[i];
+        }
+        psum += __shfl_xor(psum, 16);
+        psum += __shfl_xor(psum, 32);
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        float al[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
+#pragma unroll
+        for (int nb = 0; nb < kAttnD / 16; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[nb][i] *= al[i];
+
+        u32x4 ph_u, pl_u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint16_t h_a = bf16_bits(p[2 * i]), h_b = bf16_bits(p[2 * i + 1]);
+            const uint16_t l_a = bf16_bits(p[2 * i] - bf16_value(h_a));
+            const uint16_t l_b = bf16_bits(p[2 * i + 1] - bf16_value(h_b));
+            ph_u[i] = (uint32_t)h_a | ((uint32_t)h_b << 16);
+            pl_u[i] = (uint32_t)l_a | ((uint32_t)l_b << 16);
+        }
+        const bf16x8 ph = bitcast<bf16x8>(ph_u), pl = bitcast<bf16x8>(pl_u);
+#pragma unroll
+        for (int nb = 0; nb < kAttnD / 16; ++nb) {
+            const uint16_t* vd = s_vdj + (16 * nb + c16) * kVdjLd + 4 * g;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vd);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vd + 16);
+            const bf16x8 bv = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bv, o[nb], 0, 0, 0);
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bv, o[nb], 0, 0, 0);
+        }
+    }
+    if (!wave_active) return;
+
+    float lh[4], mh[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        lh[i] = __shfl(l_run, 4 * g + i);
+        mh[i] = __shfl(m_run, 4 * g + i);
+    }
+    if (n_splits == 1) {
+#pragma unroll
+        for (int nb = 0; nb < kAttnD / 16; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int head = h0 + 4 * g + i;
+                out[((size_t)b * Hq + head) * kAttnD + 16 * nb + c16] =
+                    lh[i] > 0.f ? o[nb][i] / lh[i] : 0.f;
+            }
+        if (lse && l < 16)
+            lse[(size_t)b * Hq + h0 + l] =
+                l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
+    } else {
+        const size_t base = ((size_t)b * n_splits + split) * Hq;
+#pragma unroll
+        for (int nb = 0; nb < kAttnD / 16; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int head = h0 + 4 * g + i;
+                part_o[(base + head) * kAttnD + 16 * nb + c16] = o[nb][i];
+            }
+        if (l < 16) {
+            part_ml[(base + h0 + l) * 2 + 0] = m_run;
+            part_ml[(base + h0 + l) * 2 + 1] = l_run;
+        }
+        (void)mh;
+    }
+}
+
+// Log-sum-exp merge of the split partials: one workgroup per (head, sequence),
+// 128 threads x 4 output elements.
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                           const float* __restrict__ part_ml,
+                                                           int Hq, int n_splits,
+                                                           float* __restrict__ out,
+                                                           float* __restrict__ lse) {
+    const int h = blockIdx.x, b = blockIdx.y;
+    float M = -INFINITY;
+    for (int s = 0; s < n_splits; ++s)
+        M = fmaxf(M, part_ml[(((size_t)b * n_splits + s) * Hq + h) * 2]);
+    float* o = out + ((size_t)b * Hq + h) * kAttnD + 4 * threadIdx.x;
+    if (M == -INFINITY) {
+        *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (lse && threadIdx.x == 0) lse[(size_t)b * Hq + h] = -INFINITY;
+        return;
+    }
+    float lsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < n_splits; ++s) {
+        const size_t base = ((size_t)b * n_splits + s) * Hq + h;
+        const float ms = part_ml[base * 2], ls = part_ml[base * 2 + 1];
+        const float wgt = exp2f(ms - M);   // 0 for an empty split (ms = -inf)
+        lsum += wgt * ls;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + base * kAttnD + 4 * threadIdx.x);
+        acc += wgt * v;
+    }
+    *reinterpret_cast<f32x4*>(o) = acc / lsum;
+    if (lse && threadIdx.x == 0)
+        lse[(size_t)b * Hq + h] = (M + log2f(lsum)) * 0.69314718055994531f;
+}
+
+int sparse_attn_splits(int B, int Hq, int k, int window) {
+    const int tiles = (k + window + kAttnRows - 1) / kAttnRows;
+    const int n_hg = (Hq + kHeadsPerWg - 1) / kHeadsPerWg;
+    const long long wgs = (long long)(B > 0 ? B : 1) * n_hg;
+    int want = (int)((256 + wgs - 1) / wgs);
+    int cap = tiles / 2 > 1 ? tiles / 2 : 1;
+    if (want > cap) want = cap;
+    return want < 1 ? 1 : want;
+}
+
+size_t sparse_attn_ws_bytes(int B, int Hq, int D, int k, int window) {
+    (void)D;
+    const int ns = sparse_attn_splits(B, Hq, k, window);
+    if (ns <= 1) return 0;
+    const size_t n = (size_t)B * ns * Hq;
+    return round_up(n * kAttnD * 4, 256) + round_up(n * 2 * 4, 256);
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* kv_fp4,
+                                       const unsigned char* kv_scale, const long long* row_off,
+                                       const int* len, long long max_len, const int* sel_pos,
+                                       const int* sel_len, int B, int Hq, int D, int k,
+                                       int window, float sm_scale, float* out, float* lse,
+                                       void* ws, size_t ws_bytes, void* stream) {
+    if (B < 0 || max_len < 0 || k < 0 || window < 0)
+        return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: negative size");
+    if (B == 0) return CSA2_OK;
+    if (!q_bf16 || !kv_fp4 || !kv_scale || !row_off || !len || !sel_len || !out ||
+        (k > 0 && !sel_pos))
+        return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: null pointer");
+    if (D != kAttnD) return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: D must be 512");
+    if (Hq < 16 || Hq % 16 != 0)
+        return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: Hq must be a positive multiple of 16");
+    if (B > 65535 || Hq > 1024) return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: B or Hq too large");
+    if (!aligned(q_bf16, 16) || !aligned(kv_fp4, 4) || !aligned(out, 16) || !aligned(row_off, 8))
+        return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: misaligned pointer");
+    const int ns = sparse_attn_splits(B, Hq, k, window);
+    const size_t need = sparse_attn_ws_bytes(B, Hq, D, k, window);
+    if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+        return fail(CSA2_ERR_WORKSPACE,
+                    "csa2_sparse_attn_decode: workspace needs %zu bytes (256-aligned)", need);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    float* part_o = nullptr;
+    float* part_ml = nullptr;
+    if (ns > 1) {
+        part_o = reinterpret_cast<float*>(ws);
+        const size_t n = (size_t)B * ns * Hq;
+        part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + round_up(n * kAttnD * 4, 256));
+    }
+    const float scale_log2 = sm_scale * 1.4426950408889634f;
+    const dim3 grid(ns, B, (Hq + kHeadsPerWg - 1) / kHeadsPerWg);
+    hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(kAttnThreads), 0, s,
+                       reinterpret_cast<const uint16_t*>(q_bf16), kv_fp4, kv_scale, row_off, len,
+                       sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse);
+    if (int e = launch_status("csa2_sparse_attn_decode launch")) return e;
+    if (ns > 1) {
+        hipLaunchKernelGGL(attn_combine_kernel, dim3(Hq, B), dim3(128), 0, s, part_o, part_ml, Hq,
+                           ns, out, lse);
+        return launch_status("csa2_sparse_attn_decode combine launch");
+    }
+    return CSA2_OK;
+}

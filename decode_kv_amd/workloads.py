@@ -90,6 +90,9 @@ WORKLOADS = {
 }
 
 
+KV_POOL_ROWS = 1 << 20
+
+
 class Case:
     """Seeded inputs of one workload.  Device-agnostic: the same (workload,
     seed) gives bit-identical tensors on the CPU and on the GPU."""
@@ -151,20 +154,36 @@ class Case:
         return torch.stack([self.attn_q(step, layer, b) for b in range(self.wl.B)]).contiguous()
 
     # ---- latent KV rows (bf16, before quantisation) ----------------------
-    def kv_bf16(self, layer: int, b: int, positions) -> torch.Tensor:
-        """bf16 latent rows of layer `layer`, sequence b, at `positions`."""
-        D = self.wl.D
+    # The latent row of (layer, sequence, position) is row `kv_row_id` of a
+    # pool of KV_POOL_ROWS seeded N(0,1) rows: generating every element of a
+    # 20-layer, multi-million-token cache by hashing would dominate set-up, and
+    # a pool of 2^20 rows keeps repeats inside one attended set rare.
+    def kv_row_id(self, layer: int, b: int, positions) -> torch.Tensor:
         pos = torch.as_tensor(positions, dtype=torch.int64, device=self.device).reshape(-1)
         key = I.stream_key(self.seed, I.TAG_KV, layer, b)
-        table = I._on(self.device, "bf16", I._bf16_table_cpu)
-        e = pos[:, None] * D + torch.arange(D, dtype=torch.int64, device=self.device)[None, :]
+        return I._srl(I.hash_stream(key, pos), 44)           # top 20 bits
+
+    def kv_pool_rows(self, row_ids, device=None) -> torch.Tensor:
+        """bf16 rows of the pool, [n, D]."""
+        dev = torch.device(device) if device is not None else self.device
+        D = self.wl.D
+        rid = torch.as_tensor(row_ids, dtype=torch.int64, device=dev).reshape(-1)
+        key = I.stream_key(self.seed, I.TAG_KV, 0xFFFF)
+        table = I._on(dev, "bf16", I._bf16_table_cpu)
+        e = rid[:, None] * D + torch.arange(D, dtype=torch.int64, device=dev)[None, :]
         h = I.hash_stream(key, e >> 2)
         idx = (h >> ((e & 3) * 16)) & 0xFFFF
         return table[idx].view(torch.bfloat16)
 
-    def kv_bf16_range(self, layer: int, b: int, first: int, count: int) -> torch.Tensor:
-        key = I.stream_key(self.seed, I.TAG_KV, layer, b)
-        return I.bf16_normal(key, first * self.wl.D, count * self.wl.D, self.device).view(count, self.wl.D)
+    def kv_pool_range(self, first: int, count: int, device=None) -> torch.Tensor:
+        dev = torch.device(device) if device is not None else self.device
+        key = I.stream_key(self.seed, I.TAG_KV, 0xFFFF)
+        D = self.wl.D
+        return I.bf16_normal(key, first * D, count * D, dev).view(count, D)
+
+    def kv_bf16(self, layer: int, b: int, positions) -> torch.Tensor:
+        """bf16 latent rows of layer `layer`, sequence b, at `positions`."""
+        return self.kv_pool_rows(self.kv_row_id(layer, b, positions))
 
     # ---- index keys ------------------------------------------------------
     def aligned_vector(self, b: int) -> np.ndarray:
@@ -247,6 +266,16 @@ class Case:
         if len(pos):
             k[torch.as_tensor(pos, device=dev)] = torch.as_tensor(rows, device=dev)
         return k
+
+    def key_row(self, b: int, pos: int, device=None) -> torch.Tensor:
+        """Index key of sequence b at a position that was not planted (the
+        base distribution), e.g. a token appended during decode."""
+        dev = torch.device(device) if device is not None else self.device
+        wl = self.wl
+        key = I.stream_key(self.seed, I.TAG_KEYS, b)
+        if wl.keys == "uniform8":
+            return I.int8_uniform(key, pos * wl.Dk, wl.Dk, dev)
+        return I.int8_normal(key, pos * wl.Dk, wl.Dk, 30.0, dev)
 
     def keys_all(self, device=None) -> torch.Tensor:
         dev = torch.device(device) if device is not None else self.device

@@ -26,3 +26,12 @@ def oracle_lib():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+def pytest_collection_modifyitems(config, items):
+    if gpu_available():
+        return
+    skip = pytest.mark.skip(reason="no GPU visible to torch")
+    for it in items:
+        if "gpu" in it.keywords:
+            it.add_marker(skip)

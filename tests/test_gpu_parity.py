@@ -1,0 +1,419 @@
+"""GPU parity: every C-ABI entry point against the CPU oracle on the same
+seeded inputs.  Bar: bit-exact pool / selection / scores / FP4 bytes;
+attention within 1e-3 * max|out| per (sequence, layer) and lse within 1e-3."""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from decode_kv_amd import csa2
+from decode_kv_amd import inputs as I
+from decode_kv_amd import pipeline
+from decode_kv_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def u16(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def check_attention(out_gpu, lse_gpu, out_ref, lse_ref, what=""):
+    out_gpu = np.asarray(out_gpu, dtype=np.float64)
+    m = np.abs(out_ref).max()
+    err = np.abs(out_gpu - out_ref).max()
+    assert err <= 1e-3 * m, "%s: max err %.3g vs 1e-3*max|out| = %.3g" % (what, err, 1e-3 * m)
+    lse_gpu = np.asarray(lse_gpu, dtype=np.float64)
+    fin = np.isfinite(lse_ref)
+    assert np.array_equal(np.isfinite(lse_gpu), fin), what
+    if fin.any():
+        assert np.abs(lse_gpu[fin] - lse_ref[fin]).max() <= 1e-3, what
+
+
+# ---------------------------------------------------------------------------
+# generator agreement (inputs for both sides)
+# ---------------------------------------------------------------------------
+
+def test_generator_cpu_gpu_agree():
+    key = I.stream_key(5, 6)
+    a = I.bf16_normal(key, 123, 100000, "cpu")
+    b = I.bf16_normal(key, 123, 100000, DEV).cpu()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    c = I.int8_normal(key, 0, 100000, 30.0, "cpu")
+    d = I.int8_normal(key, 0, 100000, 30.0, DEV).cpu()
+    assert torch.equal(c, d)
+    case_c = W.Case(W.WORKLOADS["ragged32_1m"], 0, "cpu")
+    case_g = W.Case(W.WORKLOADS["ragged32_1m"], 0, DEV)
+    assert case_c.lengths == case_g.lengths
+    assert torch.equal(u16_t(case_c.kv_bf16(3, 5, [0, 77, 99999])),
+                       u16_t(case_g.kv_bf16(3, 5, [0, 77, 99999]).cpu()))
+    assert torch.equal(case_c.index_q(2, 4, 7), case_g.index_q(2, 4, 7).cpu())
+
+
+def u16_t(t):
+    return t.view(torch.int16)
+
+
+# ---------------------------------------------------------------------------
+# csa2_kv_append_fp4
+# ---------------------------------------------------------------------------
+
+def _finite_bf16_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    exp = (bits >> 7) & 0xFF
+    return bits[exp != 0xFF]
+
+
+def test_kv_append_bitexact():
+    rng = np.random.default_rng(0)
+    rows = []
+    allv = _finite_bf16_patterns()
+    rng.shuffle(allv)
+    n = len(allv) // 512 * 512
+    rows.append(allv[:n].reshape(-1, 512))
+    for s in [-127, -125, -40, -3, 0, 7, 60, 125]:         # anchored blocks: fixed scale
+        anchor = np.uint16((np.array([2.0 ** (s + 2)], np.float32).view(np.uint32) >> 16)[0])
+        vals = oracle.bf16_to_f64(allv)
+        ok = allv[np.abs(vals) < 2.0 ** (s + 3)]
+        m = len(ok) // 31 * 31
+        blk = np.zeros((m // 31, 32), np.uint16)
+        blk[:, 0] = anchor
+        blk[:, 1:] = ok[:m].reshape(-1, 31)
+        nb = len(blk) // 16 * 16
+        rows.append(blk[:nb].reshape(-1, 512))
+    g = (rng.standard_normal((300, 512)) * 2.0 ** rng.integers(-30, 30, size=(300, 1)))
+    rows.append((g.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+    z = np.zeros((4, 512), np.uint16)
+    z[1, ::3] = 0x8000
+    z[2] = rng.integers(0, 128, size=512)                   # subnormals only
+    z[3] = rng.integers(0, 128, size=512) | 0x8000
+    rows.append(z)
+    x = np.concatenate(rows)
+    n = x.shape[0]
+    _say("append rows", n)
+    perm = rng.permutation(n + 17)[:n]
+    dst = torch.tensor(perm, dtype=torch.int64, device=DEV)
+    kv = torch.full((n + 17, 256), 0xEE, dtype=torch.uint8, device=DEV)
+    sc = torch.full((n + 17, 16), 0xEE, dtype=torch.uint8, device=DEV)
+    xt = torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+    csa2.kv_append_fp4(xt, dst, kv, sc)
+    torch.cuda.synchronize()
+    codes_ref, sc_ref = oracle.fp4_quantize(x)
+    assert np.array_equal(kv.cpu().numpy()[perm], codes_ref)
+    assert np.array_equal(sc.cpu().numpy()[perm], sc_ref)
+    untouched = np.setdiff1d(np.arange(n + 17), perm)
+    assert (kv.cpu().numpy()[untouched] == 0xEE).all()
+
+
+def test_kv_append_wide_rows():
+    rng = np.random.default_rng(1)
+    for D in [32, 96, 1024]:
+        x = (rng.standard_normal((7, D)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        xt = torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16)
+        kv = torch.zeros((7, D // 2), dtype=torch.uint8, device=DEV)
+        sc = torch.zeros((7, D // 32), dtype=torch.uint8, device=DEV)
+        csa2.kv_append_fp4(xt, torch.arange(7, device=DEV), kv, sc)
+        c, s = oracle.fp4_quantize(x)
+        assert np.array_equal(kv.cpu().numpy(), c) and np.array_equal(sc.cpu().numpy(), s)
+
+
+# ---------------------------------------------------------------------------
+# csa2_index_full
+# ---------------------------------------------------------------------------
+
+def run_full(keys_np, row_off, lens, q_np, w_np, window, P):
+    B = len(lens)
+    keys = torch.from_numpy(keys_np).to(DEV)
+    ro = torch.tensor(row_off, dtype=torch.int64, device=DEV)
+    ln = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q = torch.from_numpy(np.ascontiguousarray(q_np)).to(DEV)
+    w = torch.from_numpy(np.ascontiguousarray(w_np)).to(DEV)
+    pos = torch.full((B, P), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    scr = torch.full((B, P), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    plen = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    max_len, total_len = max(lens + [0]), keys_np.shape[0]
+    ws = csa2.workspace(csa2.workspace_bytes(csa2.OP_INDEX_FULL, B, max_len, total_len, q.shape[1], P))
+    csa2.index_full(q, w, keys, ro, ln, max_len, total_len, window, P, pos, scr, plen, ws)
+    torch.cuda.synchronize()
+    return pos.cpu().numpy(), scr.cpu().numpy(), plen.cpu().numpy()
+
+
+def check_full(keys_np, row_off, lens, q_np, w_np, window, P, what=""):
+    pos, scr, plen = run_full(keys_np, row_off, lens, q_np, w_np, window, P)
+    for b, L in enumerate(lens):
+        rp, rs = oracle.index_full(keys_np, row_off[b], L, q_np[b], w_np[b], window, P)
+        n = len(rp)
+        assert plen[b] == n, (what, b)
+        assert np.array_equal(pos[b, :n], rp), (what, b)
+        assert np.array_equal(scr[b, :n], rs), (what, b)
+        assert (pos[b, n:] == -1).all() and (scr[b, n:] == -1).all(), (what, b)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_index_full_tiny_seeds(seed):
+    case = W.Case(W.WORKLOADS["tiny_4k"], seed, "cpu")
+    keys = case.keys_all().numpy()
+    q, w = case.index_qw_batch(0, 0)
+    check_full(keys, list(case.row_off), case.lengths, q.numpy(), w.numpy(), 128, 1024,
+               "tiny seed %d" % seed)
+
+
+def test_index_full_tie_adversarial():
+    rng = np.random.default_rng(7)
+    L, W_, P = 9000, 128, 1024
+    keys = rng.integers(-127, 128, size=(L, 64)).astype(np.int8)
+    q = rng.integers(-127, 128, size=(1, 64, 64)).astype(np.int8)
+    w = rng.integers(0, 16, size=(1, 64)).astype(np.int8)
+    check_full(keys, [0], [L], np.zeros_like(q), w, W_, P, "q=0")         # all scores 0
+    check_full(keys, [0], [L], q, np.zeros_like(w), W_, P, "w=0")
+    same = np.tile(keys[:1], (L, 1))
+    check_full(same, [0], [L], q, w, W_, P, "identical keys")
+    two = np.where(rng.random((L, 1)) < 0.5, keys[:1], keys[1:2]).astype(np.int8)
+    check_full(two, [0], [L], q, w, W_, P, "two distinct keys")
+    few = keys[rng.integers(0, 40, size=L)]
+    check_full(few, [0], [L], q, w, W_, P, "40 distinct keys")
+    onehot = np.zeros_like(q)
+    onehot[0, 0, 0] = 1
+    w1 = np.zeros_like(w)
+    w1[0, 0] = 1
+    check_full(keys, [0], [L], onehot, w1, W_, P, "scores = relu(K[:,0])")
+
+
+def test_index_full_ragged_batch_and_edges():
+    rng = np.random.default_rng(11)
+    lens = [0, 100, 128, 129, 1152, 1153, 2048 * 3 + 128 + 17, 70001, 5000]
+    gaps = [0, 3, 0, 64, 1, 0, 5, 2, 9]
+    row_off, cur = [], 0
+    for L, g in zip(lens, gaps):
+        cur += g
+        row_off.append(cur)
+        cur += L
+    keys = rng.integers(-127, 128, size=(cur + 5, 64)).astype(np.int8)
+    B = len(lens)
+    for H in [64, 4, 17]:
+        q = rng.integers(-127, 128, size=(B, H, 64)).astype(np.int8)
+        w = rng.integers(0, 16, size=(B, H)).astype(np.int8)
+        check_full(keys, row_off, lens, q, w, 128, 1024, "ragged H=%d" % H)
+    q = rng.integers(-127, 128, size=(B, 64, 64)).astype(np.int8)
+    w = rng.integers(0, 16, size=(B, 64)).astype(np.int8)
+    check_full(keys, row_off, lens, q, w, 0, 1, "window 0, P 1")
+    check_full(keys, row_off, lens, q, w, 128, 16384, "P 16384")
+
+
+def test_index_full_extreme_scores():
+    """Maximal scores (64 heads x 15 x 64 x 127^2) stay exact in int32."""
+    L = 3000
+    keys = np.full((L, 64), 127, dtype=np.int8)
+    keys[::7] = -127
+    keys[5::11, :3] = 0
+    q = np.full((1, 64, 64), 127, dtype=np.int8)
+    w = np.full((1, 64), 15, dtype=np.int8)
+    check_full(keys, [0], [L], q, w, 128, 700, "extreme")
+
+
+# ---------------------------------------------------------------------------
+# csa2_index_reindex and csa2_select_topk
+# ---------------------------------------------------------------------------
+
+def test_index_reindex_matches_oracle():
+    rng = np.random.default_rng(3)
+    B, P, H = 3, 16384, 64
+    lens = [200000, 5000, 130]
+    row_off = [0, 200000, 205000]
+    keys = rng.integers(-127, 128, size=(sum(lens), 64)).astype(np.int8)
+    cand_len = [16384, 4872, 2]
+    cand = np.full((B, P), -1, dtype=np.int32)
+    for b in range(B):
+        cand[b, :cand_len[b]] = np.sort(rng.choice(max(lens[b] - 128, 2), cand_len[b], replace=False))
+    q = rng.integers(-127, 128, size=(B, H, 64)).astype(np.int8)
+    w = rng.integers(0, 16, size=(B, H)).astype(np.int8)
+    score = torch.full((B, P), 0x7777, dtype=torch.int32, device=DEV)
+    csa2.index_reindex(torch.from_numpy(q).to(DEV), torch.from_numpy(w).to(DEV),
+                       torch.from_numpy(keys).to(DEV),
+                       torch.tensor(row_off, dtype=torch.int64, device=DEV),
+                       torch.from_numpy(cand).to(DEV),
+                       torch.tensor(cand_len, dtype=torch.int32, device=DEV), score)
+    got = score.cpu().numpy()
+    for b in range(B):
+        n = cand_len[b]
+        ref = oracle.index_reindex(keys, row_off[b], cand[b, :n], q[b], w[b])
+        assert np.array_equal(got[b, :n], ref)
+        assert (got[b, n:] == -1).all()
+
+
+@pytest.mark.parametrize("span", [3, 50, 100000, 1 << 30])
+def test_select_topk_matches_oracle(span):
+    rng = np.random.default_rng(span % 1000)
+    B, P = 4, 16384
+    cand_len = [16384, 9000, 512, 37]
+    score = rng.integers(0, span, size=(B, P)).astype(np.int32)
+    cand = np.zeros((B, P), dtype=np.int32)
+    for b in range(B):
+        cand[b] = np.sort(rng.choice(10_000_000, P, replace=False))
+    for k in [1, 64, 512, 16384]:
+        sel = torch.full((B, k), 0x3333, dtype=torch.int32, device=DEV)
+        sl = torch.zeros(B, dtype=torch.int32, device=DEV)
+        csa2.select_topk(torch.from_numpy(score).to(DEV), torch.from_numpy(cand).to(DEV),
+                         torch.tensor(cand_len, dtype=torch.int32, device=DEV), k, sel, sl)
+        got, gl = sel.cpu().numpy(), sl.cpu().numpy()
+        for b in range(B):
+            n = cand_len[b]
+            ref, _ = oracle.topk(score[b, :n], cand[b, :n], k)
+            assert gl[b] == len(ref)
+            assert np.array_equal(got[b, :len(ref)], ref), (span, k, b)
+            assert (got[b, len(ref):] == -1).all()
+
+
+# ---------------------------------------------------------------------------
+# csa2_sparse_attn_decode
+# ---------------------------------------------------------------------------
+
+def run_attention(codes, scales, row_off, lens, sel, sel_len, q_bits, k, window):
+    B, Hq, D = q_bits.shape
+    qt = torch.from_numpy(q_bits.view(np.int16)).to(DEV).view(torch.bfloat16)
+    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=DEV)
+    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
+    ws = csa2.workspace(csa2.workspace_bytes(csa2.OP_SPARSE_ATTN, B, 0, 0, 0, 0, k, Hq, D, window))
+    csa2.sparse_attn_decode(qt, torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                            torch.tensor(row_off, dtype=torch.int64, device=DEV),
+                            torch.tensor(lens, dtype=torch.int32, device=DEV), max(lens + [0]),
+                            torch.from_numpy(sel).to(DEV),
+                            torch.tensor(sel_len, dtype=torch.int32, device=DEV), k, window,
+                            1 / math.sqrt(D), out, lse, ws)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), lse.cpu().numpy()
+
+
+def attention_case(seed, lens, k, Hq, scale_lo=118, scale_hi=130, window=128):
+    rng = np.random.default_rng(seed)
+    B = len(lens)
+    row_off = list(np.cumsum([0] + lens[:-1]))
+    n = max(1, sum(lens))
+    codes_t, scales_t = W.raw_fp4_rows(seed, n, 512, scale_lo, scale_hi)
+    codes, scales = codes_t.numpy(), scales_t.numpy()
+    sel = np.full((B, k), -1, dtype=np.int32)
+    sel_len = []
+    for b, L in enumerate(lens):
+        E = max(0, L - window)
+        m = min(k, E, int(rng.integers(0, k + 1)) if seed % 3 == 0 else k)
+        if m:
+            sel[b, :m] = np.sort(rng.choice(E, m, replace=False))
+        sel_len.append(m)
+    q = (rng.standard_normal((B, Hq, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    out, lse = run_attention(codes, scales, row_off, lens, sel, sel_len, q, k, window)
+    for b, L in enumerate(lens):
+        S = oracle.attention_positions(L, sel[b, :sel_len[b]], window)
+        rows = row_off[b] + S
+        ro, rl = oracle.attention(q[b], codes[rows], scales[rows], 1 / math.sqrt(512))
+        check_attention(out[b], lse[b], ro, rl, "seed %d b %d L %d" % (seed, b, L))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_attention_random_fp4(seed):
+    attention_case(seed, [4096, 70000, 1000, 640, 129], 512, 64)
+
+
+def test_attention_small_heads_and_short_contexts():
+    attention_case(10, [4096], 64, 16)
+    attention_case(11, [50, 128, 129, 0, 300], 64, 16)
+    attention_case(12, [5000] * 3, 64, 128)
+    attention_case(13, [100000], 512, 64, window=0)
+    attention_case(14, [3000] * 32, 512, 64)
+
+
+def test_attention_scale_ranges():
+    attention_case(20, [4096, 2000], 512, 64, scale_lo=100, scale_hi=150)
+    attention_case(21, [4096, 2000], 512, 64, scale_lo=1, scale_hi=1)
+
+
+def test_attention_empty_sequence():
+    out, lse = run_attention(np.zeros((8, 256), np.uint8), np.zeros((8, 16), np.uint8), [0, 0],
+                             [0, 8], np.full((2, 16), -1, np.int32), [0, 0],
+                             np.ones((2, 16, 512), np.uint16), 16, 128)
+    assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
+    assert np.isfinite(out[1]).all()
+
+
+# ---------------------------------------------------------------------------
+# whole decode steps through the pipeline
+# ---------------------------------------------------------------------------
+
+def check_engine_step(eng: pipeline.Engine, cpu_case: W.Case, step: int, seqs, keys_np):
+    wl = eng.wl
+    lens = cpu_case.lengths_at(step)
+    for b in seqs:
+        off = int(cpu_case.row_off[b])
+        kb = keys_np[off:off + cpu_case.caps[b]]
+        idx_q = {l: cpu_case.index_q(step, l, b).numpy() for l, c in enumerate(wl.pattern) if c in "FR"}
+        idx_w = {l: cpu_case.index_w(step, l, b).numpy() for l, c in enumerate(wl.pattern) if c in "FR"}
+        attn_q = [u16(cpu_case.attn_q(step, l, b)) for l in range(wl.n_layers)]
+        res = oracle.decode_step(wl.pattern, kb, 0, lens[b], wl.window, wl.P, wl.k, idx_q, idx_w,
+                                 attn_q, lambda l, S: u16(cpu_case.kv_bf16(l, b, S)), wl.sm_scale)
+        pool_len = int(eng.pool_len[b])
+        pool = eng.pool_pos[b].cpu().numpy()
+        assert pool_len == len(res[0]["pool_pos"]), (step, b)
+        assert np.array_equal(pool[:pool_len], res[0]["pool_pos"]), (step, b)
+        assert np.array_equal(eng.pool_score[b].cpu().numpy()[:pool_len], res[0]["pool_score"])
+        assert (pool[pool_len:] == -1).all()
+        for l, r in enumerate(res):
+            src = eng.selection_layer(l)
+            sl = int(eng.sel_len[src, b])
+            sel = eng.sel_pos[src, b].cpu().numpy()
+            assert sl == len(r["sel"]), (step, b, l)
+            assert np.array_equal(sel[:sl], r["sel"]), (step, b, l)
+            if r["kind"] == "R":
+                rs = eng.rscore[l, b].cpu().numpy()
+                assert np.array_equal(rs[:pool_len], r["reindex_score"]), (step, b, l)
+            check_attention(eng.out[l, b].cpu().numpy(), eng.lse[l, b].cpu().numpy(), r["out"],
+                            r["lse"], "step %d seq %d layer %d" % (step, b, l))
+        _say("  checked step", step, "seq", b, "L", lens[b])
+
+
+def run_workload(name, steps, seqs=None, **scale):
+    wl = W.WORKLOADS[name].scaled(**scale) if scale else W.WORKLOADS[name]
+    _say("workload", wl.name, "B", wl.B, "layers", wl.n_layers)
+    eng = pipeline.Engine(W.Case(wl, 0, DEV), DEV)
+    keys_np = eng.keys.cpu().numpy()                       # generator output, before any step
+    cpu_case = W.Case(wl, 0, "cpu")
+    for step in range(steps):
+        eng.run_step(eng.step_inputs(step))
+        torch.cuda.synchronize()
+        check_engine_step(eng, cpu_case, step, seqs if seqs is not None else range(wl.B), keys_np)
+    return eng
+
+
+def test_workload_tiny_4k():
+    run_workload("tiny_4k", 1)
+
+
+def test_workload_single_64k():
+    run_workload("single_64k", 1)
+
+
+def test_workload_batch8_256k_two_steps():
+    run_workload("batch8_256k", 2)
+
+
+def test_workload_ctx_1m():
+    eng = run_workload("ctx_1m", 1)
+    # determinism: the same step again gives identical bits
+    out1, pool1 = eng.out.clone(), eng.pool_pos.clone()
+    eng.run_step(eng.step_inputs(0))
+    torch.cuda.synchronize()
+    assert torch.equal(out1, eng.out) and torch.equal(pool1, eng.pool_pos)
+
+
+def test_workload_ragged32_sampled():
+    case = W.Case(W.WORKLOADS["ragged32_1m"], 0, "cpu")
+    order = np.argsort(case.lengths)
+    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 5})
+    run_workload("ragged32_1m", 2, seqs)

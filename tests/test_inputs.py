@@ -63,9 +63,11 @@ def test_case_planted_and_kv_rows():
     assert pos.max() < 4096 - 128
     assert torch.equal(keys[torch.as_tensor(pos)], torch.as_tensor(rows))
     kv = c.kv_bf16(0, 0, [5, 17])
-    kr = c.kv_bf16_range(0, 0, 5, 13)
-    assert torch.equal(kv[0].view(torch.int16), kr[0].view(torch.int16))
-    assert torch.equal(kv[1].view(torch.int16), kr[12].view(torch.int16))
+    ids = c.kv_row_id(0, 0, [5, 17])
+    assert ids.min() >= 0 and ids.max() < W.KV_POOL_ROWS
+    pr = c.kv_pool_range(int(ids[0]), 1)
+    assert torch.equal(kv[0].view(torch.int16), pr[0].view(torch.int16))
+    assert not torch.equal(c.kv_bf16(1, 0, [5]).view(torch.int16), kv[:1].view(torch.int16))
 
 
 def test_log_distance_planting():

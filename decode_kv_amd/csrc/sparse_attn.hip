@@ -31,29 +31,23 @@ constexpr int kAttnD = 512;
 constexpr int kHeadsPerWg = 64;
 constexpr int kVjdLd = kAttnD + 8;      // bf16 per row-major row (padded)
 constexpr int kVdjLd = kAttnRows + 8;   // bf16 per d-major row (80 B: 16-B aligned)
+constexpr int kAttnMaxTilesPerWg = 16;  // rows staged per workgroup: 16 x 32
+constexpr int kAttnMaxSplits = 32;
 
-// bf16 bits of one E2M1 code (sign + 3 magnitude bits) times 2^(sb - 127);
-// exact, including bf16 subnormal results.  sb <= 252.
-__device__ __forceinline__ uint32_t e2m1_bf16(uint32_t c, int sb) {
-    const uint32_t m = c & 7u;
-    const uint32_t sign = (c & 8u) << 12;
-    const int ex = sb - 1 + (int)(m >> 1);
-    const uint32_t mant = ((m & 1u) && m > 1u) ? 64u : 0u;
-    uint32_t mag;
-    if (m == 0) mag = 0;
-    else if (ex >= 1) mag = ((uint32_t)ex << 7) | mant;
-    else mag = (128u + mant) >> (1 - ex);
-    return sign | mag;
-}
-
+// Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
+// times 2^(sb - 127), to eight bf16 (element 2i in the low half of word i).
+// v_cvt_scalef32_pk_bf16_fp4 converts the two codes of one byte and applies
+// the fp32 scale; the scale 2^(sb-127) is built from its bits (sb = 0 gives
+// the subnormal 2^-127).  Exact for every code and every scale byte <= 252:
+// the results have at most two significant bits and bf16 has fp32's exponent
+// range, subnormals included.
 __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, int sb) {
+    const float scale = __builtin_bit_cast(float, sb ? (uint32_t)sb << 23 : 0x00400000u);
     u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = e2m1_bf16((codes >> (8 * i)) & 0xFu, sb);
-        const uint32_t hi = e2m1_bf16((codes >> (8 * i + 4)) & 0xFu, sb);
-        r[i] = lo | (hi << 16);
-    }
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
     return r;
 }
 
@@ -65,7 +59,7 @@ __device__ __forceinline__ float bf16_value(uint16_t b) {
     return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
-__global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_fp4,
     const uint8_t* __restrict__ kv_scale, const long long* __restrict__ row_off,
     const int* __restrict__ len, const int* __restrict__ sel_pos,
@@ -74,7 +68,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     float* __restrict__ out, float* __restrict__ lse) {
     __shared__ __attribute__((aligned(16))) uint16_t s_vjd[kAttnRows * kVjdLd];
     __shared__ __attribute__((aligned(16))) uint16_t s_vdj[kAttnD * kVdjLd];
-    __shared__ long long s_row[kAttnRows];
+    __shared__ long long s_rows[kAttnMaxTilesPerWg * kAttnRows];   // cache row, -1 = none
 
     const int split = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
     const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
@@ -91,6 +85,16 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     const int t_end = (int)((long long)(split + 1) * ntile / n_splits);
     const long long roff = row_off[b];
 
+    // cache rows of this workgroup's attended positions: selection, then window
+    const int j0 = t_begin * kAttnRows, nrows = (t_end - t_begin) * kAttnRows;
+    for (int i = tid; i < nrows; i += kAttnThreads) {
+        const int j = j0 + i;
+        long long pos = -1;
+        if (j < nsel) pos = sel_pos[(size_t)b * k + j];
+        else if (j < S) pos = L - win + (j - nsel);
+        s_rows[i] = pos >= 0 ? roff + pos : -1;
+    }
+
     bf16x8 qb[kAttnD / 32];
     if (wave_active) {
         const uint16_t* qh = q + ((size_t)b * Hq + h0 + c16) * kAttnD + 8 * g;
@@ -103,32 +107,34 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     for (int nb = 0; nb < kAttnD / 16; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
+    // dequantisation work split: thread owns rows 8rg..8rg+7 x elements 8dc..8dc+7
+    const int dc = tid >> 2, rg = tid & 3;
+    uint32_t nx_codes[8], nx_sb[8];
+    uint32_t nx_valid = 0;
+    auto prefetch = [&](int tile) {   // issue the global loads of one tile
+        const long long first = s_rows[(tile - t_begin) * kAttnRows];   // always valid
+        nx_valid = 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            long long row = s_rows[(tile - t_begin) * kAttnRows + 8 * rg + r];
+            nx_valid |= (row >= 0 ? 1u : 0u) << r;
+            row = row >= 0 ? row : first;
+            nx_codes[r] = *reinterpret_cast<const uint32_t*>(kv_fp4 + row * (kAttnD / 2) + 4 * dc);
+            nx_sb[r] = kv_scale[row * (kAttnD / 32) + (dc >> 2)];
+        }
+    };
+    __syncthreads();
+    if (t_begin < t_end) prefetch(t_begin);
+
     for (int tile = t_begin; tile < t_end; ++tile) {
         __syncthreads();  // previous tile's LDS reads are done
-        if (tid < kAttnRows) {
-            const int j = tile * kAttnRows + tid;
-            long long pos = -1;
-            if (j < nsel) pos = sel_pos[(size_t)b * k + j];
-            else if (j < S) pos = L - win + (j - nsel);
-            s_row[tid] = pos >= 0 ? roff + pos : -1;
-        }
-        __syncthreads();
-        {   // dequantise: thread owns rows 8rg..8rg+7 x elements 8dc..8dc+7
-            const int dc = tid >> 2, rg = tid & 3;
+        {
             u32x4 v[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                const int j = 8 * rg + r;
-                const long long row = s_row[j];
-                if (row >= 0) {
-                    const uint32_t codes =
-                        *reinterpret_cast<const uint32_t*>(kv_fp4 + row * (kAttnD / 2) + 4 * dc);
-                    const int sb = kv_scale[row * (kAttnD / 32) + (dc >> 2)];
-                    v[r] = fp4x8_to_bf16x8(codes, sb);
-                } else {
-                    v[r] = u32x4{0u, 0u, 0u, 0u};
-                }
-                *reinterpret_cast<u32x4*>(s_vjd + j * kVjdLd + 8 * dc) = v[r];
+                v[r] = fp4x8_to_bf16x8(nx_codes[r], (int)nx_sb[r]);
+                if (!((nx_valid >> r) & 1u)) v[r] = u32x4{0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4*>(s_vjd + (8 * rg + r) * kVjdLd + 8 * dc) = v[r];
             }
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
@@ -144,6 +150,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             }
         }
         __syncthreads();
+        if (tile + 1 < t_end) prefetch(tile + 1);   // in flight during the MFMAs
         if (!wave_active) continue;
 
         // S^T[row][head] = V[row] . q[head]
@@ -158,11 +165,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[ks], s1, 0, 0, 0);
         }
         // lane holds head h0 + c16, rows 4g+i (s0) and 16+4g+i (s1)
+        const int jt = tile * kAttnRows;
         float t[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            t[i] = s_row[4 * g + i] >= 0 ? s0[i] * scale_log2 : -INFINITY;
-            t[4 + i] = s_row[16 + 4 * g + i] >= 0 ? s1[i] * scale_log2 : -INFINITY;
+            t[i] = (jt + 4 * g + i < S) ? s0[i] * scale_log2 : -INFINITY;
+            t[4 + i] = (jt + 16 + 4 * g + i < S) ? s1[i] * scale_log2 : -INFINITY;
         }
         float tmax = t[0];
 #pragma unroll
@@ -211,12 +219,9 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     }
     if (!wave_active) return;
 
-    float lh[4], mh[4];
+    float lh[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        lh[i] = __shfl(l_run, 4 * g + i);
-        mh[i] = __shfl(m_run, 4 * g + i);
-    }
+    for (int i = 0; i < 4; ++i) lh[i] = __shfl(l_run, 4 * g + i);
     if (n_splits == 1) {
 #pragma unroll
         for (int nb = 0; nb < kAttnD / 16; ++nb)
@@ -242,36 +247,48 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
             part_ml[(base + h0 + l) * 2 + 0] = m_run;
             part_ml[(base + h0 + l) * 2 + 1] = l_run;
         }
-        (void)mh;
     }
 }
 
 // Log-sum-exp merge of the split partials: one workgroup per (head, sequence),
-// 128 threads x 4 output elements.
+// 128 threads x 4 output elements.  Every split's (m, l, o) is loaded in one
+// round trip (up to kAttnMaxSplits splits), then merged.
+template <int NS>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            int Hq, int n_splits,
                                                            float* __restrict__ out,
                                                            float* __restrict__ lse) {
     const int h = blockIdx.x, b = blockIdx.y;
+    float ms[NS], ls[NS];
+    f32x4 os[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        const int s = min(u, n_splits - 1);
+        const size_t base = ((size_t)b * n_splits + s) * Hq + h;
+        ms[u] = part_ml[base * 2];
+        ls[u] = part_ml[base * 2 + 1];
+        os[u] = *reinterpret_cast<const f32x4*>(part_o + base * kAttnD + 4 * threadIdx.x);
+    }
     float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s)
-        M = fmaxf(M, part_ml[(((size_t)b * n_splits + s) * Hq + h) * 2]);
+#pragma unroll
+    for (int u = 0; u < NS; ++u)
+        if (u < n_splits) M = fmaxf(M, ms[u]);
     float* o = out + ((size_t)b * Hq + h) * kAttnD + 4 * threadIdx.x;
-    if (M == -INFINITY) {
+    if (M == -INFINITY) {                         // nothing attended
         *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
         if (lse && threadIdx.x == 0) lse[(size_t)b * Hq + h] = -INFINITY;
         return;
     }
     float lsum = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < n_splits; ++s) {
-        const size_t base = ((size_t)b * n_splits + s) * Hq + h;
-        const float ms = part_ml[base * 2], ls = part_ml[base * 2 + 1];
-        const float wgt = exp2f(ms - M);   // 0 for an empty split (ms = -inf)
-        lsum += wgt * ls;
-        const f32x4 v = *reinterpret_cast<const f32x4*>(part_o + base * kAttnD + 4 * threadIdx.x);
-        acc += wgt * v;
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+        if (u < n_splits) {
+            const float wgt = exp2f(ms[u] - M);   // 0 for an empty split
+            lsum += wgt * ls[u];
+            acc += wgt * os[u];
+        }
     }
     *reinterpret_cast<f32x4*>(o) = acc / lsum;
     if (lse && threadIdx.x == 0)
@@ -279,12 +296,17 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
 }
 
 int sparse_attn_splits(int B, int Hq, int k, int window) {
+    // Enough workgroups to cover the chip at small batch (one 32-row tile per
+    // split at B = 1); never more splits than tiles, never more than
+    // kAttnMaxTilesPerWg tiles staged per workgroup.
     const int tiles = (k + window + kAttnRows - 1) / kAttnRows;
     const int n_hg = (Hq + kHeadsPerWg - 1) / kHeadsPerWg;
     const long long wgs = (long long)(B > 0 ? B : 1) * n_hg;
     int want = (int)((256 + wgs - 1) / wgs);
-    int cap = tiles / 2 > 1 ? tiles / 2 : 1;
-    if (want > cap) want = cap;
+    if (want > tiles) want = tiles;
+    if (want > kAttnMaxSplits) want = kAttnMaxSplits;
+    const int min_splits = (tiles + kAttnMaxTilesPerWg - 1) / kAttnMaxTilesPerWg;
+    if (want < min_splits) want = min_splits;
     return want < 1 ? 1 : want;
 }
 
@@ -318,6 +340,9 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
     if (B > 65535 || Hq > 1024) return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: B or Hq too large");
     if (!aligned(q_bf16, 16) || !aligned(kv_fp4, 4) || !aligned(out, 16) || !aligned(row_off, 8))
         return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: misaligned pointer");
+    if ((long long)k + window > (long long)kAttnMaxSplits * kAttnMaxTilesPerWg * kAttnRows)
+        return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: k + window > %d",
+                    kAttnMaxSplits * kAttnMaxTilesPerWg * kAttnRows);
     const int ns = sparse_attn_splits(B, Hq, k, window);
     const size_t need = sparse_attn_ws_bytes(B, Hq, D, k, window);
     if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
@@ -338,8 +363,15 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
                        sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse);
     if (int e = launch_status("csa2_sparse_attn_decode launch")) return e;
     if (ns > 1) {
-        hipLaunchKernelGGL(attn_combine_kernel, dim3(Hq, B), dim3(128), 0, s, part_o, part_ml, Hq,
-                           ns, out, lse);
+        if (ns <= 8)
+            hipLaunchKernelGGL(attn_combine_kernel<8>, dim3(Hq, B), dim3(128), 0, s, part_o,
+                               part_ml, Hq, ns, out, lse);
+        else if (ns <= 16)
+            hipLaunchKernelGGL(attn_combine_kernel<16>, dim3(Hq, B), dim3(128), 0, s, part_o,
+                               part_ml, Hq, ns, out, lse);
+        else
+            hipLaunchKernelGGL(attn_combine_kernel<kAttnMaxSplits>, dim3(Hq, B), dim3(128), 0, s,
+                               part_o, part_ml, Hq, ns, out, lse);
         return launch_status("csa2_sparse_attn_decode combine launch");
     }
     return CSA2_OK;

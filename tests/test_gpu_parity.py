@@ -36,7 +36,9 @@ def check_attention(out_gpu, lse_gpu, out_ref, lse_ref, what=""):
     fin = np.isfinite(lse_ref)
     assert np.array_equal(np.isfinite(lse_gpu), fin), what
     if fin.any():
-        assert np.abs(lse_gpu[fin] - lse_ref[fin]).max() <= 1e-3, what
+        # 1e-3 absolute, plus a few fp32 spacings (2^-23 |lse|) for large |lse|
+        tol = 1e-3 + 1e-6 * np.abs(lse_ref[fin])
+        assert (np.abs(lse_gpu[fin] - lse_ref[fin]) <= tol).all(), what
 
 
 # ---------------------------------------------------------------------------

@@ -5,7 +5,7 @@
 #include <stddef.h>
 #include <stdint.h>
 
-#include "../../include/csa2.h"
+#include "csa2.h"
 
 namespace csa2 {
 

@@ -3,14 +3,15 @@
 // Works", item 2: the 512 most relevant KV entries; "DeepSeek Has Done It
 // Again...": up to 512 global positions).
 //
-// One workgroup (1,024 threads) per sequence.  The candidate scores (<= 16,384
-// x 4 B) are loaded with all of a thread's loads in flight and kept both in
-// registers and in LDS.  An exact radix select finds the threshold T and the
+// One workgroup (1,024 threads) per sequence.  The candidate scores and
+// positions (<= 16,384 each) are loaded with all of a thread's loads in
+// flight and kept in registers (entry i lives in thread i mod 1,024).  An exact radix select finds the threshold T and the
 // number of ties to keep: a first histogram over a float-like 12-bit key
 // (exponent + 7 mantissa bits, so pool scores spread over many bins and the
 // LDS atomics rarely collide), then 13-bit refinement digits inside the chosen
-// bin until one value remains.  An ordered compaction writes s > T plus the
-// first ties in list order.  Candidate lists are ascending in position, so
+// bin until it holds one value or at most 64 entries, which are ranked
+// exactly.  An ordered compaction (wave ballots plus one prefix over
+// (slot, wave) counts) writes s > T plus the first ties in list order.  Candidate lists are ascending in position, so
 // list order is position order.
 #include "abi_common.h"
 #include "common.h"
@@ -82,36 +83,70 @@ __device__ __forceinline__ void sel_find_bin(const uint32_t* s_hist, int nb, int
     __syncthreads();
 }
 
+__device__ __forceinline__ int lane_rank(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Exclusive prefix, in (slot j, wave) order, of per-(j, wave) counts in
+// s_cnt[j * kSelWaves + wave]; result in s_pre.  Wave 0 scans 4 entries/lane.
+__device__ __forceinline__ void slot_wave_scan(const int* s_cnt, int* s_pre) {
+    __syncthreads();
+    if (threadIdx.x < kWave) {
+        const int l = threadIdx.x;
+        int c[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c[i] = s_cnt[4 * l + i];
+            sum += c[i];
+        }
+        int x = sum;
+        for (int o = 1; o < kWave; o <<= 1) {
+            const int y = __shfl_up(x, o);
+            if (l >= o) x += y;
+        }
+        int run = x - sum;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            s_pre[4 * l + i] = run;
+            run += c[i];
+        }
+    }
+    __syncthreads();
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     const int* __restrict__ score, const int* __restrict__ cand_pos,
     const int* __restrict__ cand_len, int P, int k, int* __restrict__ sel_pos,
     int* __restrict__ sel_len) {
-    __shared__ int s_sc[kSelMaxP];
+    constexpr int PER = kSelMaxP / kSelThreads;   // 16
+    static_assert(PER * kSelWaves == 4 * kWave, "slot_wave_scan covers 256 entries");
     __shared__ uint32_t s_hist[kSelRefBins];
     __shared__ int s_tmp[kSelWaves];
-    __shared__ int s_res[2];
-    __shared__ int s_cs[kSelThreads], s_ci[kSelThreads];   // threshold-bin entries
-    constexpr int PER = kSelMaxP / kSelThreads;   // 16
+    __shared__ int s_res[4];
+    __shared__ unsigned long long s_key[64];
+    __shared__ int s_cnt[PER * kSelWaves], s_pre[PER * kSelWaves];
     const int b = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int n = max(0, min(cand_len[b], P));
     const int keff = min(k, n);
     const int* sc = score + (size_t)b * P;
+    const int* cp = cand_pos + (size_t)b * P;
 
-    // all 16 loads of a thread in flight at once; strided for coalescing
-    int v[PER];
+    // entry i = tid + 1024 j; scores and positions, all loads in flight
+    int v[PER], pos[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int i = tid + j * kSelThreads;
         v[j] = i < n ? sc[i] : -1;          // valid scores are >= 0
+        pos[j] = i < n ? cp[i] : -1;
     }
-#pragma unroll
-    for (int j = 0; j < PER; ++j) s_sc[tid + j * kSelThreads] = v[j];
 
     int T = 0x7FFFFFFF, needT = 0;
     if (keff > 0) {
         // pass 0: float-like key, fine enough that the atomics rarely collide
         for (int i = tid; i < kSelKeyBins; i += kSelThreads) s_hist[i] = 0;
+        if (tid == 0) s_res[2] = 0;
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < PER; ++j)
@@ -120,7 +155,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         sel_find_bin(s_hist, kSelKeyBins, keff, s_tmp, s_res);
         const int kb = s_res[0];
         int need = keff - s_res[1];
-        const int m = (int)s_hist[kb];        // entries inside the threshold bin
+        int cnt = (int)s_hist[kb];            // entries inside the bin
         int lo, hi;
         if (kb < 128) {
             lo = hi = kb;
@@ -129,96 +164,92 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
             lo = (128 + (kb & 127)) << (e - 7);
             hi = lo + (1 << (e - 7)) - 1;
         }
-        if (m <= kSelThreads) {
-            // few entries in the bin: rank them exactly by (score desc, index asc)
-            int cnt = 0;
+        // 13-bit refinement passes until the bin is one value or holds <= 64
+        while (lo < hi && cnt > 64) {
+            const unsigned width = (unsigned)(hi - lo) + 1u;
+            const int bits = 32 - __clz(width - 1u);
+            const int sh = bits > 13 ? bits - 13 : 0;
+            const int nb = (int)(((width - 1u) >> sh) + 1u);
+            __syncthreads();
+            for (int i = tid; i < nb; i += kSelThreads) s_hist[i] = 0;
+            __syncthreads();
 #pragma unroll
-            for (int j = 0; j < PER; ++j) cnt += v[j] >= lo && v[j] <= hi;
-            int tot;
-            int o = sel_block_scan(cnt, s_tmp, tot);
+            for (int j = 0; j < PER; ++j)
+                if (v[j] >= lo && v[j] <= hi) atomicAdd(&s_hist[(v[j] - lo) >> sh], 1u);
+            __syncthreads();
+            sel_find_bin(s_hist, nb, need, s_tmp, s_res);
+            const int d = s_res[0];
+            need -= s_res[1];
+            cnt = (int)s_hist[d];
+            const int nlo = lo + (d << sh);
+            const int nhi = (sh == 0) ? nlo : min(hi, nlo + (1 << sh) - 1);
+            lo = nlo;
+            hi = nhi;
+        }
+        if (lo == hi) {
+            T = lo;
+            needT = need;
+        } else {
+            // <= 64 entries in [lo, hi]: rank them by the key (score, ~index)
+            __syncthreads();
 #pragma unroll
             for (int j = 0; j < PER; ++j)
                 if (v[j] >= lo && v[j] <= hi) {
-                    s_cs[o] = v[j];
-                    s_ci[o] = tid + j * kSelThreads;
-                    ++o;
+                    const int slot = atomicAdd(&s_res[2], 1);
+                    s_key[slot] = ((unsigned long long)(uint32_t)v[j] << 32) |
+                                  (uint32_t)~(uint32_t)(tid + j * kSelThreads);
                 }
             __syncthreads();
-            if (tid < m) {
-                const int cs = s_cs[tid], ci = s_ci[tid];
-                int gt = 0, eq_lower = 0;
-                for (int u = 0; u < m; ++u) {
-                    const int us = s_cs[u];
-                    gt += us > cs;
-                    eq_lower += (us == cs) & (s_ci[u] < ci);
-                }
-                if (gt + eq_lower == need - 1) {   // exactly one entry has this rank
-                    s_res[0] = cs;
-                    s_res[1] = eq_lower + 1;
+            if (tid < cnt) {
+                const unsigned long long mine = s_key[tid];
+                int rank = 0;
+                for (int u = 0; u < cnt; ++u) rank += s_key[u] > mine;
+                if (rank == need - 1) {
+                    const uint32_t ts = (uint32_t)(mine >> 32);
+                    int ties = 0;             // entries of score ts ranked up to here
+                    for (int u = 0; u < cnt; ++u)
+                        ties += ((uint32_t)(s_key[u] >> 32) == ts) & (s_key[u] >= mine);
+                    s_res[0] = (int)ts;
+                    s_res[1] = ties;
                 }
             }
             __syncthreads();
             T = s_res[0];
             needT = s_res[1];
-        } else {
-            // many entries: 13-bit refinement passes inside [lo, hi]
-            while (lo < hi) {
-                const unsigned width = (unsigned)(hi - lo) + 1u;
-                const int bits = 32 - __clz(width - 1u);
-                const int sh = bits > 13 ? bits - 13 : 0;
-                const int nb = (int)(((width - 1u) >> sh) + 1u);
-                __syncthreads();
-                for (int i = tid; i < nb; i += kSelThreads) s_hist[i] = 0;
-                __syncthreads();
-#pragma unroll
-                for (int j = 0; j < PER; ++j)
-                    if (v[j] >= lo && v[j] <= hi) atomicAdd(&s_hist[(v[j] - lo) >> sh], 1u);
-                __syncthreads();
-                sel_find_bin(s_hist, nb, need, s_tmp, s_res);
-                const int d = s_res[0];
-                need -= s_res[1];
-                const int nlo = lo + (d << sh);
-                const int nhi = (sh == 0) ? nlo : min(hi, nlo + (1 << sh) - 1);
-                lo = nlo;
-                hi = nhi;
-            }
-            T = lo;
-            needT = need;
         }
+    }
+
+    // ordered compaction over entries i = tid + 1024 j (slot j, then thread)
+    uint64_t meq[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        meq[j] = __ballot(v[j] >= 0 && v[j] == T);
+        if (lane == 0) s_cnt[j * kSelWaves + wave] = __popcll(meq[j]);
+    }
+    slot_wave_scan(s_cnt, s_pre);
+    bool take[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const bool eq = (meq[j] >> lane) & 1ull;
+        const int eq_rank = s_pre[j * kSelWaves + wave] + lane_rank(meq[j]);
+        take[j] = (v[j] > T) || (eq && eq_rank < needT);
     }
     __syncthreads();
-
-    // ordered compaction: thread t owns entries [16t, 16t + 16)
-    const int i0 = tid * PER;
-    int w[PER];
-    int n_eq = 0;
+    uint64_t mt[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        w[j] = s_sc[i0 + j];
-        n_eq += (w[j] >= 0) & (w[j] == T);
+        mt[j] = __ballot(take[j]);
+        if (lane == 0) s_cnt[j * kSelWaves + wave] = __popcll(mt[j]);
     }
-    int tot;
-    int eq_rank = sel_block_scan(n_eq, s_tmp, tot);
-    int n_sel = 0;
-    uint32_t take = 0;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        bool tk = false;
-        if (w[j] < 0) tk = false;
-        else if (w[j] > T) tk = true;
-        else if (w[j] == T) {
-            tk = eq_rank < needT;
-            ++eq_rank;
-        }
-        take |= (uint32_t)tk << j;
-        n_sel += tk;
-    }
-    int off = sel_block_scan(n_sel, s_tmp, tot);
+    slot_wave_scan(s_cnt, s_pre);
     int* out = sel_pos + (size_t)b * k;
-    const int* cp = cand_pos + (size_t)b * P;
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-        if ((take & (1u << j)) && off < keff) out[off++] = cp[i0 + j];
+    for (int j = 0; j < PER; ++j) {
+        if (take[j]) {
+            const int o = s_pre[j * kSelWaves + wave] + lane_rank(mt[j]);
+            if (o < keff) out[o] = pos[j];
+        }
+    }
     for (int i = keff + tid; i < k; i += kSelThreads) out[i] = -1;
     if (tid == 0) sel_len[b] = keff;
 }

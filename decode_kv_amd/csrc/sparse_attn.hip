@@ -5,17 +5,22 @@
 // to 512 global positions alongside the 128 most recent tokens).  MQA with
 // K = V = the dequantised 512-wide latent row.
 //
-// Workgroup = (split, sequence, group of 64 heads); wave w owns 16 heads.
-// Per tile of 32 attended rows:
+// Workgroup = (split, sequence, group of 16 heads), four waves.  Per tile of
+// 32 attended rows:
 //   * gather the FP4 codes and E8M0 scales of the rows, dequantise exactly to
 //     bf16 and stage them in LDS twice: row-major (for q.v) and d-major (for
 //     p.v), so both products read contiguous 16- or 8-byte operands;
-//   * S^T = V q^T on bf16 MFMA (16x16x32), fp32 accumulation;
-//   * online softmax in base 2, per head;
-//   * O += P V on bf16 MFMA, with P split into a bf16 high part and a bf16
-//     residual so the weights carry ~16 significant bits.
+//   * S^T = V q^T on bf16 MFMA (16x16x32), fp32 accumulation, the latent
+//     dimension split over the four waves and the partial sums added in LDS;
+//   * online softmax in base 2, per head (every wave holds the full scores);
+//   * O^T += V^T P^T on bf16 MFMA, each wave owning a quarter of the output
+//     dimension, with P split into a bf16 high part and a bf16 residual so the
+//     weights carry ~16 significant bits.
 // The k-slots of P's MFMA operand are the rows the S^T result left in each
 // lane, and V's operand is read with the same row order, so P never moves.
+// Computing O^T (M = latent dim, N = head) leaves each lane four consecutive
+// outputs of its own head: the softmax rescale needs no lane exchange and the
+// partials leave in 16-byte stores.
 // Splits write (m, l, O) partials; a second kernel merges them with a
 // log-sum-exp combine.
 #include <math.h>
@@ -28,7 +33,7 @@ namespace csa2 {
 constexpr int kAttnThreads = 256;
 constexpr int kAttnRows = 32;
 constexpr int kAttnD = 512;
-constexpr int kHeadsPerWg = 64;
+constexpr int kHeadsPerWg = 16;
 constexpr int kVjdLd = kAttnD + 8;      // bf16 per row-major row (padded)
 constexpr int kVdjLd = kAttnRows + 8;   // bf16 per d-major row (80 B: 16-B aligned)
 constexpr int kAttnMaxTilesPerWg = 16;  // rows staged per workgroup: 16 x 32
@@ -59,7 +64,7 @@ __device__ __forceinline__ float bf16_value(uint16_t b) {
     return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
-__global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
+__global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_fp4,
     const uint8_t* __restrict__ kv_scale, const long long* __restrict__ row_off,
     const int* __restrict__ len, const int* __restrict__ sel_pos,
@@ -69,12 +74,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t s_vjd[kAttnRows * kVjdLd];
     __shared__ __attribute__((aligned(16))) uint16_t s_vdj[kAttnD * kVdjLd];
     __shared__ long long s_rows[kAttnMaxTilesPerWg * kAttnRows];   // cache row, -1 = none
+    __shared__ f32x4 s_red[kAttnThreads / kWave][2][kWave];           // S^T partial sums
 
-    const int split = blockIdx.x, b = blockIdx.y, hg = blockIdx.z;
+    const int split = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
     const int g = l >> 4, c16 = l & 15;
-    const int h0 = hg * kHeadsPerWg + wave * 16;
-    const bool wave_active = h0 < Hq;
+    const int head = blockIdx.z * kHeadsPerWg + c16;      // this lane's head
 
     const int L = max(0, len[b]);
     const int win = min(window, L);
@@ -95,16 +100,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         s_rows[i] = pos >= 0 ? roff + pos : -1;
     }
 
-    bf16x8 qb[kAttnD / 32];
-    if (wave_active) {
-        const uint16_t* qh = q + ((size_t)b * Hq + h0 + c16) * kAttnD + 8 * g;
+    // q . v is split over the latent dimension: wave w owns d in [128w, 128w+128)
+    constexpr int kKs = kAttnD / 32 / (kAttnThreads / kWave);   // 4 k-steps per wave
+    bf16x8 qb[kKs];
+    {
+        const uint16_t* qh = q + ((size_t)b * Hq + head) * kAttnD + 32 * kKs * wave + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < kAttnD / 32; ++ks)
+        for (int ks = 0; ks < kKs; ++ks)
             qb[ks] = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(qh + 32 * ks));
     }
-    f32x4 o[kAttnD / 16];
+    // p . v is split over the output dimension: wave w owns d-blocks [8w, 8w+8)
+    constexpr int kNb = kAttnD / 16 / (kAttnThreads / kWave);   // 8 blocks of 16
+    f32x4 o[kNb];
 #pragma unroll
-    for (int nb = 0; nb < kAttnD / 16; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < kNb; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
     // dequantisation work split: thread owns rows 8rg..8rg+7 x elements 8dc..8dc+7
@@ -151,20 +160,27 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         }
         __syncthreads();
         if (tile + 1 < t_end) prefetch(tile + 1);   // in flight during the MFMAs
-        if (!wave_active) continue;
 
-        // S^T[row][head] = V[row] . q[head]
+        // partial S^T[row][head] over this wave's quarter of the latent dimension
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+        {
+            const uint16_t* r0 = s_vjd + c16 * kVjdLd + 32 * kKs * wave + 8 * g;
+            const uint16_t* r1 = r0 + 16 * kVjdLd;
 #pragma unroll
-        for (int ks = 0; ks < kAttnD / 32; ++ks) {
-            const bf16x8 a0 = bitcast<bf16x8>(
-                *reinterpret_cast<const u32x4*>(s_vjd + c16 * kVjdLd + 32 * ks + 8 * g));
-            const bf16x8 a1 = bitcast<bf16x8>(
-                *reinterpret_cast<const u32x4*>(s_vjd + (16 + c16) * kVjdLd + 32 * ks + 8 * g));
-            s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[ks], s0, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[ks], s1, 0, 0, 0);
+            for (int ks = 0; ks < kKs; ++ks) {
+                const bf16x8 a0 = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(r0 + 32 * ks));
+                const bf16x8 a1 = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(r1 + 32 * ks));
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[ks], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[ks], s1, 0, 0, 0);
+            }
         }
-        // lane holds head h0 + c16, rows 4g+i (s0) and 16+4g+i (s1)
+        s_red[wave][0][l] = s0;
+        s_red[wave][1][l] = s1;
+        __syncthreads();
+        s0 = s_red[0][0][l] + s_red[1][0][l] + s_red[2][0][l] + s_red[3][0][l];
+        s1 = s_red[0][1][l] + s_red[1][1][l] + s_red[2][1][l] + s_red[3][1][l];
+
+        // every wave now holds the full scores: head c16, rows 4g+i and 16+4g+i
         const int jt = tile * kAttnRows;
         float t[8];
 #pragma unroll
@@ -189,13 +205,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         psum += __shfl_xor(psum, 32);
         l_run = l_run * alpha + psum;
         m_run = m_new;
-        float al[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i);
-#pragma unroll
-        for (int nb = 0; nb < kAttnD / 16; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) o[nb][i] *= al[i];
+        for (int nb = 0; nb < kNb; ++nb) o[nb] *= alpha;   // this lane's head
 
         u32x4 ph_u, pl_u;
 #pragma unroll
@@ -208,44 +219,36 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         }
         const bf16x8 ph = bitcast<bf16x8>(ph_u), pl = bitcast<bf16x8>(pl_u);
 #pragma unroll
-        for (int nb = 0; nb < kAttnD / 16; ++nb) {
-            const uint16_t* vd = s_vdj + (16 * nb + c16) * kVdjLd + 4 * g;
+        for (int nb = 0; nb < kNb; ++nb) {
+            const uint16_t* vd = s_vdj + (16 * (kNb * wave + nb) + c16) * kVdjLd + 4 * g;
             const u32x2 lo = *reinterpret_cast<const u32x2*>(vd);
             const u32x2 hi = *reinterpret_cast<const u32x2*>(vd + 16);
             const bf16x8 bv = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, bv, o[nb], 0, 0, 0);
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, bv, o[nb], 0, 0, 0);
+            // O^T[d][head]: A = V^T (M = latent dim), B = P^T (N = head)
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, ph, o[nb], 0, 0, 0);
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, pl, o[nb], 0, 0, 0);
         }
     }
-    if (!wave_active) return;
 
-    float lh[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) lh[i] = __shfl(l_run, 4 * g + i);
+    // lane holds head `head`, latent elements 16 (8 wave + nb) + 4 g + (0..3)
+    const int d0 = 16 * kNb * wave + 4 * g;
     if (n_splits == 1) {
+        float* ob = out + ((size_t)b * Hq + head) * kAttnD + d0;
+        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
-        for (int nb = 0; nb < kAttnD / 16; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int head = h0 + 4 * g + i;
-                out[((size_t)b * Hq + head) * kAttnD + 16 * nb + c16] =
-                    lh[i] > 0.f ? o[nb][i] / lh[i] : 0.f;
-            }
-        if (lse && l < 16)
-            lse[(size_t)b * Hq + h0 + l] =
+        for (int nb = 0; nb < kNb; ++nb)
+            *reinterpret_cast<f32x4*>(ob + 16 * nb) = o[nb] * inv;
+        if (lse && wave == 0 && g == 0)
+            lse[(size_t)b * Hq + head] =
                 l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
     } else {
-        const size_t base = ((size_t)b * n_splits + split) * Hq;
+        const size_t base = ((size_t)b * n_splits + split) * Hq + head;
+        float* ob = part_o + base * kAttnD + d0;
 #pragma unroll
-        for (int nb = 0; nb < kAttnD / 16; ++nb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int head = h0 + 4 * g + i;
-                part_o[(base + head) * kAttnD + 16 * nb + c16] = o[nb][i];
-            }
-        if (l < 16) {
-            part_ml[(base + h0 + l) * 2 + 0] = m_run;
-            part_ml[(base + h0 + l) * 2 + 1] = l_run;
+        for (int nb = 0; nb < kNb; ++nb) *reinterpret_cast<f32x4*>(ob + 16 * nb) = o[nb];
+        if (wave == 0 && g == 0) {
+            part_ml[base * 2 + 0] = m_run;
+            part_ml[base * 2 + 1] = l_run;
         }
     }
 }
@@ -302,7 +305,7 @@ int sparse_attn_splits(int B, int Hq, int k, int window) {
     const int tiles = (k + window + kAttnRows - 1) / kAttnRows;
     const int n_hg = (Hq + kHeadsPerWg - 1) / kHeadsPerWg;
     const long long wgs = (long long)(B > 0 ? B : 1) * n_hg;
-    int want = (int)((256 + wgs - 1) / wgs);
+    int want = (int)((512 + wgs - 1) / wgs);
     if (want > tiles) want = tiles;
     if (want > kAttnMaxSplits) want = kAttnMaxSplits;
     const int min_splits = (tiles + kAttnMaxTilesPerWg - 1) / kAttnMaxTilesPerWg;

@@ -4,21 +4,24 @@
 // pool; "How DeepSeek V4.1 Flash Actually Works", item 2: up to 16,384
 // candidate positions).
 //
-// Five kernels, all sequences of the batch at once, tiles of 1,024 positions:
-//   1. prep       zero the first-level histogram and candidate counters;
-//                 per-sequence E, P_eff and tile range
-//   2. score      stream the int8 keys once (each wave issues all of its tile
-//                 loads at once, 16 KB in flight), int8 MFMA scoring, int32 scores to
-//                 scratch, LDS histogram of a float-like key (exponent + 5
-//                 mantissa bits, 832 bins), flushed with one atomic per
-//                 non-empty bin
-//   3. gather     every tile finds the bin holding the P_eff-th score from the
-//                 histogram, counts its entries above that bin and appends the
-//                 entries inside it to a candidate list (one atomic per tile)
-//   4. threshold  one workgroup per sequence: exact radix select over the
-//                 candidates (13-bit digits) gives the threshold T and the
-//                 number of ties at T to keep; per-tile counts and an
-//                 exclusive prefix give every tile its output offsets
+// Five kernels, all sequences of the batch at once, tiles of 1,024 positions,
+// no device-wide atomics on hot addresses:
+//   1. score      stream the int8 keys once (each wave issues all of its tile
+//                 loads before scoring), int8 MFMA scoring, int32 scores to
+//                 scratch, and a per-tile histogram of a float-like key
+//                 (exponent + 5 mantissa bits, 832 bins) written with plain
+//                 stores; workgroup 0 also writes the per-sequence layout
+//   2. reduce     sum the per-tile histograms of each sequence (workgroups
+//                 split the bins), reset the candidate counters
+//   3. gather     every tile finds the bin holding the P_eff-th score, counts
+//                 its entries above that bin and appends the entries inside it
+//                 to one of 8 candidate regions (one counter per region, so the
+//                 atomics of the 8 XCDs do not queue on one address)
+//   4. threshold  one workgroup per sequence: exact select among the
+//                 candidates (14-bit digits, then exact ranking of <= 64
+//                 entries) gives the threshold T and the number of ties at T
+//                 to keep; per-tile counts and an exclusive prefix give every
+//                 tile its output offsets
 //   5. write      ordered compaction: s > T, plus the first ties in position
 //                 order; ascending positions, tail -1
 // The result is exact and independent of the launch shape.
@@ -30,10 +33,12 @@ namespace csa2 {
 constexpr int kTile = 1024;
 constexpr int kScanThreads = 256;
 constexpr int kKeyBins = 832;            // float-like key of a score < 2^31
-constexpr int kThrThreads = 1024;
-constexpr int kThrWaves = kThrThreads / kWave;
+constexpr int kRedBins = 32;             // bins per reduce workgroup
+constexpr int kRegions = 8;              // candidate regions (XCDs)
+constexpr int kThrThreads = 256;
 constexpr int kMaxTilesPerSeq = 8192;    // LDS tile counters of the threshold kernel (8M positions)
-constexpr int kRefBins = 8192;           // 13-bit refinement digit
+constexpr int kRefBits = 14;
+constexpr int kRefBins = 1 << kRefBits;  // refinement digit
 constexpr int kMaxBatch = 4096;
 
 struct FullState {
@@ -41,21 +46,22 @@ struct FullState {
     int Peff;    // pool size
     int tile0;   // first global tile of this sequence
     int ntiles;  // tiles of this sequence
-    int cand0;   // first slot of this sequence's candidate list
+    int cand0;   // first candidate slot of this sequence
+    int cap;     // slots per candidate region
     int T;       // take s > T ...
     int needT;   // ... plus the first needT entries with s == T
-    int pad;
 };
 static_assert(sizeof(FullState) == 32, "FullState size");
 
 struct FullWs {
     FullState* st;        // [B]
     uint32_t* hist;       // [B][kKeyBins]
-    int* cand_cnt;        // [B]
+    int* cand_cnt;        // [B][kRegions]
     int* tile_above;      // [Tmax] entries of the tile above the threshold bin
     int* tile_off;        // [Tmax][2] output offsets among s > T and among s == T
     int* meta;            // [0] total tiles
-    int2* cand;           // [total_len] (score, position)
+    uint16_t* tile_hist;  // [Tmax][kKeyBins]
+    int2* cand;           // [(Tmax + kRegions * B) * kTile] (score, position)
     int* scores;          // [Tmax * kTile]
 };
 
@@ -74,11 +80,12 @@ static size_t full_ws_layout(int B, long long total_len, char* base, FullWs* w) 
     FullWs x;
     x.st = reinterpret_cast<FullState*>(take(sizeof(FullState) * (size_t)B));
     x.hist = reinterpret_cast<uint32_t*>(take(4ull * B * kKeyBins));
-    x.cand_cnt = reinterpret_cast<int*>(take(4ull * B));
+    x.cand_cnt = reinterpret_cast<int*>(take(4ull * B * kRegions));
     x.tile_above = reinterpret_cast<int*>(take(4ull * T));
     x.tile_off = reinterpret_cast<int*>(take(8ull * T));
     x.meta = reinterpret_cast<int*>(take(256));
-    x.cand = reinterpret_cast<int2*>(take(8ull * (size_t)(total_len > 0 ? total_len : 1)));
+    x.tile_hist = reinterpret_cast<uint16_t*>(take(2ull * (size_t)T * kKeyBins));
+    x.cand = reinterpret_cast<int2*>(take(8ull * (size_t)(T + (long long)kRegions * B) * kTile));
     x.scores = reinterpret_cast<int*>(take(4ull * (size_t)T * kTile));
     if (w) *w = x;
     return off;
@@ -109,18 +116,6 @@ __device__ __forceinline__ void key_interval(int key, int& lo, int& hi) {
     hi = (key == kKeyBins - 1) ? 0x7FFFFFFF : lo + (1 << (e - 5)) - 1;
 }
 
-// Sequence owning global tile t (threads of the block cooperate; result in LDS).
-__device__ int find_tile_seq(const FullState* __restrict__ st, int B, int t, int* s_b) {
-    if (threadIdx.x == 0) *s_b = -1;
-    __syncthreads();
-    for (int b = threadIdx.x; b < B; b += blockDim.x) {
-        const int t0 = st[b].tile0;
-        if (t >= t0 && t < t0 + st[b].ntiles) *s_b = b;
-    }
-    __syncthreads();
-    return *s_b;
-}
-
 // Exclusive prefix sum of one int per thread over the block.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
@@ -145,18 +140,18 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int& tota
 
 // Bin holding the need-th largest entry of a histogram (bins ascending in
 // value); every thread gets (bin, entries in higher bins).  Requires
-// 1 <= need <= total count.
-template <int NT, int PER>
-__device__ __forceinline__ void find_bin(const uint32_t* h, int nb, int need, int* s_tmp,
-                                         int* s_res, int& bin_out, int& above_out) {
+// 1 <= need <= total count.  Thread t owns PER consecutive bins from the top.
+template <int NT, int PER, typename H>
+__device__ __forceinline__ void find_bin(const H* h, int nb, int need, int* s_tmp, int* s_res,
+                                         int& bin_out, int& above_out) {
     const int r = NT - 1 - threadIdx.x;          // thread 0 owns the highest bins
-    uint32_t c[PER];
+    int c[PER];
     int mysum = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         const int bin = r * PER + i;
-        c[i] = bin < nb ? h[bin] : 0u;
-        mysum += (int)c[i];
+        c[i] = bin < nb ? (int)h[bin] : 0;
+        mysum += c[i];
     }
     int tot;
     const int above = block_exclusive_scan<NT>(mysum, s_tmp, tot);
@@ -164,11 +159,11 @@ __device__ __forceinline__ void find_bin(const uint32_t* h, int nb, int need, in
         int acc = above;
 #pragma unroll
         for (int i = PER - 1; i >= 0; --i) {
-            if (acc < need && need <= acc + (int)c[i]) {
+            if (acc < need && need <= acc + c[i]) {
                 s_res[0] = r * PER + i;
                 s_res[1] = acc;
             }
-            acc += (int)c[i];
+            acc += c[i];
         }
     }
     __syncthreads();
@@ -177,64 +172,89 @@ __device__ __forceinline__ void find_bin(const uint32_t* h, int nb, int need, in
     __syncthreads();
 }
 
-// ---- 1. prep ---------------------------------------------------------------
-__global__ __launch_bounds__(kScanThreads) void full_prep_kernel(
-    const int* __restrict__ len, int B, int window, int P, FullWs w) {
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < (size_t)B * kKeyBins;
-         i += (size_t)gridDim.x * blockDim.x)
-        w.hist[i] = 0;
-    if (blockIdx.x != 0) return;
+// Tile t -> sequence, from the lengths (up to kMaxBatch sequences, 16 per
+// thread).  Returns the sequence (or -1 past the last tile) and the layout of
+// that sequence; with write_state the block also writes every sequence's
+// state and the total tile count.
+struct TileInfo {
+    int b, tile0, E;
+    long long roff;
+};
+
+__device__ TileInfo map_tile(const int* __restrict__ len, const long long* __restrict__ row_off,
+                             int B, int window, int P, int t, FullWs w, bool write_state) {
+    constexpr int SPT = kMaxBatch / kScanThreads;         // sequences per thread
     __shared__ int s_tmp[kScanThreads / kWave];
-    __shared__ int s_carry[2];
-    if (threadIdx.x == 0) s_carry[0] = s_carry[1] = 0;
-    __syncthreads();
-    for (int base = 0; base < B; base += kScanThreads) {   // uniform trip count
-        const int b = base + threadIdx.x;
+    __shared__ int s_b, s_tile0, s_E;
+    __shared__ long long s_roff;
+    const int first = threadIdx.x * SPT;
+    int nt[SPT], Ev[SPT], cp[SPT];
+    int sum_t = 0, sum_c = 0;
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int b = first + i;
         int E = 0;
         if (b < B) {
             const int L = len[b];
             E = L > window ? L - window : 0;
         }
-        const int nt = (E + kTile - 1) / kTile;
-        int tot_t, tot_e;
-        const int pre_t = block_exclusive_scan<kScanThreads>(nt, s_tmp, tot_t);
-        const int pre_e = block_exclusive_scan<kScanThreads>(E, s_tmp, tot_e);
-        if (b < B) {
-            FullState s;
-            s.E = E;
-            s.Peff = E < P ? E : P;
-            s.tile0 = s_carry[0] + pre_t;
-            s.ntiles = nt;
-            s.cand0 = s_carry[1] + pre_e;
-            s.T = 0x7FFFFFFF;
-            s.needT = 0;
-            s.pad = 0;
-            w.st[b] = s;
-            w.cand_cnt[b] = 0;
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            s_carry[0] += tot_t;
-            s_carry[1] += tot_e;
-        }
-        __syncthreads();
+        Ev[i] = E;
+        nt[i] = (E + kTile - 1) / kTile;
+        cp[i] = (nt[i] + kRegions - 1) / kRegions;    // tiles per candidate region
+        sum_t += nt[i];
+        sum_c += cp[i];
     }
-    if (threadIdx.x == 0) w.meta[0] = s_carry[0];
+    if (threadIdx.x == 0) s_b = -1;
+    int tot_t, tot_c;
+    int pre_t = block_exclusive_scan<kScanThreads>(sum_t, s_tmp, tot_t);
+    int pre_c = block_exclusive_scan<kScanThreads>(sum_c, s_tmp, tot_c);
+#pragma unroll
+    for (int i = 0; i < SPT; ++i) {
+        const int b = first + i;
+        if (b < B) {
+            if (t >= pre_t && t < pre_t + nt[i]) {
+                s_b = b;
+                s_tile0 = pre_t;
+                s_E = Ev[i];
+                s_roff = row_off[b];
+            }
+            if (write_state) {
+                FullState s;
+                s.E = Ev[i];
+                s.Peff = Ev[i] < P ? Ev[i] : P;
+                s.tile0 = pre_t;
+                s.ntiles = nt[i];
+                s.cand0 = pre_c * kRegions * kTile;
+                s.cap = cp[i] * kTile;
+                s.T = 0x7FFFFFFF;
+                s.needT = 0;
+                w.st[b] = s;
+            }
+        }
+        pre_t += nt[i];
+        pre_c += cp[i];
+    }
+    if (write_state && threadIdx.x == 0) w.meta[0] = tot_t;
+    __syncthreads();
+    TileInfo r;
+    r.b = s_b;
+    r.tile0 = s_tile0;
+    r.E = s_E;
+    r.roff = s_roff;
+    return r;
 }
 
-// ---- 2. score + first-level histogram ----------------------------------------
+// ---- 1. score + per-tile histogram -------------------------------------------------
 template <int NB>
 __global__ __launch_bounds__(kScanThreads) void full_score_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ wts,
-    const int8_t* __restrict__ keys, const long long* __restrict__ row_off, int B, int H,
-    FullWs w) {
+    const int8_t* __restrict__ keys, const long long* __restrict__ row_off,
+    const int* __restrict__ len, int B, int H, int window, int P, FullWs w) {
     __shared__ uint32_t s_hist[kKeyBins];
-    __shared__ int s_b;
     const int t = blockIdx.x;
-    if (t >= w.meta[0]) return;
-    const int b = find_tile_seq(w.st, B, t, &s_b);
-    if (b < 0) return;
-    const FullState st = w.st[b];
+    const TileInfo ti = map_tile(len, row_off, B, window, P, t, w, t == 0);
+    if (ti.b < 0) return;                              // past the last tile
+    const int b = ti.b;
     for (int i = threadIdx.x; i < kKeyBins; i += kScanThreads) s_hist[i] = 0;
 
     i32x4 qa[NB];
@@ -243,22 +263,22 @@ __global__ __launch_bounds__(kScanThreads) void full_score_kernel(
 
     const int l = lane_id();
     const int wave = threadIdx.x / kWave;
-    const int p_tile = (t - st.tile0) * kTile;                 // first position
-    const int8_t* kbase = keys + ((size_t)row_off[b] + p_tile) * kDk + (l >> 4) * 16;
+    const int p_tile = (t - ti.tile0) * kTile;                 // first position
+    const int8_t* kbase = keys + ((size_t)ti.roff + p_tile) * kDk + (l >> 4) * 16;
     int* sc_out = w.scores + (size_t)t * kTile;
-    const int nvalid = min(kTile, st.E - p_tile);
+    const int nvalid = min(kTile, ti.E - p_tile);
     // wave w scores tokens [256w, 256w + 256): 16 groups of 16, all loads issued
     // before the first MFMA so 16 KB per wave are in flight
     constexpr int kGroups = kTile / (4 * 16);
     const int t0 = (kTile / 4) * wave;
     i32x4 kop[kGroups];
-    __syncthreads();
 #pragma unroll
     for (int u = 0; u < kGroups; ++u) {
         int tok = t0 + 16 * u + (l & 15);
         tok = tok < nvalid ? tok : 0;
         kop[u] = *reinterpret_cast<const i32x4*>(kbase + (size_t)tok * kDk);
     }
+    __syncthreads();                                           // histogram zeroed
 #pragma unroll
     for (int it = 0; it < kGroups / 4; ++it) {
         if (t0 + 64 * it >= nvalid) break;                     // wave-uniform
@@ -274,11 +294,62 @@ __global__ __launch_bounds__(kScanThreads) void full_score_kernel(
         }
     }
     __syncthreads();
-    uint32_t* gh = w.hist + (size_t)b * kKeyBins;
-    for (int i = threadIdx.x; i < kKeyBins; i += kScanThreads) {
-        const uint32_t c = s_hist[i];
-        if (c) atomicAdd(&gh[i], c);
+    // per-tile histogram, u16 (a tile has <= 1,024 entries), two bins per word
+    uint32_t* th = reinterpret_cast<uint32_t*>(w.tile_hist + (size_t)t * kKeyBins);
+    for (int i = threadIdx.x; i < kKeyBins / 2; i += kScanThreads)
+        th[i] = s_hist[2 * i] | (s_hist[2 * i + 1] << 16);
+}
+
+// ---- 2. reduce the per-tile histograms ---------------------------------------------
+// workgroup (c, b): bins [32c, 32c + 32) of sequence b; thread (r, k) sums
+// bins 8k .. 8k+7 over tiles r, r + 64, ...
+__global__ __launch_bounds__(kScanThreads) void full_reduce_kernel(FullWs w) {
+    __shared__ uint32_t s_part[kScanThreads / 4][kRedBins + 1];
+    const int c = blockIdx.x, b = blockIdx.y;
+    const FullState st = w.st[b];
+    if (c == 0 && threadIdx.x < kRegions) w.cand_cnt[b * kRegions + threadIdx.x] = 0;
+    const int r = threadIdx.x >> 2, k = threadIdx.x & 3;
+    uint32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    constexpr int U = 8;
+    for (int base = 0; base < st.ntiles; base += 64 * U) {
+        u32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int tile = base + r + 64 * u;
+            v[u] = tile < st.ntiles
+                       ? *reinterpret_cast<const u32x4*>(w.tile_hist +
+                                                         (size_t)(st.tile0 + tile) * kKeyBins +
+                                                         kRedBins * c + 8 * k)
+                       : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc[2 * i] += v[u][i] & 0xFFFFu;
+                acc[2 * i + 1] += v[u][i] >> 16;
+            }
     }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s_part[r][8 * k + i] = acc[i];
+    __syncthreads();
+    if (threadIdx.x < kRedBins) {
+        uint32_t s = 0;
+        for (int i = 0; i < kScanThreads / 4; ++i) s += s_part[i][threadIdx.x];
+        w.hist[(size_t)b * kKeyBins + kRedBins * c + threadIdx.x] = s;
+    }
+}
+
+// Sequence owning global tile t, from the per-sequence state (result in LDS).
+__device__ int tile_seq(const FullState* __restrict__ st, int B, int t, int* s_b) {
+    if (threadIdx.x == 0) *s_b = -1;
+    __syncthreads();
+    for (int b = threadIdx.x; b < B; b += blockDim.x) {
+        const int t0 = st[b].tile0;
+        if (t >= t0 && t < t0 + st[b].ntiles) *s_b = b;
+    }
+    __syncthreads();
+    return *s_b;
 }
 
 // ---- 3. gather: entries above / inside the threshold bin ------------------------
@@ -288,14 +359,9 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
     __shared__ int s_res[2];
     const int t = blockIdx.x;
     if (t >= w.meta[0]) return;
-    const int b = find_tile_seq(w.st, B, t, &s_b);
+    const int b = tile_seq(w.st, B, t, &s_b);
     if (b < 0) return;
     const FullState st = w.st[b];
-    int kb, above;
-    find_bin<kScanThreads, (kKeyBins + kScanThreads - 1) / kScanThreads>(
-        w.hist + (size_t)b * kKeyBins, kKeyBins, st.Peff, s_tmp, s_res, kb, above);
-    int lo, hi;
-    key_interval(kb, lo, hi);
     const int p_tile = (t - st.tile0) * kTile;
     const int nvalid = min(kTile, st.E - p_tile);
     const int* sc = w.scores + (size_t)t * kTile;
@@ -306,6 +372,11 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
         const int i = threadIdx.x + j * kScanThreads;
         v[j] = i < nvalid ? sc[i] : -1;
     }
+    int kb, above;
+    find_bin<kScanThreads, (kKeyBins + kScanThreads - 1) / kScanThreads>(
+        w.hist + (size_t)b * kKeyBins, kKeyBins, st.Peff, s_tmp, s_res, kb, above);
+    int lo, hi;
+    key_interval(kb, lo, hi);
     // per-thread counts of entries above / inside the bin, packed in one scan
     int n_above = 0, n_in = 0;
 #pragma unroll
@@ -316,18 +387,19 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
     int tot;
     const int pre = block_exclusive_scan<kScanThreads>((n_in << 16) | n_above, s_tmp, tot);
     const int tot_in = tot >> 16;
+    const int region = t % kRegions;
     if (threadIdx.x == 0) {
         w.tile_above[t] = tot & 0xFFFF;
-        s_res[0] = tot_in ? atomicAdd(&w.cand_cnt[b], tot_in) : 0;   // one atomic per tile
+        s_res[0] = tot_in ? atomicAdd(&w.cand_cnt[b * kRegions + region], tot_in) : 0;
     }
     __syncthreads();
     int slot = s_res[0] + (pre >> 16);
+    int2* out = w.cand + st.cand0 + (size_t)region * st.cap;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if (v[j] >= lo && v[j] <= hi) {
-            if (slot < st.E)                           // at most E candidates
-                w.cand[(size_t)st.cand0 + slot] =
-                    make_int2(v[j], p_tile + (int)threadIdx.x + j * kScanThreads);
+            if (slot < st.cap)                         // region capacity
+                out[slot] = make_int2(v[j], p_tile + (int)threadIdx.x + j * kScanThreads);
             ++slot;
         }
     }
@@ -335,26 +407,21 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
 
 // ---- 4. threshold: exact select among the candidates, tile offsets ---------------
 __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
+    constexpr int kWaves = kThrThreads / kWave;
     __shared__ uint32_t s_hist[kRefBins];
     __shared__ uint32_t s_cgt[kMaxTilesPerSeq];
     __shared__ uint32_t s_ceq[kMaxTilesPerSeq];
-    __shared__ int s_tmp[kThrWaves];
-    __shared__ int s_res[2];
+    __shared__ int s_tmp[kWaves];
+    __shared__ int s_res[4];
+    __shared__ unsigned long long s_key[64];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const FullState st = w.st[b];
     if (st.Peff == 0) return;
-    int kb, above;
-    find_bin<kThrThreads, 1>(w.hist + (size_t)b * kKeyBins, kKeyBins, st.Peff, s_tmp, s_res, kb,
-                             above);
-    int lo, hi;
-    key_interval(kb, lo, hi);
-    int need = st.Peff - above;
-    const int nc = min(w.cand_cnt[b], st.E);
-    const int2* cand = w.cand + st.cand0;
-    constexpr int PER = 16;
-    constexpr int CHUNK = kThrThreads * PER;
-    // this thread's tiles' above-bin counts, loaded early
+    // region counts and this thread's tiles' above-bin counts, loaded early
+    int rc[kRegions], rpre[kRegions + 1];
+#pragma unroll
+    for (int r = 0; r < kRegions; ++r) rc[r] = min(w.cand_cnt[b * kRegions + r], st.cap);
     constexpr int TPT = kMaxTilesPerSeq / kThrThreads;
     int above_t[TPT];
 #pragma unroll
@@ -362,18 +429,37 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         const int i = tid * TPT + u;
         above_t[u] = i < st.ntiles ? w.tile_above[st.tile0 + i] : 0;
     }
+    rpre[0] = 0;
+#pragma unroll
+    for (int r = 0; r < kRegions; ++r) rpre[r + 1] = rpre[r] + rc[r];
+    const int nc = rpre[kRegions];
+    auto cand_at = [&](int i) -> int2 {              // i-th candidate over the regions
+        int r = 0;
+#pragma unroll
+        for (int x = 1; x < kRegions; ++x) r += i >= rpre[x];
+        return w.cand[(size_t)st.cand0 + (size_t)r * st.cap + (i - rpre[r])];
+    };
+    int kb, above;
+    find_bin<kThrThreads, (kKeyBins + kThrThreads - 1) / kThrThreads>(
+        w.hist + (size_t)b * kKeyBins, kKeyBins, st.Peff, s_tmp, s_res, kb, above);
+    int lo, hi;
+    key_interval(kb, lo, hi);
+    int need = st.Peff - above;
+    int cnt = nc;                                    // entries inside [lo, hi]
+    constexpr int PER = 32;
+    constexpr int CHUNK = kThrThreads * PER;
     // first chunk of candidates stays in registers for every pass
     int2 c0v[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int i = tid + j * kThrThreads;
-        c0v[j] = i < nc ? cand[i] : make_int2(-1, 0);
+        c0v[j] = i < nc ? cand_at(i) : make_int2(-1, 0);
     }
-    // refine [lo, hi] with 13-bit digits until one value remains
-    while (lo < hi) {                                  // uniform: lo, hi from LDS
+    // refine [lo, hi] with 14-bit digits until one value or <= 64 entries remain
+    while (lo < hi && cnt > 64) {                    // uniform: lo, hi, cnt from LDS
         const unsigned width = (unsigned)(hi - lo) + 1u;
         const int bits = 32 - __clz(width - 1u);
-        const int sh = bits > 13 ? bits - 13 : 0;
+        const int sh = bits > kRefBits ? bits - kRefBits : 0;
         const int nb = (int)(((width - 1u) >> sh) + 1u);
         for (int i = tid; i < nb; i += kThrThreads) s_hist[i] = 0;
         __syncthreads();
@@ -381,26 +467,65 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         for (int j = 0; j < PER; ++j)
             if (c0v[j].x >= lo && c0v[j].x <= hi) atomicAdd(&s_hist[(c0v[j].x - lo) >> sh], 1u);
         for (int c0 = CHUNK; c0 < nc; c0 += CHUNK) {   // many candidates: stream the rest
-            int v[PER];
-#pragma unroll
             for (int j = 0; j < PER; ++j) {
                 const int i = c0 + tid + j * kThrThreads;
-                v[j] = i < nc ? cand[i].x : -1;
+                if (i < nc) {
+                    const int v = cand_at(i).x;
+                    if (v >= lo && v <= hi) atomicAdd(&s_hist[(v - lo) >> sh], 1u);
+                }
             }
-#pragma unroll
-            for (int j = 0; j < PER; ++j)
-                if (v[j] >= lo && v[j] <= hi) atomicAdd(&s_hist[(v[j] - lo) >> sh], 1u);
         }
         __syncthreads();
         int d, a;
         find_bin<kThrThreads, kRefBins / kThrThreads>(s_hist, nb, need, s_tmp, s_res, d, a);
         need -= a;
+        cnt = (int)s_hist[d];
+        __syncthreads();
         const int nlo = lo + (d << sh);
         const int nhi = (sh == 0) ? nlo : min(hi, nlo + (1 << sh) - 1);
         lo = nlo;
         hi = nhi;
     }
-    const int T = lo, needT = need;
+    int T, needT;
+    if (lo == hi) {
+        T = lo;
+        needT = need;
+    } else {
+        // <= 64 entries in [lo, hi]: rank them by the key (score, ~position)
+        if (tid == 0) s_res[2] = 0;
+        __syncthreads();
+        auto put = [&](int2 v) {
+            if (v.x >= lo && v.x <= hi) {
+                const int slot = atomicAdd(&s_res[2], 1);
+                if (slot < 64)
+                    s_key[slot] = ((unsigned long long)(uint32_t)v.x << 32) | (uint32_t)~(uint32_t)v.y;
+            }
+        };
+#pragma unroll
+        for (int j = 0; j < PER; ++j) put(c0v[j]);
+        for (int c0 = CHUNK; c0 < nc; c0 += CHUNK)
+            for (int j = 0; j < PER; ++j) {
+                const int i = c0 + tid + j * kThrThreads;
+                if (i < nc) put(cand_at(i));
+            }
+        __syncthreads();
+        if (tid < cnt) {
+            const unsigned long long mine = s_key[tid];
+            int rank = 0;
+            for (int u = 0; u < cnt; ++u) rank += s_key[u] > mine;
+            if (rank == need - 1) {
+                const uint32_t ts = (uint32_t)(mine >> 32);
+                int ties = 0;
+                for (int u = 0; u < cnt; ++u)
+                    ties += ((uint32_t)(s_key[u] >> 32) == ts) & (s_key[u] >= mine);
+                s_res[0] = (int)ts;
+                s_res[1] = ties;
+            }
+        }
+        __syncthreads();
+        T = s_res[0];
+        needT = s_res[1];
+    }
 
     // per-tile counts of candidates above / at the threshold
     for (int i = tid; i < st.ntiles; i += kThrThreads) {
@@ -408,24 +533,18 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         s_ceq[i] = 0;
     }
     __syncthreads();
-    auto count_tiles = [&](const int2 (&v)[PER]) {
-#pragma unroll
-        for (int j = 0; j < PER; ++j) {
-            const int tile = min(max(v[j].y, 0) / kTile, kMaxTilesPerSeq - 1);
-            if (v[j].x > T) atomicAdd(&s_cgt[tile], 1u);
-            else if (v[j].x >= 0 && v[j].x == T) atomicAdd(&s_ceq[tile], 1u);
-        }
+    auto count_one = [&](int2 v) {
+        const int tile = min(max(v.y, 0) / kTile, kMaxTilesPerSeq - 1);
+        if (v.x > T) atomicAdd(&s_cgt[tile], 1u);
+        else if (v.x >= 0 && v.x == T) atomicAdd(&s_ceq[tile], 1u);
     };
-    count_tiles(c0v);
-    for (int c0 = CHUNK; c0 < nc; c0 += CHUNK) {
-        int2 v[PER];
 #pragma unroll
+    for (int j = 0; j < PER; ++j) count_one(c0v[j]);
+    for (int c0 = CHUNK; c0 < nc; c0 += CHUNK)
         for (int j = 0; j < PER; ++j) {
             const int i = c0 + tid + j * kThrThreads;
-            v[j] = i < nc ? cand[i] : make_int2(-1, 0);
+            if (i < nc) count_one(cand_at(i));
         }
-        count_tiles(v);
-    }
     __syncthreads();
     // exclusive prefix over this sequence's tiles, TPT tiles per thread
     int gl[TPT], el[TPT];
@@ -476,13 +595,13 @@ __global__ __launch_bounds__(kScanThreads) void full_write_kernel(int B, int P,
         if (threadIdx.x == 0) pool_len[t] = Peff;
     }
     if (t >= w.meta[0]) return;
-    const int b = find_tile_seq(w.st, B, t, &s_b);
+    const int b = tile_seq(w.st, B, t, &s_b);
     if (b < 0) return;
     const FullState st = w.st[b];
     const int p_tile = (t - st.tile0) * kTile;
     const int nvalid = min(kTile, st.E - p_tile);
     const int* sc = w.scores + (size_t)t * kTile;
-    constexpr int PER = kTile / kScanThreads;   // 8 contiguous positions per thread
+    constexpr int PER = kTile / kScanThreads;   // contiguous positions per thread
     const int i0 = threadIdx.x * PER;
     int v[PER];
     int n_eq = 0;
@@ -558,25 +677,21 @@ extern "C" int csa2_index_full(const signed char* q, const signed char* w,
     const unsigned tiles = (unsigned)full_tile_bound(B, total_len);
     const dim3 blk(kScanThreads);
 
-    const unsigned prep_grid =
-        (unsigned)std::min<long long>(64, ((long long)B * kKeyBins + 4095) / 4096);
-    hipLaunchKernelGGL(full_prep_kernel, dim3(prep_grid), blk, 0, s, len, B, window, P, fw);
-    if (int e = launch_status("full_prep")) return e;
-
     if (g_scan_ev_start) hipEventRecord(g_scan_ev_start, s);
     const int NB = (H + 15) / 16;
     const int8_t* q8 = reinterpret_cast<const int8_t*>(q);
     const int8_t* w8 = reinterpret_cast<const int8_t*>(w);
     const int8_t* k8 = reinterpret_cast<const int8_t*>(keys);
     switch (NB) {
-        case 1: hipLaunchKernelGGL(full_score_kernel<1>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, B, H, fw); break;
-        case 2: hipLaunchKernelGGL(full_score_kernel<2>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, B, H, fw); break;
-        case 3: hipLaunchKernelGGL(full_score_kernel<3>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, B, H, fw); break;
-        default: hipLaunchKernelGGL(full_score_kernel<4>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, B, H, fw); break;
+        case 1: hipLaunchKernelGGL(full_score_kernel<1>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw); break;
+        case 2: hipLaunchKernelGGL(full_score_kernel<2>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw); break;
+        case 3: hipLaunchKernelGGL(full_score_kernel<3>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw); break;
+        default: hipLaunchKernelGGL(full_score_kernel<4>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw); break;
     }
     if (int e = launch_status("full_score")) return e;
     if (g_scan_ev_stop) hipEventRecord(g_scan_ev_stop, s);
 
+    hipLaunchKernelGGL(full_reduce_kernel, dim3(kKeyBins / kRedBins, B), blk, 0, s, fw);
     hipLaunchKernelGGL(full_gather_kernel, dim3(tiles), blk, 0, s, B, fw);
     hipLaunchKernelGGL(full_threshold_kernel, dim3(B), dim3(kThrThreads), 0, s, fw);
     const unsigned wgrid = tiles > (unsigned)B ? tiles : (unsigned)B;

@@ -55,6 +55,8 @@ def lib():
         L.csa2_kv_append_fp4.argtypes = [V, V, I, I, V, V, V]
         L.csa2_index_full.restype = I
         L.csa2_index_full.argtypes = [V, V, V, V, V, I, LL, LL, I, I, I, I, V, V, V, V, SZ, V]
+        L.csa2_index_score.restype = I
+        L.csa2_index_score.argtypes = [V, V, V, V, V, I, LL, LL, I, I, I, V, V, SZ, V]
         L.csa2_index_reindex.restype = I
         L.csa2_index_reindex.argtypes = [V, V, V, V, V, V, I, I, I, I, V, V]
         L.csa2_select_topk.restype = I
@@ -62,8 +64,6 @@ def lib():
         L.csa2_sparse_attn_decode.restype = I
         L.csa2_sparse_attn_decode.argtypes = [V, V, V, V, V, LL, V, V, I, I, I, I, I, F, V, V,
                                               V, SZ, V]
-        L.csa2_set_scan_timer.restype = I
-        L.csa2_set_scan_timer.argtypes = [V, V]
         _lib = L
     return _lib
 
@@ -133,6 +133,15 @@ def index_full(q, w, keys, row_off, lens, max_len, total_len, window, P, pool_po
                                  _p(pool_len), _p(ws), nbytes, _s(stream)))
 
 
+def index_score(q, w, keys, row_off, lens, max_len, total_len, window, score, ws, stream=None):
+    B, H, Dk = q.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("csa2_index_score",
+           lib().csa2_index_score(_p(q), _p(w), _p(keys), _p(row_off), _p(lens), B, int(max_len),
+                                  int(total_len), H, Dk, window, _p(score), _p(ws), nbytes,
+                                  _s(stream)))
+
+
 def index_reindex(q, w, keys, row_off, cand_pos, cand_len, score, stream=None):
     B, H, Dk = q.shape
     P = cand_pos.shape[1]
@@ -158,10 +167,3 @@ def sparse_attn_decode(q, kv_fp4, kv_scale, row_off, lens, max_len, sel_pos, sel
                                          int(max_len), _p(sel_pos), _p(sel_len), B, Hq, D, k,
                                          window, float(sm_scale), _p(out), _p(lse), _p(ws),
                                          nbytes, _s(stream)))
-
-
-def set_scan_timer(ev_start=None, ev_stop=None):
-    """Record torch.cuda.Event pair around the Full scan's scoring kernel."""
-    a = None if ev_start is None else ev_start.cuda_event
-    b = None if ev_stop is None else ev_stop.cuda_event
-    _check("csa2_set_scan_timer", lib().csa2_set_scan_timer(a, b))

@@ -9,8 +9,6 @@ namespace csa2 {
 
 static thread_local char t_last_error[512] = "";
 
-hipEvent_t g_scan_ev_start = nullptr;
-hipEvent_t g_scan_ev_stop = nullptr;
 
 int fail(int code, const char* fmt, ...) {
     va_list ap;
@@ -60,12 +58,4 @@ extern "C" size_t csa2_workspace_bytes(int op, int B, long long max_len, long lo
             fail(CSA2_ERR_INVALID, "csa2_workspace_bytes: unknown op %d", op);
             return 0;
     }
-}
-
-extern "C" int csa2_set_scan_timer(void* ev_start, void* ev_stop) {
-    if ((ev_start == nullptr) != (ev_stop == nullptr))
-        return fail(CSA2_ERR_INVALID, "csa2_set_scan_timer: pass both events or neither");
-    g_scan_ev_start = reinterpret_cast<hipEvent_t>(ev_start);
-    g_scan_ev_stop = reinterpret_cast<hipEvent_t>(ev_stop);
-    return CSA2_OK;
 }

@@ -26,9 +26,6 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 size_t index_full_ws_bytes(int B, long long total_len, int P);
 size_t sparse_attn_ws_bytes(int B, int Hq, int D, int k, int window);
 int sparse_attn_splits(int B, int Hq, int k, int window);
-
-// Events set by csa2_set_scan_timer (NULL when disabled).
-extern hipEvent_t g_scan_ev_start;
-extern hipEvent_t g_scan_ev_stop;
+int sparse_attn_tiles_per_wg(int B, int Hq, int k, int window);
 
 }  // namespace csa2

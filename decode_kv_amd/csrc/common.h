@@ -72,4 +72,43 @@ __device__ __forceinline__ void load_index_query(const int8_t* __restrict__ q,
     }
 }
 
+// Exact rank step of a radix select: s_key[0 .. cnt) holds distinct 64-bit
+// keys (score << 32 | ~position), cnt <= 256, in LDS.  Finds the key of rank
+// need - 1 (0 = largest) and writes its score to s_res[0], the number of
+// entries with that score ranked at or above it to s_res[1], and whether that
+// is every entry with that score to s_res[2].  Four consecutive threads rank
+// one key, each comparing it with a quarter of the keys.  Needs blockDim.x >=
+// 4 * cnt; the caller synchronises before reading s_res.
+__device__ __forceinline__ void rank_select_key(const unsigned long long* s_key, int cnt,
+                                                int need, int* s_res) {
+    const int tid = threadIdx.x;
+    if (tid >= 4 * cnt) return;                    // whole groups of four lanes
+    const unsigned long long mine = s_key[tid >> 2];
+    const int q = (cnt + 3) >> 2;
+    const int u0 = (tid & 3) * q, u1 = min(cnt, u0 + q);
+    int rank = 0;
+#pragma unroll 8
+    for (int u = u0; u < u1; ++u) rank += s_key[u] > mine;
+    rank += __shfl_xor(rank, 1);
+    rank += __shfl_xor(rank, 2);
+    if (rank != need - 1) return;                  // uniform within the group
+    const uint32_t ts = (uint32_t)(mine >> 32);
+    int ties = 0, all = 0;
+#pragma unroll 8
+    for (int u = u0; u < u1; ++u) {
+        const bool same = (uint32_t)(s_key[u] >> 32) == ts;
+        ties += same & (s_key[u] >= mine);
+        all += same;
+    }
+    ties += __shfl_xor(ties, 1);
+    ties += __shfl_xor(ties, 2);
+    all += __shfl_xor(all, 1);
+    all += __shfl_xor(all, 2);
+    if ((tid & 3) == 0) {
+        s_res[0] = (int)ts;
+        s_res[1] = ties;
+        s_res[2] = ties == all;
+    }
+}
+
 }  // namespace csa2

@@ -2,26 +2,27 @@
 // ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 2": the first
 // full-mode indexing layer searches the whole context and builds a candidate
 // pool; "How DeepSeek V4.1 Flash Actually Works", item 2: up to 16,384
-// candidate positions).
+// candidate positions).  csa2_index_score exposes the scoring stage alone.
 //
 // Five kernels, all sequences of the batch at once, tiles of 1,024 positions,
-// no device-wide atomics on hot addresses:
+// no returning device-wide atomics:
 //   1. score      stream the int8 keys once (each wave issues all of its tile
 //                 loads before scoring), int8 MFMA scoring, int32 scores to
 //                 scratch, and a per-tile histogram of a float-like key
 //                 (exponent + 5 mantissa bits, 832 bins) written with plain
 //                 stores; workgroup 0 also writes the per-sequence layout
 //   2. reduce     sum the per-tile histograms of each sequence (workgroups
-//                 split the bins), reset the candidate counters
-//   3. gather     every tile finds the bin holding the P_eff-th score, counts
-//                 its entries above that bin and appends the entries inside it
-//                 to one of 8 candidate regions (one counter per region, so the
-//                 atomics of the 8 XCDs do not queue on one address)
-//   4. threshold  one workgroup per sequence: exact select among the
-//                 candidates (14-bit digits, then exact ranking of <= 64
-//                 entries) gives the threshold T and the number of ties at T
-//                 to keep; per-tile counts and an exclusive prefix give every
-//                 tile its output offsets
+//                 split the bins), clear the second-level histogram
+//   3. gather     every tile finds the bin B1 holding the P_eff-th score,
+//                 counts its entries above B1, copies its entries inside B1 to
+//                 its own candidate slots and adds them to a 4,096-bin
+//                 histogram of the next 12 bits inside B1 (atomics whose
+//                 result is not waited for)
+//   4. threshold  one workgroup per sequence: the second-level histogram
+//                 narrows B1 to one sub-bin; its entries (<= 256, else more
+//                 12-bit passes over the candidates) are ranked exactly, giving
+//                 the threshold T and the number of ties at T to keep; per-tile
+//                 counts and an exclusive prefix give every tile its offsets
 //   5. write      ordered compaction: s > T, plus the first ties in position
 //                 order; ascending positions, tail -1
 // The result is exact and independent of the launch shape.
@@ -34,11 +35,11 @@ constexpr int kTile = 1024;
 constexpr int kScanThreads = 256;
 constexpr int kKeyBins = 832;            // float-like key of a score < 2^31
 constexpr int kRedBins = 32;             // bins per reduce workgroup
-constexpr int kRegions = 8;              // candidate regions (XCDs)
-constexpr int kThrThreads = 256;
-constexpr int kMaxTilesPerSeq = 8192;    // LDS tile counters of the threshold kernel (8M positions)
-constexpr int kRefBits = 14;
-constexpr int kRefBins = 1 << kRefBits;  // refinement digit
+constexpr int kSubBits = 12;
+constexpr int kSubBins = 1 << kSubBits;  // second-level histogram / refinement digit
+constexpr int kThrThreads = 1024;
+constexpr int kMaxTilesPerSeq = 8192;    // LDS tile tables of the threshold kernel (8M positions)
+constexpr int kRankMax = 256;            // entries ranked exactly
 constexpr int kMaxBatch = 4096;
 
 struct FullState {
@@ -46,23 +47,23 @@ struct FullState {
     int Peff;    // pool size
     int tile0;   // first global tile of this sequence
     int ntiles;  // tiles of this sequence
-    int cand0;   // first candidate slot of this sequence
-    int cap;     // slots per candidate region
     int T;       // take s > T ...
     int needT;   // ... plus the first needT entries with s == T
+    int kb;      // first-level bin holding the Peff-th score
+    int above;   // entries in higher first-level bins
 };
 static_assert(sizeof(FullState) == 32, "FullState size");
 
 struct FullWs {
     FullState* st;        // [B]
     uint32_t* hist;       // [B][kKeyBins]
-    int* cand_cnt;        // [B][kRegions]
-    int* tile_above;      // [Tmax] entries of the tile above the threshold bin
+    uint32_t* hist2;      // [B][kSubBins]
+    int* tile_above;      // [Tmax] entries of the tile above bin B1
+    int* tile_cnt;        // [Tmax] entries of the tile inside bin B1
     int* tile_off;        // [Tmax][2] output offsets among s > T and among s == T
-    int* meta;            // [0] total tiles
     uint16_t* tile_hist;  // [Tmax][kKeyBins]
-    int2* cand;           // [(Tmax + kRegions * B) * kTile] (score, position)
-    int* scores;          // [Tmax * kTile]
+    int2* cand;           // [Tmax][kTile] (score, position) inside bin B1, per tile
+    int* scores;          // [Tmax][kTile]
 };
 
 static long long full_tile_bound(int B, long long total_len) {
@@ -80,12 +81,12 @@ static size_t full_ws_layout(int B, long long total_len, char* base, FullWs* w) 
     FullWs x;
     x.st = reinterpret_cast<FullState*>(take(sizeof(FullState) * (size_t)B));
     x.hist = reinterpret_cast<uint32_t*>(take(4ull * B * kKeyBins));
-    x.cand_cnt = reinterpret_cast<int*>(take(4ull * B * kRegions));
+    x.hist2 = reinterpret_cast<uint32_t*>(take(4ull * B * kSubBins));
     x.tile_above = reinterpret_cast<int*>(take(4ull * T));
+    x.tile_cnt = reinterpret_cast<int*>(take(4ull * T));
     x.tile_off = reinterpret_cast<int*>(take(8ull * T));
-    x.meta = reinterpret_cast<int*>(take(256));
     x.tile_hist = reinterpret_cast<uint16_t*>(take(2ull * (size_t)T * kKeyBins));
-    x.cand = reinterpret_cast<int2*>(take(8ull * (size_t)(T + (long long)kRegions * B) * kTile));
+    x.cand = reinterpret_cast<int2*>(take(8ull * (size_t)T * kTile));
     x.scores = reinterpret_cast<int*>(take(4ull * (size_t)T * kTile));
     if (w) *w = x;
     return off;
@@ -116,6 +117,14 @@ __device__ __forceinline__ void key_interval(int key, int& lo, int& hi) {
     hi = (key == kKeyBins - 1) ? 0x7FFFFFFF : lo + (1 << (e - 5)) - 1;
 }
 
+// Digit of at most kSubBits bits over [lo, hi]: shift and bin count.
+__device__ __forceinline__ void sub_digit(int lo, int hi, int& sh, int& nb) {
+    const unsigned width = (unsigned)(hi - lo) + 1u;
+    const int bits = 32 - __clz(width - 1u);
+    sh = bits > kSubBits ? bits - kSubBits : 0;
+    nb = (int)(((width - 1u) >> sh) + 1u);
+}
+
 // Exclusive prefix sum of one int per thread over the block.
 template <int NT>
 __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
@@ -139,11 +148,12 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int& tota
 }
 
 // Bin holding the need-th largest entry of a histogram (bins ascending in
-// value); every thread gets (bin, entries in higher bins).  Requires
-// 1 <= need <= total count.  Thread t owns PER consecutive bins from the top.
+// value); every thread gets (bin, entries in higher bins, entries in the bin).
+// Requires 1 <= need <= total count.  Thread t owns PER consecutive bins from
+// the top.
 template <int NT, int PER, typename H>
 __device__ __forceinline__ void find_bin(const H* h, int nb, int need, int* s_tmp, int* s_res,
-                                         int& bin_out, int& above_out) {
+                                         int& bin_out, int& above_out, int& cnt_out) {
     const int r = NT - 1 - threadIdx.x;          // thread 0 owns the highest bins
     int c[PER];
     int mysum = 0;
@@ -162,6 +172,7 @@ __device__ __forceinline__ void find_bin(const H* h, int nb, int need, int* s_tm
             if (acc < need && need <= acc + c[i]) {
                 s_res[0] = r * PER + i;
                 s_res[1] = acc;
+                s_res[2] = c[i];
             }
             acc += c[i];
         }
@@ -169,13 +180,14 @@ __device__ __forceinline__ void find_bin(const H* h, int nb, int need, int* s_tm
     __syncthreads();
     bin_out = s_res[0];
     above_out = s_res[1];
+    cnt_out = s_res[2];
     __syncthreads();
 }
 
 // Tile t -> sequence, from the lengths (up to kMaxBatch sequences, 16 per
 // thread).  Returns the sequence (or -1 past the last tile) and the layout of
 // that sequence; with write_state the block also writes every sequence's
-// state and the total tile count.
+// state.
 struct TileInfo {
     int b, tile0, E;
     long long roff;
@@ -188,8 +200,8 @@ __device__ TileInfo map_tile(const int* __restrict__ len, const long long* __res
     __shared__ int s_b, s_tile0, s_E;
     __shared__ long long s_roff;
     const int first = threadIdx.x * SPT;
-    int nt[SPT], Ev[SPT], cp[SPT];
-    int sum_t = 0, sum_c = 0;
+    int nt[SPT], Ev[SPT];
+    int sum_t = 0;
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
         const int b = first + i;
@@ -200,14 +212,11 @@ __device__ TileInfo map_tile(const int* __restrict__ len, const long long* __res
         }
         Ev[i] = E;
         nt[i] = (E + kTile - 1) / kTile;
-        cp[i] = (nt[i] + kRegions - 1) / kRegions;    // tiles per candidate region
         sum_t += nt[i];
-        sum_c += cp[i];
     }
     if (threadIdx.x == 0) s_b = -1;
-    int tot_t, tot_c;
+    int tot_t;
     int pre_t = block_exclusive_scan<kScanThreads>(sum_t, s_tmp, tot_t);
-    int pre_c = block_exclusive_scan<kScanThreads>(sum_c, s_tmp, tot_c);
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
         const int b = first + i;
@@ -224,17 +233,15 @@ __device__ TileInfo map_tile(const int* __restrict__ len, const long long* __res
                 s.Peff = Ev[i] < P ? Ev[i] : P;
                 s.tile0 = pre_t;
                 s.ntiles = nt[i];
-                s.cand0 = pre_c * kRegions * kTile;
-                s.cap = cp[i] * kTile;
                 s.T = 0x7FFFFFFF;
                 s.needT = 0;
+                s.kb = 0;
+                s.above = 0;
                 w.st[b] = s;
             }
         }
         pre_t += nt[i];
-        pre_c += cp[i];
     }
-    if (write_state && threadIdx.x == 0) w.meta[0] = tot_t;
     __syncthreads();
     TileInfo r;
     r.b = s_b;
@@ -245,11 +252,13 @@ __device__ TileInfo map_tile(const int* __restrict__ len, const long long* __res
 }
 
 // ---- 1. score + per-tile histogram -------------------------------------------------
+// Scores go to score_out + (seq_stride < 0 ? t * kTile : b * seq_stride + p).
 template <int NB>
 __global__ __launch_bounds__(kScanThreads) void full_score_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ wts,
     const int8_t* __restrict__ keys, const long long* __restrict__ row_off,
-    const int* __restrict__ len, int B, int H, int window, int P, FullWs w) {
+    const int* __restrict__ len, int B, int H, int window, int P, FullWs w,
+    int* __restrict__ score_out, long long seq_stride) {
     __shared__ uint32_t s_hist[kKeyBins];
     const int t = blockIdx.x;
     const TileInfo ti = map_tile(len, row_off, B, window, P, t, w, t == 0);
@@ -265,7 +274,8 @@ __global__ __launch_bounds__(kScanThreads) void full_score_kernel(
     const int wave = threadIdx.x / kWave;
     const int p_tile = (t - ti.tile0) * kTile;                 // first position
     const int8_t* kbase = keys + ((size_t)ti.roff + p_tile) * kDk + (l >> 4) * 16;
-    int* sc_out = w.scores + (size_t)t * kTile;
+    int* sc_out = score_out + (seq_stride < 0 ? (size_t)t * kTile
+                                              : (size_t)b * (size_t)seq_stride + p_tile);
     const int nvalid = min(kTile, ti.E - p_tile);
     // wave w scores tokens [256w, 256w + 256): 16 groups of 16, all loads issued
     // before the first MFMA so 16 KB per wave are in flight
@@ -307,7 +317,8 @@ __global__ __launch_bounds__(kScanThreads) void full_reduce_kernel(FullWs w) {
     __shared__ uint32_t s_part[kScanThreads / 4][kRedBins + 1];
     const int c = blockIdx.x, b = blockIdx.y;
     const FullState st = w.st[b];
-    if (c == 0 && threadIdx.x < kRegions) w.cand_cnt[b * kRegions + threadIdx.x] = 0;
+    const int z = c * kScanThreads + threadIdx.x;              // clear the sub-bin histogram
+    if (z < kSubBins) w.hist2[(size_t)b * kSubBins + z] = 0;
     const int r = threadIdx.x >> 2, k = threadIdx.x & 3;
     uint32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     constexpr int U = 8;
@@ -352,31 +363,29 @@ __device__ int tile_seq(const FullState* __restrict__ st, int B, int t, int* s_b
     return *s_b;
 }
 
-// ---- 3. gather: entries above / inside the threshold bin ------------------------
+// ---- 3. gather: entries above / inside bin B1 --------------------------------------
 __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs w) {
     __shared__ int s_b;
     __shared__ int s_tmp[kScanThreads / kWave];
-    __shared__ int s_res[2];
+    __shared__ int s_res[3];
     const int t = blockIdx.x;
-    if (t >= w.meta[0]) return;
     const int b = tile_seq(w.st, B, t, &s_b);
     if (b < 0) return;
     const FullState st = w.st[b];
     const int p_tile = (t - st.tile0) * kTile;
     const int nvalid = min(kTile, st.E - p_tile);
     const int* sc = w.scores + (size_t)t * kTile;
-    constexpr int PER = kTile / kScanThreads;
+    constexpr int PER = kTile / kScanThreads;   // contiguous positions per thread
+    const int i0 = threadIdx.x * PER;
     int v[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int i = threadIdx.x + j * kScanThreads;
-        v[j] = i < nvalid ? sc[i] : -1;
-    }
-    int kb, above;
+    for (int j = 0; j < PER; ++j) v[j] = i0 + j < nvalid ? sc[i0 + j] : -1;
+    int kb, above, cnt;
     find_bin<kScanThreads, (kKeyBins + kScanThreads - 1) / kScanThreads>(
-        w.hist + (size_t)b * kKeyBins, kKeyBins, st.Peff, s_tmp, s_res, kb, above);
-    int lo, hi;
+        w.hist + (size_t)b * kKeyBins, kKeyBins, st.Peff, s_tmp, s_res, kb, above, cnt);
+    int lo, hi, sh, nb;
     key_interval(kb, lo, hi);
+    sub_digit(lo, hi, sh, nb);
     // per-thread counts of entries above / inside the bin, packed in one scan
     int n_above = 0, n_in = 0;
 #pragma unroll
@@ -385,181 +394,161 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
         n_in += v[j] >= lo && v[j] <= hi;
     }
     int tot;
-    const int pre = block_exclusive_scan<kScanThreads>((n_in << 16) | n_above, s_tmp, tot);
-    const int tot_in = tot >> 16;
-    const int region = t % kRegions;
+    int slot = block_exclusive_scan<kScanThreads>((n_in << 16) | n_above, s_tmp, tot) >> 16;
     if (threadIdx.x == 0) {
         w.tile_above[t] = tot & 0xFFFF;
-        s_res[0] = tot_in ? atomicAdd(&w.cand_cnt[b * kRegions + region], tot_in) : 0;
+        w.tile_cnt[t] = tot >> 16;
+        if (t == st.tile0) {
+            w.st[b].kb = kb;
+            w.st[b].above = above;
+        }
     }
-    __syncthreads();
-    int slot = s_res[0] + (pre >> 16);
-    int2* out = w.cand + st.cand0 + (size_t)region * st.cap;
+    int2* out = w.cand + (size_t)t * kTile;
+    uint32_t* h2 = w.hist2 + (size_t)b * kSubBins;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if (v[j] >= lo && v[j] <= hi) {
-            if (slot < st.cap)                         // region capacity
-                out[slot] = make_int2(v[j], p_tile + (int)threadIdx.x + j * kScanThreads);
-            ++slot;
+            out[slot++] = make_int2(v[j], p_tile + i0 + j);
+            atomicAdd(&h2[(unsigned)(v[j] - lo) >> sh], 1u);
         }
     }
 }
 
 // ---- 4. threshold: exact select among the candidates, tile offsets ---------------
 __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
-    constexpr int kWaves = kThrThreads / kWave;
-    __shared__ uint32_t s_hist[kRefBins];
-    __shared__ uint32_t s_cgt[kMaxTilesPerSeq];
-    __shared__ uint32_t s_ceq[kMaxTilesPerSeq];
-    __shared__ int s_tmp[kWaves];
+    constexpr int NT = kThrThreads;
+    constexpr int TPT = kMaxTilesPerSeq / NT;        // tiles per thread (contiguous)
+    constexpr int PER = 8;                           // candidates per thread kept in registers
+    constexpr int CHUNK = NT * PER;
+    __shared__ uint32_t s_hist[kSubBins];
+    __shared__ uint32_t s_cc[kMaxTilesPerSeq];      // per tile: (# s > T) | (# s == T) << 16
+    __shared__ int s_coff[kMaxTilesPerSeq + 1];     // exclusive prefix of the tile counts
+    __shared__ int s_tmp[NT / kWave];
     __shared__ int s_res[4];
-    __shared__ unsigned long long s_key[64];
+    __shared__ unsigned long long s_key[kRankMax];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const FullState st = w.st[b];
     if (st.Peff == 0) return;
-    // region counts and this thread's tiles' above-bin counts, loaded early
-    int rc[kRegions], rpre[kRegions + 1];
-#pragma unroll
-    for (int r = 0; r < kRegions; ++r) rc[r] = min(w.cand_cnt[b * kRegions + r], st.cap);
-    constexpr int TPT = kMaxTilesPerSeq / kThrThreads;
-    int above_t[TPT];
+    int tc[TPT], ta[TPT];
+    int csum = 0;
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
         const int i = tid * TPT + u;
-        above_t[u] = i < st.ntiles ? w.tile_above[st.tile0 + i] : 0;
+        tc[u] = i < st.ntiles ? w.tile_cnt[st.tile0 + i] : 0;
+        ta[u] = i < st.ntiles ? w.tile_above[st.tile0 + i] : 0;
+        csum += tc[u];
     }
-    rpre[0] = 0;
+    int lo, hi, sh, nb;
+    key_interval(st.kb, lo, hi);
+    sub_digit(lo, hi, sh, nb);
+    int need = st.Peff - st.above;
+    int d, a, cnt;
+    find_bin<NT, kSubBins / NT>(w.hist2 + (size_t)b * kSubBins, nb, need, s_tmp, s_res, d, a, cnt);
+    need -= a;
+    {
+        const int nlo = lo + (d << sh);
+        hi = (sh == 0) ? nlo : min(hi, nlo + (1 << sh) - 1);
+        lo = nlo;
+    }
+    // candidate index space: tile-major, s_coff[i] = first candidate of tile i
+    int nc;
+    int pre = block_exclusive_scan<NT>(csum, s_tmp, nc);
 #pragma unroll
-    for (int r = 0; r < kRegions; ++r) rpre[r + 1] = rpre[r] + rc[r];
-    const int nc = rpre[kRegions];
-    auto cand_at = [&](int i) -> int2 {              // i-th candidate over the regions
-        int r = 0;
-#pragma unroll
-        for (int x = 1; x < kRegions; ++x) r += i >= rpre[x];
-        return w.cand[(size_t)st.cand0 + (size_t)r * st.cap + (i - rpre[r])];
+    for (int u = 0; u < TPT; ++u) {
+        const int i = tid * TPT + u;
+        if (i < st.ntiles) {
+            s_coff[i] = pre;
+            s_cc[i] = 0;
+        }
+        pre += tc[u];
+    }
+    if (tid == 0) s_coff[st.ntiles] = nc;
+    __syncthreads();
+    auto cand_at = [&](int i) -> int2 {              // i-th candidate, 0 <= i < nc
+        int lo_t = 0, hi_t = st.ntiles - 1;          // last tile with s_coff <= i
+        while (lo_t < hi_t) {
+            const int mid = (lo_t + hi_t + 1) >> 1;
+            if (s_coff[mid] <= i) lo_t = mid;
+            else hi_t = mid - 1;
+        }
+        return w.cand[(size_t)(st.tile0 + lo_t) * kTile + (i - s_coff[lo_t])];
     };
-    int kb, above;
-    find_bin<kThrThreads, (kKeyBins + kThrThreads - 1) / kThrThreads>(
-        w.hist + (size_t)b * kKeyBins, kKeyBins, st.Peff, s_tmp, s_res, kb, above);
-    int lo, hi;
-    key_interval(kb, lo, hi);
-    int need = st.Peff - above;
-    int cnt = nc;                                    // entries inside [lo, hi]
-    constexpr int PER = 32;
-    constexpr int CHUNK = kThrThreads * PER;
-    // first chunk of candidates stays in registers for every pass
-    int2 c0v[PER];
+    int2 cv[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        const int i = tid + j * kThrThreads;
-        c0v[j] = i < nc ? cand_at(i) : make_int2(-1, 0);
+        const int i = tid + j * NT;
+        cv[j] = i < nc ? cand_at(i) : make_int2(-1, 0);
     }
-    // refine [lo, hi] with 14-bit digits until one value or <= 64 entries remain
-    while (lo < hi && cnt > 64) {                    // uniform: lo, hi, cnt from LDS
-        const unsigned width = (unsigned)(hi - lo) + 1u;
-        const int bits = 32 - __clz(width - 1u);
-        const int sh = bits > kRefBits ? bits - kRefBits : 0;
-        const int nb = (int)(((width - 1u) >> sh) + 1u);
-        for (int i = tid; i < nb; i += kThrThreads) s_hist[i] = 0;
+    // more 12-bit passes while the sub-bin holds several values and > kRankMax entries
+    while (lo < hi && cnt > kRankMax) {              // uniform: lo, hi, cnt from LDS
+        int sh2, nb2;
+        sub_digit(lo, hi, sh2, nb2);
+        for (int i = tid; i < nb2; i += NT) s_hist[i] = 0;
         __syncthreads();
+        auto add = [&](int v) {
+            if (v >= lo && v <= hi) atomicAdd(&s_hist[(unsigned)(v - lo) >> sh2], 1u);
+        };
 #pragma unroll
-        for (int j = 0; j < PER; ++j)
-            if (c0v[j].x >= lo && c0v[j].x <= hi) atomicAdd(&s_hist[(c0v[j].x - lo) >> sh], 1u);
-        for (int c0 = CHUNK; c0 < nc; c0 += CHUNK) {   // many candidates: stream the rest
-            for (int j = 0; j < PER; ++j) {
-                const int i = c0 + tid + j * kThrThreads;
-                if (i < nc) {
-                    const int v = cand_at(i).x;
-                    if (v >= lo && v <= hi) atomicAdd(&s_hist[(v - lo) >> sh], 1u);
-                }
-            }
-        }
+        for (int j = 0; j < PER; ++j) add(cv[j].x);
+        for (int i = CHUNK + tid; i < nc; i += NT) add(cand_at(i).x);
         __syncthreads();
-        int d, a;
-        find_bin<kThrThreads, kRefBins / kThrThreads>(s_hist, nb, need, s_tmp, s_res, d, a);
+        find_bin<NT, kSubBins / NT>(s_hist, nb2, need, s_tmp, s_res, d, a, cnt);
         need -= a;
-        cnt = (int)s_hist[d];
-        __syncthreads();
-        const int nlo = lo + (d << sh);
-        const int nhi = (sh == 0) ? nlo : min(hi, nlo + (1 << sh) - 1);
+        const int nlo = lo + (d << sh2);
+        hi = (sh2 == 0) ? nlo : min(hi, nlo + (1 << sh2) - 1);
         lo = nlo;
-        hi = nhi;
     }
     int T, needT;
     if (lo == hi) {
         T = lo;
         needT = need;
     } else {
-        // <= 64 entries in [lo, hi]: rank them by the key (score, ~position)
-        if (tid == 0) s_res[2] = 0;
+        // <= kRankMax entries in [lo, hi]: rank them by the key (score, ~position)
+        if (tid == 0) s_res[3] = 0;
         __syncthreads();
         auto put = [&](int2 v) {
             if (v.x >= lo && v.x <= hi) {
-                const int slot = atomicAdd(&s_res[2], 1);
-                if (slot < 64)
+                const int slot = atomicAdd(&s_res[3], 1);
+                if (slot < kRankMax)
                     s_key[slot] = ((unsigned long long)(uint32_t)v.x << 32) | (uint32_t)~(uint32_t)v.y;
             }
         };
 #pragma unroll
-        for (int j = 0; j < PER; ++j) put(c0v[j]);
-        for (int c0 = CHUNK; c0 < nc; c0 += CHUNK)
-            for (int j = 0; j < PER; ++j) {
-                const int i = c0 + tid + j * kThrThreads;
-                if (i < nc) put(cand_at(i));
-            }
+        for (int j = 0; j < PER; ++j) put(cv[j]);
+        for (int i = CHUNK + tid; i < nc; i += NT) put(cand_at(i));
         __syncthreads();
-        if (tid < cnt) {
-            const unsigned long long mine = s_key[tid];
-            int rank = 0;
-            for (int u = 0; u < cnt; ++u) rank += s_key[u] > mine;
-            if (rank == need - 1) {
-                const uint32_t ts = (uint32_t)(mine >> 32);
-                int ties = 0;
-                for (int u = 0; u < cnt; ++u)
-                    ties += ((uint32_t)(s_key[u] >> 32) == ts) & (s_key[u] >= mine);
-                s_res[0] = (int)ts;
-                s_res[1] = ties;
-            }
-        }
+        rank_select_key(s_key, cnt, need, s_res);
         __syncthreads();
         T = s_res[0];
         needT = s_res[1];
     }
 
     // per-tile counts of candidates above / at the threshold
-    for (int i = tid; i < st.ntiles; i += kThrThreads) {
-        s_cgt[i] = 0;
-        s_ceq[i] = 0;
-    }
-    __syncthreads();
     auto count_one = [&](int2 v) {
-        const int tile = min(max(v.y, 0) / kTile, kMaxTilesPerSeq - 1);
-        if (v.x > T) atomicAdd(&s_cgt[tile], 1u);
-        else if (v.x >= 0 && v.x == T) atomicAdd(&s_ceq[tile], 1u);
+        if (v.x < 0 || v.x < T) return;
+        const int tile = min(v.y / kTile, kMaxTilesPerSeq - 1);
+        atomicAdd(&s_cc[tile], v.x > T ? 1u : 0x10000u);
     };
 #pragma unroll
-    for (int j = 0; j < PER; ++j) count_one(c0v[j]);
-    for (int c0 = CHUNK; c0 < nc; c0 += CHUNK)
-        for (int j = 0; j < PER; ++j) {
-            const int i = c0 + tid + j * kThrThreads;
-            if (i < nc) count_one(cand_at(i));
-        }
+    for (int j = 0; j < PER; ++j) count_one(cv[j]);
+    for (int i = CHUNK + tid; i < nc; i += NT) count_one(cand_at(i));
     __syncthreads();
-    // exclusive prefix over this sequence's tiles, TPT tiles per thread
+    // exclusive prefix over this sequence's tiles
     int gl[TPT], el[TPT];
     int gs = 0, es = 0;
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
         const int i = tid * TPT + u;
-        gl[u] = i < st.ntiles ? above_t[u] + (int)s_cgt[i] : 0;
-        el[u] = i < st.ntiles ? (int)s_ceq[i] : 0;
+        const uint32_t c = i < st.ntiles ? s_cc[i] : 0u;
+        gl[u] = ta[u] + (int)(c & 0xFFFFu);
+        el[u] = (int)(c >> 16);
         gs += gl[u];
         es += el[u];
     }
     int tot;
-    int og = block_exclusive_scan<kThrThreads>(gs, s_tmp, tot);
-    int oe = block_exclusive_scan<kThrThreads>(es, s_tmp, tot);
+    int og = block_exclusive_scan<NT>(gs, s_tmp, tot);
+    int oe = block_exclusive_scan<NT>(es, s_tmp, tot);
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
         const int i = tid * TPT + u;
@@ -594,7 +583,6 @@ __global__ __launch_bounds__(kScanThreads) void full_write_kernel(int B, int P,
         }
         if (threadIdx.x == 0) pool_len[t] = Peff;
     }
-    if (t >= w.meta[0]) return;
     const int b = tile_seq(w.st, B, t, &s_b);
     if (b < 0) return;
     const FullState st = w.st[b];
@@ -643,6 +631,45 @@ __global__ __launch_bounds__(kScanThreads) void full_write_kernel(int B, int P,
     }
 }
 
+// Argument checks shared by the two entry points; CSA2_OK or an error code.
+static int check_scan_args(const char* fn, const signed char* q, const signed char* w,
+                           const signed char* keys, const long long* row_off, const int* len,
+                           int B, long long max_len, long long total_len, int H, int Dk,
+                           int window) {
+    if (B < 0 || max_len < 0 || total_len < 0)
+        return fail(CSA2_ERR_INVALID, "%s: negative size", fn);
+    if (B > kMaxBatch) return fail(CSA2_ERR_UNSUPPORTED, "%s: B > %d", fn, kMaxBatch);
+    if (B == 0) return CSA2_OK;
+    if (!q || !w || !keys || !row_off || !len)
+        return fail(CSA2_ERR_INVALID, "%s: null pointer", fn);
+    if (Dk != kDk) return fail(CSA2_ERR_UNSUPPORTED, "%s: Dk must be 64", fn);
+    if (H < 1 || H > 64) return fail(CSA2_ERR_INVALID, "%s: H must be in [1, 64]", fn);
+    if (window < 0) return fail(CSA2_ERR_INVALID, "%s: window < 0", fn);
+    if (max_len > (long long)kMaxTilesPerSeq * kTile)
+        return fail(CSA2_ERR_UNSUPPORTED, "%s: max_len > %lld", fn,
+                    (long long)kMaxTilesPerSeq * kTile);
+    if (!aligned(q, 16) || !aligned(keys, 16) || !aligned(row_off, 8) || !aligned(len, 4))
+        return fail(CSA2_ERR_INVALID, "%s: misaligned pointer", fn);
+    return CSA2_OK;
+}
+
+static int launch_score(int H, unsigned tiles, hipStream_t s, const signed char* q,
+                        const signed char* w, const signed char* keys, const long long* row_off,
+                        const int* len, int B, int window, int P, const FullWs& fw, int* out,
+                        long long seq_stride) {
+    const int8_t* q8 = reinterpret_cast<const int8_t*>(q);
+    const int8_t* w8 = reinterpret_cast<const int8_t*>(w);
+    const int8_t* k8 = reinterpret_cast<const int8_t*>(keys);
+    const dim3 grid(tiles), blk(kScanThreads);
+    switch ((H + 15) / 16) {
+        case 1: hipLaunchKernelGGL(full_score_kernel<1>, grid, blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw, out, seq_stride); break;
+        case 2: hipLaunchKernelGGL(full_score_kernel<2>, grid, blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw, out, seq_stride); break;
+        case 3: hipLaunchKernelGGL(full_score_kernel<3>, grid, blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw, out, seq_stride); break;
+        default: hipLaunchKernelGGL(full_score_kernel<4>, grid, blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw, out, seq_stride); break;
+    }
+    return launch_status("full_score");
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -653,20 +680,13 @@ extern "C" int csa2_index_full(const signed char* q, const signed char* w,
                                int H, int Dk, int window, int P, int* pool_pos,
                                int* pool_score, int* pool_len, void* ws, size_t ws_bytes,
                                void* stream) {
-    if (B < 0 || max_len < 0 || total_len < 0)
-        return fail(CSA2_ERR_INVALID, "csa2_index_full: negative size");
-    if (B > kMaxBatch) return fail(CSA2_ERR_UNSUPPORTED, "csa2_index_full: B > %d", kMaxBatch);
+    if (int e = check_scan_args("csa2_index_full", q, w, keys, row_off, len, B, max_len,
+                                total_len, H, Dk, window))
+        return e;
     if (B == 0) return CSA2_OK;
-    if (!q || !w || !keys || !row_off || !len || !pool_pos || !pool_score || !pool_len)
+    if (!pool_pos || !pool_score || !pool_len)
         return fail(CSA2_ERR_INVALID, "csa2_index_full: null pointer");
-    if (Dk != kDk) return fail(CSA2_ERR_UNSUPPORTED, "csa2_index_full: Dk must be 64");
-    if (H < 1 || H > 64) return fail(CSA2_ERR_INVALID, "csa2_index_full: H must be in [1, 64]");
-    if (P < 1 || window < 0) return fail(CSA2_ERR_INVALID, "csa2_index_full: P < 1 or window < 0");
-    if (max_len > (long long)kMaxTilesPerSeq * kTile)
-        return fail(CSA2_ERR_UNSUPPORTED, "csa2_index_full: max_len > %lld",
-                    (long long)kMaxTilesPerSeq * kTile);
-    if (!aligned(q, 16) || !aligned(keys, 16) || !aligned(row_off, 8) || !aligned(len, 4))
-        return fail(CSA2_ERR_INVALID, "csa2_index_full: misaligned pointer");
+    if (P < 1) return fail(CSA2_ERR_INVALID, "csa2_index_full: P < 1");
     const size_t need = index_full_ws_bytes(B, total_len, P);
     if (!ws || ws_bytes < need || !aligned(ws, 256))
         return fail(CSA2_ERR_WORKSPACE, "csa2_index_full: workspace needs %zu bytes (256-aligned)",
@@ -677,20 +697,9 @@ extern "C" int csa2_index_full(const signed char* q, const signed char* w,
     const unsigned tiles = (unsigned)full_tile_bound(B, total_len);
     const dim3 blk(kScanThreads);
 
-    if (g_scan_ev_start) hipEventRecord(g_scan_ev_start, s);
-    const int NB = (H + 15) / 16;
-    const int8_t* q8 = reinterpret_cast<const int8_t*>(q);
-    const int8_t* w8 = reinterpret_cast<const int8_t*>(w);
-    const int8_t* k8 = reinterpret_cast<const int8_t*>(keys);
-    switch (NB) {
-        case 1: hipLaunchKernelGGL(full_score_kernel<1>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw); break;
-        case 2: hipLaunchKernelGGL(full_score_kernel<2>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw); break;
-        case 3: hipLaunchKernelGGL(full_score_kernel<3>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw); break;
-        default: hipLaunchKernelGGL(full_score_kernel<4>, dim3(tiles), blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw); break;
-    }
-    if (int e = launch_status("full_score")) return e;
-    if (g_scan_ev_stop) hipEventRecord(g_scan_ev_stop, s);
-
+    if (int e = launch_score(H, tiles, s, q, w, keys, row_off, len, B, window, P, fw, fw.scores,
+                             -1))
+        return e;
     hipLaunchKernelGGL(full_reduce_kernel, dim3(kKeyBins / kRedBins, B), blk, 0, s, fw);
     hipLaunchKernelGGL(full_gather_kernel, dim3(tiles), blk, 0, s, B, fw);
     hipLaunchKernelGGL(full_threshold_kernel, dim3(B), dim3(kThrThreads), 0, s, fw);
@@ -698,4 +707,25 @@ extern "C" int csa2_index_full(const signed char* q, const signed char* w,
     hipLaunchKernelGGL(full_write_kernel, dim3(wgrid), blk, 0, s, B, P, pool_pos, pool_score,
                        pool_len, fw);
     return launch_status("csa2_index_full launch");
+}
+
+extern "C" int csa2_index_score(const signed char* q, const signed char* w,
+                                const signed char* keys, const long long* row_off,
+                                const int* len, int B, long long max_len, long long total_len,
+                                int H, int Dk, int window, int* score, void* ws, size_t ws_bytes,
+                                void* stream) {
+    if (int e = check_scan_args("csa2_index_score", q, w, keys, row_off, len, B, max_len,
+                                total_len, H, Dk, window))
+        return e;
+    if (B == 0) return CSA2_OK;
+    if (!score) return fail(CSA2_ERR_INVALID, "csa2_index_score: null pointer");
+    const size_t need = index_full_ws_bytes(B, total_len, 1);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+        return fail(CSA2_ERR_WORKSPACE,
+                    "csa2_index_score: workspace needs %zu bytes (256-aligned)", need);
+    FullWs fw;
+    full_ws_layout(B, total_len, reinterpret_cast<char*>(ws), &fw);
+    const unsigned tiles = (unsigned)full_tile_bound(B, total_len);
+    return launch_score(H, tiles, reinterpret_cast<hipStream_t>(stream), q, w, keys, row_off, len,
+                        B, window, 1, fw, score, max_len);
 }

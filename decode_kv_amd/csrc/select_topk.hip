@@ -9,7 +9,7 @@
 // number of ties to keep: a first histogram over a float-like 12-bit key
 // (exponent + 7 mantissa bits, so pool scores spread over many bins and the
 // LDS atomics rarely collide), then 13-bit refinement digits inside the chosen
-// bin until it holds one value or at most 64 entries, which are ranked
+// bin until it holds one value or at most 256 entries, which are ranked
 // exactly.  An ordered compaction (wave ballots plus one prefix over
 // (slot, wave) counts) writes s > T plus the first ties in list order.  Candidate lists are ascending in position, so
 // list order is position order.
@@ -53,6 +53,7 @@ __device__ __forceinline__ int sel_key(int s) {
 
 constexpr int kSelKeyBins = 3200;
 constexpr int kSelRefBins = 8192;   // 13-bit refinement digit
+constexpr int kSelRank = 256;       // entries ranked exactly
 
 // The bin holding the need-th largest entry of an LDS histogram (bins in
 // ascending value order): writes (bin, entries in higher bins) to s_res.
@@ -124,7 +125,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     __shared__ uint32_t s_hist[kSelRefBins];
     __shared__ int s_tmp[kSelWaves];
     __shared__ int s_res[4];
-    __shared__ unsigned long long s_key[64];
+    __shared__ unsigned long long s_key[kSelRank];
     __shared__ int s_cnt[PER * kSelWaves], s_pre[PER * kSelWaves];
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -143,10 +144,11 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     }
 
     int T = 0x7FFFFFFF, needT = 0;
+    bool all_ties = true;                     // every entry with s == T is taken
     if (keff > 0) {
         // pass 0: float-like key, fine enough that the atomics rarely collide
         for (int i = tid; i < kSelKeyBins; i += kSelThreads) s_hist[i] = 0;
-        if (tid == 0) s_res[2] = 0;
+        if (tid == 0) s_res[3] = 0;
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < PER; ++j)
@@ -164,8 +166,8 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
             lo = (128 + (kb & 127)) << (e - 7);
             hi = lo + (1 << (e - 7)) - 1;
         }
-        // 13-bit refinement passes until the bin is one value or holds <= 64
-        while (lo < hi && cnt > 64) {
+        // 13-bit refinement passes until the bin is one value or holds <= kSelRank
+        while (lo < hi && cnt > kSelRank) {
             const unsigned width = (unsigned)(hi - lo) + 1u;
             const int bits = 32 - __clz(width - 1u);
             const int sh = bits > 13 ? bits - 13 : 0;
@@ -189,52 +191,49 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         if (lo == hi) {
             T = lo;
             needT = need;
+            all_ties = need == cnt;
         } else {
-            // <= 64 entries in [lo, hi]: rank them by the key (score, ~index)
+            // <= kSelRank entries in [lo, hi]: rank them by the key (score, ~index)
             __syncthreads();
 #pragma unroll
             for (int j = 0; j < PER; ++j)
                 if (v[j] >= lo && v[j] <= hi) {
-                    const int slot = atomicAdd(&s_res[2], 1);
-                    s_key[slot] = ((unsigned long long)(uint32_t)v[j] << 32) |
-                                  (uint32_t)~(uint32_t)(tid + j * kSelThreads);
+                    const int slot = atomicAdd(&s_res[3], 1);
+                    if (slot < kSelRank)
+                        s_key[slot] = ((unsigned long long)(uint32_t)v[j] << 32) |
+                                      (uint32_t)~(uint32_t)(tid + j * kSelThreads);
                 }
             __syncthreads();
-            if (tid < cnt) {
-                const unsigned long long mine = s_key[tid];
-                int rank = 0;
-                for (int u = 0; u < cnt; ++u) rank += s_key[u] > mine;
-                if (rank == need - 1) {
-                    const uint32_t ts = (uint32_t)(mine >> 32);
-                    int ties = 0;             // entries of score ts ranked up to here
-                    for (int u = 0; u < cnt; ++u)
-                        ties += ((uint32_t)(s_key[u] >> 32) == ts) & (s_key[u] >= mine);
-                    s_res[0] = (int)ts;
-                    s_res[1] = ties;
-                }
-            }
+            rank_select_key(s_key, cnt, need, s_res);
             __syncthreads();
             T = s_res[0];
             needT = s_res[1];
+            all_ties = s_res[2] != 0;
         }
     }
 
-    // ordered compaction over entries i = tid + 1024 j (slot j, then thread)
-    uint64_t meq[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        meq[j] = __ballot(v[j] >= 0 && v[j] == T);
-        if (lane == 0) s_cnt[j * kSelWaves + wave] = __popcll(meq[j]);
-    }
-    slot_wave_scan(s_cnt, s_pre);
+    // ordered compaction over entries i = tid + 1024 j (slot j, then thread);
+    // ties at T are ranked in list order only when some of them are dropped
     bool take[PER];
+    if (all_ties) {
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const bool eq = (meq[j] >> lane) & 1ull;
-        const int eq_rank = s_pre[j * kSelWaves + wave] + lane_rank(meq[j]);
-        take[j] = (v[j] > T) || (eq && eq_rank < needT);
+        for (int j = 0; j < PER; ++j) take[j] = v[j] >= 0 && v[j] >= T;
+    } else {
+        uint64_t meq[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            meq[j] = __ballot(v[j] >= 0 && v[j] == T);
+            if (lane == 0) s_cnt[j * kSelWaves + wave] = __popcll(meq[j]);
+        }
+        slot_wave_scan(s_cnt, s_pre);
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const bool eq = (meq[j] >> lane) & 1ull;
+            const int eq_rank = s_pre[j * kSelWaves + wave] + lane_rank(meq[j]);
+            take[j] = (v[j] > T) || (eq && eq_rank < needT);
+        }
+        __syncthreads();
     }
-    __syncthreads();
     uint64_t mt[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {

@@ -5,11 +5,14 @@
 // to 512 global positions alongside the 128 most recent tokens).  MQA with
 // K = V = the dequantised 512-wide latent row.
 //
-// Workgroup = (split, sequence, group of 16 heads), four waves.  Per tile of
-// 32 attended rows:
-//   * gather the FP4 codes and E8M0 scales of the rows, dequantise exactly to
-//     bf16 and stage them in LDS twice: row-major (for q.v) and d-major (for
-//     p.v), so both products read contiguous 16- or 8-byte operands;
+// Workgroup = (split, sequence, group of 16 heads), four waves, up to four
+// 32-row tiles of attended rows.  All of a workgroup's global loads are issued
+// up front (sequence scalars and selection entries, then the FP4 codes and
+// scales of every tile into registers), so the gather latency is paid once.
+// Per tile:
+//   * dequantise the rows exactly to bf16 and stage them in LDS twice:
+//     row-major (for q.v) and d-major (for p.v), so both products read
+//     contiguous 16- or 8-byte operands;
 //   * S^T = V q^T on bf16 MFMA (16x16x32), fp32 accumulation, the latent
 //     dimension split over the four waves and the partial sums added in LDS;
 //   * online softmax in base 2, per head (every wave holds the full scores);
@@ -36,8 +39,9 @@ constexpr int kAttnD = 512;
 constexpr int kHeadsPerWg = 16;
 constexpr int kVjdLd = kAttnD + 8;      // bf16 per row-major row (padded)
 constexpr int kVdjLd = kAttnRows + 8;   // bf16 per d-major row (80 B: 16-B aligned)
-constexpr int kAttnMaxTilesPerWg = 16;  // rows staged per workgroup: 16 x 32
-constexpr int kAttnMaxSplits = 32;
+constexpr int kAttnMaxTilesPerWg = 4;   // tiles whose loads one workgroup keeps in flight
+constexpr int kAttnMaxRows = 16384;     // k + window
+constexpr int kAttnMinWgs = 64;         // workgroups wanted per launch
 
 // Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
 // times 2^(sb - 127), to eight bf16 (element 2i in the low half of word i).
@@ -64,7 +68,13 @@ __device__ __forceinline__ float bf16_value(uint16_t b) {
     return __builtin_bit_cast(float, (uint32_t)b << 16);
 }
 
-__global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
+// Attention of one workgroup over tiles [TPW * split, TPW * split + TPW) of
+// its sequence's attended rows.  Every global load the workgroup needs is
+// issued before the first tile is processed: the per-sequence scalars and the
+// selection entries in one round trip, then the FP4 codes and scales of all
+// TPW tiles in a second one, held in registers until their tile's turn.
+template <int TPW>
+__global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_fp4,
     const uint8_t* __restrict__ kv_scale, const long long* __restrict__ row_off,
     const int* __restrict__ len, const int* __restrict__ sel_pos,
@@ -73,33 +83,27 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     float* __restrict__ out, float* __restrict__ lse) {
     __shared__ __attribute__((aligned(16))) uint16_t s_vjd[kAttnRows * kVjdLd];
     __shared__ __attribute__((aligned(16))) uint16_t s_vdj[kAttnD * kVdjLd];
-    __shared__ long long s_rows[kAttnMaxTilesPerWg * kAttnRows];   // cache row, -1 = none
     __shared__ f32x4 s_red[kAttnThreads / kWave][2][kWave];           // S^T partial sums
 
     const int split = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
     const int g = l >> 4, c16 = l & 15;
     const int head = blockIdx.z * kHeadsPerWg + c16;      // this lane's head
+    // dequantisation work split: thread owns rows 8rg..8rg+7 x elements 8dc..8dc+7
+    const int dc = tid >> 2, rg = tid & 3;
+    const int t_begin = split * TPW;
 
-    const int L = max(0, len[b]);
-    const int win = min(window, L);
-    const int nsel = max(0, min(sel_len[b], k));
-    const int S = nsel + win;
-    const int ntile = (S + kAttnRows - 1) / kAttnRows;
-    const int t_begin = (int)((long long)split * ntile / n_splits);
-    const int t_end = (int)((long long)(split + 1) * ntile / n_splits);
+    // round trip 1: sequence scalars, this thread's selection entries, q
+    const int len_b = len[b], sel_b = sel_len[b];
     const long long roff = row_off[b];
-
-    // cache rows of this workgroup's attended positions: selection, then window
-    const int j0 = t_begin * kAttnRows, nrows = (t_end - t_begin) * kAttnRows;
-    for (int i = tid; i < nrows; i += kAttnThreads) {
-        const int j = j0 + i;
-        long long pos = -1;
-        if (j < nsel) pos = sel_pos[(size_t)b * k + j];
-        else if (j < S) pos = L - win + (j - nsel);
-        s_rows[i] = pos >= 0 ? roff + pos : -1;
-    }
-
+    int sp[TPW][8];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int j = (t_begin + t) * kAttnRows + 8 * rg + r;
+            sp[t][r] = j < k ? sel_pos[(size_t)b * k + j] : -1;
+        }
     // q . v is split over the latent dimension: wave w owns d in [128w, 128w+128)
     constexpr int kKs = kAttnD / 32 / (kAttnThreads / kWave);   // 4 k-steps per wave
     bf16x8 qb[kKs];
@@ -109,6 +113,35 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
         for (int ks = 0; ks < kKs; ++ks)
             qb[ks] = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(qh + 32 * ks));
     }
+    const int L = max(0, len_b);
+    const int win = min(window, L);
+    const int nsel = max(0, min(sel_b, k));
+    const int S = nsel + win;
+    const int ntile = (S + kAttnRows - 1) / kAttnRows;
+    const int t_end = min(t_begin + TPW, ntile);
+
+    // round trip 2: codes and scales of every row this thread dequantises
+    uint32_t codes[TPW][8], sbs[TPW][8], valid[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+        valid[t] = 0;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int j = (t_begin + t) * kAttnRows + 8 * rg + r;
+            long long pos = -1;
+            if (j < nsel) pos = sp[t][r];
+            else if (j < S) pos = L - win + (j - nsel);
+            codes[t][r] = 0;
+            sbs[t][r] = 0;
+            if (pos >= 0) {
+                const long long row = roff + pos;
+                valid[t] |= 1u << r;
+                codes[t][r] = *reinterpret_cast<const uint32_t*>(kv_fp4 + row * (kAttnD / 2) + 4 * dc);
+                sbs[t][r] = kv_scale[row * (kAttnD / 32) + (dc >> 2)];
+            }
+        }
+    }
+
     // p . v is split over the output dimension: wave w owns d-blocks [8w, 8w+8)
     constexpr int kNb = kAttnD / 16 / (kAttnThreads / kWave);   // 8 blocks of 16
     f32x4 o[kNb];
@@ -116,50 +149,33 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
     for (int nb = 0; nb < kNb; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = -INFINITY, l_run = 0.f;
 
-    // dequantisation work split: thread owns rows 8rg..8rg+7 x elements 8dc..8dc+7
-    const int dc = tid >> 2, rg = tid & 3;
-    uint32_t nx_codes[8], nx_sb[8];
-    uint32_t nx_valid = 0;
-    auto prefetch = [&](int tile) {   // issue the global loads of one tile
-        const long long first = s_rows[(tile - t_begin) * kAttnRows];   // always valid
-        nx_valid = 0;
 #pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            long long row = s_rows[(tile - t_begin) * kAttnRows + 8 * rg + r];
-            nx_valid |= (row >= 0 ? 1u : 0u) << r;
-            row = row >= 0 ? row : first;
-            nx_codes[r] = *reinterpret_cast<const uint32_t*>(kv_fp4 + row * (kAttnD / 2) + 4 * dc);
-            nx_sb[r] = kv_scale[row * (kAttnD / 32) + (dc >> 2)];
-        }
-    };
-    __syncthreads();
-    if (t_begin < t_end) prefetch(t_begin);
-
-    for (int tile = t_begin; tile < t_end; ++tile) {
-        __syncthreads();  // previous tile's LDS reads are done
+    for (int t = 0; t < TPW; ++t) {
+        const int tile = t_begin + t;
+        if (tile >= t_end) break;                           // uniform
+        if (t > 0) __syncthreads();                          // previous tile's LDS reads are done
         {
             u32x4 v[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                v[r] = fp4x8_to_bf16x8(nx_codes[r], (int)nx_sb[r]);
-                if (!((nx_valid >> r) & 1u)) v[r] = u32x4{0u, 0u, 0u, 0u};
+                v[r] = fp4x8_to_bf16x8(codes[t][r], (int)sbs[t][r]);
+                if (!((valid[t] >> r) & 1u)) v[r] = u32x4{0u, 0u, 0u, 0u};
                 *reinterpret_cast<u32x4*>(s_vjd + (8 * rg + r) * kVjdLd + 8 * dc) = v[r];
             }
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
                 const int half = (c & 1) * 16;
-                u32x4 t;
+                u32x4 tr;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const uint32_t a = (v[2 * i][c >> 1] >> half) & 0xFFFFu;
                     const uint32_t bb = (v[2 * i + 1][c >> 1] >> half) & 0xFFFFu;
-                    t[i] = a | (bb << 16);
+                    tr[i] = a | (bb << 16);
                 }
-                *reinterpret_cast<u32x4*>(s_vdj + (8 * dc + c) * kVdjLd + 8 * rg) = t;
+                *reinterpret_cast<u32x4*>(s_vdj + (8 * dc + c) * kVdjLd + 8 * rg) = tr;
             }
         }
         __syncthreads();
-        if (tile + 1 < t_end) prefetch(tile + 1);   // in flight during the MFMAs
 
         // partial S^T[row][head] over this wave's quarter of the latent dimension
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
@@ -182,15 +198,15 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
 
         // every wave now holds the full scores: head c16, rows 4g+i and 16+4g+i
         const int jt = tile * kAttnRows;
-        float t[8];
+        float ts[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            t[i] = (jt + 4 * g + i < S) ? s0[i] * scale_log2 : -INFINITY;
-            t[4 + i] = (jt + 16 + 4 * g + i < S) ? s1[i] * scale_log2 : -INFINITY;
+            ts[i] = (jt + 4 * g + i < S) ? s0[i] * scale_log2 : -INFINITY;
+            ts[4 + i] = (jt + 16 + 4 * g + i < S) ? s1[i] * scale_log2 : -INFINITY;
         }
-        float tmax = t[0];
+        float tmax = ts[0];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, t[i]);
+        for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, ts[i]);
         tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
         const float m_new = fmaxf(m_run, tmax);   // finite: every tile has a valid row
@@ -198,7 +214,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
         float p[8], psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            p[i] = exp2f(t[i] - m_new);
+            p[i] = exp2f(ts[i] - m_new);
             psum += p[i];
         }
         psum += __shfl_xor(psum, 16);
@@ -241,84 +257,108 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sparse_attn_kernel(
         if (lse && wave == 0 && g == 0)
             lse[(size_t)b * Hq + head] =
                 l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
-    } else {
-        const size_t base = ((size_t)b * n_splits + split) * Hq + head;
-        float* ob = part_o + base * kAttnD + d0;
+        return;
+    }
+    // split partial: unnormalised O, running max and sum
+    const size_t base = ((size_t)b * n_splits + split) * Hq + head;
+    float* ob = part_o + base * kAttnD + d0;
 #pragma unroll
-        for (int nb = 0; nb < kNb; ++nb) *reinterpret_cast<f32x4*>(ob + 16 * nb) = o[nb];
-        if (wave == 0 && g == 0) {
-            part_ml[base * 2 + 0] = m_run;
-            part_ml[base * 2 + 1] = l_run;
-        }
+    for (int nb = 0; nb < kNb; ++nb) *reinterpret_cast<f32x4*>(ob + 16 * nb) = o[nb];
+    if (wave == 0 && g == 0) {
+        part_ml[base * 2 + 0] = m_run;
+        part_ml[base * 2 + 1] = l_run;
     }
 }
 
 // Log-sum-exp merge of the split partials: one workgroup per (head, sequence),
-// 128 threads x 4 output elements.  Every split's (m, l, o) is loaded in one
-// round trip (up to kAttnMaxSplits splits), then merged.
-template <int NS>
+// 128 threads x 4 output elements.  Splits are taken CH at a time, each chunk
+// loaded in one round trip and folded into a running (max, sum, output) in
+// split order.  An empty split has m = -inf and contributes nothing.
+template <int CH>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            int Hq, int n_splits,
                                                            float* __restrict__ out,
                                                            float* __restrict__ lse) {
     const int h = blockIdx.x, b = blockIdx.y;
-    float ms[NS], ls[NS];
-    f32x4 os[NS];
+    float M = -INFINITY, lsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < n_splits; c0 += CH) {
+        float ms[CH], ls[CH];
+        f32x4 os[CH];
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-        const int s = min(u, n_splits - 1);
-        const size_t base = ((size_t)b * n_splits + s) * Hq + h;
-        ms[u] = part_ml[base * 2];
-        ls[u] = part_ml[base * 2 + 1];
-        os[u] = *reinterpret_cast<const f32x4*>(part_o + base * kAttnD + 4 * threadIdx.x);
+        for (int u = 0; u < CH; ++u) {
+            const int s = min(c0 + u, n_splits - 1);
+            const size_t row = ((size_t)b * n_splits + s) * Hq + h;
+            ms[u] = part_ml[row * 2];
+            ls[u] = part_ml[row * 2 + 1];
+            os[u] = *reinterpret_cast<const f32x4*>(part_o + row * kAttnD + 4 * threadIdx.x);
+        }
+        float Mc = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < CH; ++u)
+            if (c0 + u < n_splits) Mc = fmaxf(Mc, ms[u]);
+        if (Mc == -INFINITY) continue;                // nothing attended in this chunk
+        const float Mn = fmaxf(M, Mc);
+        const float sc = exp2f(M - Mn);               // 0 while M = -inf
+        lsum *= sc;
+        acc *= sc;
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            if (c0 + u < n_splits) {
+                const float wgt = exp2f(ms[u] - Mn);   // 0 for an empty split
+                lsum += wgt * ls[u];
+                acc += wgt * os[u];
+            }
+        }
+        M = Mn;
     }
-    float M = -INFINITY;
-#pragma unroll
-    for (int u = 0; u < NS; ++u)
-        if (u < n_splits) M = fmaxf(M, ms[u]);
     float* o = out + ((size_t)b * Hq + h) * kAttnD + 4 * threadIdx.x;
-    if (M == -INFINITY) {                         // nothing attended
+    if (M == -INFINITY) {                             // nothing attended
         *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
         if (lse && threadIdx.x == 0) lse[(size_t)b * Hq + h] = -INFINITY;
         return;
-    }
-    float lsum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-        if (u < n_splits) {
-            const float wgt = exp2f(ms[u] - M);   // 0 for an empty split
-            lsum += wgt * ls[u];
-            acc += wgt * os[u];
-        }
     }
     *reinterpret_cast<f32x4*>(o) = acc / lsum;
     if (lse && threadIdx.x == 0)
         lse[(size_t)b * Hq + h] = (M + log2f(lsum)) * 0.69314718055994531f;
 }
 
-int sparse_attn_splits(int B, int Hq, int k, int window) {
-    // Enough workgroups to cover the chip at small batch (one 32-row tile per
-    // split at B = 1); never more splits than tiles, never more than
-    // kAttnMaxTilesPerWg tiles staged per workgroup.
+// Tiles per workgroup: the most (up to 4) that still leave at least
+// kAttnMinWgs workgroups for the chip, so small batches spread the selection
+// over many CUs and large batches amortise each workgroup's set-up.
+int sparse_attn_tiles_per_wg(int B, int Hq, int k, int window) {
     const int tiles = (k + window + kAttnRows - 1) / kAttnRows;
-    const int n_hg = (Hq + kHeadsPerWg - 1) / kHeadsPerWg;
-    const long long wgs = (long long)(B > 0 ? B : 1) * n_hg;
-    int want = (int)((512 + wgs - 1) / wgs);
-    if (want > tiles) want = tiles;
-    if (want > kAttnMaxSplits) want = kAttnMaxSplits;
-    const int min_splits = (tiles + kAttnMaxTilesPerWg - 1) / kAttnMaxTilesPerWg;
-    if (want < min_splits) want = min_splits;
-    return want < 1 ? 1 : want;
+    const long long wgs = (long long)(B > 0 ? B : 1) * ((Hq + kHeadsPerWg - 1) / kHeadsPerWg);
+    for (int tpw = kAttnMaxTilesPerWg; tpw > 1; tpw /= 2)
+        if (wgs * ((tiles + tpw - 1) / tpw) >= kAttnMinWgs) return tpw;
+    return 1;
+}
+
+int sparse_attn_splits(int B, int Hq, int k, int window) {
+    const int tiles = (k + window + kAttnRows - 1) / kAttnRows;
+    const int tpw = sparse_attn_tiles_per_wg(B, Hq, k, window);
+    const int ns = (tiles + tpw - 1) / tpw;
+    return ns < 1 ? 1 : ns;
+}
+
+// Workspace: the partial O, then (m, l), of every (sequence, split, head).
+static size_t attn_ws_layout(int B, int Hq, int ns, char* base, float** part_o,
+                             float** part_ml) {
+    const size_t n = (size_t)B * ns * Hq;
+    const size_t o_bytes = round_up(n * kAttnD * 4, 256);
+    if (base) {
+        *part_o = reinterpret_cast<float*>(base);
+        *part_ml = reinterpret_cast<float*>(base + o_bytes);
+    }
+    return o_bytes + round_up(n * 2 * 4, 256);
 }
 
 size_t sparse_attn_ws_bytes(int B, int Hq, int D, int k, int window) {
     (void)D;
     const int ns = sparse_attn_splits(B, Hq, k, window);
     if (ns <= 1) return 0;
-    const size_t n = (size_t)B * ns * Hq;
-    return round_up(n * kAttnD * 4, 256) + round_up(n * 2 * 4, 256);
+    return attn_ws_layout(B, Hq, ns, nullptr, nullptr, nullptr);
 }
 
 }  // namespace csa2
@@ -343,9 +383,9 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
     if (B > 65535 || Hq > 1024) return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: B or Hq too large");
     if (!aligned(q_bf16, 16) || !aligned(kv_fp4, 4) || !aligned(out, 16) || !aligned(row_off, 8))
         return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: misaligned pointer");
-    if ((long long)k + window > (long long)kAttnMaxSplits * kAttnMaxTilesPerWg * kAttnRows)
-        return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: k + window > %d",
-                    kAttnMaxSplits * kAttnMaxTilesPerWg * kAttnRows);
+    if ((long long)k + window > kAttnMaxRows)
+        return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: k + window > %d", kAttnMaxRows);
+    const int tpw = sparse_attn_tiles_per_wg(B, Hq, k, window);
     const int ns = sparse_attn_splits(B, Hq, k, window);
     const size_t need = sparse_attn_ws_bytes(B, Hq, D, k, window);
     if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
@@ -354,27 +394,23 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     float* part_o = nullptr;
     float* part_ml = nullptr;
-    if (ns > 1) {
-        part_o = reinterpret_cast<float*>(ws);
-        const size_t n = (size_t)B * ns * Hq;
-        part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + round_up(n * kAttnD * 4, 256));
-    }
+    if (ns > 1) attn_ws_layout(B, Hq, ns, reinterpret_cast<char*>(ws), &part_o, &part_ml);
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-    const dim3 grid(ns, B, (Hq + kHeadsPerWg - 1) / kHeadsPerWg);
-    hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(kAttnThreads), 0, s,
-                       reinterpret_cast<const uint16_t*>(q_bf16), kv_fp4, kv_scale, row_off, len,
-                       sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse);
+    const dim3 grid(ns, B, (Hq + kHeadsPerWg - 1) / kHeadsPerWg), blk(kAttnThreads);
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q_bf16);
+    switch (tpw) {
+        case 1: hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse); break;
+        case 2: hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse); break;
+        default: hipLaunchKernelGGL(sparse_attn_kernel<4>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse); break;
+    }
     if (int e = launch_status("csa2_sparse_attn_decode launch")) return e;
     if (ns > 1) {
         if (ns <= 8)
             hipLaunchKernelGGL(attn_combine_kernel<8>, dim3(Hq, B), dim3(128), 0, s, part_o,
                                part_ml, Hq, ns, out, lse);
-        else if (ns <= 16)
+        else
             hipLaunchKernelGGL(attn_combine_kernel<16>, dim3(Hq, B), dim3(128), 0, s, part_o,
                                part_ml, Hq, ns, out, lse);
-        else
-            hipLaunchKernelGGL(attn_combine_kernel<kAttnMaxSplits>, dim3(Hq, B), dim3(128), 0, s,
-                               part_o, part_ml, Hq, ns, out, lse);
         return launch_status("csa2_sparse_attn_decode combine launch");
     }
     return CSA2_OK;

@@ -129,6 +129,25 @@ int csa2_index_full(const signed char* q, const signed char* w, const signed cha
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * csa2_index_score -- the scoring stage of csa2_index_full alone: the exact
+ * index score of every eligible position p < E_b = max(len[b] - window, 0),
+ *   score[b][p] = sum_h w[b][h] * max(0, q[b][h] . keys[row_off[b] + p]).
+ * ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 2": the indexer
+ * scores the context with a small int8 query per head; the score is the
+ * weighted sum of the per-head ReLU dot products.)
+ *   q, w, keys, row_off, len, max_len, total_len, H, Dk, window: as
+ *            csa2_index_full (window = 0 scores every cached position).
+ *   score    [B][max_len] int32 out; entries p >= E_b are not written.
+ *   ws, ws_bytes: as csa2_index_full (same size query, P ignored);
+ *            no initialisation needed, contents not preserved.
+ * Requires Dk == 64, 1 <= H <= 64, max_len <= 8,388,608.
+ */
+int csa2_index_score(const signed char* q, const signed char* w, const signed char* keys,
+                     const long long* row_off, const int* len, int B, long long max_len,
+                     long long total_len, int H, int Dk, int window, int* score,
+                     void* ws, size_t ws_bytes, void* stream);
+
+/*
  * csa2_index_reindex -- Reindex mode: re-score only the candidate list with
  * this layer's own index query and weights, reading the same index keys.
  * ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 2": later layers
@@ -181,7 +200,8 @@ int csa2_select_topk(const int* score, const int* cand_pos, const int* cand_len,
  * The selection is split across workgroups and the partial softmax states
  * are merged with a log-sum-exp combine, so fp32 results are deterministic
  * for a given (B, Hq, k, window).  A sequence with L_b == 0 gets out = 0 and
- * lse = -inf.  Requires D == 512, Hq % 16 == 0, 1 <= Hq <= 128, k >= 0.
+ * lse = -inf.  Requires D == 512, Hq a positive multiple of 16 (<= 1024), k >= 0,
+ * k + window <= 16384.
  */
 int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* kv_fp4,
                             const unsigned char* kv_scale, const long long* row_off,
@@ -190,14 +210,6 @@ int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* kv_fp4,
                             float sm_scale, float* out, float* lse,
                             void* ws, size_t ws_bytes, void* stream);
 
-/*
- * Profiling hook: when both events are non-NULL, csa2_index_full records
- * ev_start immediately before and ev_stop immediately after its scoring
- * kernel (the one that streams the index keys) on the call's stream, so a
- * caller can time that kernel alone.  The events are hipEvent_t passed as
- * void*.  Pass NULLs to disable.  Process-wide; not for concurrent use.
- */
-int csa2_set_scan_timer(void* ev_start, void* ev_stop);
 
 #ifdef __cplusplus
 }

@@ -19,7 +19,8 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = csa2.header_functions()
-    assert {"csa2_kv_append_fp4", "csa2_index_full", "csa2_index_reindex", "csa2_select_topk",
+    assert {"csa2_kv_append_fp4", "csa2_index_full", "csa2_index_score", "csa2_index_reindex",
+            "csa2_select_topk",
             "csa2_sparse_attn_decode", "csa2_workspace_bytes", "csa2_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -80,6 +81,25 @@ def test_index_full_rejects_bad_arguments(lib):
     assert _full(lib, max_len=1 << 31) == csa2.CSA2_ERR_UNSUPPORTED
 
 
+def test_index_score_rejects_bad_arguments(lib):
+    f = lib.csa2_index_score
+    a = [256, 256, 256, 256, 256, 1, 4096, 4096, 64, 64, 0, 256, 256, 1 << 40, None]
+    assert f(*a[:5], 0, *a[6:]) == csa2.CSA2_OK                    # B == 0: no-op
+    bad = list(a)
+    bad[11] = None                                                  # score
+    assert f(*bad) == csa2.CSA2_ERR_INVALID
+    bad = list(a)
+    bad[9] = 128                                                    # Dk
+    assert f(*bad) == csa2.CSA2_ERR_UNSUPPORTED
+    bad = list(a)
+    bad[10] = -1                                                    # window
+    assert f(*bad) == csa2.CSA2_ERR_INVALID
+    bad = list(a)
+    bad[13] = 64                                                    # ws_bytes
+    assert f(*bad) == csa2.CSA2_ERR_WORKSPACE
+    assert "csa2_index_score" in csa2.last_error()
+
+
 def test_reindex_select_attention_reject_bad_arguments(lib):
     r = lib.csa2_index_reindex
     assert r(256, 256, 256, 256, 256, 256, 1, 64, 64, 0, 256, None) == csa2.CSA2_ERR_INVALID
@@ -101,5 +121,3 @@ def test_reindex_select_attention_reject_bad_arguments(lib):
     no_ws = list(args)
     no_ws[16] = None
     assert a(*no_ws) == csa2.CSA2_ERR_WORKSPACE
-    assert lib.csa2_set_scan_timer(256, None) == csa2.CSA2_ERR_INVALID
-    assert lib.csa2_set_scan_timer(None, None) == csa2.CSA2_OK

@@ -190,6 +190,60 @@ def test_index_full_tie_adversarial():
     check_full(keys, [0], [L], onehot, w1, W_, P, "scores = relu(K[:,0])")
 
 
+def test_index_full_clustered_scores():
+    """Many distinct scores inside one second-level sub-bin, so the threshold
+    needs further refinement passes before exact ranking."""
+    rng = np.random.default_rng(5)
+    L, W_ = 9000, 128
+    keys = np.zeros((L, 64), dtype=np.int8)
+    keys[:, 0] = 50
+    hot = rng.choice(L - W_, 1000, replace=False)
+    keys[hot, 0] = 127
+    q = np.zeros((1, 64, 64), dtype=np.int8)
+    q[0, 1:, 0] = 127
+    q[0, 0, 1] = 1
+    w = np.full((1, 64), 15, dtype=np.int8)
+    w[0, 0] = 1
+    # score = 120015 * k0 + relu(k1): 1,000 scores within 64 of each other
+    keys[:, 1] = rng.integers(0, 64, size=L)
+    check_full(keys, [0], [L], q, w, W_, 700, "64 close values")
+    keys[:, 1] = rng.integers(0, 2, size=L)
+    check_full(keys, [0], [L], q, w, W_, 700, "two close values, many ties")
+    keys[:, 1] = rng.integers(0, 300, size=L)
+    check_full(keys, [0], [L], q, w, W_, 999, "300 close values")
+
+
+def test_index_score_matches_oracle():
+    rng = np.random.default_rng(13)
+    lens = [0, 1, 1023, 1024, 1025, 70001, 3000]
+    row_off, cur = [], 0
+    for L in lens:
+        cur += 3
+        row_off.append(cur)
+        cur += L
+    keys_np = rng.integers(-127, 128, size=(cur, 64)).astype(np.int8)
+    B, H = len(lens), 64
+    q_np = rng.integers(-127, 128, size=(B, H, 64)).astype(np.int8)
+    w_np = rng.integers(0, 16, size=(B, H)).astype(np.int8)
+    keys = torch.from_numpy(keys_np).to(DEV)
+    ro = torch.tensor(row_off, dtype=torch.int64, device=DEV)
+    ln = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q = torch.from_numpy(q_np).to(DEV)
+    w = torch.from_numpy(w_np).to(DEV)
+    max_len = max(lens)
+    ws = csa2.workspace(csa2.workspace_bytes(csa2.OP_INDEX_FULL, B, max_len, cur, H, 1))
+    for window in [0, 128]:
+        out = torch.full((B, max_len), -7, dtype=torch.int32, device=DEV)
+        csa2.index_score(q, w, keys, ro, ln, max_len, cur, window, out, ws)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for b, L in enumerate(lens):
+            E = max(L - window, 0)
+            ref = oracle.index_scores(keys_np, row_off[b] + np.arange(E), q_np[b], w_np[b])
+            assert np.array_equal(got[b, :E], ref), (window, b)
+            assert (got[b, E:] == -7).all(), (window, b)
+
+
 def test_index_full_ragged_batch_and_edges():
     rng = np.random.default_rng(11)
     lens = [0, 100, 128, 129, 1152, 1153, 2048 * 3 + 128 + 17, 70001, 5000]
@@ -280,19 +334,26 @@ def test_select_topk_matches_oracle(span):
 # ---------------------------------------------------------------------------
 
 def run_attention(codes, scales, row_off, lens, sel, sel_len, q_bits, k, window):
+    """Two calls on one workspace: the second (into fresh NaN outputs) must be
+    bit-identical, which also shows the first left its split counters reset."""
     B, Hq, D = q_bits.shape
     qt = torch.from_numpy(q_bits.view(np.int16)).to(DEV).view(torch.bfloat16)
-    out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=DEV)
-    lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
     ws = csa2.workspace(csa2.workspace_bytes(csa2.OP_SPARSE_ATTN, B, 0, 0, 0, 0, k, Hq, D, window))
-    csa2.sparse_attn_decode(qt, torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
-                            torch.tensor(row_off, dtype=torch.int64, device=DEV),
-                            torch.tensor(lens, dtype=torch.int32, device=DEV), max(lens + [0]),
-                            torch.from_numpy(sel).to(DEV),
-                            torch.tensor(sel_len, dtype=torch.int32, device=DEV), k, window,
-                            1 / math.sqrt(D), out, lse, ws)
-    torch.cuda.synchronize()
-    return out.cpu().numpy(), lse.cpu().numpy()
+    args = (torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+            torch.tensor(row_off, dtype=torch.int64, device=DEV),
+            torch.tensor(lens, dtype=torch.int32, device=DEV), max(lens + [0]),
+            torch.from_numpy(sel).to(DEV), torch.tensor(sel_len, dtype=torch.int32, device=DEV),
+            k, window, 1 / math.sqrt(D))
+    res = []
+    for _ in range(2):
+        out = torch.full((B, Hq, D), float("nan"), dtype=torch.float32, device=DEV)
+        lse = torch.full((B, Hq), float("nan"), dtype=torch.float32, device=DEV)
+        csa2.sparse_attn_decode(qt, *args, out, lse, ws)
+        torch.cuda.synchronize()
+        res.append((out.cpu().numpy(), lse.cpu().numpy()))
+    assert np.array_equal(res[0][0], res[1][0], equal_nan=True)
+    assert np.array_equal(res[0][1], res[1][1], equal_nan=True)
+    return res[0]
 
 
 def attention_case(seed, lens, k, Hq, scale_lo=118, scale_hi=130, window=128):
@@ -330,6 +391,11 @@ def test_attention_small_heads_and_short_contexts():
     attention_case(12, [5000] * 3, 64, 128)
     attention_case(13, [100000], 512, 64, window=0)
     attention_case(14, [3000] * 32, 512, 64)
+
+
+def test_attention_many_splits():
+    attention_case(15, [40000], 8192, 64)           # 260 tiles over 65 splits
+    attention_case(16, [20000, 300, 9000], 2048, 32)
 
 
 def test_attention_scale_ranges():

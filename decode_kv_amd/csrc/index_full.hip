@@ -195,10 +195,34 @@ struct TileInfo {
 
 __device__ TileInfo map_tile(const int* __restrict__ len, const long long* __restrict__ row_off,
                              int B, int window, int P, int t, FullWs w, bool write_state) {
-    constexpr int SPT = kMaxBatch / kScanThreads;         // sequences per thread
     __shared__ int s_tmp[kScanThreads / kWave];
     __shared__ int s_b, s_tile0, s_E;
     __shared__ long long s_roff;
+    TileInfo r;
+    if (B == 1) {                                         // one sequence: no scan
+        const int L = len[0];
+        const long long roff = row_off[0];
+        const int E = L > window ? L - window : 0;
+        const int nt = (E + kTile - 1) / kTile;
+        if (write_state && threadIdx.x == 0) {
+            FullState s;
+            s.E = E;
+            s.Peff = E < P ? E : P;
+            s.tile0 = 0;
+            s.ntiles = nt;
+            s.T = 0x7FFFFFFF;
+            s.needT = 0;
+            s.kb = 0;
+            s.above = 0;
+            w.st[0] = s;
+        }
+        r.b = t < nt ? 0 : -1;
+        r.tile0 = 0;
+        r.E = E;
+        r.roff = roff;
+        return r;
+    }
+    constexpr int SPT = kMaxBatch / kScanThreads;         // sequences per thread
     const int first = threadIdx.x * SPT;
     int nt[SPT], Ev[SPT];
     int sum_t = 0;
@@ -243,7 +267,6 @@ __device__ TileInfo map_tile(const int* __restrict__ len, const long long* __res
         pre_t += nt[i];
     }
     __syncthreads();
-    TileInfo r;
     r.b = s_b;
     r.tile0 = s_tile0;
     r.E = s_E;

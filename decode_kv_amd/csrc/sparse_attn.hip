@@ -42,6 +42,7 @@ constexpr int kVdjLd = kAttnRows + 8;   // bf16 per d-major row (80 B: 16-B alig
 constexpr int kAttnMaxTilesPerWg = 4;   // tiles whose loads one workgroup keeps in flight
 constexpr int kAttnMaxRows = 16384;     // k + window
 constexpr int kAttnMinWgs = 64;         // workgroups wanted per launch
+constexpr int kAttnMaxSplits = kAttnMaxRows / kAttnRows;   // one tile per split at most
 
 // Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
 // times 2^(sb - 127), to eight bf16 (element 2i in the low half of word i).
@@ -271,53 +272,59 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
 }
 
 // Log-sum-exp merge of the split partials: one workgroup per (head, sequence),
-// 128 threads x 4 output elements.  Splits are taken CH at a time, each chunk
-// loaded in one round trip and folded into a running (max, sum, output) in
-// split order.  An empty split has m = -inf and contributes nothing.
+// 128 threads x 4 output elements.  Every split's (m, l) is read with one
+// vector load (thread s takes split s) and shared through LDS, while each
+// thread's partial outputs of up to CH splits are in flight at the same time,
+// so the merge costs one memory round trip; splits beyond CH follow in further
+// chunks.  Splits are folded in split order; an empty split has m = -inf and
+// contributes nothing.
 template <int CH>
 __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml,
                                                            int Hq, int n_splits,
                                                            float* __restrict__ out,
                                                            float* __restrict__ lse) {
+    __shared__ float2 s_ml[kAttnMaxSplits];
     const int h = blockIdx.x, b = blockIdx.y;
-    float M = -INFINITY, lsum = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c0 = 0; c0 < n_splits; c0 += CH) {
-        float ms[CH], ls[CH];
-        f32x4 os[CH];
+    const size_t row0 = (size_t)b * n_splits * Hq + h;          // split s at row0 + s * Hq
+    for (int s = threadIdx.x; s < n_splits; s += 128)
+        s_ml[s] = *reinterpret_cast<const float2*>(part_ml + (row0 + (size_t)s * Hq) * 2);
+    f32x4 os[CH];
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            const int s = min(c0 + u, n_splits - 1);
-            const size_t row = ((size_t)b * n_splits + s) * Hq + h;
-            ms[u] = part_ml[row * 2];
-            ls[u] = part_ml[row * 2 + 1];
-            os[u] = *reinterpret_cast<const f32x4*>(part_o + row * kAttnD + 4 * threadIdx.x);
-        }
-        float Mc = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < CH; ++u)
-            if (c0 + u < n_splits) Mc = fmaxf(Mc, ms[u]);
-        if (Mc == -INFINITY) continue;                // nothing attended in this chunk
-        const float Mn = fmaxf(M, Mc);
-        const float sc = exp2f(M - Mn);               // 0 while M = -inf
-        lsum *= sc;
-        acc *= sc;
-#pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            if (c0 + u < n_splits) {
-                const float wgt = exp2f(ms[u] - Mn);   // 0 for an empty split
-                lsum += wgt * ls[u];
-                acc += wgt * os[u];
-            }
-        }
-        M = Mn;
+    for (int u = 0; u < CH; ++u) {
+        const int s = min(u, n_splits - 1);
+        os[u] = *reinterpret_cast<const f32x4*>(part_o + (row0 + (size_t)s * Hq) * kAttnD +
+                                                4 * threadIdx.x);
     }
+    __syncthreads();
+    float M = -INFINITY;
+    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, s_ml[s].x);
     float* o = out + ((size_t)b * Hq + h) * kAttnD + 4 * threadIdx.x;
-    if (M == -INFINITY) {                             // nothing attended
+    if (M == -INFINITY) {                                       // nothing attended
         *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
         if (lse && threadIdx.x == 0) lse[(size_t)b * Hq + h] = -INFINITY;
         return;
+    }
+    float lsum = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < n_splits; c0 += CH) {
+        if (c0 > 0) {
+#pragma unroll
+            for (int u = 0; u < CH; ++u) {
+                const int s = min(c0 + u, n_splits - 1);
+                os[u] = *reinterpret_cast<const f32x4*>(part_o + (row0 + (size_t)s * Hq) * kAttnD +
+                                                        4 * threadIdx.x);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < CH; ++u) {
+            if (c0 + u < n_splits) {
+                const float2 ml = s_ml[c0 + u];
+                const float wgt = exp2f(ml.x - M);                // 0 for an empty split
+                lsum += wgt * ml.y;
+                acc += wgt * os[u];
+            }
+        }
     }
     *reinterpret_cast<f32x4*>(o) = acc / lsum;
     if (lse && threadIdx.x == 0)
@@ -409,7 +416,7 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
             hipLaunchKernelGGL(attn_combine_kernel<8>, dim3(Hq, B), dim3(128), 0, s, part_o,
                                part_ml, Hq, ns, out, lse);
         else
-            hipLaunchKernelGGL(attn_combine_kernel<16>, dim3(Hq, B), dim3(128), 0, s, part_o,
+            hipLaunchKernelGGL(attn_combine_kernel<32>, dim3(Hq, B), dim3(128), 0, s, part_o,
                                part_ml, Hq, ns, out, lse);
         return launch_status("csa2_sparse_attn_decode combine launch");
     }

@@ -72,6 +72,12 @@ __device__ __forceinline__ void load_index_query(const int8_t* __restrict__ q,
     }
 }
 
+// Rank of this lane among the set lanes of a wave mask (lanes below it).
+__device__ __forceinline__ int lane_rank64(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // Exact rank step of a radix select: s_key[0 .. cnt) holds distinct 64-bit
 // keys (score << 32 | ~position), cnt <= 256, in LDS.  Finds the key of rank
 // need - 1 (0 = largest) and writes its score to s_res[0], the number of

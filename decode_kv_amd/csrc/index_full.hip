@@ -149,20 +149,16 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int& tota
 
 // Bin holding the need-th largest entry of a histogram (bins ascending in
 // value); every thread gets (bin, entries in higher bins, entries in the bin).
-// Requires 1 <= need <= total count.  Thread t owns PER consecutive bins from
-// the top.
-template <int NT, int PER, typename H>
-__device__ __forceinline__ void find_bin(const H* h, int nb, int need, int* s_tmp, int* s_res,
-                                         int& bin_out, int& above_out, int& cnt_out) {
+// Requires 1 <= need <= total count.  Thread t owns the PER consecutive bins
+// starting at (NT - 1 - t) * PER, whose counts it passes in c.
+template <int NT, int PER>
+__device__ __forceinline__ void find_bin_counts(const int (&c)[PER], int need, int* s_tmp,
+                                                int* s_res, int& bin_out, int& above_out,
+                                                int& cnt_out) {
     const int r = NT - 1 - threadIdx.x;          // thread 0 owns the highest bins
-    int c[PER];
     int mysum = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        const int bin = r * PER + i;
-        c[i] = bin < nb ? (int)h[bin] : 0;
-        mysum += c[i];
-    }
+    for (int i = 0; i < PER; ++i) mysum += c[i];
     int tot;
     const int above = block_exclusive_scan<NT>(mysum, s_tmp, tot);
     if (above < need && need <= above + mysum) {
@@ -182,6 +178,19 @@ __device__ __forceinline__ void find_bin(const H* h, int nb, int need, int* s_tm
     above_out = s_res[1];
     cnt_out = s_res[2];
     __syncthreads();
+}
+
+template <int NT, int PER, typename H>
+__device__ __forceinline__ void find_bin(const H* h, int nb, int need, int* s_tmp, int* s_res,
+                                         int& bin_out, int& above_out, int& cnt_out) {
+    const int r = NT - 1 - threadIdx.x;
+    int c[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int bin = r * PER + i;
+        c[i] = bin < nb ? (int)h[bin] : 0;
+    }
+    find_bin_counts<NT, PER>(c, need, s_tmp, s_res, bin_out, above_out, cnt_out);
 }
 
 // Tile t -> sequence, from the lengths (up to kMaxBatch sequences, 16 per
@@ -438,83 +447,118 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
 }
 
 // ---- 4. threshold: exact select among the candidates, tile offsets ---------------
+// One workgroup per sequence.  Tile i belongs to thread i mod 1,024 (round u =
+// i / 1,024).  The candidates are copied once into LDS in tile order (slot
+// owners first, so every thread then issues its global loads at once); past
+// kCandLds entries they are read from global memory through a binary search
+// over the tile offsets.
 __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
     constexpr int NT = kThrThreads;
-    constexpr int TPT = kMaxTilesPerSeq / NT;        // tiles per thread (contiguous)
-    constexpr int PER = 8;                           // candidates per thread kept in registers
-    constexpr int CHUNK = NT * PER;
+    constexpr int TPT = kMaxTilesPerSeq / NT;        // tile rounds
+    constexpr int HPT = kSubBins / NT;               // sub-bins per thread
+    constexpr int kCandLds = 8192;                   // candidates staged in LDS
+    constexpr int SPT = kCandLds / NT;               // LDS slots per thread
     __shared__ uint32_t s_hist[kSubBins];
     __shared__ uint32_t s_cc[kMaxTilesPerSeq];      // per tile: (# s > T) | (# s == T) << 16
-    __shared__ int s_coff[kMaxTilesPerSeq + 1];     // exclusive prefix of the tile counts
+    __shared__ int s_coff[kMaxTilesPerSeq + 1];     // first candidate of each tile
+    __shared__ int2 s_cand[kCandLds];               // (score, position); first holds slot owners
     __shared__ int s_tmp[NT / kWave];
     __shared__ int s_res[4];
     __shared__ unsigned long long s_key[kRankMax];
+    uint32_t* s_owner = reinterpret_cast<uint32_t*>(s_cand);   // tile << 10 | index in tile
     const int b = blockIdx.x;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    // the second-level histogram's address needs no state: load it first
+    int h2[HPT];
+#pragma unroll
+    for (int i = 0; i < HPT; ++i)
+        h2[i] = (int)w.hist2[(size_t)b * kSubBins + (NT - 1 - tid) * HPT + i];
     const FullState st = w.st[b];
     if (st.Peff == 0) return;
+    const int rounds = (st.ntiles + NT - 1) / NT;    // uniform
     int tc[TPT], ta[TPT];
-    int csum = 0;
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
-        const int i = tid * TPT + u;
+        const int i = tid + u * NT;
         tc[u] = i < st.ntiles ? w.tile_cnt[st.tile0 + i] : 0;
         ta[u] = i < st.ntiles ? w.tile_above[st.tile0 + i] : 0;
-        csum += tc[u];
     }
     int lo, hi, sh, nb;
     key_interval(st.kb, lo, hi);
     sub_digit(lo, hi, sh, nb);
     int need = st.Peff - st.above;
     int d, a, cnt;
-    find_bin<NT, kSubBins / NT>(w.hist2 + (size_t)b * kSubBins, nb, need, s_tmp, s_res, d, a, cnt);
+    find_bin_counts<NT, HPT>(h2, need, s_tmp, s_res, d, a, cnt);   // sub-bins >= nb hold 0
     need -= a;
     {
         const int nlo = lo + (d << sh);
         hi = (sh == 0) ? nlo : min(hi, nlo + (1 << sh) - 1);
         lo = nlo;
     }
-    // candidate index space: tile-major, s_coff[i] = first candidate of tile i
-    int nc;
-    int pre = block_exclusive_scan<NT>(csum, s_tmp, nc);
+    // tile offsets in tile order, one block scan per round; slot owners
+    int coff[TPT];
+    int nc = 0;
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
-        const int i = tid * TPT + u;
-        if (i < st.ntiles) {
-            s_coff[i] = pre;
-            s_cc[i] = 0;
+        coff[u] = 0;
+        if (u < rounds) {
+            int tot;
+            coff[u] = nc + block_exclusive_scan<NT>(tc[u], s_tmp, tot);
+            nc += tot;
         }
-        pre += tc[u];
+    }
+#pragma unroll
+    for (int u = 0; u < TPT; ++u) {
+        const int i = tid + u * NT;
+        if (i < st.ntiles) {
+            s_coff[i] = coff[u];
+            s_cc[i] = 0;
+            for (int k = 0; k < tc[u] && coff[u] + k < kCandLds; ++k)
+                s_owner[coff[u] + k] = ((uint32_t)i << 10) | (uint32_t)k;
+        }
     }
     if (tid == 0) s_coff[st.ntiles] = nc;
     __syncthreads();
-    auto cand_at = [&](int i) -> int2 {              // i-th candidate, 0 <= i < nc
-        int lo_t = 0, hi_t = st.ntiles - 1;          // last tile with s_coff <= i
-        while (lo_t < hi_t) {
-            const int mid = (lo_t + hi_t + 1) >> 1;
-            if (s_coff[mid] <= i) lo_t = mid;
-            else hi_t = mid - 1;
-        }
-        return w.cand[(size_t)(st.tile0 + lo_t) * kTile + (i - s_coff[lo_t])];
-    };
-    int2 cv[PER];
+    const int n_lds = min(nc, kCandLds);
+    uint32_t own[SPT];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
+    for (int j = 0; j < SPT; ++j) {
         const int i = tid + j * NT;
-        cv[j] = i < nc ? cand_at(i) : make_int2(-1, 0);
+        own[j] = i < n_lds ? s_owner[i] : 0u;
     }
+    __syncthreads();                                 // owners read: slots become candidates
+    {
+        int2 c[SPT];
+#pragma unroll
+        for (int j = 0; j < SPT; ++j) {
+            const int i = tid + j * NT;
+            c[j] = i < n_lds ? w.cand[(size_t)(st.tile0 + (own[j] >> 10)) * kTile + (own[j] & 1023u)]
+                             : make_int2(-1, 0);
+        }
+#pragma unroll
+        for (int j = 0; j < SPT; ++j)
+            if (tid + j * NT < n_lds) s_cand[tid + j * NT] = c[j];
+    }
+    __syncthreads();
+    auto cand_at = [&](int i) -> int2 {              // 0 <= i < nc
+        if (i < kCandLds) return s_cand[i];
+        int t = 0;                                   // last tile with s_coff <= i
+        for (int step = kMaxTilesPerSeq / 2; step > 0; step >>= 1) {
+            const int m = t + step;
+            if (m < st.ntiles && s_coff[m] <= i) t = m;
+        }
+        return w.cand[(size_t)(st.tile0 + t) * kTile + (i - s_coff[t])];
+    };
     // more 12-bit passes while the sub-bin holds several values and > kRankMax entries
     while (lo < hi && cnt > kRankMax) {              // uniform: lo, hi, cnt from LDS
         int sh2, nb2;
         sub_digit(lo, hi, sh2, nb2);
         for (int i = tid; i < nb2; i += NT) s_hist[i] = 0;
         __syncthreads();
-        auto add = [&](int v) {
+        for (int i = tid; i < nc; i += NT) {
+            const int v = cand_at(i).x;
             if (v >= lo && v <= hi) atomicAdd(&s_hist[(unsigned)(v - lo) >> sh2], 1u);
-        };
-#pragma unroll
-        for (int j = 0; j < PER; ++j) add(cv[j].x);
-        for (int i = CHUNK + tid; i < nc; i += NT) add(cand_at(i).x);
+        }
         __syncthreads();
         find_bin<NT, kSubBins / NT>(s_hist, nb2, need, s_tmp, s_res, d, a, cnt);
         need -= a;
@@ -527,19 +571,24 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         T = lo;
         needT = need;
     } else {
-        // <= kRankMax entries in [lo, hi]: rank them by the key (score, ~position)
+        // <= kRankMax entries in [lo, hi]: rank them by the key (score, ~position);
+        // slots are taken one wave at a time (ballot, one LDS atomic per wave)
         if (tid == 0) s_res[3] = 0;
         __syncthreads();
-        auto put = [&](int2 v) {
-            if (v.x >= lo && v.x <= hi) {
-                const int slot = atomicAdd(&s_res[3], 1);
-                if (slot < kRankMax)
+        for (int base = 0; base < nc; base += NT) {  // uniform trip count
+            const int i = base + tid;
+            const int2 v = i < nc ? cand_at(i) : make_int2(-1, 0);
+            const bool in = v.x >= lo && v.x <= hi;
+            const uint64_t m = __ballot(in);
+            if (m) {
+                int first = 0;
+                if (lane == 0) first = atomicAdd(&s_res[3], __popcll(m));
+                first = __shfl(first, 0);
+                const int slot = first + lane_rank64(m);
+                if (in && slot < kRankMax)
                     s_key[slot] = ((unsigned long long)(uint32_t)v.x << 32) | (uint32_t)~(uint32_t)v.y;
             }
-        };
-#pragma unroll
-        for (int j = 0; j < PER; ++j) put(cv[j]);
-        for (int i = CHUNK + tid; i < nc; i += NT) put(cand_at(i));
+        }
         __syncthreads();
         rank_select_key(s_key, cnt, need, s_res);
         __syncthreads();
@@ -548,39 +597,30 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
     }
 
     // per-tile counts of candidates above / at the threshold
-    auto count_one = [&](int2 v) {
-        if (v.x < 0 || v.x < T) return;
-        const int tile = min(v.y / kTile, kMaxTilesPerSeq - 1);
-        atomicAdd(&s_cc[tile], v.x > T ? 1u : 0x10000u);
-    };
-#pragma unroll
-    for (int j = 0; j < PER; ++j) count_one(cv[j]);
-    for (int i = CHUNK + tid; i < nc; i += NT) count_one(cand_at(i));
-    __syncthreads();
-    // exclusive prefix over this sequence's tiles
-    int gl[TPT], el[TPT];
-    int gs = 0, es = 0;
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-        const int i = tid * TPT + u;
-        const uint32_t c = i < st.ntiles ? s_cc[i] : 0u;
-        gl[u] = ta[u] + (int)(c & 0xFFFFu);
-        el[u] = (int)(c >> 16);
-        gs += gl[u];
-        es += el[u];
+    for (int i = tid; i < nc; i += NT) {
+        const int2 v = cand_at(i);
+        if (v.x >= 0 && v.x >= T)
+            atomicAdd(&s_cc[min(v.y / kTile, kMaxTilesPerSeq - 1)], v.x > T ? 1u : 0x10000u);
     }
-    int tot;
-    int og = block_exclusive_scan<NT>(gs, s_tmp, tot);
-    int oe = block_exclusive_scan<NT>(es, s_tmp, tot);
+    __syncthreads();
+    // exclusive prefix over this sequence's tiles, in tile order
+    int og = 0, oe = 0;
 #pragma unroll
     for (int u = 0; u < TPT; ++u) {
-        const int i = tid * TPT + u;
-        if (i < st.ntiles) {
-            w.tile_off[2 * (st.tile0 + i)] = og;
-            w.tile_off[2 * (st.tile0 + i) + 1] = oe;
+        if (u < rounds) {
+            const int i = tid + u * NT;
+            const uint32_t c = i < st.ntiles ? s_cc[i] : 0u;
+            const int gl = ta[u] + (int)(c & 0xFFFFu), el = (int)(c >> 16);
+            int tg, te;
+            const int pg = block_exclusive_scan<NT>(gl, s_tmp, tg);
+            const int pe = block_exclusive_scan<NT>(el, s_tmp, te);
+            if (i < st.ntiles) {
+                w.tile_off[2 * (st.tile0 + i)] = og + pg;
+                w.tile_off[2 * (st.tile0 + i) + 1] = oe + pe;
+            }
+            og += tg;
+            oe += te;
         }
-        og += gl[u];
-        oe += el[u];
     }
     if (tid == 0) {
         w.st[b].T = T;

@@ -129,19 +129,27 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     __shared__ int s_cnt[PER * kSelWaves], s_pre[PER * kSelWaves];
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    const int n = max(0, min(cand_len[b], P));
-    const int keff = min(k, n);
     const int* sc = score + (size_t)b * P;
     const int* cp = cand_pos + (size_t)b * P;
-
-    // entry i = tid + 1024 j; scores and positions, all loads in flight
+    // entry i = tid + 1024 j: every score of the row is loaded without waiting
+    // for the list length (one memory round trip for both); positions follow
+    const int len_b = cand_len[b];
     int v[PER], pos[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int i = tid + j * kSelThreads;
-        v[j] = i < n ? sc[i] : -1;          // valid scores are >= 0
-        pos[j] = i < n ? cp[i] : -1;
+        v[j] = i < P ? sc[i] : -1;
     }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int i = tid + j * kSelThreads;
+        pos[j] = i < P ? cp[i] : -1;
+    }
+    const int n = max(0, min(len_b, P));
+    const int keff = min(k, n);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (tid + j * kSelThreads >= n) v[j] = -1;     // valid scores are >= 0
 
     int T = 0x7FFFFFFF, needT = 0;
     bool all_ties = true;                     // every entry with s == T is taken
@@ -195,14 +203,21 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         } else {
             // <= kSelRank entries in [lo, hi]: rank them by the key (score, ~index)
             __syncthreads();
+            // slots are taken one wave at a time (ballot, one LDS atomic per wave)
 #pragma unroll
-            for (int j = 0; j < PER; ++j)
-                if (v[j] >= lo && v[j] <= hi) {
-                    const int slot = atomicAdd(&s_res[3], 1);
-                    if (slot < kSelRank)
+            for (int j = 0; j < PER; ++j) {
+                const bool in = v[j] >= lo && v[j] <= hi;
+                const uint64_t m = __ballot(in);
+                if (m) {                              // wave-uniform
+                    int first = 0;
+                    if (lane == 0) first = atomicAdd(&s_res[3], __popcll(m));
+                    first = __shfl(first, 0);
+                    const int slot = first + lane_rank(m);
+                    if (in && slot < kSelRank)
                         s_key[slot] = ((unsigned long long)(uint32_t)v[j] << 32) |
                                       (uint32_t)~(uint32_t)(tid + j * kSelThreads);
                 }
+            }
             __syncthreads();
             rank_select_key(s_key, cnt, need, s_res);
             __syncthreads();

@@ -33,9 +33,18 @@ FLAGS = [
 ]
 
 
+# The scoring kernels read every int8 MFMA result straight into VALU
+# arithmetic (ReLU and head weight): keeping the results in VGPRs saves one
+# accumulator-register read per head and token.
+EXTRA = {
+    "index_full.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "index_reindex.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, src.replace(".hip", ".o"))
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("hipcc failed for %s:\n%s\n%s" % (src, " ".join(cmd), r.stderr))

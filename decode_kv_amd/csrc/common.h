@@ -29,24 +29,41 @@ __device__ __forceinline__ T bitcast(const auto& x) {
 // operands, so any hardware ordering of K is the same for A and B and the dot
 // product is exact.  The 16x16 int32 result gives lane l the dot products of
 // token (l & 15) with heads 16*mb + 4*(l>>4) + i, i = 0..3; the epilogue applies
-// ReLU and the head weight, then the four lane groups are summed.
+// ReLU and the head weight.  Returned: lane l's partial sum over its heads,
+// before the four lane rows (l >> 4) are added (reduce_rows4).
 template <int NB>
-__device__ __forceinline__ int score_group16(const i32x4 (&qa)[NB], const uint32_t (&wr)[NB][4],
-                                             i32x4 keyop) {
+__device__ __forceinline__ uint32_t score_partial16(const i32x4 (&qa)[NB],
+                                                    const uint32_t (&wr)[NB][4], i32x4 keyop) {
+    i32x4 acc[NB];
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb)
+        acc[mb] = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mb], keyop, i32x4{0, 0, 0, 0}, 0, 0, 0);
     uint32_t part = 0;
 #pragma unroll
-    for (int mb = 0; mb < NB; ++mb) {
-        i32x4 acc = {0, 0, 0, 0};
-        acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(qa[mb], keyop, acc, 0, 0, 0);
+    for (int mb = 0; mb < NB; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            int r = acc[i] > 0 ? acc[i] : 0;          // ReLU, < 2^21
-            part += __umul24(wr[mb][i], (uint32_t)r);  // weight <= 15
+            const int r = acc[mb][i] > 0 ? acc[mb][i] : 0;   // ReLU, < 2^21
+            part += __umul24(wr[mb][i], (uint32_t)r);         // weight <= 15
         }
-    }
-    part += __shfl_xor(part, 16);
-    part += __shfl_xor(part, 32);
-    return (int)part;
+    return part;
+}
+
+// Four 16-token groups at once: part[u] holds lane l's partial of group u
+// (token l & 15, the heads of lane row l >> 4).  Returns, in lane (r, c) =
+// (l >> 4, l & 15), the full score of token c of group r: two exchanges across
+// the wave halves and one across neighbouring rows (v_permlane32_swap and
+// v_permlane16_swap, no LDS), three adds.
+__device__ __forceinline__ uint32_t reduce_rows4(const uint32_t (&part)[4]) {
+    // halves: lanes 0-31 keep groups 0/1 and receive them from lanes 32-63,
+    // lanes 32-63 keep groups 2/3
+    const auto x02 = __builtin_amdgcn_permlane32_swap(part[0], part[2], false, false);
+    const auto x13 = __builtin_amdgcn_permlane32_swap(part[1], part[3], false, false);
+    const uint32_t s02 = x02[0] + x02[1];   // rows 0,1: group 0 | rows 2,3: group 2 (rows r, r^2)
+    const uint32_t s13 = x13[0] + x13[1];   // rows 0,1: group 1 | rows 2,3: group 3
+    // rows: even rows keep s02, odd rows keep s13, each adding its neighbour's
+    const auto y = __builtin_amdgcn_permlane16_swap(s02, s13, false, false);
+    return y[0] + y[1];
 }
 
 // Load the q operands and per-lane weights of one sequence's index query.

@@ -33,6 +33,7 @@ namespace csa2 {
 
 constexpr int kTile = 1024;
 constexpr int kScanThreads = 256;
+constexpr int kScoreThreads = 512;       // scoring kernel: 8 waves x 128 tokens
 constexpr int kKeyBins = 832;            // float-like key of a score < 2^31
 constexpr int kRedBins = 32;             // bins per reduce workgroup
 constexpr int kSubBits = 12;
@@ -202,36 +203,46 @@ struct TileInfo {
     long long roff;
 };
 
-__device__ TileInfo map_tile(const int* __restrict__ len, const long long* __restrict__ row_off,
-                             int B, int window, int P, int t, FullWs w, bool write_state) {
-    __shared__ int s_tmp[kScanThreads / kWave];
+__device__ __forceinline__ FullState initial_state(int E, int P, int tile0, int nt) {
+    FullState s;
+    s.E = E;
+    s.Peff = E < P ? E : P;
+    s.tile0 = tile0;
+    s.ntiles = nt;
+    s.T = 0x7FFFFFFF;
+    s.needT = 0;
+    s.kb = 0;
+    s.above = 0;
+    return s;
+}
+
+// One sequence: no scan, no LDS, no barrier.
+__device__ __forceinline__ TileInfo map_tile_one(const int* __restrict__ len,
+                                                 const long long* __restrict__ row_off,
+                                                 int window, int P, int t, FullWs w,
+                                                 bool write_state) {
+    const int L = len[0];
+    const long long roff = row_off[0];
+    const int E = L > window ? L - window : 0;
+    const int nt = (E + kTile - 1) / kTile;
+    if (write_state && threadIdx.x == 0) w.st[0] = initial_state(E, P, 0, nt);
+    TileInfo r;
+    r.b = t < nt ? 0 : -1;
+    r.tile0 = 0;
+    r.E = E;
+    r.roff = roff;
+    return r;
+}
+
+template <int NT>
+__device__ __noinline__ TileInfo map_tile(const int* __restrict__ len,
+                                          const long long* __restrict__ row_off, int B,
+                                          int window, int P, int t, FullWs w, bool write_state) {
+    __shared__ int s_tmp[NT / kWave];
     __shared__ int s_b, s_tile0, s_E;
     __shared__ long long s_roff;
     TileInfo r;
-    if (B == 1) {                                         // one sequence: no scan
-        const int L = len[0];
-        const long long roff = row_off[0];
-        const int E = L > window ? L - window : 0;
-        const int nt = (E + kTile - 1) / kTile;
-        if (write_state && threadIdx.x == 0) {
-            FullState s;
-            s.E = E;
-            s.Peff = E < P ? E : P;
-            s.tile0 = 0;
-            s.ntiles = nt;
-            s.T = 0x7FFFFFFF;
-            s.needT = 0;
-            s.kb = 0;
-            s.above = 0;
-            w.st[0] = s;
-        }
-        r.b = t < nt ? 0 : -1;
-        r.tile0 = 0;
-        r.E = E;
-        r.roff = roff;
-        return r;
-    }
-    constexpr int SPT = kMaxBatch / kScanThreads;         // sequences per thread
+    constexpr int SPT = kMaxBatch / NT;                   // sequences per thread
     const int first = threadIdx.x * SPT;
     int nt[SPT], Ev[SPT];
     int sum_t = 0;
@@ -249,7 +260,7 @@ __device__ TileInfo map_tile(const int* __restrict__ len, const long long* __res
     }
     if (threadIdx.x == 0) s_b = -1;
     int tot_t;
-    int pre_t = block_exclusive_scan<kScanThreads>(sum_t, s_tmp, tot_t);
+    int pre_t = block_exclusive_scan<NT>(sum_t, s_tmp, tot_t);
 #pragma unroll
     for (int i = 0; i < SPT; ++i) {
         const int b = first + i;
@@ -260,18 +271,7 @@ __device__ TileInfo map_tile(const int* __restrict__ len, const long long* __res
                 s_E = Ev[i];
                 s_roff = row_off[b];
             }
-            if (write_state) {
-                FullState s;
-                s.E = Ev[i];
-                s.Peff = Ev[i] < P ? Ev[i] : P;
-                s.tile0 = pre_t;
-                s.ntiles = nt[i];
-                s.T = 0x7FFFFFFF;
-                s.needT = 0;
-                s.kb = 0;
-                s.above = 0;
-                w.st[b] = s;
-            }
+            if (write_state) w.st[b] = initial_state(Ev[i], P, pre_t, nt[i]);
         }
         pre_t += nt[i];
     }
@@ -285,34 +285,55 @@ __device__ TileInfo map_tile(const int* __restrict__ len, const long long* __res
 
 // ---- 1. score + per-tile histogram -------------------------------------------------
 // Scores go to score_out + (seq_stride < 0 ? t * kTile : b * seq_stride + p).
+// Eight waves per workgroup, 128 tokens (8 groups of 16) per wave, so a CU
+// holds many waves whose scoring overlaps the others' key loads.
+// Load order: the index query and head weights first (with one sequence they
+// need no lookup, so they travel together with the length), then all of the
+// wave's key loads, and only then the first barrier, so nothing waits between
+// the length arriving and the key stream starting.
 template <int NB>
-__global__ __launch_bounds__(kScanThreads) void full_score_kernel(
+__global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ wts,
     const int8_t* __restrict__ keys, const long long* __restrict__ row_off,
     const int* __restrict__ len, int B, int H, int window, int P, FullWs w,
     int* __restrict__ score_out, long long seq_stride) {
     __shared__ uint32_t s_hist[kKeyBins];
+    __shared__ uint32_t s_w[kDk / 4];                          // head weights, byte h = head h
     const int t = blockIdx.x;
-    const TileInfo ti = map_tile(len, row_off, B, window, P, t, w, t == 0);
-    if (ti.b < 0) return;                              // past the last tile
-    const int b = ti.b;
-    for (int i = threadIdx.x; i < kKeyBins; i += kScanThreads) s_hist[i] = 0;
-
-    i32x4 qa[NB];
-    uint32_t wr[NB][4];
-    load_index_query<NB>(q + (size_t)b * H * kDk, wts + (size_t)b * H, H, qa, wr);
-
     const int l = lane_id();
     const int wave = threadIdx.x / kWave;
+    i32x4 qa[NB];
+    int wv = 0;
+    auto load_query = [&](int b) {
+        const int8_t* qb = q + (size_t)b * H * kDk + (l >> 4) * 16;
+#pragma unroll
+        for (int mb = 0; mb < NB; ++mb) {
+            const int h = mb * 16 + (l & 15);
+            qa[mb] = h < H ? *reinterpret_cast<const i32x4*>(qb + (size_t)h * kDk)
+                           : i32x4{0, 0, 0, 0};
+        }
+        if (threadIdx.x < H) wv = (uint8_t)wts[(size_t)b * H + threadIdx.x];
+    };
+    TileInfo ti;
+    if (B == 1) {
+        load_query(0);
+        ti = map_tile_one(len, row_off, window, P, t, w, t == 0);
+        if (ti.b < 0) return;                              // past the last tile
+    } else {
+        ti = map_tile<kScoreThreads>(len, row_off, B, window, P, t, w, t == 0);
+        if (ti.b < 0) return;
+        load_query(ti.b);
+    }
+    const int b = ti.b;
+
     const int p_tile = (t - ti.tile0) * kTile;                 // first position
     const int8_t* kbase = keys + ((size_t)ti.roff + p_tile) * kDk + (l >> 4) * 16;
-    int* sc_out = score_out + (seq_stride < 0 ? (size_t)t * kTile
-                                              : (size_t)b * (size_t)seq_stride + p_tile);
     const int nvalid = min(kTile, ti.E - p_tile);
-    // wave w scores tokens [256w, 256w + 256): 16 groups of 16, all loads issued
-    // before the first MFMA so 16 KB per wave are in flight
-    constexpr int kGroups = kTile / (4 * 16);
-    const int t0 = (kTile / 4) * wave;
+    // wave w scores tokens [128w, 128w + 128): 8 groups of 16, all loads issued
+    // before the first MFMA
+    constexpr int kWaves = kScoreThreads / kWave;
+    constexpr int kGroups = kTile / (kWaves * 16);
+    const int t0 = (kTile / kWaves) * wave;
     i32x4 kop[kGroups];
 #pragma unroll
     for (int u = 0; u < kGroups; ++u) {
@@ -320,15 +341,27 @@ __global__ __launch_bounds__(kScanThreads) void full_score_kernel(
         tok = tok < nvalid ? tok : 0;
         kop[u] = *reinterpret_cast<const i32x4*>(kbase + (size_t)tok * kDk);
     }
-    __syncthreads();                                           // histogram zeroed
+    asm volatile("" ::: "memory");                             // keys are in flight first
+    for (int i = threadIdx.x; i < kKeyBins; i += kScoreThreads) s_hist[i] = 0;
+    if (threadIdx.x < kDk) reinterpret_cast<uint8_t*>(s_w)[threadIdx.x] = (uint8_t)wv;
+    __syncthreads();                                           // histogram zeroed, weights in LDS
+    // lane l weighs heads 16 mb + 4 (l >> 4) + i, i = 0..3: one LDS word per block
+    uint32_t wr[NB][4];
+#pragma unroll
+    for (int mb = 0; mb < NB; ++mb) {
+        const uint32_t word = s_w[4 * mb + (l >> 4)];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wr[mb][i] = (word >> (8 * i)) & 0xFFu;
+    }
+    int* sc_out = score_out + (seq_stride < 0 ? (size_t)t * kTile
+                                              : (size_t)b * (size_t)seq_stride + p_tile);
 #pragma unroll
     for (int it = 0; it < kGroups / 4; ++it) {
         if (t0 + 64 * it >= nvalid) break;                     // wave-uniform
-        int sc[4];
+        uint32_t part[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) sc[u] = score_group16<NB>(qa, wr, kop[4 * it + u]);
-        const int g = l >> 4;
-        const int mine = g == 0 ? sc[0] : (g == 1 ? sc[1] : (g == 2 ? sc[2] : sc[3]));
+        for (int u = 0; u < 4; ++u) part[u] = score_partial16<NB>(qa, wr, kop[4 * it + u]);
+        const int mine = (int)reduce_rows4(part);              // token t0 + 64 it + l
         const int tok = t0 + 64 * it + l;
         if (tok < nvalid) {
             sc_out[tok] = mine;
@@ -338,7 +371,7 @@ __global__ __launch_bounds__(kScanThreads) void full_score_kernel(
     __syncthreads();
     // per-tile histogram, u16 (a tile has <= 1,024 entries), two bins per word
     uint32_t* th = reinterpret_cast<uint32_t*>(w.tile_hist + (size_t)t * kKeyBins);
-    for (int i = threadIdx.x; i < kKeyBins / 2; i += kScanThreads)
+    for (int i = threadIdx.x; i < kKeyBins / 2; i += kScoreThreads)
         th[i] = s_hist[2 * i] | (s_hist[2 * i + 1] << 16);
 }
 
@@ -723,7 +756,7 @@ static int launch_score(int H, unsigned tiles, hipStream_t s, const signed char*
     const int8_t* q8 = reinterpret_cast<const int8_t*>(q);
     const int8_t* w8 = reinterpret_cast<const int8_t*>(w);
     const int8_t* k8 = reinterpret_cast<const int8_t*>(keys);
-    const dim3 grid(tiles), blk(kScanThreads);
+    const dim3 grid(tiles), blk(kScoreThreads);
     switch ((H + 15) / 16) {
         case 1: hipLaunchKernelGGL(full_score_kernel<1>, grid, blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw, out, seq_stride); break;
         case 2: hipLaunchKernelGGL(full_score_kernel<2>, grid, blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw, out, seq_stride); break;

@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kReThreads) void reindex_kernel(
     uint32_t wr[NB][4];
     load_index_query<NB>(q + (size_t)b * H * kDk, wts + (size_t)b * H, H, qa, wr);
     const int8_t* kb = keys + (size_t)row_off[b] * kDk;
-    int sc[4] = {0, 0, 0, 0};
+    uint32_t part[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
         const int g0 = base + 16 * u;
@@ -45,11 +45,10 @@ __global__ __launch_bounds__(kReThreads) void reindex_kernel(
             const int pos = max(cp[i], 0);             // valid entries are >= 0
             const i32x4 kop =
                 *reinterpret_cast<const i32x4*>(kb + (size_t)pos * kDk + (l >> 4) * 16);
-            sc[u] = score_group16<NB>(qa, wr, kop);
+            part[u] = score_partial16<NB>(qa, wr, kop);
         }
     }
-    const int g = l >> 4;
-    const int mine = g == 0 ? sc[0] : (g == 1 ? sc[1] : (g == 2 ? sc[2] : sc[3]));
+    const int mine = (int)reduce_rows4(part);          // candidate base + l
     const int i = base + l;
     if (i < P) out[i] = i < n ? mine : -1;
 }

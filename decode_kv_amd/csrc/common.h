@@ -89,6 +89,41 @@ __device__ __forceinline__ void load_index_query(const int8_t* __restrict__ q,
     }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave, in DPP: row shifts by 1,
+// 2, 4 and 8 inside each row of 16 lanes (lanes shifted in from outside the
+// row add 0), then lane 15 broadcast into rows 1 and 3 and lane 31 into rows
+// 2 and 3.
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return x;
+}
+
+// Exclusive prefix sum of one int per thread over a block of NT threads (in
+// thread order); total gets the block sum.  s_tmp holds NT / 64 ints.  Every
+// thread of the block must call it (two barriers).
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
+    const int l = lane_id(), wv = threadIdx.x / kWave;
+    const int x = wave_inclusive_scan(v);
+    if (l == kWave - 1) s_tmp[wv] = x;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int i = 0; i < NT / kWave; ++i) {
+        const int c = s_tmp[i];
+        if (i < wv) before += c;
+        total += c;
+    }
+    __syncthreads();
+    return before + x - v;
+}
+
 // Rank of this lane among the set lanes of a wave mask (lanes below it).
 __device__ __forceinline__ int lane_rank64(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),

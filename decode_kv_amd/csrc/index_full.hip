@@ -126,28 +126,6 @@ __device__ __forceinline__ void sub_digit(int lo, int hi, int& sh, int& nb) {
     nb = (int)(((width - 1u) >> sh) + 1u);
 }
 
-// Exclusive prefix sum of one int per thread over the block.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int& total) {
-    const int l = lane_id(), wv = threadIdx.x / kWave;
-    int x = v;
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (l >= o) x += y;
-    }
-    if (l == kWave - 1) s_tmp[wv] = x;
-    __syncthreads();
-    int before = 0;
-    total = 0;
-    for (int i = 0; i < NT / kWave; ++i) {
-        const int c = s_tmp[i];
-        if (i < wv) before += c;
-        total += c;
-    }
-    __syncthreads();
-    return before + x - v;
-}
-
 // Bin holding the need-th largest entry of a histogram (bins ascending in
 // value); every thread gets (bin, entries in higher bins, entries in the bin).
 // Requires 1 <= need <= total count.  Thread t owns the PER consecutive bins

@@ -22,27 +22,6 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelMaxP = 16384;
 constexpr int kSelWaves = kSelThreads / kWave;
 
-// Exclusive prefix sum over the block (1,024 threads).
-__device__ __forceinline__ int sel_block_scan(int v, int* s_tmp, int& total) {
-    const int l = lane_id(), wv = threadIdx.x / kWave;
-    int x = v;
-    for (int o = 1; o < kWave; o <<= 1) {
-        const int y = __shfl_up(x, o);
-        if (l >= o) x += y;
-    }
-    if (l == kWave - 1) s_tmp[wv] = x;
-    __syncthreads();
-    int before = 0;
-    total = 0;
-    for (int i = 0; i < kSelWaves; ++i) {
-        const int c = s_tmp[i];
-        if (i < wv) before += c;
-        total += c;
-    }
-    __syncthreads();
-    return before + x - v;
-}
-
 // Monotone 12-bit key of a non-negative score: exact below 128, otherwise the
 // exponent and the 7 bits below the leading one.
 __device__ __forceinline__ int sel_key(int s) {
@@ -67,7 +46,7 @@ __device__ __forceinline__ void sel_find_bin(const uint32_t* s_hist, int nb, int
         mysum += bin < nb ? (int)s_hist[bin] : 0;
     }
     int tot;
-    const int above = sel_block_scan(mysum, s_tmp, tot);
+    const int above = block_exclusive_scan<kSelThreads>(mysum, s_tmp, tot);
     if (above < need && need <= above + mysum) {
         int acc = above;
         for (int i = per - 1; i >= 0; --i) {
@@ -101,12 +80,7 @@ __device__ __forceinline__ void slot_wave_scan(const int* s_cnt, int* s_pre) {
             c[i] = s_cnt[4 * l + i];
             sum += c[i];
         }
-        int x = sum;
-        for (int o = 1; o < kWave; o <<= 1) {
-            const int y = __shfl_up(x, o);
-            if (l >= o) x += y;
-        }
-        int run = x - sum;
+        int run = wave_inclusive_scan(sum) - sum;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             s_pre[4 * l + i] = run;
@@ -145,6 +119,10 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         const int i = tid + j * kSelThreads;
         pos[j] = i < P ? cp[i] : -1;
     }
+    // the first histogram is cleared while the loads are in flight
+    for (int i = tid; i < kSelKeyBins; i += kSelThreads) s_hist[i] = 0;
+    if (tid == 0) s_res[3] = 0;
+    __syncthreads();
     const int n = max(0, min(len_b, P));
     const int keff = min(k, n);
 #pragma unroll
@@ -155,9 +133,6 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     bool all_ties = true;                     // every entry with s == T is taken
     if (keff > 0) {
         // pass 0: float-like key, fine enough that the atomics rarely collide
-        for (int i = tid; i < kSelKeyBins; i += kSelThreads) s_hist[i] = 0;
-        if (tid == 0) s_res[3] = 0;
-        __syncthreads();
 #pragma unroll
         for (int j = 0; j < PER; ++j)
             if (v[j] >= 0) atomicAdd(&s_hist[sel_key(v[j])], 1u);
@@ -203,20 +178,25 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         } else {
             // <= kSelRank entries in [lo, hi]: rank them by the key (score, ~index)
             __syncthreads();
-            // slots are taken one wave at a time (ballot, one LDS atomic per wave)
+            // slots: one LDS atomic per wave for all of its entries in the bin
+            uint64_t min_[PER];
+            int wcount = 0;
 #pragma unroll
             for (int j = 0; j < PER; ++j) {
-                const bool in = v[j] >= lo && v[j] <= hi;
-                const uint64_t m = __ballot(in);
-                if (m) {                              // wave-uniform
-                    int first = 0;
-                    if (lane == 0) first = atomicAdd(&s_res[3], __popcll(m));
-                    first = __shfl(first, 0);
-                    const int slot = first + lane_rank(m);
-                    if (in && slot < kSelRank)
-                        s_key[slot] = ((unsigned long long)(uint32_t)v[j] << 32) |
-                                      (uint32_t)~(uint32_t)(tid + j * kSelThreads);
-                }
+                min_[j] = __ballot(v[j] >= lo && v[j] <= hi);
+                wcount += __popcll(min_[j]);
+            }
+            int first = 0;
+            if (lane == 0 && wcount) first = atomicAdd(&s_res[3], wcount);
+            first = __builtin_amdgcn_readfirstlane(first);
+#pragma unroll
+            for (int j = 0; j < PER; ++j) {
+                const bool in = (min_[j] >> lane) & 1ull;
+                const int slot = first + lane_rank(min_[j]);
+                if (in && slot < kSelRank)
+                    s_key[slot] = ((unsigned long long)(uint32_t)v[j] << 32) |
+                                  (uint32_t)~(uint32_t)(tid + j * kSelThreads);
+                first += __popcll(min_[j]);
             }
             __syncthreads();
             rank_select_key(s_key, cnt, need, s_res);

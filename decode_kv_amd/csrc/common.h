@@ -89,6 +89,23 @@ __device__ __forceinline__ void load_index_query(const int8_t* __restrict__ q,
     }
 }
 
+// Max / sum of one value over the four lane rows of a wave (lanes l, l ^ 16,
+// l ^ 32, l ^ 48): v_permlane32_swap then v_permlane16_swap exchange whole
+// rows between registers, with no LDS round trip.
+__device__ __forceinline__ float rows4_max(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float rows4_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave, in DPP: row shifts by 1,
 // 2, 4 and 8 inside each row of 16 lanes (lanes shifted in from outside the
 // row add 0), then lane 15 broadcast into rows 1 and 3 and lane 31 into rows

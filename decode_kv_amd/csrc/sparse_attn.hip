@@ -194,6 +194,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         s_red[wave][0][l] = s0;
         s_red[wave][1][l] = s1;
         __syncthreads();
+        // this wave's V^T operands of the P.V product, read before the softmax
+        // so their LDS latency overlaps it
+        bf16x8 bv[kNb];
+#pragma unroll
+        for (int nb = 0; nb < kNb; ++nb) {
+            const uint16_t* vd = s_vdj + (16 * (kNb * wave + nb) + c16) * kVdjLd + 4 * g;
+            const u32x2 lo = *reinterpret_cast<const u32x2*>(vd);
+            const u32x2 hi = *reinterpret_cast<const u32x2*>(vd + 16);
+            bv[nb] = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+        }
         s0 = s_red[0][0][l] + s_red[1][0][l] + s_red[2][0][l] + s_red[3][0][l];
         s1 = s_red[0][1][l] + s_red[1][1][l] + s_red[2][1][l] + s_red[3][1][l];
 
@@ -208,8 +218,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         float tmax = ts[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, ts[i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = rows4_max(tmax);
         const float m_new = fmaxf(m_run, tmax);   // finite: every tile has a valid row
         const float alpha = exp2f(m_run - m_new);
         float p[8], psum = 0.f;
@@ -218,8 +227,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
             p[i] = exp2f(ts[i] - m_new);
             psum += p[i];
         }
-        psum += __shfl_xor(psum, 16);
-        psum += __shfl_xor(psum, 32);
+        psum = rows4_sum(psum);
         l_run = l_run * alpha + psum;
         m_run = m_new;
 #pragma unroll
@@ -237,13 +245,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         const bf16x8 ph = bitcast<bf16x8>(ph_u), pl = bitcast<bf16x8>(pl_u);
 #pragma unroll
         for (int nb = 0; nb < kNb; ++nb) {
-            const uint16_t* vd = s_vdj + (16 * (kNb * wave + nb) + c16) * kVdjLd + 4 * g;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vd);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vd + 16);
-            const bf16x8 bv = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
             // O^T[d][head]: A = V^T (M = latent dim), B = P^T (N = head)
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, ph, o[nb], 0, 0, 0);
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv, pl, o[nb], 0, 0, 0);
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[nb], ph, o[nb], 0, 0, 0);
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[nb], pl, o[nb], 0, 0, 0);
         }
     }
 

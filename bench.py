@@ -56,13 +56,24 @@ def algorithmic_bytes(wl, L: int) -> dict:
             "scan_kernel": (64 * E + 65 * wl.H) * wl.B}
 
 
-def stale_traffic(profile_path: str, src_path: str):
+SCAN_SOURCES = ("decode_kv_amd/csrc/index_full.hip", "decode_kv_amd/csrc/common.h")
+
+
+def scan_source_hash() -> str:
+    """sha256 over the scanning kernel's sources (the file that holds it and
+    the shared device helpers it uses)."""
+    h = hashlib.sha256()
+    for rel in SCAN_SOURCES:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()
+
+
+def stale_traffic(profile_path: str):
     """HBM traffic of the scan kernel from a committed counter summary, or
-    None if the kernel source changed since the counters were taken."""
+    None if the kernel's sources changed since the counters were taken."""
     try:
         rec = json.load(open(profile_path))
-        sha = hashlib.sha256(open(src_path, "rb").read()).hexdigest()
-        if rec.get("source_sha256") != sha:
+        if rec.get("source_sha256") != scan_source_hash():
             return None
         return rec.get("traffic_bytes_per_launch")
     except Exception:
@@ -225,8 +236,7 @@ def main():
     ab = algorithmic_bytes(wl, L)
     step_bytes = ab["full"] + ab["select"] + ab["reindex"] + ab["attn"]
     scan_gbs = ab["scan_kernel"] / (scan_avg_ms * 1e-3) / 1e9
-    traffic = stale_traffic(os.path.join(ROOT, "profiles", "full_score_ctx_1m_counters.json"),
-                            os.path.join(ROOT, "decode_kv_amd", "csrc", "index_full.hip"))
+    traffic = stale_traffic(os.path.join(ROOT, "profiles", "full_score_ctx_1m_counters.json"))
     res = {
         "metric": "decode steps/s at 1M ctx (index+sparse attn) + achieved HBM GB/s vs peak",
         "value": round(1000.0 / ms, 2),

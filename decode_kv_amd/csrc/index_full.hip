@@ -41,6 +41,7 @@ constexpr int kSubBins = 1 << kSubBits;  // second-level histogram / refinement 
 constexpr int kThrThreads = 1024;
 constexpr int kMaxTilesPerSeq = 8192;    // LDS tile tables of the threshold kernel (8M positions)
 constexpr int kRankMax = 256;            // entries ranked exactly
+constexpr int kCandHead = 16;            // candidates per tile in the dense head array
 constexpr int kMaxBatch = 4096;
 
 struct FullState {
@@ -63,7 +64,9 @@ struct FullWs {
     int* tile_cnt;        // [Tmax] entries of the tile inside bin B1
     int* tile_off;        // [Tmax][2] output offsets among s > T and among s == T
     uint16_t* tile_hist;  // [Tmax][kKeyBins]
-    int2* cand;           // [Tmax][kTile] (score, position) inside bin B1, per tile
+    int2* cand_head;      // [Tmax][kCandHead] first candidates of every tile, dense
+    int2* cand;           // [Tmax][kTile] (score, position) inside bin B1, per tile (slots
+                          // >= kCandHead; the first kCandHead live in cand_head)
     int* scores;          // [Tmax][kTile]
 };
 
@@ -87,6 +90,7 @@ static size_t full_ws_layout(int B, long long total_len, char* base, FullWs* w) 
     x.tile_cnt = reinterpret_cast<int*>(take(4ull * T));
     x.tile_off = reinterpret_cast<int*>(take(8ull * T));
     x.tile_hist = reinterpret_cast<uint16_t*>(take(2ull * (size_t)T * kKeyBins));
+    x.cand_head = reinterpret_cast<int2*>(take(8ull * (size_t)T * kCandHead));
     x.cand = reinterpret_cast<int2*>(take(8ull * (size_t)T * kTile));
     x.scores = reinterpret_cast<int*>(take(4ull * (size_t)T * kTile));
     if (w) *w = x;
@@ -406,23 +410,40 @@ __device__ int tile_seq(const FullState* __restrict__ st, int B, int t, int* s_b
     return *s_b;
 }
 
+// Sequence of global tile t (-1 past the last tile) and its state.  With one
+// sequence that is a single load; a batch looks the tile up first.
+__device__ __forceinline__ int tile_state(const FullState* __restrict__ sts, int B, int t, int* s_b,
+                                          FullState& st) {
+    if (B == 1) {
+        st = sts[0];                                  // tile0 == 0
+        return t < st.ntiles ? 0 : -1;
+    }
+    const int b = tile_seq(sts, B, t, s_b);
+    if (b >= 0) st = sts[b];
+    return b;
+}
+
 // ---- 3. gather: entries above / inside bin B1 --------------------------------------
 __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs w) {
     __shared__ int s_b;
     __shared__ int s_tmp[kScanThreads / kWave];
     __shared__ int s_res[3];
     const int t = blockIdx.x;
-    const int b = tile_seq(w.st, B, t, &s_b);
-    if (b < 0) return;
-    const FullState st = w.st[b];
-    const int p_tile = (t - st.tile0) * kTile;
-    const int nvalid = min(kTile, st.E - p_tile);
+    // the tile's scores sit at t * kTile whatever its sequence: load them first
     const int* sc = w.scores + (size_t)t * kTile;
     constexpr int PER = kTile / kScanThreads;   // contiguous positions per thread
     const int i0 = threadIdx.x * PER;
     int v[PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) v[j] = i0 + j < nvalid ? sc[i0 + j] : -1;
+    for (int j = 0; j < PER; ++j) v[j] = sc[i0 + j];
+    FullState st;
+    const int b = tile_state(w.st, B, t, &s_b, st);
+    if (b < 0) return;
+    const int p_tile = (t - st.tile0) * kTile;
+    const int nvalid = min(kTile, st.E - p_tile);
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+        if (i0 + j >= nvalid) v[j] = -1;
     int kb, above, cnt;
     find_bin<kScanThreads, (kKeyBins + kScanThreads - 1) / kScanThreads>(
         w.hist + (size_t)b * kKeyBins, kKeyBins, st.Peff, s_tmp, s_res, kb, above, cnt);
@@ -446,12 +467,16 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
             w.st[b].above = above;
         }
     }
+    int2* head = w.cand_head + (size_t)t * kCandHead;
     int2* out = w.cand + (size_t)t * kTile;
     uint32_t* h2 = w.hist2 + (size_t)b * kSubBins;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if (v[j] >= lo && v[j] <= hi) {
-            out[slot++] = make_int2(v[j], p_tile + i0 + j);
+            const int2 c = make_int2(v[j], p_tile + i0 + j);
+            if (slot < kCandHead) head[slot] = c;
+            else out[slot] = c;
+            ++slot;
             atomicAdd(&h2[(unsigned)(v[j] - lo) >> sh], 1u);
         }
     }
@@ -459,41 +484,61 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
 
 // ---- 4. threshold: exact select among the candidates, tile offsets ---------------
 // One workgroup per sequence.  Tile i belongs to thread i mod 1,024 (round u =
-// i / 1,024).  The candidates are copied once into LDS in tile order (slot
-// owners first, so every thread then issues its global loads at once); past
-// kCandLds entries they are read from global memory through a binary search
-// over the tile offsets.
+// i / 1,024).  Every thread loads its first tile's counts and the tile's
+// first kCandHead candidates (dense across tiles, so the threads' loads are
+// contiguous) with the sub-histogram; candidates beyond those (a tile with
+// more than kCandHead entries in bin B1, or rounds past the first) are read
+// from global memory where they are needed.
 __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
     constexpr int NT = kThrThreads;
-    constexpr int TPT = kMaxTilesPerSeq / NT;        // tile rounds
     constexpr int HPT = kSubBins / NT;               // sub-bins per thread
-    constexpr int kCandLds = 8192;                   // candidates staged in LDS
-    constexpr int SPT = kCandLds / NT;               // LDS slots per thread
+    constexpr int kCandReg = kCandHead;              // candidates of the first tile in registers
     __shared__ uint32_t s_hist[kSubBins];
-    __shared__ uint32_t s_cc[kMaxTilesPerSeq];      // per tile: (# s > T) | (# s == T) << 16
-    __shared__ int s_coff[kMaxTilesPerSeq + 1];     // first candidate of each tile
-    __shared__ int2 s_cand[kCandLds];               // (score, position); first holds slot owners
     __shared__ int s_tmp[NT / kWave];
     __shared__ int s_res[4];
     __shared__ unsigned long long s_key[kRankMax];
-    uint32_t* s_owner = reinterpret_cast<uint32_t*>(s_cand);   // tile << 10 | index in tile
     const int b = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    // the second-level histogram's address needs no state: load it first
+    const int tid = threadIdx.x;
+    // round trip 1: second-level histogram, state, first tile's counts and candidates
     int h2[HPT];
 #pragma unroll
     for (int i = 0; i < HPT; ++i)
         h2[i] = (int)w.hist2[(size_t)b * kSubBins + (NT - 1 - tid) * HPT + i];
     const FullState st = w.st[b];
-    if (st.Peff == 0) return;
-    const int rounds = (st.ntiles + NT - 1) / NT;    // uniform
-    int tc[TPT], ta[TPT];
+    if (st.Peff == 0) return;                        // uniform
+    // every load is unconditional (a thread past the last tile reads tile 0 and
+    // then counts nothing), so none of them waits for another
+    const bool has0 = tid < st.ntiles;
+    const size_t tile0 = (size_t)st.tile0 + (has0 ? tid : 0);
+    const int2* head0 = w.cand_head + tile0 * kCandHead;
+    int2 cr[kCandReg];                               // slots past tc0 hold stale data, unused
 #pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-        const int i = tid + u * NT;
-        tc[u] = i < st.ntiles ? w.tile_cnt[st.tile0 + i] : 0;
-        ta[u] = i < st.ntiles ? w.tile_above[st.tile0 + i] : 0;
+    for (int j = 0; j < kCandReg; j += 2) {
+        const int4 two = *reinterpret_cast<const int4*>(head0 + j);
+        cr[j] = make_int2(two.x, two.y);
+        cr[j + 1] = make_int2(two.z, two.w);
     }
+    const int tc0 = has0 ? w.tile_cnt[tile0] : 0;
+    const int ta0 = has0 ? w.tile_above[tile0] : 0;
+    const int rounds = (st.ntiles + NT - 1) / NT;    // uniform
+    // fn(candidate) for every candidate of this thread's tile in round u
+    auto visit = [&](int u, auto&& fn) {
+        const int i = tid + u * NT;
+        if (i >= st.ntiles) return;
+        const size_t t = (size_t)st.tile0 + i;
+        const int2* cg = w.cand + t * kTile;
+        const int2* ch = w.cand_head + t * kCandHead;
+        if (u == 0) {
+#pragma unroll
+            for (int j = 0; j < kCandReg; ++j)
+                if (j < tc0) fn(cr[j]);
+            for (int j = kCandReg; j < tc0; ++j) fn(cg[j]);
+        } else {
+            const int tc = w.tile_cnt[t];
+            for (int j = 0; j < tc; ++j) fn(j < kCandHead ? ch[j] : cg[j]);
+        }
+    };
+
     int lo, hi, sh, nb;
     key_interval(st.kb, lo, hi);
     sub_digit(lo, hi, sh, nb);
@@ -506,70 +551,16 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         hi = (sh == 0) ? nlo : min(hi, nlo + (1 << sh) - 1);
         lo = nlo;
     }
-    // tile offsets in tile order, one block scan per round; slot owners
-    int coff[TPT];
-    int nc = 0;
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-        coff[u] = 0;
-        if (u < rounds) {
-            int tot;
-            coff[u] = nc + block_exclusive_scan<NT>(tc[u], s_tmp, tot);
-            nc += tot;
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-        const int i = tid + u * NT;
-        if (i < st.ntiles) {
-            s_coff[i] = coff[u];
-            s_cc[i] = 0;
-            for (int k = 0; k < tc[u] && coff[u] + k < kCandLds; ++k)
-                s_owner[coff[u] + k] = ((uint32_t)i << 10) | (uint32_t)k;
-        }
-    }
-    if (tid == 0) s_coff[st.ntiles] = nc;
-    __syncthreads();
-    const int n_lds = min(nc, kCandLds);
-    uint32_t own[SPT];
-#pragma unroll
-    for (int j = 0; j < SPT; ++j) {
-        const int i = tid + j * NT;
-        own[j] = i < n_lds ? s_owner[i] : 0u;
-    }
-    __syncthreads();                                 // owners read: slots become candidates
-    {
-        int2 c[SPT];
-#pragma unroll
-        for (int j = 0; j < SPT; ++j) {
-            const int i = tid + j * NT;
-            c[j] = i < n_lds ? w.cand[(size_t)(st.tile0 + (own[j] >> 10)) * kTile + (own[j] & 1023u)]
-                             : make_int2(-1, 0);
-        }
-#pragma unroll
-        for (int j = 0; j < SPT; ++j)
-            if (tid + j * NT < n_lds) s_cand[tid + j * NT] = c[j];
-    }
-    __syncthreads();
-    auto cand_at = [&](int i) -> int2 {              // 0 <= i < nc
-        if (i < kCandLds) return s_cand[i];
-        int t = 0;                                   // last tile with s_coff <= i
-        for (int step = kMaxTilesPerSeq / 2; step > 0; step >>= 1) {
-            const int m = t + step;
-            if (m < st.ntiles && s_coff[m] <= i) t = m;
-        }
-        return w.cand[(size_t)(st.tile0 + t) * kTile + (i - s_coff[t])];
-    };
     // more 12-bit passes while the sub-bin holds several values and > kRankMax entries
     while (lo < hi && cnt > kRankMax) {              // uniform: lo, hi, cnt from LDS
         int sh2, nb2;
         sub_digit(lo, hi, sh2, nb2);
         for (int i = tid; i < nb2; i += NT) s_hist[i] = 0;
         __syncthreads();
-        for (int i = tid; i < nc; i += NT) {
-            const int v = cand_at(i).x;
-            if (v >= lo && v <= hi) atomicAdd(&s_hist[(unsigned)(v - lo) >> sh2], 1u);
-        }
+        for (int u = 0; u < rounds; ++u)
+            visit(u, [&](int2 c) {
+                if (c.x >= lo && c.x <= hi) atomicAdd(&s_hist[(unsigned)(c.x - lo) >> sh2], 1u);
+            });
         __syncthreads();
         find_bin<NT, kSubBins / NT>(s_hist, nb2, need, s_tmp, s_res, d, a, cnt);
         need -= a;
@@ -582,24 +573,17 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         T = lo;
         needT = need;
     } else {
-        // <= kRankMax entries in [lo, hi]: rank them by the key (score, ~position);
-        // slots are taken one wave at a time (ballot, one LDS atomic per wave)
+        // <= kRankMax entries in [lo, hi]: rank them by the key (score, ~position)
         if (tid == 0) s_res[3] = 0;
         __syncthreads();
-        for (int base = 0; base < nc; base += NT) {  // uniform trip count
-            const int i = base + tid;
-            const int2 v = i < nc ? cand_at(i) : make_int2(-1, 0);
-            const bool in = v.x >= lo && v.x <= hi;
-            const uint64_t m = __ballot(in);
-            if (m) {
-                int first = 0;
-                if (lane == 0) first = atomicAdd(&s_res[3], __popcll(m));
-                first = __shfl(first, 0);
-                const int slot = first + lane_rank64(m);
-                if (in && slot < kRankMax)
-                    s_key[slot] = ((unsigned long long)(uint32_t)v.x << 32) | (uint32_t)~(uint32_t)v.y;
-            }
-        }
+        for (int u = 0; u < rounds; ++u)
+            visit(u, [&](int2 c) {
+                if (c.x >= lo && c.x <= hi) {
+                    const int slot = atomicAdd(&s_res[3], 1);
+                    if (slot < kRankMax)
+                        s_key[slot] = ((unsigned long long)(uint32_t)c.x << 32) | (uint32_t)~(uint32_t)c.y;
+                }
+            });
         __syncthreads();
         rank_select_key(s_key, cnt, need, s_res);
         __syncthreads();
@@ -607,31 +591,28 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         needT = s_res[1];
     }
 
-    // per-tile counts of candidates above / at the threshold
-    for (int i = tid; i < nc; i += NT) {
-        const int2 v = cand_at(i);
-        if (v.x >= 0 && v.x >= T)
-            atomicAdd(&s_cc[min(v.y / kTile, kMaxTilesPerSeq - 1)], v.x > T ? 1u : 0x10000u);
-    }
-    __syncthreads();
-    // exclusive prefix over this sequence's tiles, in tile order
+    // per tile: entries above T (above bin B1 or candidates > T) and at T; exclusive
+    // prefix over this sequence's tiles, in tile order
     int og = 0, oe = 0;
-#pragma unroll
-    for (int u = 0; u < TPT; ++u) {
-        if (u < rounds) {
-            const int i = tid + u * NT;
-            const uint32_t c = i < st.ntiles ? s_cc[i] : 0u;
-            const int gl = ta[u] + (int)(c & 0xFFFFu), el = (int)(c >> 16);
-            int tg, te;
-            const int pg = block_exclusive_scan<NT>(gl, s_tmp, tg);
-            const int pe = block_exclusive_scan<NT>(el, s_tmp, te);
-            if (i < st.ntiles) {
-                w.tile_off[2 * (st.tile0 + i)] = og + pg;
-                w.tile_off[2 * (st.tile0 + i) + 1] = oe + pe;
-            }
-            og += tg;
-            oe += te;
+    for (int u = 0; u < rounds; ++u) {               // uniform
+        const int i = tid + u * NT;
+        int gl = 0, el = 0;
+        if (i < st.ntiles) {
+            gl = u == 0 ? ta0 : w.tile_above[st.tile0 + i];
+            visit(u, [&](int2 c) {
+                gl += c.x > T;
+                el += c.x == T;
+            });
         }
+        int tg, te;
+        const int pg = block_exclusive_scan<NT>(gl, s_tmp, tg);
+        const int pe = block_exclusive_scan<NT>(el, s_tmp, te);
+        if (i < st.ntiles) {
+            w.tile_off[2 * (st.tile0 + i)] = og + pg;
+            w.tile_off[2 * (st.tile0 + i) + 1] = oe + pe;
+        }
+        og += tg;
+        oe += te;
     }
     if (tid == 0) {
         w.st[b].T = T;
@@ -648,32 +629,35 @@ __global__ __launch_bounds__(kScanThreads) void full_write_kernel(int B, int P,
     __shared__ int s_b;
     __shared__ int s_tmp[kScanThreads / kWave];
     const int t = blockIdx.x;
+    // the tile's scores and output offsets sit at t whatever its sequence: load first
+    const int* sc = w.scores + (size_t)t * kTile;
+    constexpr int PER = kTile / kScanThreads;   // contiguous positions per thread
+    const int i0 = threadIdx.x * PER;
+    int v[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) v[j] = sc[i0 + j];
+    const int tile_gt = w.tile_off[2 * t], tile_eq = w.tile_off[2 * t + 1];
+    FullState st;
+    const int b = tile_state(w.st, B, t, &s_b, st);
     // tail fill of sequence t (each block handles at most one sequence's tail)
     if (t < B) {
-        const int Peff = w.st[t].Peff;
+        const int Peff = B == 1 ? st.Peff : w.st[t].Peff;
         for (int i = Peff + threadIdx.x; i < P; i += kScanThreads) {
             pool_pos[(size_t)t * P + i] = -1;
             pool_score[(size_t)t * P + i] = -1;
         }
         if (threadIdx.x == 0) pool_len[t] = Peff;
     }
-    const int b = tile_seq(w.st, B, t, &s_b);
     if (b < 0) return;
-    const FullState st = w.st[b];
     const int p_tile = (t - st.tile0) * kTile;
     const int nvalid = min(kTile, st.E - p_tile);
-    const int* sc = w.scores + (size_t)t * kTile;
-    constexpr int PER = kTile / kScanThreads;   // contiguous positions per thread
-    const int i0 = threadIdx.x * PER;
-    int v[PER];
     int n_eq = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        v[j] = (i0 + j < nvalid) ? sc[i0 + j] : -1;   // scores are >= 0
+        if (i0 + j >= nvalid) v[j] = -1;             // scores are >= 0
         n_eq += (v[j] >= 0) & (v[j] == st.T);
     }
     int tot;
-    const int tile_gt = w.tile_off[2 * t], tile_eq = w.tile_off[2 * t + 1];
     const int eq_before = block_exclusive_scan<kScanThreads>(n_eq, s_tmp, tot) + tile_eq;
     int n_sel = 0, eq_rank = eq_before;
     bool take[PER];

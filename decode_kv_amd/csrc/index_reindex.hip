@@ -24,30 +24,37 @@ __global__ __launch_bounds__(kReThreads) void reindex_kernel(
     const int l = lane_id();
     const int base = blockIdx.x * kReThreads + (threadIdx.x / kWave) * kWave;
     if (base >= P) return;
-    const int n = min(cand_len[b], P);
     const int* cp = cand_pos + (size_t)b * P;
     int* out = score + (size_t)b * P;
+    // round trip 1: the list length, this wave's four groups of candidate
+    // positions (indices clamped into the row, so every load is unconditional),
+    // the index query and the row offset
+    int pos[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pos[u] = cp[min(base + 16 * u + (l & 15), P - 1)];
+    const int n = min(cand_len[b], P);
+    i32x4 qa[NB];
+    uint32_t wr[NB][4];
+    load_index_query<NB>(q + (size_t)b * H * kDk, wts + (size_t)b * H, H, qa, wr);
+    const long long roff = row_off[b];
     if (base >= n) {
         if (base + l < P) out[base + l] = -1;
         return;
     }
-    i32x4 qa[NB];
-    uint32_t wr[NB][4];
-    load_index_query<NB>(q + (size_t)b * H * kDk, wts + (size_t)b * H, H, qa, wr);
-    const int8_t* kb = keys + (size_t)row_off[b] * kDk;
-    uint32_t part[4] = {0u, 0u, 0u, 0u};
+    // round trip 2: every group's key rows (entries past the list read the
+    // sequence's first candidate row, which exists since n > 0)
+    const int8_t* kb = keys + (size_t)roff * kDk + (l >> 4) * 16;
+    const int pos0 = __builtin_amdgcn_readfirstlane(pos[0]);   // lane 0 of group 0: entry base < n
+    i32x4 kop[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-        const int g0 = base + 16 * u;
-        if (g0 < n) {                                  // wave-uniform
-            int i = g0 + (l & 15);
-            i = i < n ? i : g0;
-            const int pos = max(cp[i], 0);             // valid entries are >= 0
-            const i32x4 kop =
-                *reinterpret_cast<const i32x4*>(kb + (size_t)pos * kDk + (l >> 4) * 16);
-            part[u] = score_partial16<NB>(qa, wr, kop);
-        }
+        const int i = base + 16 * u + (l & 15);
+        const int p = (i < n && pos[u] >= 0) ? pos[u] : pos0;
+        kop[u] = *reinterpret_cast<const i32x4*>(kb + (size_t)p * kDk);
     }
+    uint32_t part[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) part[u] = score_partial16<NB>(qa, wr, kop[u]);
     const int mine = (int)reduce_rows4(part);          // candidate base + l
     const int i = base + l;
     if (i < P) out[i] = i < n ? mine : -1;

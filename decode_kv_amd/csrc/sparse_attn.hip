@@ -291,8 +291,8 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
     __shared__ float2 s_ml[kAttnMaxSplits];
     const int h = blockIdx.x, b = blockIdx.y;
     const size_t row0 = (size_t)b * n_splits * Hq + h;          // split s at row0 + s * Hq
-    for (int s = threadIdx.x; s < n_splits; s += 128)
-        s_ml[s] = *reinterpret_cast<const float2*>(part_ml + (row0 + (size_t)s * Hq) * 2);
+    // partial outputs first, then this thread's (m, l): the LDS store of (m, l)
+    // must wait for its load, and nothing may wait before the partials issue
     f32x4 os[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
@@ -300,6 +300,9 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restri
         os[u] = *reinterpret_cast<const f32x4*>(part_o + (row0 + (size_t)s * Hq) * kAttnD +
                                                 4 * threadIdx.x);
     }
+    asm volatile("" ::: "memory");
+    for (int s = threadIdx.x; s < n_splits; s += 128)
+        s_ml[s] = *reinterpret_cast<const float2*>(part_ml + (row0 + (size_t)s * Hq) * 2);
     __syncthreads();
     float M = -INFINITY;
     for (int s = 0; s < n_splits; ++s) M = fmaxf(M, s_ml[s].x);

@@ -11,8 +11,14 @@
 // LDS atomics rarely collide), then 13-bit refinement digits inside the chosen
 // bin until it holds one value or at most 256 entries, which are ranked
 // exactly.  An ordered compaction (wave ballots plus one prefix over
-// (slot, wave) counts) writes s > T plus the first ties in list order.  Candidate lists are ascending in position, so
-// list order is position order.
+// (slot, wave) counts) writes s > T plus the first ties in list order.
+// Candidate lists are ascending in position, so list order is position order.
+//
+// Usually the first histogram's chosen bin and the bins above it hold at most
+// 1,024 entries: they are then compacted to LDS once, right after that
+// histogram, one per thread, and the refinement, ranking, tie order and output
+// all run on that set instead of on all 16 entries of every thread.  Lists
+// with more entries there (heavy ties, k near P) take the general path.
 #include "abi_common.h"
 #include "common.h"
 
@@ -90,6 +96,101 @@ __device__ __forceinline__ void slot_wave_scan(const int* s_cnt, int* s_pre) {
     __syncthreads();
 }
 
+// The usual case: the bin holding the keff-th largest score and the bins above
+// it hold at most one entry per thread.  One ordered compaction moves those
+// entries (in list order, which is position order) to LDS, one per thread,
+// and the threshold, the ties and the output are found among them; no later
+// pass touches the other entries.
+//   v, pos: this thread's 16 entries (i = tid + 1024 j), invalid ones -1;
+//   [lo, hi]: value range of that bin, cnt entries in it, need of them taken;
+//   M: entries in the bin or above it (<= 1,024).
+__device__ __forceinline__ void select_compacted(const int (&v)[kSelMaxP / kSelThreads],
+                                                 const int (&pos)[kSelMaxP / kSelThreads], int lo,
+                                                 int hi, int cnt, int need, int keff, int M, int k,
+                                                 int* __restrict__ out, int* __restrict__ out_len,
+                                                 uint32_t* s_hist, int* s_tmp, int* s_res,
+                                                 unsigned long long* s_key, int* s_cnt, int* s_pre,
+                                                 int* s_cs, int* s_cp) {
+    constexpr int PER = kSelMaxP / kSelThreads;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    // ordered compaction: slot = rank of (j, wave, lane) among the entries >= lo
+    uint64_t mi[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        mi[j] = __ballot(v[j] >= lo);                    // lo >= 0 excludes invalid entries
+        if (lane == 0) s_cnt[j * kSelWaves + wave] = __popcll(mi[j]);
+    }
+    slot_wave_scan(s_cnt, s_pre);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        if ((mi[j] >> lane) & 1ull) {
+            const int slot = s_pre[j * kSelWaves + wave] + lane_rank(mi[j]);
+            s_cs[slot] = v[j];
+            s_cp[slot] = pos[j];
+        }
+    }
+    __syncthreads();
+    const int sv = tid < M ? s_cs[tid] : -1;             // this thread's compacted entry
+    // narrow the bin with 13-bit digits until it is one value or <= kSelRank entries
+    while (lo < hi && cnt > kSelRank) {                  // uniform: lo, hi, cnt from LDS
+        const unsigned width = (unsigned)(hi - lo) + 1u;
+        const int bits = 32 - __clz(width - 1u);
+        const int sh = bits > 13 ? bits - 13 : 0;
+        const int nb = (int)(((width - 1u) >> sh) + 1u);
+        __syncthreads();
+        for (int i = tid; i < nb; i += kSelThreads) s_hist[i] = 0;
+        __syncthreads();
+        if (sv >= lo && sv <= hi) atomicAdd(&s_hist[(sv - lo) >> sh], 1u);
+        __syncthreads();
+        sel_find_bin(s_hist, nb, need, s_tmp, s_res);
+        const int d = s_res[0];
+        need -= s_res[1];
+        cnt = (int)s_hist[d];
+        const int nlo = lo + (d << sh);
+        hi = (sh == 0) ? nlo : min(hi, nlo + (1 << sh) - 1);
+        lo = nlo;
+    }
+    int T, needT;
+    bool all_ties;
+    if (lo == hi) {
+        T = lo;
+        needT = need;
+        all_ties = need == cnt;
+    } else {
+        // <= kSelRank entries in [lo, hi]: rank them by (score, ~compacted index)
+        if (tid == 0) s_res[3] = 0;
+        __syncthreads();
+        const bool in = sv >= lo && sv <= hi;
+        const uint64_t m = __ballot(in);
+        int first = 0;
+        if (lane == 0 && m) first = atomicAdd(&s_res[3], __popcll(m));
+        first = __builtin_amdgcn_readfirstlane(first);
+        if (in)
+            s_key[first + lane_rank(m)] =
+                ((unsigned long long)(uint32_t)sv << 32) | (uint32_t)~(uint32_t)tid;
+        __syncthreads();
+        rank_select_key(s_key, cnt, need, s_res);
+        __syncthreads();
+        T = s_res[0];
+        needT = s_res[1];
+        all_ties = s_res[2] != 0;
+    }
+    // take s > T, plus the first needT entries with s == T in position order
+    const bool eq = tid < M && sv == T;
+    bool take = tid < M && sv > T;
+    int tot;
+    if (all_ties) {
+        take = take || eq;
+    } else {
+        const int eq_before = block_exclusive_scan<kSelThreads>(eq ? 1 : 0, s_tmp, tot);
+        take = take || (eq && eq_before < needT);
+    }
+    const int o = block_exclusive_scan<kSelThreads>(take ? 1 : 0, s_tmp, tot);
+    if (take && o < keff) out[o] = s_cp[tid];
+    for (int i = keff + tid; i < k; i += kSelThreads) out[i] = -1;
+    if (tid == 0) *out_len = keff;
+}
+
 __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     const int* __restrict__ score, const int* __restrict__ cand_pos,
     const int* __restrict__ cand_len, int P, int k, int* __restrict__ sel_pos,
@@ -101,6 +202,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     __shared__ int s_res[4];
     __shared__ unsigned long long s_key[kSelRank];
     __shared__ int s_cnt[PER * kSelWaves], s_pre[PER * kSelWaves];
+    __shared__ int s_cs[kSelThreads], s_cp[kSelThreads];   // compacted scores, positions
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int* sc = score + (size_t)b * P;
@@ -148,6 +250,12 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
             const int e = (kb >> 7) + 6;
             lo = (128 + (kb & 127)) << (e - 7);
             hi = lo + (1 << (e - 7)) - 1;
+        }
+        if (s_res[1] + cnt <= kSelThreads) {  // uniform: the usual case
+            select_compacted(v, pos, lo, hi, cnt, need, keff, s_res[1] + cnt, k,
+                             sel_pos + (size_t)b * k, sel_len + b, s_hist, s_tmp, s_res, s_key,
+                             s_cnt, s_pre, s_cs, s_cp);
+            return;
         }
         // 13-bit refinement passes until the bin is one value or holds <= kSelRank
         while (lo < hi && cnt > kSelRank) {

@@ -329,6 +329,35 @@ def test_select_topk_matches_oracle(span):
             assert (got[b, len(ref):] == -1).all()
 
 
+@pytest.mark.parametrize("top_span", [40, 2000, 1 << 20])
+def test_select_topk_clustered(top_span):
+    """A cluster of 700 scores near 2^20 above a low background: the bin that
+    holds the 512th score then has far more than 256 entries, so the select
+    narrows it with further digits (to one value with ties when top_span is
+    small); the shorter lists keep the cluster and drop the background."""
+    rng = np.random.default_rng(top_span)
+    B, P = 3, 16384
+    cand_len = [16384, 5000, 1100]
+    score = rng.integers(0, 1000, size=(B, P)).astype(np.int32)
+    cand = np.zeros((B, P), dtype=np.int32)
+    for b in range(B):
+        hot = rng.choice(cand_len[b], 700, replace=False)
+        score[b, hot] = (1 << 20) + rng.integers(0, top_span, size=700)
+        cand[b] = np.sort(rng.choice(10_000_000, P, replace=False))
+    for k in [1, 300, 512, 699, 700, 1024]:
+        sel = torch.full((B, k), 0x3333, dtype=torch.int32, device=DEV)
+        sl = torch.zeros(B, dtype=torch.int32, device=DEV)
+        csa2.select_topk(torch.from_numpy(score).to(DEV), torch.from_numpy(cand).to(DEV),
+                         torch.tensor(cand_len, dtype=torch.int32, device=DEV), k, sel, sl)
+        got, gl = sel.cpu().numpy(), sl.cpu().numpy()
+        for b in range(B):
+            n = cand_len[b]
+            ref, _ = oracle.topk(score[b, :n], cand[b, :n], k)
+            assert gl[b] == len(ref)
+            assert np.array_equal(got[b, :len(ref)], ref), (top_span, k, b)
+            assert (got[b, len(ref):] == -1).all()
+
+
 # ---------------------------------------------------------------------------
 # csa2_sparse_attn_decode
 # ---------------------------------------------------------------------------

@@ -147,42 +147,63 @@ __device__ __forceinline__ int lane_rank64(uint64_t m) {
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
-// Exact rank step of a radix select: s_key[0 .. cnt) holds distinct 64-bit
-// keys (score << 32 | ~position), cnt <= 256, in LDS.  Finds the key of rank
-// need - 1 (0 = largest) and writes its score to s_res[0], the number of
-// entries with that score ranked at or above it to s_res[1], and whether that
-// is every entry with that score to s_res[2].  Four consecutive threads rank
-// one key, each comparing it with a quarter of the keys.  Needs blockDim.x >=
-// 4 * cnt; the caller synchronises before reading s_res.
-__device__ __forceinline__ void rank_select_key(const unsigned long long* s_key, int cnt,
-                                                int need, int* s_res) {
+// Upper end of the sub-range [nlo, nlo + 2^sh) of a radix digit, clipped to
+// hi; unsigned so that ranges ending at INT_MAX do not overflow.
+__device__ __forceinline__ int sub_range_hi(int nlo, int sh, int hi) {
+    return (int)min((unsigned)hi, (unsigned)nlo + ((1u << sh) - 1u));
+}
+
+// Last digits of a radix select.  [lo, hi] (0 <= lo <= hi) holds cnt entries,
+// one per thread at most (x; a thread without one passes a value outside the
+// range), and the need-th largest of them (1 <= need <= cnt) is wanted.  Each
+// pass splits the range into at most 256 sub-ranges of equal width (the top 8
+// bits of x - lo), counts them in LDS, and keeps the one holding the need-th
+// largest, until the range is one value.  On return lo == hi is that value,
+// need counts how many entries equal to it are taken, and cnt how many there
+// are.  Block-uniform arguments; s_h (256 words) and s_res[0..2] are LDS the
+// caller may reuse only after a barrier; at most 4 passes for 31-bit values.
+__device__ __forceinline__ void narrow_to_value(int x, int& lo, int& hi, int& need, int& cnt,
+                                                uint32_t* s_h, int* s_res) {
     const int tid = threadIdx.x;
-    if (tid >= 4 * cnt) return;                    // whole groups of four lanes
-    const unsigned long long mine = s_key[tid >> 2];
-    const int q = (cnt + 3) >> 2;
-    const int u0 = (tid & 3) * q, u1 = min(cnt, u0 + q);
-    int rank = 0;
-#pragma unroll 8
-    for (int u = u0; u < u1; ++u) rank += s_key[u] > mine;
-    rank += __shfl_xor(rank, 1);
-    rank += __shfl_xor(rank, 2);
-    if (rank != need - 1) return;                  // uniform within the group
-    const uint32_t ts = (uint32_t)(mine >> 32);
-    int ties = 0, all = 0;
-#pragma unroll 8
-    for (int u = u0; u < u1; ++u) {
-        const bool same = (uint32_t)(s_key[u] >> 32) == ts;
-        ties += same & (s_key[u] >= mine);
-        all += same;
-    }
-    ties += __shfl_xor(ties, 1);
-    ties += __shfl_xor(ties, 2);
-    all += __shfl_xor(all, 1);
-    all += __shfl_xor(all, 2);
-    if ((tid & 3) == 0) {
-        s_res[0] = (int)ts;
-        s_res[1] = ties;
-        s_res[2] = ties == all;
+    while (lo < hi) {
+        const unsigned width_m1 = (unsigned)(hi - lo);
+        const int bits = 32 - __clz(width_m1);
+        const int sh = bits > 8 ? bits - 8 : 0;
+        if (tid < 256) s_h[tid] = 0;
+        __syncthreads();
+        if (x >= lo && x <= hi) atomicAdd(&s_h[(unsigned)(x - lo) >> sh], 1u);
+        __syncthreads();
+        if (tid < kWave) {
+            // lane l holds sub-ranges 255-4l .. 252-4l: lane 0 the highest
+            uint32_t c[4];
+            int sum = 0;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                c[i] = s_h[255 - 4 * tid - i];
+                sum += (int)c[i];
+            }
+            const int incl = wave_inclusive_scan(sum);
+            int above = incl - sum;
+            if (above < need && need <= incl) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (above + (int)c[i] >= need) {
+                        s_res[0] = 255 - 4 * tid - i;
+                        s_res[1] = above;
+                        s_res[2] = (int)c[i];
+                        break;
+                    }
+                    above += (int)c[i];
+                }
+            }
+        }
+        __syncthreads();
+        const int d = s_res[0];
+        need -= s_res[1];
+        cnt = s_res[2];
+        const int nlo = lo + (d << sh);
+        hi = sub_range_hi(nlo, sh, hi);
+        lo = nlo;
     }
 }
 

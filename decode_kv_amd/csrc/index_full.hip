@@ -40,7 +40,7 @@ constexpr int kSubBits = 12;
 constexpr int kSubBins = 1 << kSubBits;  // second-level histogram / refinement digit
 constexpr int kThrThreads = 1024;
 constexpr int kMaxTilesPerSeq = 8192;    // LDS tile tables of the threshold kernel (8M positions)
-constexpr int kRankMax = 256;            // entries ranked exactly
+constexpr int kLastMax = kThrThreads;    // entries the last digits take, one per thread
 constexpr int kCandHead = 16;            // candidates per tile in the dense head array
 constexpr int kMaxBatch = 4096;
 
@@ -64,10 +64,12 @@ struct FullWs {
     int* tile_cnt;        // [Tmax] entries of the tile inside bin B1
     int* tile_off;        // [Tmax][2] output offsets among s > T and among s == T
     uint16_t* tile_hist;  // [Tmax][kKeyBins]
-    int2* cand_head;      // [Tmax][kCandHead] first candidates of every tile, dense
-    int2* cand;           // [Tmax][kTile] (score, position) inside bin B1, per tile (slots
-                          // >= kCandHead; the first kCandHead live in cand_head)
+    int* cand_head;       // [kCandHead][Tmax] scores of every tile's first candidates,
+                          // slot-major so that one slot of consecutive tiles is contiguous
+    int* cand;            // [Tmax][kTile] scores inside bin B1, per tile (slots >= kCandHead;
+                          // the first kCandHead live in cand_head)
     int* scores;          // [Tmax][kTile]
+    int tmax;             // Tmax: the slot stride of cand_head
 };
 
 static long long full_tile_bound(int B, long long total_len) {
@@ -90,9 +92,10 @@ static size_t full_ws_layout(int B, long long total_len, char* base, FullWs* w) 
     x.tile_cnt = reinterpret_cast<int*>(take(4ull * T));
     x.tile_off = reinterpret_cast<int*>(take(8ull * T));
     x.tile_hist = reinterpret_cast<uint16_t*>(take(2ull * (size_t)T * kKeyBins));
-    x.cand_head = reinterpret_cast<int2*>(take(8ull * (size_t)T * kCandHead));
-    x.cand = reinterpret_cast<int2*>(take(8ull * (size_t)T * kTile));
+    x.cand_head = reinterpret_cast<int*>(take(4ull * (size_t)T * kCandHead));
+    x.cand = reinterpret_cast<int*>(take(4ull * (size_t)T * kTile));
     x.scores = reinterpret_cast<int*>(take(4ull * (size_t)T * kTile));
+    x.tmax = (int)T;
     if (w) *w = x;
     return off;
 }
@@ -467,15 +470,14 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
             w.st[b].above = above;
         }
     }
-    int2* head = w.cand_head + (size_t)t * kCandHead;
-    int2* out = w.cand + (size_t)t * kTile;
+    int* head = w.cand_head + t;
+    int* out = w.cand + (size_t)t * kTile;
     uint32_t* h2 = w.hist2 + (size_t)b * kSubBins;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if (v[j] >= lo && v[j] <= hi) {
-            const int2 c = make_int2(v[j], p_tile + i0 + j);
-            if (slot < kCandHead) head[slot] = c;
-            else out[slot] = c;
+            if (slot < kCandHead) head[(size_t)slot * w.tmax] = v[j];
+            else out[slot] = v[j];
             ++slot;
             atomicAdd(&h2[(unsigned)(v[j] - lo) >> sh], 1u);
         }
@@ -496,7 +498,7 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
     __shared__ uint32_t s_hist[kSubBins];
     __shared__ int s_tmp[NT / kWave];
     __shared__ int s_res[4];
-    __shared__ unsigned long long s_key[kRankMax];
+    __shared__ int s_val[kLastMax];
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     // round trip 1: second-level histogram, state, first tile's counts and candidates
@@ -510,32 +512,26 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
     // then counts nothing), so none of them waits for another
     const bool has0 = tid < st.ntiles;
     const size_t tile0 = (size_t)st.tile0 + (has0 ? tid : 0);
-    const int2* head0 = w.cand_head + tile0 * kCandHead;
-    int2 cr[kCandReg];                               // slots past tc0 hold stale data, unused
+    // slot j of consecutive tiles is contiguous: each load is coalesced
+    int cr[kCandReg];                                // slots past tc0 hold stale data, unused
 #pragma unroll
-    for (int j = 0; j < kCandReg; j += 2) {
-        const int4 two = *reinterpret_cast<const int4*>(head0 + j);
-        cr[j] = make_int2(two.x, two.y);
-        cr[j + 1] = make_int2(two.z, two.w);
-    }
-    const int tc0 = has0 ? w.tile_cnt[tile0] : 0;
-    const int ta0 = has0 ? w.tile_above[tile0] : 0;
+    for (int j = 0; j < kCandReg; ++j) cr[j] = w.cand_head[(size_t)j * w.tmax + tile0];
+    const int tc0 = w.tile_cnt[tile0];               // read for tile 0 too, then masked
+    const int ta0 = w.tile_above[tile0];
+    const int ncr = has0 ? min(tc0, kCandReg) : 0;   // candidates held in cr
     const int rounds = (st.ntiles + NT - 1) / NT;    // uniform
-    // fn(candidate) for every candidate of this thread's tile in round u
-    auto visit = [&](int u, auto&& fn) {
+    // fn(score) for every candidate of this thread's tile in round u that is
+    // not held in cr (round 0 slots >= kCandReg, every slot of later rounds)
+    auto visit_mem = [&](int u, auto&& fn) {
         const int i = tid + u * NT;
         if (i >= st.ntiles) return;
         const size_t t = (size_t)st.tile0 + i;
-        const int2* cg = w.cand + t * kTile;
-        const int2* ch = w.cand_head + t * kCandHead;
+        const int* cg = w.cand + t * kTile;
         if (u == 0) {
-#pragma unroll
-            for (int j = 0; j < kCandReg; ++j)
-                if (j < tc0) fn(cr[j]);
             for (int j = kCandReg; j < tc0; ++j) fn(cg[j]);
         } else {
             const int tc = w.tile_cnt[t];
-            for (int j = 0; j < tc; ++j) fn(j < kCandHead ? ch[j] : cg[j]);
+            for (int j = 0; j < tc; ++j) fn(j < kCandHead ? w.cand_head[(size_t)j * w.tmax + t] : cg[j]);
         }
     };
 
@@ -548,48 +544,60 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
     need -= a;
     {
         const int nlo = lo + (d << sh);
-        hi = (sh == 0) ? nlo : min(hi, nlo + (1 << sh) - 1);
+        hi = sub_range_hi(nlo, sh, hi);
         lo = nlo;
     }
-    // more 12-bit passes while the sub-bin holds several values and > kRankMax entries
-    while (lo < hi && cnt > kRankMax) {              // uniform: lo, hi, cnt from LDS
+    // more 12-bit passes while the sub-bin holds several values and > kLastMax entries
+    while (lo < hi && cnt > kLastMax) {              // uniform: lo, hi, cnt from LDS
         int sh2, nb2;
         sub_digit(lo, hi, sh2, nb2);
         for (int i = tid; i < nb2; i += NT) s_hist[i] = 0;
         __syncthreads();
+#pragma unroll
+        for (int j = 0; j < kCandReg; ++j)
+            if (j < ncr && cr[j] >= lo && cr[j] <= hi) atomicAdd(&s_hist[(unsigned)(cr[j] - lo) >> sh2], 1u);
         for (int u = 0; u < rounds; ++u)
-            visit(u, [&](int2 c) {
-                if (c.x >= lo && c.x <= hi) atomicAdd(&s_hist[(unsigned)(c.x - lo) >> sh2], 1u);
+            visit_mem(u, [&](int c) {
+                if (c >= lo && c <= hi) atomicAdd(&s_hist[(unsigned)(c - lo) >> sh2], 1u);
             });
         __syncthreads();
         find_bin<NT, kSubBins / NT>(s_hist, nb2, need, s_tmp, s_res, d, a, cnt);
         need -= a;
         const int nlo = lo + (d << sh2);
-        hi = (sh2 == 0) ? nlo : min(hi, nlo + (1 << sh2) - 1);
+        hi = sub_range_hi(nlo, sh2, hi);
         lo = nlo;
     }
-    int T, needT;
-    if (lo == hi) {
-        T = lo;
-        needT = need;
-    } else {
-        // <= kRankMax entries in [lo, hi]: rank them by the key (score, ~position)
+    if (lo < hi) {
+        // <= kLastMax entries in [lo, hi]: gather their scores, one per thread,
+        // and take the last digits on them; ties at the resulting value are
+        // taken in position order by the write kernel
         if (tid == 0) s_res[3] = 0;
         __syncthreads();
+        // candidates in registers: one LDS atomic per wave and slot
+        const int lane = tid & (kWave - 1);
+#pragma unroll
+        for (int j = 0; j < kCandReg; ++j) {
+            const bool in = j < ncr && cr[j] >= lo && cr[j] <= hi;
+            const uint64_t m = __ballot(in);
+            if (m) {                                 // uniform within the wave
+                int first = 0;
+                if (lane == 0) first = atomicAdd(&s_res[3], __popcll(m));
+                first = __builtin_amdgcn_readfirstlane(first);
+                const int slot = first + lane_rank64(m);
+                if (in && slot < kLastMax) s_val[slot] = cr[j];
+            }
+        }
         for (int u = 0; u < rounds; ++u)
-            visit(u, [&](int2 c) {
-                if (c.x >= lo && c.x <= hi) {
+            visit_mem(u, [&](int c) {
+                if (c >= lo && c <= hi) {
                     const int slot = atomicAdd(&s_res[3], 1);
-                    if (slot < kRankMax)
-                        s_key[slot] = ((unsigned long long)(uint32_t)c.x << 32) | (uint32_t)~(uint32_t)c.y;
+                    if (slot < kLastMax) s_val[slot] = c;
                 }
             });
         __syncthreads();
-        rank_select_key(s_key, cnt, need, s_res);
-        __syncthreads();
-        T = s_res[0];
-        needT = s_res[1];
+        narrow_to_value(tid < cnt ? s_val[tid] : -1, lo, hi, need, cnt, s_hist, s_res);
     }
+    const int T = lo, needT = need;
 
     // per tile: entries above T (above bin B1 or candidates > T) and at T; exclusive
     // prefix over this sequence's tiles, in tile order
@@ -599,9 +607,16 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         int gl = 0, el = 0;
         if (i < st.ntiles) {
             gl = u == 0 ? ta0 : w.tile_above[st.tile0 + i];
-            visit(u, [&](int2 c) {
-                gl += c.x > T;
-                el += c.x == T;
+            if (u == 0) {
+#pragma unroll
+                for (int j = 0; j < kCandReg; ++j) {
+                    gl += j < ncr && cr[j] > T;
+                    el += j < ncr && cr[j] == T;
+                }
+            }
+            visit_mem(u, [&](int c) {
+                gl += c > T;
+                el += c == T;
             });
         }
         int tg, te;

@@ -38,7 +38,7 @@ __device__ __forceinline__ int sel_key(int s) {
 
 constexpr int kSelKeyBins = 3200;
 constexpr int kSelRefBins = 8192;   // 13-bit refinement digit
-constexpr int kSelRank = 256;       // entries ranked exactly
+constexpr int kSelLast = kSelThreads;   // entries the last digits take, one per thread
 
 // The bin holding the need-th largest entry of an LDS histogram (bins in
 // ascending value order): writes (bin, entries in higher bins) to s_res.
@@ -109,8 +109,7 @@ __device__ __forceinline__ void select_compacted(const int (&v)[kSelMaxP / kSelT
                                                  int hi, int cnt, int need, int keff, int M, int k,
                                                  int* __restrict__ out, int* __restrict__ out_len,
                                                  uint32_t* s_hist, int* s_tmp, int* s_res,
-                                                 unsigned long long* s_key, int* s_cnt, int* s_pre,
-                                                 int* s_cs, int* s_cp) {
+                                                 int* s_cnt, int* s_pre, int* s_cs, int* s_cp) {
     constexpr int PER = kSelMaxP / kSelThreads;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     // ordered compaction: slot = rank of (j, wave, lane) among the entries >= lo
@@ -131,50 +130,9 @@ __device__ __forceinline__ void select_compacted(const int (&v)[kSelMaxP / kSelT
     }
     __syncthreads();
     const int sv = tid < M ? s_cs[tid] : -1;             // this thread's compacted entry
-    // narrow the bin with 13-bit digits until it is one value or <= kSelRank entries
-    while (lo < hi && cnt > kSelRank) {                  // uniform: lo, hi, cnt from LDS
-        const unsigned width = (unsigned)(hi - lo) + 1u;
-        const int bits = 32 - __clz(width - 1u);
-        const int sh = bits > 13 ? bits - 13 : 0;
-        const int nb = (int)(((width - 1u) >> sh) + 1u);
-        __syncthreads();
-        for (int i = tid; i < nb; i += kSelThreads) s_hist[i] = 0;
-        __syncthreads();
-        if (sv >= lo && sv <= hi) atomicAdd(&s_hist[(sv - lo) >> sh], 1u);
-        __syncthreads();
-        sel_find_bin(s_hist, nb, need, s_tmp, s_res);
-        const int d = s_res[0];
-        need -= s_res[1];
-        cnt = (int)s_hist[d];
-        const int nlo = lo + (d << sh);
-        hi = (sh == 0) ? nlo : min(hi, nlo + (1 << sh) - 1);
-        lo = nlo;
-    }
-    int T, needT;
-    bool all_ties;
-    if (lo == hi) {
-        T = lo;
-        needT = need;
-        all_ties = need == cnt;
-    } else {
-        // <= kSelRank entries in [lo, hi]: rank them by (score, ~compacted index)
-        if (tid == 0) s_res[3] = 0;
-        __syncthreads();
-        const bool in = sv >= lo && sv <= hi;
-        const uint64_t m = __ballot(in);
-        int first = 0;
-        if (lane == 0 && m) first = atomicAdd(&s_res[3], __popcll(m));
-        first = __builtin_amdgcn_readfirstlane(first);
-        if (in)
-            s_key[first + lane_rank(m)] =
-                ((unsigned long long)(uint32_t)sv << 32) | (uint32_t)~(uint32_t)tid;
-        __syncthreads();
-        rank_select_key(s_key, cnt, need, s_res);
-        __syncthreads();
-        T = s_res[0];
-        needT = s_res[1];
-        all_ties = s_res[2] != 0;
-    }
+    narrow_to_value(sv, lo, hi, need, cnt, s_hist, s_res);
+    const int T = lo, needT = need;
+    const bool all_ties = need == cnt;
     // take s > T, plus the first needT entries with s == T in position order
     const bool eq = tid < M && sv == T;
     bool take = tid < M && sv > T;
@@ -200,7 +158,6 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     __shared__ uint32_t s_hist[kSelRefBins];
     __shared__ int s_tmp[kSelWaves];
     __shared__ int s_res[4];
-    __shared__ unsigned long long s_key[kSelRank];
     __shared__ int s_cnt[PER * kSelWaves], s_pre[PER * kSelWaves];
     __shared__ int s_cs[kSelThreads], s_cp[kSelThreads];   // compacted scores, positions
     const int b = blockIdx.x;
@@ -253,12 +210,12 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         }
         if (s_res[1] + cnt <= kSelThreads) {  // uniform: the usual case
             select_compacted(v, pos, lo, hi, cnt, need, keff, s_res[1] + cnt, k,
-                             sel_pos + (size_t)b * k, sel_len + b, s_hist, s_tmp, s_res, s_key,
-                             s_cnt, s_pre, s_cs, s_cp);
+                             sel_pos + (size_t)b * k, sel_len + b, s_hist, s_tmp, s_res, s_cnt,
+                             s_pre, s_cs, s_cp);
             return;
         }
-        // 13-bit refinement passes until the bin is one value or holds <= kSelRank
-        while (lo < hi && cnt > kSelRank) {
+        // 13-bit refinement passes until the bin is one value or holds <= kSelLast
+        while (lo < hi && cnt > kSelLast) {
             const unsigned width = (unsigned)(hi - lo) + 1u;
             const int bits = 32 - __clz(width - 1u);
             const int sh = bits > 13 ? bits - 13 : 0;
@@ -275,18 +232,15 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
             need -= s_res[1];
             cnt = (int)s_hist[d];
             const int nlo = lo + (d << sh);
-            const int nhi = (sh == 0) ? nlo : min(hi, nlo + (1 << sh) - 1);
+            const int nhi = sub_range_hi(nlo, sh, hi);
             lo = nlo;
             hi = nhi;
         }
-        if (lo == hi) {
-            T = lo;
-            needT = need;
-            all_ties = need == cnt;
-        } else {
-            // <= kSelRank entries in [lo, hi]: rank them by the key (score, ~index)
+        if (lo < hi) {
+            // <= kSelLast entries in [lo, hi]: gather their scores, one per
+            // thread (one LDS atomic per wave for the slots), and take the last
+            // digits on them
             __syncthreads();
-            // slots: one LDS atomic per wave for all of its entries in the bin
             uint64_t min_[PER];
             int wcount = 0;
 #pragma unroll
@@ -301,18 +255,15 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
             for (int j = 0; j < PER; ++j) {
                 const bool in = (min_[j] >> lane) & 1ull;
                 const int slot = first + lane_rank(min_[j]);
-                if (in && slot < kSelRank)
-                    s_key[slot] = ((unsigned long long)(uint32_t)v[j] << 32) |
-                                  (uint32_t)~(uint32_t)(tid + j * kSelThreads);
+                if (in && slot < kSelLast) s_cs[slot] = v[j];
                 first += __popcll(min_[j]);
             }
             __syncthreads();
-            rank_select_key(s_key, cnt, need, s_res);
-            __syncthreads();
-            T = s_res[0];
-            needT = s_res[1];
-            all_ties = s_res[2] != 0;
+            narrow_to_value(tid < cnt ? s_cs[tid] : -1, lo, hi, need, cnt, s_hist, s_res);
         }
+        T = lo;
+        needT = need;
+        all_ties = need == cnt;
     }
 
     // ordered compaction over entries i = tid + 1024 j (slot j, then thread);

@@ -220,7 +220,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, ts[i]);
         tmax = rows4_max(tmax);
         const float m_new = fmaxf(m_run, tmax);   // finite: every tile has a valid row
-        const float alpha = exp2f(m_run - m_new);
         float p[8], psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -228,10 +227,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
             psum += p[i];
         }
         psum = rows4_sum(psum);
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+        if (t == 0) {                              // nothing accumulated yet
+            l_run = psum;
+        } else {
+            const float alpha = exp2f(m_run - m_new);
+            l_run = l_run * alpha + psum;
 #pragma unroll
-        for (int nb = 0; nb < kNb; ++nb) o[nb] *= alpha;   // this lane's head
+            for (int nb = 0; nb < kNb; ++nb) o[nb] *= alpha;   // this lane's head
+        }
+        m_run = m_new;
 
         u32x4 ph_u, pl_u;
 #pragma unroll
@@ -276,66 +280,88 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
 }
 
 // Log-sum-exp merge of the split partials: one workgroup per (head, sequence),
-// 128 threads x 4 output elements.  Every split's (m, l) is read with one
-// vector load (thread s takes split s) and shared through LDS, while each
-// thread's partial outputs of up to CH splits are in flight at the same time,
-// so the merge costs one memory round trip; splits beyond CH follow in further
-// chunks.  Splits are folded in split order; an empty split has m = -inf and
-// contributes nothing.
+// 128 threads x 4 output elements.  Each thread issues the loads of its
+// partial outputs of CH splits (indices past the last split reread it and get
+// weight 0) and, for split s = thread, that split's (m, l), all before any of
+// them is used, so the merge costs one memory round trip; splits beyond CH
+// follow in further chunks.  CH is the smallest of 8, 16, 24, 32 that covers
+// the splits when it can.
+// The running maxima and sums are reduced once per workgroup: the split
+// weights 2^(m_s - M) go to LDS and every thread reads them four at a time.
+// An empty split has m = -inf and weight 0.  The pointers are not
+// __restrict__ so that the loads keep their order around the empty asm.
 template <int CH>
-__global__ __launch_bounds__(128) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml,
+__global__ __launch_bounds__(128) void attn_combine_kernel(const float* part_o,
+                                                           const float* part_ml,
                                                            int Hq, int n_splits,
                                                            float* __restrict__ out,
                                                            float* __restrict__ lse) {
-    __shared__ float2 s_ml[kAttnMaxSplits];
-    const int h = blockIdx.x, b = blockIdx.y;
+    __shared__ __attribute__((aligned(16))) float s_w[kAttnMaxSplits + 32];   // zero-padded to CH
+    __shared__ float s_red[2][2];
+    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
     const size_t row0 = (size_t)b * n_splits * Hq + h;          // split s at row0 + s * Hq
-    // partial outputs first, then this thread's (m, l): the LDS store of (m, l)
-    // must wait for its load, and nothing may wait before the partials issue
     f32x4 os[CH];
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
         const int s = min(u, n_splits - 1);
-        os[u] = *reinterpret_cast<const f32x4*>(part_o + (row0 + (size_t)s * Hq) * kAttnD +
-                                                4 * threadIdx.x);
+        os[u] = *reinterpret_cast<const f32x4*>(part_o + (row0 + (size_t)s * Hq) * kAttnD + 4 * tid);
     }
+    const float2 ml = *reinterpret_cast<const float2*>(
+        part_ml + (row0 + (size_t)min(tid, n_splits - 1) * Hq) * 2);   // used for tid < n_splits
     asm volatile("" ::: "memory");
-    for (int s = threadIdx.x; s < n_splits; s += 128)
-        s_ml[s] = *reinterpret_cast<const float2*>(part_ml + (row0 + (size_t)s * Hq) * 2);
+    // M = max over splits of m_s; weights w_s = 2^(m_s - M); lsum = sum w_s l_s
+    float mloc = tid < n_splits ? ml.x : -INFINITY;
+    for (int s = tid + 128; s < n_splits; s += 128)
+        mloc = fmaxf(mloc, part_ml[(row0 + (size_t)s * Hq) * 2]);
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
+    if ((tid & (kWave - 1)) == 0) s_red[0][tid / kWave] = mloc;
     __syncthreads();
-    float M = -INFINITY;
-    for (int s = 0; s < n_splits; ++s) M = fmaxf(M, s_ml[s].x);
-    float* o = out + ((size_t)b * Hq + h) * kAttnD + 4 * threadIdx.x;
+    const float M = fmaxf(s_red[0][0], s_red[0][1]);
+    float* o = out + ((size_t)b * Hq + h) * kAttnD + 4 * tid;
     if (M == -INFINITY) {                                       // nothing attended
         *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (lse && threadIdx.x == 0) lse[(size_t)b * Hq + h] = -INFINITY;
+        if (lse && tid == 0) lse[(size_t)b * Hq + h] = -INFINITY;
         return;
     }
-    float lsum = 0.f;
+    float lpart = 0.f;
+    const int n_pad = (n_splits + CH - 1) / CH * CH;
+    for (int s = tid; s < n_pad; s += 128) {
+        float w = 0.f;
+        if (s < n_splits) {
+            float ms = ml.x, ls = ml.y;
+            if (s >= 128) {
+                ms = part_ml[(row0 + (size_t)s * Hq) * 2];
+                ls = part_ml[(row0 + (size_t)s * Hq) * 2 + 1];
+            }
+            w = exp2f(ms - M);                                  // 0 for an empty split
+            lpart += w * ls;
+        }
+        s_w[s] = w;
+    }
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) lpart += __shfl_xor(lpart, off);
+    if ((tid & (kWave - 1)) == 0) s_red[1][tid / kWave] = lpart;
+    __syncthreads();
+    const float lsum = s_red[1][0] + s_red[1][1];
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < n_splits; c0 += CH) {
         if (c0 > 0) {
 #pragma unroll
             for (int u = 0; u < CH; ++u) {
                 const int s = min(c0 + u, n_splits - 1);
-                os[u] = *reinterpret_cast<const f32x4*>(part_o + (row0 + (size_t)s * Hq) * kAttnD +
-                                                        4 * threadIdx.x);
+                os[u] = *reinterpret_cast<const f32x4*>(part_o + (row0 + (size_t)s * Hq) * kAttnD + 4 * tid);
             }
         }
 #pragma unroll
-        for (int u = 0; u < CH; ++u) {
-            if (c0 + u < n_splits) {
-                const float2 ml = s_ml[c0 + u];
-                const float wgt = exp2f(ml.x - M);                // 0 for an empty split
-                lsum += wgt * ml.y;
-                acc += wgt * os[u];
-            }
+        for (int u4 = 0; u4 < CH; u4 += 4) {
+            const f32x4 w = *reinterpret_cast<const f32x4*>(s_w + c0 + u4);   // zero past n_splits
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc += w[i] * os[u4 + i];
         }
     }
     *reinterpret_cast<f32x4*>(o) = acc / lsum;
-    if (lse && threadIdx.x == 0)
-        lse[(size_t)b * Hq + h] = (M + log2f(lsum)) * 0.69314718055994531f;
+    if (lse && tid == 0) lse[(size_t)b * Hq + h] = (M + log2f(lsum)) * 0.69314718055994531f;
 }
 
 // Tiles per workgroup: the most (up to 4) that still leave at least
@@ -419,12 +445,15 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
     }
     if (int e = launch_status("csa2_sparse_attn_decode launch")) return e;
     if (ns > 1) {
+        const dim3 cg(Hq, B), cb(128);
         if (ns <= 8)
-            hipLaunchKernelGGL(attn_combine_kernel<8>, dim3(Hq, B), dim3(128), 0, s, part_o,
-                               part_ml, Hq, ns, out, lse);
+            hipLaunchKernelGGL(attn_combine_kernel<8>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse);
+        else if (ns <= 16)
+            hipLaunchKernelGGL(attn_combine_kernel<16>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse);
+        else if (ns <= 24)
+            hipLaunchKernelGGL(attn_combine_kernel<24>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse);
         else
-            hipLaunchKernelGGL(attn_combine_kernel<32>, dim3(Hq, B), dim3(128), 0, s, part_o,
-                               part_ml, Hq, ns, out, lse);
+            hipLaunchKernelGGL(attn_combine_kernel<32>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse);
         return launch_status("csa2_sparse_attn_decode combine launch");
     }
     return CSA2_OK;

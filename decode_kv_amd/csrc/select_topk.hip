@@ -29,11 +29,12 @@ constexpr int kSelMaxP = 16384;
 constexpr int kSelWaves = kSelThreads / kWave;
 
 // Monotone 12-bit key of a non-negative score: exact below 128, otherwise the
-// exponent and the 7 bits below the leading one.
+// exponent and the 7 bits below the leading one.  With sh = max(e - 7, 0) for
+// the leading-one position e, s >> sh is the 8 leading bits (or s itself) and
+// sh << 7 counts the octaves above 128, so the key is their sum (< 3200).
 __device__ __forceinline__ int sel_key(int s) {
-    if (s < 128) return s;
-    const int e = 31 - __clz(s);
-    return ((e - 6) << 7) | ((s >> (e - 7)) & 127);    // < 25 * 128 = 3200
+    const int sh = max(24 - (int)__builtin_clz((unsigned)s | 1u), 0);
+    return (s >> sh) + (sh << 7);
 }
 
 constexpr int kSelKeyBins = 3200;
@@ -75,7 +76,9 @@ __device__ __forceinline__ int lane_rank(uint64_t m) {
 }
 
 // Exclusive prefix, in (slot j, wave) order, of per-(j, wave) counts in
-// s_cnt[j * kSelWaves + wave]; result in s_pre.  Wave 0 scans 4 entries/lane.
+// s_cnt[j * kSelWaves + wave]; result in s_pre[wave * 16 + j], so that each
+// wave reads its 16 prefixes as four 16-byte loads (wave_prefixes).  Wave 0
+// scans 4 entries per lane.
 __device__ __forceinline__ void slot_wave_scan(const int* s_cnt, int* s_pre) {
     __syncthreads();
     if (threadIdx.x < kWave) {
@@ -89,11 +92,25 @@ __device__ __forceinline__ void slot_wave_scan(const int* s_cnt, int* s_pre) {
         int run = wave_inclusive_scan(sum) - sum;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            s_pre[4 * l + i] = run;
+            const int flat = 4 * l + i;                      // j * kSelWaves + wave
+            s_pre[(flat % kSelWaves) * 16 + flat / kSelWaves] = run;
             run += c[i];
         }
     }
     __syncthreads();
+}
+
+// This wave's 16 slot prefixes, all read before any is used.
+__device__ __forceinline__ void wave_prefixes(const int* s_pre, int (&base)[16]) {
+    const int4* p = reinterpret_cast<const int4*>(s_pre + (threadIdx.x / kWave) * 16);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int4 x = p[q];
+        base[4 * q] = x.x;
+        base[4 * q + 1] = x.y;
+        base[4 * q + 2] = x.z;
+        base[4 * q + 3] = x.w;
+    }
 }
 
 // The usual case: the bin holding the keff-th largest score and the bins above
@@ -120,10 +137,12 @@ __device__ __forceinline__ void select_compacted(const int (&v)[kSelMaxP / kSelT
         if (lane == 0) s_cnt[j * kSelWaves + wave] = __popcll(mi[j]);
     }
     slot_wave_scan(s_cnt, s_pre);
+    int base[PER];
+    wave_prefixes(s_pre, base);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if ((mi[j] >> lane) & 1ull) {
-            const int slot = s_pre[j * kSelWaves + wave] + lane_rank(mi[j]);
+            const int slot = base[j] + lane_rank(mi[j]);
             s_cs[slot] = v[j];
             s_cp[slot] = pos[j];
         }
@@ -132,18 +151,16 @@ __device__ __forceinline__ void select_compacted(const int (&v)[kSelMaxP / kSelT
     const int sv = tid < M ? s_cs[tid] : -1;             // this thread's compacted entry
     narrow_to_value(sv, lo, hi, need, cnt, s_hist, s_res);
     const int T = lo, needT = need;
-    const bool all_ties = need == cnt;
-    // take s > T, plus the first needT entries with s == T in position order
+    // take s > T, plus the first needT entries with s == T in position order:
+    // one scan of (count above T) << 16 | (count at T) gives both prefixes
+    // (each total <= 1,024), and the output slot is the entries taken before
+    const bool gt = tid < M && sv > T;
     const bool eq = tid < M && sv == T;
-    bool take = tid < M && sv > T;
     int tot;
-    if (all_ties) {
-        take = take || eq;
-    } else {
-        const int eq_before = block_exclusive_scan<kSelThreads>(eq ? 1 : 0, s_tmp, tot);
-        take = take || (eq && eq_before < needT);
-    }
-    const int o = block_exclusive_scan<kSelThreads>(take ? 1 : 0, s_tmp, tot);
+    const int pre = block_exclusive_scan<kSelThreads>(gt ? 1 << 16 : (eq ? 1 : 0), s_tmp, tot);
+    const int eq_before = pre & 0xFFFF;
+    const bool take = gt || (eq && eq_before < needT);
+    const int o = (pre >> 16) + min(eq_before, needT);
     if (take && o < keff) out[o] = s_cp[tid];
     for (int i = keff + tid; i < k; i += kSelThreads) out[i] = -1;
     if (tid == 0) *out_len = keff;
@@ -158,7 +175,9 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     __shared__ uint32_t s_hist[kSelRefBins];
     __shared__ int s_tmp[kSelWaves];
     __shared__ int s_res[4];
-    __shared__ int s_cnt[PER * kSelWaves], s_pre[PER * kSelWaves];
+    static_assert(PER == 16 && kSelWaves == 16, "slot prefixes are 16 x 16");
+    __shared__ int s_cnt[PER * kSelWaves];
+    __shared__ __attribute__((aligned(16))) int s_pre[PER * kSelWaves];
     __shared__ int s_cs[kSelThreads], s_cp[kSelThreads];   // compacted scores, positions
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
@@ -168,16 +187,11 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     // for the list length (one memory round trip for both); positions follow
     const int len_b = cand_len[b];
     int v[PER], pos[PER];
+    // (indices past P reread entry P - 1; they are past n and masked below)
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int i = tid + j * kSelThreads;
-        v[j] = i < P ? sc[i] : -1;
-    }
+    for (int j = 0; j < PER; ++j) v[j] = sc[min(tid + j * kSelThreads, P - 1)];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        const int i = tid + j * kSelThreads;
-        pos[j] = i < P ? cp[i] : -1;
-    }
+    for (int j = 0; j < PER; ++j) pos[j] = cp[min(tid + j * kSelThreads, P - 1)];
     // the first histogram is cleared while the loads are in flight
     for (int i = tid; i < kSelKeyBins; i += kSelThreads) s_hist[i] = 0;
     if (tid == 0) s_res[3] = 0;
@@ -191,10 +205,15 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     int T = 0x7FFFFFFF, needT = 0;
     bool all_ties = true;                     // every entry with s == T is taken
     if (keff > 0) {
-        // pass 0: float-like key, fine enough that the atomics rarely collide
+        // pass 0: float-like key, fine enough that the atomics rarely collide;
+        // masked entries count in bins past the key range (256 of them, one
+        // per lane of a wave, so they do not collide either), never read
+        const int spill = kSelKeyBins + (tid & 255);
 #pragma unroll
-        for (int j = 0; j < PER; ++j)
-            if (v[j] >= 0) atomicAdd(&s_hist[sel_key(v[j])], 1u);
+        for (int j = 0; j < PER; ++j) {
+            const int key = sel_key(v[j]);          // defined for any int; used if v >= 0
+            atomicAdd(&s_hist[v[j] >= 0 ? key : spill], 1u);
+        }
         __syncthreads();
         sel_find_bin(s_hist, kSelKeyBins, keff, s_tmp, s_res);
         const int kb = s_res[0];
@@ -280,10 +299,12 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
             if (lane == 0) s_cnt[j * kSelWaves + wave] = __popcll(meq[j]);
         }
         slot_wave_scan(s_cnt, s_pre);
+        int base[PER];
+        wave_prefixes(s_pre, base);
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const bool eq = (meq[j] >> lane) & 1ull;
-            const int eq_rank = s_pre[j * kSelWaves + wave] + lane_rank(meq[j]);
+            const int eq_rank = base[j] + lane_rank(meq[j]);
             take[j] = (v[j] > T) || (eq && eq_rank < needT);
         }
         __syncthreads();
@@ -295,11 +316,13 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
         if (lane == 0) s_cnt[j * kSelWaves + wave] = __popcll(mt[j]);
     }
     slot_wave_scan(s_cnt, s_pre);
+    int obase[PER];
+    wave_prefixes(s_pre, obase);
     int* out = sel_pos + (size_t)b * k;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if (take[j]) {
-            const int o = s_pre[j * kSelWaves + wave] + lane_rank(mt[j]);
+            const int o = obase[j] + lane_rank(mt[j]);
             if (o < keff) out[o] = pos[j];
         }
     }

@@ -14,14 +14,17 @@
 //   2. reduce     sum the per-tile histograms of each sequence (workgroups
 //                 split the bins), clear the second-level histogram
 //   3. gather     every tile finds the bin B1 holding the P_eff-th score,
-//                 counts its entries above B1, copies its entries inside B1 to
-//                 its own candidate slots and adds them to a 4,096-bin
+//                 counts its entries above B1, copies the scores of its
+//                 entries inside B1 to its own candidate slots (the first 16
+//                 slot-major across tiles) and adds them to a 4,096-bin
 //                 histogram of the next 12 bits inside B1 (atomics whose
 //                 result is not waited for)
-//   4. threshold  one workgroup per sequence: the second-level histogram
-//                 narrows B1 to one sub-bin; its entries (<= 256, else more
-//                 12-bit passes over the candidates) are ranked exactly, giving
-//                 the threshold T and the number of ties at T to keep; per-tile
+//   4. threshold  one workgroup per sequence, one tile per thread: the
+//                 second-level histogram narrows B1 to one sub-bin; its
+//                 scores (<= 1,024, else more 12-bit passes over the
+//                 candidates) are gathered one per thread and 8-bit digit
+//                 passes narrow them to the threshold T and the number of
+//                 ties at T to keep (taken in position order); per-tile
 //                 counts and an exclusive prefix give every tile its offsets
 //   5. write      ordered compaction: s > T, plus the first ties in position
 //                 order; ascending positions, tail -1

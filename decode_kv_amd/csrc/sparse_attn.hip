@@ -84,7 +84,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     float* __restrict__ out, float* __restrict__ lse) {
     __shared__ __attribute__((aligned(16))) uint16_t s_vjd[kAttnRows * kVjdLd];
     __shared__ __attribute__((aligned(16))) uint16_t s_vdj[kAttnD * kVdjLd];
-    __shared__ f32x4 s_red[kAttnThreads / kWave][2][kWave];           // S^T partial sums
+    // The S^T partial sums of wave w go to rows 0..7 of the latent columns
+    // [128w, 128w + 128) of s_vjd, which only wave w reads for its scores:
+    // each wave overwrites its own band once its reads are done, so this
+    // needs no extra barrier, and the workgroup stays under 80 KB of LDS
+    // (two per CU).  Slot q = 64 m + lane (m: 16-row tile) is row q >> 4,
+    // 16-byte column q & 15 of the band.
+    auto red_slot = [&](int w, int m, int lane) -> f32x4* {
+        const int q = 64 * m + lane;
+        return reinterpret_cast<f32x4*>(s_vjd + (q >> 4) * kVjdLd + 128 * w + 8 * (q & 15));
+    };
 
     const int split = blockIdx.x, b = blockIdx.y;
     const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
@@ -191,8 +200,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[ks], s1, 0, 0, 0);
             }
         }
-        s_red[wave][0][l] = s0;
-        s_red[wave][1][l] = s1;
+        *red_slot(wave, 0, l) = s0;
+        *red_slot(wave, 1, l) = s1;
         __syncthreads();
         // this wave's V^T operands of the P.V product, read before the softmax
         // so their LDS latency overlaps it
@@ -204,8 +213,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
             const u32x2 hi = *reinterpret_cast<const u32x2*>(vd + 16);
             bv[nb] = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
         }
-        s0 = s_red[0][0][l] + s_red[1][0][l] + s_red[2][0][l] + s_red[3][0][l];
-        s1 = s_red[0][1][l] + s_red[1][1][l] + s_red[2][1][l] + s_red[3][1][l];
+        s0 = *red_slot(0, 0, l) + *red_slot(1, 0, l) + *red_slot(2, 0, l) + *red_slot(3, 0, l);
+        s1 = *red_slot(0, 1, l) + *red_slot(1, 1, l) + *red_slot(2, 1, l) + *red_slot(3, 1, l);
 
         // every wave now holds the full scores: head c16, rows 4g+i and 16+4g+i
         const int jt = tile * kAttnRows;

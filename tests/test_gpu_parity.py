@@ -213,6 +213,26 @@ def test_index_full_clustered_scores():
     check_full(keys, [0], [L], q, w, W_, 999, "300 close values")
 
 
+def test_index_full_crowded_sub_bin():
+    """More than 1,024 candidates inside the second-level sub-bin, spread over
+    64 values: the threshold takes a further 12-bit pass over the candidates
+    (most tiles hold far more than 16 of them) before its last digits."""
+    rng = np.random.default_rng(9)
+    L, W_ = 20000, 128
+    keys = np.zeros((L, 64), dtype=np.int8)
+    keys[:, 0] = 50
+    hot = rng.choice(L - W_, 5000, replace=False)
+    keys[hot, 0] = 127
+    keys[:, 1] = rng.integers(0, 64, size=L)
+    q = np.zeros((1, 64, 64), dtype=np.int8)
+    q[0, 1:, 0] = 127
+    q[0, 0, 1] = 1
+    w = np.full((1, 64), 15, dtype=np.int8)
+    w[0, 0] = 1
+    for P in [4000, 2500, 4999]:
+        check_full(keys, [0], [L], q, w, W_, P, "5,000 hot over 64 values, P %d" % P)
+
+
 def test_index_score_matches_oracle():
     rng = np.random.default_rng(13)
     lens = [0, 1, 1023, 1024, 1025, 70001, 3000]

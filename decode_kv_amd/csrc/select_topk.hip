@@ -5,20 +5,23 @@
 //
 // One workgroup (1,024 threads) per sequence.  The candidate scores and
 // positions (<= 16,384 each) are loaded with all of a thread's loads in
-// flight and kept in registers (entry i lives in thread i mod 1,024).  An exact radix select finds the threshold T and the
-// number of ties to keep: a first histogram over a float-like 12-bit key
-// (exponent + 7 mantissa bits, so pool scores spread over many bins and the
-// LDS atomics rarely collide), then 13-bit refinement digits inside the chosen
-// bin until it holds one value or at most 256 entries, which are ranked
-// exactly.  An ordered compaction (wave ballots plus one prefix over
-// (slot, wave) counts) writes s > T plus the first ties in list order.
-// Candidate lists are ascending in position, so list order is position order.
+// flight and kept in registers (entry i lives in thread i mod 1,024).  An
+// exact radix select finds the threshold T and the number of ties at T to
+// keep: a first histogram over a float-like 12-bit key (exponent + 7
+// mantissa bits, so pool scores spread over many bins and the LDS atomics
+// rarely collide) picks the bin holding the k-th largest score; further
+// digits inside that bin narrow it to the single value T.  The output is an
+// ordered compaction of s > T plus the first ties in list order; candidate
+// lists are ascending in position, so list order is position order.
 //
-// Usually the first histogram's chosen bin and the bins above it hold at most
-// 1,024 entries: they are then compacted to LDS once, right after that
-// histogram, one per thread, and the refinement, ranking, tie order and output
-// all run on that set instead of on all 16 entries of every thread.  Lists
-// with more entries there (heavy ties, k near P) take the general path.
+// Usually the chosen bin and the bins above it hold at most 1,024 entries:
+// they are then compacted to LDS once, in list order, one per thread, and
+// 8-bit digit passes, the tie order and the output all run on that set
+// instead of on all 16 entries of every thread.  Lists with more entries
+// there (heavy ties, k near P) take the general path: 13-bit digit passes
+// over every entry until the bin holds at most 1,024, which are gathered one
+// per thread for the last digits, then ballot-and-prefix compactions over
+// all entries for the tie order and the output.
 #include "abi_common.h"
 #include "common.h"
 
@@ -68,11 +71,6 @@ __device__ __forceinline__ void sel_find_bin(const uint32_t* s_hist, int nb, int
         }
     }
     __syncthreads();
-}
-
-__device__ __forceinline__ int lane_rank(uint64_t m) {
-    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Exclusive prefix, in (slot j, wave) order, of per-(j, wave) counts in
@@ -142,7 +140,7 @@ __device__ __forceinline__ void select_compacted(const int (&v)[kSelMaxP / kSelT
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if ((mi[j] >> lane) & 1ull) {
-            const int slot = base[j] + lane_rank(mi[j]);
+            const int slot = base[j] + lane_rank64(mi[j]);
             s_cs[slot] = v[j];
             s_cp[slot] = pos[j];
         }
@@ -273,7 +271,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
 #pragma unroll
             for (int j = 0; j < PER; ++j) {
                 const bool in = (min_[j] >> lane) & 1ull;
-                const int slot = first + lane_rank(min_[j]);
+                const int slot = first + lane_rank64(min_[j]);
                 if (in && slot < kSelLast) s_cs[slot] = v[j];
                 first += __popcll(min_[j]);
             }
@@ -304,7 +302,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
 #pragma unroll
         for (int j = 0; j < PER; ++j) {
             const bool eq = (meq[j] >> lane) & 1ull;
-            const int eq_rank = base[j] + lane_rank(meq[j]);
+            const int eq_rank = base[j] + lane_rank64(meq[j]);
             take[j] = (v[j] > T) || (eq && eq_rank < needT);
         }
         __syncthreads();
@@ -322,7 +320,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if (take[j]) {
-            const int o = obase[j] + lane_rank(mt[j]);
+            const int o = obase[j] + lane_rank64(mt[j]);
             if (o < keff) out[o] = pos[j];
         }
     }

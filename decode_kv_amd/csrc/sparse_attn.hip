@@ -38,7 +38,8 @@ constexpr int kAttnRows = 32;
 constexpr int kAttnD = 512;
 constexpr int kHeadsPerWg = 16;
 constexpr int kVjdLd = kAttnD + 8;      // bf16 per row-major row (padded)
-constexpr int kVdjLd = kAttnRows + 8;   // bf16 per d-major row (80 B: 16-B aligned)
+constexpr int kVdjLd = kAttnRows + 4;   // bf16 per d-major row (72 B: 8-B aligned)
+constexpr int kRawLd = kAttnD / 2 + 8;   // bytes per staged row of FP4 codes (66 words)
 constexpr int kAttnMaxTilesPerWg = 4;   // tiles whose loads one workgroup keeps in flight
 constexpr int kAttnMaxRows = 16384;     // k + window
 constexpr int kAttnMinWgs = 64;         // workgroups wanted per launch
@@ -84,6 +85,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     float* __restrict__ out, float* __restrict__ lse) {
     __shared__ __attribute__((aligned(16))) uint16_t s_vjd[kAttnRows * kVjdLd];
     __shared__ __attribute__((aligned(16))) uint16_t s_vdj[kAttnD * kVdjLd];
+    // one tile's raw rows as loaded: codes [32][264 B], then scales [32][16 B]
+    __shared__ __attribute__((aligned(16))) uint8_t s_raw[kAttnRows * kRawLd + kAttnRows * 16];
+    uint8_t* const s_rsc = s_raw + kAttnRows * kRawLd;
     // The S^T partial sums of wave w go to rows 0..7 of the latent columns
     // [128w, 128w + 128) of s_vjd, which only wave w reads for its scores:
     // each wave overwrites its own band once its reads are done, so this
@@ -106,14 +110,16 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     // round trip 1: sequence scalars, this thread's selection entries, q
     const int len_b = len[b], sel_b = sel_len[b];
     const long long roff = row_off[b];
-    int sp[TPW][8];
+    // loads of a tile: thread t takes 32 bytes of codes of row t >> 3 (bytes
+    // 32 (t & 7) ..), wave 0 lane l the 16 scale bytes of row l & 31
+    const int crow = tid >> 3, srow = l & 31;
+    int spc[TPW], sps[TPW];
 #pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int j = (t_begin + t) * kAttnRows + 8 * rg + r;
-            sp[t][r] = j < k ? sel_pos[(size_t)b * k + j] : -1;
-        }
+    for (int t = 0; t < TPW; ++t) {
+        const int jc = (t_begin + t) * kAttnRows + crow, js = (t_begin + t) * kAttnRows + srow;
+        spc[t] = jc < k ? sel_pos[(size_t)b * k + jc] : -1;
+        sps[t] = (wave == 0 && js < k) ? sel_pos[(size_t)b * k + js] : -1;
+    }
     // q . v is split over the latent dimension: wave w owns d in [128w, 128w+128)
     constexpr int kKs = kAttnD / 32 / (kAttnThreads / kWave);   // 4 k-steps per wave
     bf16x8 qb[kKs];
@@ -130,26 +136,26 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     const int ntile = (S + kAttnRows - 1) / kAttnRows;
     const int t_end = min(t_begin + TPW, ntile);
 
-    // round trip 2: codes and scales of every row this thread dequantises
-    uint32_t codes[TPW][8], sbs[TPW][8], valid[TPW];
+    // round trip 2: the raw rows of every tile, in 16-byte loads (a row of an
+    // invalid position reads row 0 and is staged as zeros)
+    auto pos_of = [&](int j, int p) -> long long {
+        if (j < nsel) return p;
+        if (j < S) return (long long)(L - win + (j - nsel));
+        return -1;
+    };
+    u32x4 rc0[TPW], rc1[TPW], rsc[TPW];
+    uint32_t cok = 0, sok = 0;                           // per tile: row valid
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-        valid[t] = 0;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int j = (t_begin + t) * kAttnRows + 8 * rg + r;
-            long long pos = -1;
-            if (j < nsel) pos = sp[t][r];
-            else if (j < S) pos = L - win + (j - nsel);
-            codes[t][r] = 0;
-            sbs[t][r] = 0;
-            if (pos >= 0) {
-                const long long row = roff + pos;
-                valid[t] |= 1u << r;
-                codes[t][r] = *reinterpret_cast<const uint32_t*>(kv_fp4 + row * (kAttnD / 2) + 4 * dc);
-                sbs[t][r] = kv_scale[row * (kAttnD / 32) + (dc >> 2)];
-            }
-        }
+        const long long pc = pos_of((t_begin + t) * kAttnRows + crow, spc[t]);
+        const long long ps = pos_of((t_begin + t) * kAttnRows + srow, sps[t]);
+        cok |= (uint32_t)(pc >= 0) << t;
+        sok |= (uint32_t)(ps >= 0) << t;
+        const uint8_t* cp = kv_fp4 + (roff + (pc >= 0 ? pc : 0)) * (kAttnD / 2) + 32 * (tid & 7);
+        rc0[t] = *reinterpret_cast<const u32x4*>(cp);
+        rc1[t] = *reinterpret_cast<const u32x4*>(cp + 16);
+        if (wave == 0)                                    // uniform
+            rsc[t] = *reinterpret_cast<const u32x4*>(kv_scale + (roff + (ps >= 0 ? ps : 0)) * (kAttnD / 32));
     }
 
     // p . v is split over the output dimension: wave w owns d-blocks [8w, 8w+8)
@@ -165,11 +171,27 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         if (tile >= t_end) break;                           // uniform
         if (t > 0) __syncthreads();                          // previous tile's LDS reads are done
         {
+            // stage the raw tile (rows 8-byte aligned: 264-byte stride)
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            const u32x4 a = ((cok >> t) & 1u) ? rc0[t] : z, bq = ((cok >> t) & 1u) ? rc1[t] : z;
+            uint8_t* sr = s_raw + crow * kRawLd + 32 * (tid & 7);
+            *reinterpret_cast<u32x2*>(sr) = u32x2{a[0], a[1]};
+            *reinterpret_cast<u32x2*>(sr + 8) = u32x2{a[2], a[3]};
+            *reinterpret_cast<u32x2*>(sr + 16) = u32x2{bq[0], bq[1]};
+            *reinterpret_cast<u32x2*>(sr + 24) = u32x2{bq[2], bq[3]};
+            if (wave == 0 && l < kAttnRows)
+                *reinterpret_cast<u32x4*>(s_rsc + 16 * l) = ((sok >> t) & 1u) ? rsc[t] : z;
+        }
+        __syncthreads();
+        {
+            // this thread's 8 rows x 8 dims: codes word dc of rows 8rg.., their scale
+            // bytes; a 66-word row stride puts the 4 row groups of a wave 16 banks apart
             u32x4 v[8];
 #pragma unroll
             for (int r = 0; r < 8; ++r) {
-                v[r] = fp4x8_to_bf16x8(codes[t][r], (int)sbs[t][r]);
-                if (!((valid[t] >> r) & 1u)) v[r] = u32x4{0u, 0u, 0u, 0u};
+                const uint32_t cw = *reinterpret_cast<const uint32_t*>(s_raw + (8 * rg + r) * kRawLd + 4 * dc);
+                const int sb = s_rsc[(8 * rg + r) * 16 + (dc >> 2)];
+                v[r] = fp4x8_to_bf16x8(cw, sb);
                 *reinterpret_cast<u32x4*>(s_vjd + (8 * rg + r) * kVjdLd + 8 * dc) = v[r];
             }
 #pragma unroll
@@ -182,7 +204,9 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
                     const uint32_t bb = (v[2 * i + 1][c >> 1] >> half) & 0xFFFFu;
                     tr[i] = a | (bb << 16);
                 }
-                *reinterpret_cast<u32x4*>(s_vdj + (8 * dc + c) * kVdjLd + 8 * rg) = tr;
+                uint16_t* vw = s_vdj + (8 * dc + c) * kVdjLd + 8 * rg;
+                *reinterpret_cast<u32x2*>(vw) = u32x2{tr[0], tr[1]};
+                *reinterpret_cast<u32x2*>(vw + 4) = u32x2{tr[2], tr[3]};
             }
         }
         __syncthreads();

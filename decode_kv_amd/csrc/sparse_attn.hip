@@ -301,15 +301,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
                 l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
         return;
     }
-    // split partial: unnormalised O, running max and sum
+    // split partial: unnormalised O, running max and sum.  Only the combine
+    // kernel reads them, so they are stored non-temporal (streamed past the
+    // caches instead of waiting in L2 for the end-of-kernel write-back).
     const size_t base = ((size_t)b * n_splits + split) * Hq + head;
     float* ob = part_o + base * kAttnD + d0;
 #pragma unroll
-    for (int nb = 0; nb < kNb; ++nb) *reinterpret_cast<f32x4*>(ob + 16 * nb) = o[nb];
-    if (wave == 0 && g == 0) {
-        part_ml[base * 2 + 0] = m_run;
-        part_ml[base * 2 + 1] = l_run;
-    }
+    for (int nb = 0; nb < kNb; ++nb)
+        __builtin_nontemporal_store(o[nb], reinterpret_cast<f32x4*>(ob + 16 * nb));
+    if (wave == 0 && g == 0)
+        __builtin_nontemporal_store(u32x2{__float_as_uint(m_run), __float_as_uint(l_run)},
+                                    reinterpret_cast<u32x2*>(part_ml + base * 2));
 }
 
 // Log-sum-exp merge of the split partials: one workgroup per (head, sequence),

@@ -106,6 +106,28 @@ __device__ __forceinline__ float rows4_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Max / sum of one value over all 64 lanes, in every lane: within each row
+// of 16 by DPP (lane swaps of 1 and 2 by quad permutes, then row rotations by
+// 4 and 8), then across the four rows with the lane-row swaps.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp_mov<0xB1>(x));    // quad_perm [1,0,3,2]
+    x = fmaxf(x, dpp_mov<0x4E>(x));    // quad_perm [2,3,0,1]
+    x = fmaxf(x, dpp_mov<0x124>(x));   // row_ror:4
+    x = fmaxf(x, dpp_mov<0x128>(x));   // row_ror:8
+    return rows4_max(x);
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    x += dpp_mov<0xB1>(x);
+    x += dpp_mov<0x4E>(x);
+    x += dpp_mov<0x124>(x);
+    x += dpp_mov<0x128>(x);
+    return rows4_sum(x);
+}
+
 // Inclusive prefix sum over the 64 lanes of a wave, in DPP: row shifts by 1,
 // 2, 4 and 8 inside each row of 16 lanes (lanes shifted in from outside the
 // row add 0), then lane 15 broadcast into rows 1 and 3 and lane 31 into rows

@@ -7,12 +7,13 @@
 //
 // Workgroup = (split, sequence, group of 16 heads), four waves, up to four
 // 32-row tiles of attended rows.  All of a workgroup's global loads are issued
-// up front (sequence scalars and selection entries, then the FP4 codes and
-// scales of every tile into registers), so the gather latency is paid once.
+// up front (sequence scalars and selection entries, then the raw FP4 rows of
+// every tile into registers, 32 bytes of codes per thread and the scale rows
+// by one wave, in 16-byte loads), so the gather latency is paid once.
 // Per tile:
-//   * dequantise the rows exactly to bf16 and stage them in LDS twice:
-//     row-major (for q.v) and d-major (for p.v), so both products read
-//     contiguous 16- or 8-byte operands;
+//   * stage the raw rows in LDS, then dequantise them exactly to bf16 and
+//     store them twice: row-major (for q.v) and d-major (for p.v), so both
+//     products read contiguous 16- or 8-byte operands;
 //   * S^T = V q^T on bf16 MFMA (16x16x32), fp32 accumulation, the latent
 //     dimension split over the four waves and the partial sums added in LDS;
 //   * online softmax in base 2, per head (every wave holds the full scores);
@@ -344,41 +345,59 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* part_o,
     const float2 ml = *reinterpret_cast<const float2*>(
         part_ml + (row0 + (size_t)min(tid, n_splits - 1) * Hq) * 2);   // used for tid < n_splits
     asm volatile("" ::: "memory");
-    // M = max over splits of m_s; weights w_s = 2^(m_s - M); lsum = sum w_s l_s
-    float mloc = tid < n_splits ? ml.x : -INFINITY;
-    for (int s = tid + 128; s < n_splits; s += 128)
-        mloc = fmaxf(mloc, part_ml[(row0 + (size_t)s * Hq) * 2]);
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) mloc = fmaxf(mloc, __shfl_xor(mloc, off));
-    if ((tid & (kWave - 1)) == 0) s_red[0][tid / kWave] = mloc;
-    __syncthreads();
-    const float M = fmaxf(s_red[0][0], s_red[0][1]);
+    // M = max over splits of m_s; weights w_s = 2^(m_s - M) (0 for an empty
+    // split and zero-padded to a multiple of CH); lsum = sum w_s l_s
+    const int n_pad = (n_splits + CH - 1) / CH * CH;
+    float M, lsum;
+    if (n_pad <= kWave) {                                       // uniform: wave 0 alone
+        if (tid < kWave) {
+            const bool in = tid < n_splits;
+            const float m = in ? ml.x : -INFINITY;
+            const float Mw = wave_max(m);
+            const float w = (in && Mw != -INFINITY) ? exp2f(m - Mw) : 0.f;
+            const float ls = wave_sum(w * (in ? ml.y : 0.f));
+            s_w[tid] = w;
+            if (tid == 0) {
+                s_red[0][0] = Mw;
+                s_red[1][0] = ls;
+            }
+        }
+        __syncthreads();
+        M = s_red[0][0];
+        lsum = s_red[1][0];
+    } else {
+        float mloc = tid < n_splits ? ml.x : -INFINITY;
+        for (int s = tid + 128; s < n_splits; s += 128)
+            mloc = fmaxf(mloc, part_ml[(row0 + (size_t)s * Hq) * 2]);
+        mloc = wave_max(mloc);
+        if ((tid & (kWave - 1)) == 0) s_red[0][tid / kWave] = mloc;
+        __syncthreads();
+        M = fmaxf(s_red[0][0], s_red[0][1]);
+        float lpart = 0.f;
+        for (int s = tid; s < n_pad; s += 128) {
+            float w = 0.f;
+            if (s < n_splits && M != -INFINITY) {
+                float ms = ml.x, ls = ml.y;
+                if (s >= 128) {
+                    ms = part_ml[(row0 + (size_t)s * Hq) * 2];
+                    ls = part_ml[(row0 + (size_t)s * Hq) * 2 + 1];
+                }
+                w = exp2f(ms - M);
+                lpart += w * ls;
+            }
+            s_w[s] = w;
+        }
+        lpart = wave_sum(lpart);
+        if ((tid & (kWave - 1)) == 0) s_red[1][tid / kWave] = lpart;
+        __syncthreads();
+        lsum = s_red[1][0] + s_red[1][1];
+    }
     float* o = out + ((size_t)b * Hq + h) * kAttnD + 4 * tid;
     if (M == -INFINITY) {                                       // nothing attended
         *reinterpret_cast<f32x4*>(o) = f32x4{0.f, 0.f, 0.f, 0.f};
         if (lse && tid == 0) lse[(size_t)b * Hq + h] = -INFINITY;
         return;
     }
-    float lpart = 0.f;
-    const int n_pad = (n_splits + CH - 1) / CH * CH;
-    for (int s = tid; s < n_pad; s += 128) {
-        float w = 0.f;
-        if (s < n_splits) {
-            float ms = ml.x, ls = ml.y;
-            if (s >= 128) {
-                ms = part_ml[(row0 + (size_t)s * Hq) * 2];
-                ls = part_ml[(row0 + (size_t)s * Hq) * 2 + 1];
-            }
-            w = exp2f(ms - M);                                  // 0 for an empty split
-            lpart += w * ls;
-        }
-        s_w[s] = w;
-    }
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) lpart += __shfl_xor(lpart, off);
-    if ((tid & (kWave - 1)) == 0) s_red[1][tid / kWave] = lpart;
-    __syncthreads();
-    const float lsum = s_red[1][0] + s_red[1][1];
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int c0 = 0; c0 < n_splits; c0 += CH) {
         if (c0 > 0) {

@@ -128,22 +128,26 @@ __device__ __forceinline__ void select_compacted(const int (&v)[kSelMaxP / kSelT
     constexpr int PER = kSelMaxP / kSelThreads;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     // ordered compaction: slot = rank of (j, wave, lane) among the entries >= lo
+    // (branch-free: the 16 waves' exec-mask branches would share one scalar
+    // unit; lane j stores slot j's count, unselected entries write to a spare
+    // slot of their lane)
     uint64_t mi[PER];
+    int my_cnt = 0;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         mi[j] = __ballot(v[j] >= lo);                    // lo >= 0 excludes invalid entries
-        if (lane == 0) s_cnt[j * kSelWaves + wave] = __popcll(mi[j]);
+        my_cnt = lane == j ? (int)__popcll(mi[j]) : my_cnt;
     }
+    if (lane < PER) s_cnt[lane * kSelWaves + wave] = my_cnt;
     slot_wave_scan(s_cnt, s_pre);
     int base[PER];
     wave_prefixes(s_pre, base);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
-        if ((mi[j] >> lane) & 1ull) {
-            const int slot = base[j] + lane_rank64(mi[j]);
-            s_cs[slot] = v[j];
-            s_cp[slot] = pos[j];
-        }
+        const bool sel = (mi[j] >> lane) & 1ull;
+        const int slot = sel ? base[j] + lane_rank64(mi[j]) : kSelThreads + lane;
+        s_cs[slot] = v[j];
+        s_cp[slot] = pos[j];
     }
     __syncthreads();
     const int sv = tid < M ? s_cs[tid] : -1;             // this thread's compacted entry
@@ -176,7 +180,8 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     static_assert(PER == 16 && kSelWaves == 16, "slot prefixes are 16 x 16");
     __shared__ int s_cnt[PER * kSelWaves];
     __shared__ __attribute__((aligned(16))) int s_pre[PER * kSelWaves];
-    __shared__ int s_cs[kSelThreads], s_cp[kSelThreads];   // compacted scores, positions
+    // compacted scores and positions, plus one spare slot per lane
+    __shared__ int s_cs[kSelThreads + kWave], s_cp[kSelThreads + kWave];
     const int b = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int* sc = score + (size_t)b * P;

@@ -54,7 +54,8 @@ def lib():
         L.csa2_kv_append_fp4.restype = I
         L.csa2_kv_append_fp4.argtypes = [V, V, I, I, V, V, V]
         L.csa2_index_full.restype = I
-        L.csa2_index_full.argtypes = [V, V, V, V, V, I, LL, LL, I, I, I, I, V, V, V, V, SZ, V]
+        L.csa2_index_full.argtypes = [V, V, V, V, V, I, LL, LL, I, I, I, I, V, V, V, I, V, V, V, SZ,
+                                       V]
         L.csa2_index_score.restype = I
         L.csa2_index_score.argtypes = [V, V, V, V, V, I, LL, LL, I, I, I, V, V, SZ, V]
         L.csa2_index_reindex.restype = I
@@ -124,13 +125,14 @@ def kv_append_fp4(x_bf16, dst_row, kv_fp4, kv_scale, stream=None):
 
 
 def index_full(q, w, keys, row_off, lens, max_len, total_len, window, P, pool_pos, pool_score,
-               pool_len, ws, stream=None):
+               pool_len, ws, stream=None, k=0, sel_pos=None, sel_len=None):
     B, H, Dk = q.shape
     nbytes = 0 if ws is None else ws.numel() * ws.element_size()
     _check("csa2_index_full",
            lib().csa2_index_full(_p(q), _p(w), _p(keys), _p(row_off), _p(lens), B, int(max_len),
                                  int(total_len), H, Dk, window, P, _p(pool_pos), _p(pool_score),
-                                 _p(pool_len), _p(ws), nbytes, _s(stream)))
+                                 _p(pool_len), int(k), _p(sel_pos), _p(sel_len), _p(ws), nbytes,
+                                 _s(stream)))
 
 
 def index_score(q, w, keys, row_off, lens, max_len, total_len, window, score, ws, stream=None):

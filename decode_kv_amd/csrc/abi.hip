@@ -41,11 +41,12 @@ extern "C" size_t csa2_workspace_bytes(int op, int B, long long max_len, long lo
     }
     switch (op) {
         case CSA2_OP_INDEX_FULL:
-            if (total_len < 0 || P < 1) {
-                fail(CSA2_ERR_INVALID, "csa2_workspace_bytes: total_len < 0 or P < 1");
+            if (total_len < 0 || P < 1 || k < 0 || k > P) {
+                fail(CSA2_ERR_INVALID,
+                     "csa2_workspace_bytes: total_len < 0, P < 1 or k outside [0, P]");
                 return 0;
             }
-            return index_full_ws_bytes(B, total_len, P);
+            return index_full_ws_bytes(B, total_len, P, k);
         case CSA2_OP_SELECT_TOPK:
             return 0;
         case CSA2_OP_SPARSE_ATTN:

@@ -23,7 +23,7 @@ inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace sizes (bytes) of the ops that need one.
-size_t index_full_ws_bytes(int B, long long total_len, int P);
+size_t index_full_ws_bytes(int B, long long total_len, int P, int k);
 size_t sparse_attn_ws_bytes(int B, int Hq, int D, int k, int window);
 int sparse_attn_splits(int B, int Hq, int k, int window);
 int sparse_attn_tiles_per_wg(int B, int Hq, int k, int window);

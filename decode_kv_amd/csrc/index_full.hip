@@ -28,6 +28,11 @@
 //                 counts and an exclusive prefix give every tile its offsets
 //   5. write      ordered compaction: s > T, plus the first ties in position
 //                 order; ascending positions, tail -1
+// With k > 0 the Full layer's own top-k selection comes out of the same
+// chain: it is the first min(k, E) positions under the same order (the top k
+// of the pool), so gather, threshold and write run a second target with
+// P_eff = min(k, E) side by side with the pool (grid dimension y, separate
+// candidate arrays) and no separate selection pass reads the pool back.
 // The result is exact and independent of the launch shape.
 #include "abi_common.h"
 #include "common.h"
@@ -45,6 +50,7 @@ constexpr int kThrThreads = 1024;
 constexpr int kMaxTilesPerSeq = 8192;    // LDS tile tables of the threshold kernel (8M positions)
 constexpr int kLastMax = kThrThreads;    // entries the last digits take, one per thread
 constexpr int kCandHead = 16;            // candidates per tile in the dense head array
+constexpr int kFlatMax = 8 * kThrThreads;  // threshold: candidates outside registers, loaded once
 constexpr int kMaxBatch = 4096;
 
 struct FullState {
@@ -59,27 +65,44 @@ struct FullState {
 };
 static_assert(sizeof(FullState) == 32, "FullState size");
 
-struct FullWs {
+// Arrays of one selection target.  Target 0 ranks the pool (P_eff =
+// min(P, E)); the optional target 1 ranks the top k of the same scores
+// (min(k, E)), which is the top k of the pool under the same order.
+struct FullTarget {
     FullState* st;        // [B]
-    uint32_t* hist;       // [B][kKeyBins]
     uint32_t* hist2;      // [B][kSubBins]
     int* tile_above;      // [Tmax] entries of the tile above bin B1
     int* tile_cnt;        // [Tmax] entries of the tile inside bin B1
     int* tile_off;        // [Tmax][2] output offsets among s > T and among s == T
-    uint16_t* tile_hist;  // [Tmax][kKeyBins]
     int* cand_head;       // [kCandHead][Tmax] scores of every tile's first candidates,
                           // slot-major so that one slot of consecutive tiles is contiguous
     int* cand;            // [Tmax][kTile] scores inside bin B1, per tile (slots >= kCandHead;
                           // the first kCandHead live in cand_head)
+};
+
+struct FullWs {
+    FullTarget tg[2];     // tg[1] is used when k > 0
+    uint32_t* hist;       // [B][kKeyBins]
+    uint16_t* tile_hist;  // [Tmax][kKeyBins]
     int* scores;          // [Tmax][kTile]
     int tmax;             // Tmax: the slot stride of cand_head
+    int k;                // size of target 1, 0 when there is none
+};
+
+// Where a target's result goes: pos (and score, when not null) [B][stride],
+// ascending positions, tail -1; len [B].
+struct FullOut {
+    int* pos;
+    int* score;
+    int* len;
+    int stride;
 };
 
 static long long full_tile_bound(int B, long long total_len) {
     return total_len / kTile + B + 1;
 }
 
-static size_t full_ws_layout(int B, long long total_len, char* base, FullWs* w) {
+static size_t full_ws_layout(int B, long long total_len, int ntargets, char* base, FullWs* w) {
     const long long T = full_tile_bound(B, total_len);
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -87,25 +110,29 @@ static size_t full_ws_layout(int B, long long total_len, char* base, FullWs* w) 
         off = round_up(off + bytes, 256);
         return base ? base + at : nullptr;
     };
-    FullWs x;
-    x.st = reinterpret_cast<FullState*>(take(sizeof(FullState) * (size_t)B));
+    FullWs x = {};
     x.hist = reinterpret_cast<uint32_t*>(take(4ull * B * kKeyBins));
-    x.hist2 = reinterpret_cast<uint32_t*>(take(4ull * B * kSubBins));
-    x.tile_above = reinterpret_cast<int*>(take(4ull * T));
-    x.tile_cnt = reinterpret_cast<int*>(take(4ull * T));
-    x.tile_off = reinterpret_cast<int*>(take(8ull * T));
     x.tile_hist = reinterpret_cast<uint16_t*>(take(2ull * (size_t)T * kKeyBins));
-    x.cand_head = reinterpret_cast<int*>(take(4ull * (size_t)T * kCandHead));
-    x.cand = reinterpret_cast<int*>(take(4ull * (size_t)T * kTile));
     x.scores = reinterpret_cast<int*>(take(4ull * (size_t)T * kTile));
+    for (int g = 0; g < ntargets; ++g) {
+        FullTarget& y = x.tg[g];
+        y.st = reinterpret_cast<FullState*>(take(sizeof(FullState) * (size_t)B));
+        y.hist2 = reinterpret_cast<uint32_t*>(take(4ull * B * kSubBins));
+        y.tile_above = reinterpret_cast<int*>(take(4ull * T));
+        y.tile_cnt = reinterpret_cast<int*>(take(4ull * T));
+        y.tile_off = reinterpret_cast<int*>(take(8ull * T));
+        y.cand_head = reinterpret_cast<int*>(take(4ull * (size_t)T * kCandHead));
+        y.cand = reinterpret_cast<int*>(take(4ull * (size_t)T * kTile));
+    }
     x.tmax = (int)T;
+    x.k = 0;
     if (w) *w = x;
     return off;
 }
 
-size_t index_full_ws_bytes(int B, long long total_len, int P) {
+size_t index_full_ws_bytes(int B, long long total_len, int P, int k) {
     (void)P;
-    return full_ws_layout(B, total_len, nullptr, nullptr);
+    return full_ws_layout(B, total_len, k > 0 ? 2 : 1, nullptr, nullptr);
 }
 
 // Monotone key of a score: exact below 32, otherwise the exponent and the 5
@@ -184,8 +211,8 @@ __device__ __forceinline__ void find_bin(const H* h, int nb, int need, int* s_tm
 
 // Tile t -> sequence, from the lengths (up to kMaxBatch sequences, 16 per
 // thread).  Returns the sequence (or -1 past the last tile) and the layout of
-// that sequence; with write_state the block also writes every sequence's
-// state.
+// that sequence.  Workgroup 0 also writes every sequence's state: st0 gets
+// P_eff = min(P, E) and st1 (when not null) min(k, E).
 struct TileInfo {
     int b, tile0, E;
     long long roff;
@@ -207,13 +234,16 @@ __device__ __forceinline__ FullState initial_state(int E, int P, int tile0, int 
 // One sequence: no scan, no LDS, no barrier.
 __device__ __forceinline__ TileInfo map_tile_one(const int* __restrict__ len,
                                                  const long long* __restrict__ row_off,
-                                                 int window, int P, int t, FullWs w,
-                                                 bool write_state) {
+                                                 int window, int P, int k, int t,
+                                                 FullState* st0, FullState* st1) {
     const int L = len[0];
     const long long roff = row_off[0];
     const int E = L > window ? L - window : 0;
     const int nt = (E + kTile - 1) / kTile;
-    if (write_state && threadIdx.x == 0) w.st[0] = initial_state(E, P, 0, nt);
+    if (t == 0 && threadIdx.x == 0) {
+        st0[0] = initial_state(E, P, 0, nt);
+        if (st1) st1[0] = initial_state(E, k, 0, nt);
+    }
     TileInfo r;
     r.b = t < nt ? 0 : -1;
     r.tile0 = 0;
@@ -225,7 +255,8 @@ __device__ __forceinline__ TileInfo map_tile_one(const int* __restrict__ len,
 template <int NT>
 __device__ __noinline__ TileInfo map_tile(const int* __restrict__ len,
                                           const long long* __restrict__ row_off, int B,
-                                          int window, int P, int t, FullWs w, bool write_state) {
+                                          int window, int P, int k, int t, FullState* st0,
+                                          FullState* st1) {
     __shared__ int s_tmp[NT / kWave];
     __shared__ int s_b, s_tile0, s_E;
     __shared__ long long s_roff;
@@ -259,7 +290,10 @@ __device__ __noinline__ TileInfo map_tile(const int* __restrict__ len,
                 s_E = Ev[i];
                 s_roff = row_off[b];
             }
-            if (write_state) w.st[b] = initial_state(Ev[i], P, pre_t, nt[i]);
+            if (t == 0) {
+                st0[b] = initial_state(Ev[i], P, pre_t, nt[i]);
+                if (st1) st1[b] = initial_state(Ev[i], k, pre_t, nt[i]);
+            }
         }
         pre_t += nt[i];
     }
@@ -305,10 +339,12 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
     TileInfo ti;
     if (B == 1) {
         load_query(0);
-        ti = map_tile_one(len, row_off, window, P, t, w, t == 0);
+        ti = map_tile_one(len, row_off, window, P, w.k, t, w.tg[0].st,
+                          w.k > 0 ? w.tg[1].st : nullptr);
         if (ti.b < 0) return;                              // past the last tile
     } else {
-        ti = map_tile<kScoreThreads>(len, row_off, B, window, P, t, w, t == 0);
+        ti = map_tile<kScoreThreads>(len, row_off, B, window, P, w.k, t, w.tg[0].st,
+                                     w.k > 0 ? w.tg[1].st : nullptr);
         if (ti.b < 0) return;
         load_query(ti.b);
     }
@@ -369,9 +405,12 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
 __global__ __launch_bounds__(kScanThreads) void full_reduce_kernel(FullWs w) {
     __shared__ uint32_t s_part[kScanThreads / 4][kRedBins + 1];
     const int c = blockIdx.x, b = blockIdx.y;
-    const FullState st = w.st[b];
-    const int z = c * kScanThreads + threadIdx.x;              // clear the sub-bin histogram
-    if (z < kSubBins) w.hist2[(size_t)b * kSubBins + z] = 0;
+    const FullState st = w.tg[0].st[b];                        // tile0, ntiles: both targets
+    const int z = c * kScanThreads + threadIdx.x;              // clear the sub-bin histograms
+    if (z < kSubBins) {
+        w.tg[0].hist2[(size_t)b * kSubBins + z] = 0;
+        if (w.k > 0) w.tg[1].hist2[(size_t)b * kSubBins + z] = 0;
+    }
     const int r = threadIdx.x >> 2, k = threadIdx.x & 3;
     uint32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     constexpr int U = 8;
@@ -442,8 +481,9 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
     int v[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) v[j] = sc[i0 + j];
+    const FullTarget g = w.tg[blockIdx.y];
     FullState st;
-    const int b = tile_state(w.st, B, t, &s_b, st);
+    const int b = tile_state(g.st, B, t, &s_b, st);
     if (b < 0) return;
     const int p_tile = (t - st.tile0) * kTile;
     const int nvalid = min(kTile, st.E - p_tile);
@@ -466,16 +506,16 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
     int tot;
     int slot = block_exclusive_scan<kScanThreads>((n_in << 16) | n_above, s_tmp, tot) >> 16;
     if (threadIdx.x == 0) {
-        w.tile_above[t] = tot & 0xFFFF;
-        w.tile_cnt[t] = tot >> 16;
+        g.tile_above[t] = tot & 0xFFFF;
+        g.tile_cnt[t] = tot >> 16;
         if (t == st.tile0) {
-            w.st[b].kb = kb;
-            w.st[b].above = above;
+            g.st[b].kb = kb;
+            g.st[b].above = above;
         }
     }
-    int* head = w.cand_head + t;
-    int* out = w.cand + (size_t)t * kTile;
-    uint32_t* h2 = w.hist2 + (size_t)b * kSubBins;
+    int* head = g.cand_head + t;
+    int* out = g.cand + (size_t)t * kTile;
+    uint32_t* h2 = g.hist2 + (size_t)b * kSubBins;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if (v[j] >= lo && v[j] <= hi) {
@@ -488,28 +528,37 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
 }
 
 // ---- 4. threshold: exact select among the candidates, tile offsets ---------------
-// One workgroup per sequence.  Tile i belongs to thread i mod 1,024 (round u =
-// i / 1,024).  Every thread loads its first tile's counts and the tile's
-// first kCandHead candidates (dense across tiles, so the threads' loads are
-// contiguous) with the sub-histogram; candidates beyond those (a tile with
-// more than kCandHead entries in bin B1, or rounds past the first) are read
-// from global memory where they are needed.
+// One workgroup per sequence and target.  Tile i belongs to thread i mod 1,024
+// (round u = i / 1,024).  Every thread loads its first tile's counts and the
+// tile's first kCandHead candidates (dense across tiles, so the threads' loads
+// are contiguous) with the sub-histogram.  The candidates not held that way
+// (a tile with more than kCandHead entries in bin B1, every tile of later
+// rounds) form one flat list in tile order: an exclusive prefix of the
+// per-tile counts gives every tile its start, each thread takes list entries
+// tid, tid + 1,024, ... and finds their tile by binary search over the starts,
+// so the list is loaded once, spread evenly over the threads however the
+// candidates cluster in a few tiles.  A list longer than kFlatMax is read
+// from global memory at each pass instead, each thread walking its own tiles.
 __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
     constexpr int NT = kThrThreads;
     constexpr int HPT = kSubBins / NT;               // sub-bins per thread
     constexpr int kCandReg = kCandHead;              // candidates of the first tile in registers
+    constexpr int FPT = kFlatMax / NT;               // flat-list entries per thread
     __shared__ uint32_t s_hist[kSubBins];
     __shared__ int s_tmp[NT / kWave];
     __shared__ int s_res[4];
     __shared__ int s_val[kLastMax];
+    __shared__ int s_start[kMaxTilesPerSeq];         // flat-list start of every tile
+    __shared__ uint32_t s_tc[kMaxTilesPerSeq];       // flat entries per tile: > T, == T << 16
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
+    const FullTarget g = w.tg[blockIdx.y];
     // round trip 1: second-level histogram, state, first tile's counts and candidates
     int h2[HPT];
 #pragma unroll
     for (int i = 0; i < HPT; ++i)
-        h2[i] = (int)w.hist2[(size_t)b * kSubBins + (NT - 1 - tid) * HPT + i];
-    const FullState st = w.st[b];
+        h2[i] = (int)g.hist2[(size_t)b * kSubBins + (NT - 1 - tid) * HPT + i];
+    const FullState st = g.st[b];
     if (st.Peff == 0) return;                        // uniform
     // every load is unconditional (a thread past the last tile reads tile 0 and
     // then counts nothing), so none of them waits for another
@@ -518,23 +567,66 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
     // slot j of consecutive tiles is contiguous: each load is coalesced
     int cr[kCandReg];                                // slots past tc0 hold stale data, unused
 #pragma unroll
-    for (int j = 0; j < kCandReg; ++j) cr[j] = w.cand_head[(size_t)j * w.tmax + tile0];
-    const int tc0 = w.tile_cnt[tile0];               // read for tile 0 too, then masked
-    const int ta0 = w.tile_above[tile0];
+    for (int j = 0; j < kCandReg; ++j) cr[j] = g.cand_head[(size_t)j * w.tmax + tile0];
+    const int tc0 = g.tile_cnt[tile0];               // read for tile 0 too, then masked
+    const int ta0 = g.tile_above[tile0];
     const int ncr = has0 ? min(tc0, kCandReg) : 0;   // candidates held in cr
     const int rounds = (st.ntiles + NT - 1) / NT;    // uniform
-    // fn(score) for every candidate of this thread's tile in round u that is
-    // not held in cr (round 0 slots >= kCandReg, every slot of later rounds)
+
+    // the flat list: per tile, the candidates not in cr, in tile order
+    int nflat = 0;                                   // uniform
+    for (int u = 0; u < rounds; ++u) {
+        const int i = tid + u * NT;
+        int m = 0;
+        if (i < st.ntiles) m = u == 0 ? tc0 - ncr : g.tile_cnt[st.tile0 + i];
+        int tot;
+        const int pre = block_exclusive_scan<NT>(m, s_tmp, tot);
+        if (i < st.ntiles) {
+            s_start[i] = nflat + pre;
+            s_tc[i] = 0;
+        }
+        nflat += tot;
+    }
+    const bool flat = nflat <= kFlatMax;             // uniform
+    __syncthreads();
+    int fv[FPT], fi[FPT];                            // entry value and tile (-1: none)
+#pragma unroll
+    for (int r = 0; r < FPT; ++r) {
+        const int c = tid + r * NT;
+        fi[r] = -1;
+        if (flat && c < nflat) {
+            int lo_ = 0, hi_ = st.ntiles - 1;        // last tile whose start <= c
+            while (lo_ < hi_) {
+                const int mid = (lo_ + hi_ + 1) >> 1;
+                if (s_start[mid] <= c) lo_ = mid;
+                else hi_ = mid - 1;
+            }
+            fi[r] = lo_;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < FPT; ++r) {
+        fv[r] = -1;
+        if (fi[r] >= 0) {
+            const int i = fi[r];
+            const int slot = tid + r * NT - s_start[i] + (i < NT ? kCandReg : 0);
+            const size_t t = (size_t)st.tile0 + i;
+            fv[r] = slot < kCandHead ? g.cand_head[(size_t)slot * w.tmax + t]
+                                     : g.cand[t * kTile + slot];
+        }
+    }
+    // without the flat list: fn(score) for every candidate of this thread's
+    // tile in round u that is not held in cr, read from global memory
     auto visit_mem = [&](int u, auto&& fn) {
         const int i = tid + u * NT;
         if (i >= st.ntiles) return;
         const size_t t = (size_t)st.tile0 + i;
-        const int* cg = w.cand + t * kTile;
+        const int* cg = g.cand + t * kTile;
         if (u == 0) {
             for (int j = kCandReg; j < tc0; ++j) fn(cg[j]);
         } else {
-            const int tc = w.tile_cnt[t];
-            for (int j = 0; j < tc; ++j) fn(j < kCandHead ? w.cand_head[(size_t)j * w.tmax + t] : cg[j]);
+            const int tc = g.tile_cnt[t];
+            for (int j = 0; j < tc; ++j) fn(j < kCandHead ? g.cand_head[(size_t)j * w.tmax + t] : cg[j]);
         }
     };
 
@@ -556,13 +648,19 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         sub_digit(lo, hi, sh2, nb2);
         for (int i = tid; i < nb2; i += NT) s_hist[i] = 0;
         __syncthreads();
+        auto add = [&](int c) {
+            if (c >= lo && c <= hi) atomicAdd(&s_hist[(unsigned)(c - lo) >> sh2], 1u);
+        };
 #pragma unroll
         for (int j = 0; j < kCandReg; ++j)
-            if (j < ncr && cr[j] >= lo && cr[j] <= hi) atomicAdd(&s_hist[(unsigned)(cr[j] - lo) >> sh2], 1u);
-        for (int u = 0; u < rounds; ++u)
-            visit_mem(u, [&](int c) {
-                if (c >= lo && c <= hi) atomicAdd(&s_hist[(unsigned)(c - lo) >> sh2], 1u);
-            });
+            if (j < ncr) add(cr[j]);
+        if (flat) {
+#pragma unroll
+            for (int r = 0; r < FPT; ++r)
+                if (fi[r] >= 0) add(fv[r]);
+        } else {
+            for (int u = 0; u < rounds; ++u) visit_mem(u, add);
+        }
         __syncthreads();
         find_bin<NT, kSubBins / NT>(s_hist, nb2, need, s_tmp, s_res, d, a, cnt);
         need -= a;
@@ -576,27 +674,32 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         // taken in position order by the write kernel
         if (tid == 0) s_res[3] = 0;
         __syncthreads();
-        // candidates in registers: one LDS atomic per wave and slot
+        // values in registers: one LDS atomic per wave and register
         const int lane = tid & (kWave - 1);
-#pragma unroll
-        for (int j = 0; j < kCandReg; ++j) {
-            const bool in = j < ncr && cr[j] >= lo && cr[j] <= hi;
+        auto put = [&](bool in, int c) {
             const uint64_t m = __ballot(in);
             if (m) {                                 // uniform within the wave
                 int first = 0;
                 if (lane == 0) first = atomicAdd(&s_res[3], __popcll(m));
                 first = __builtin_amdgcn_readfirstlane(first);
                 const int slot = first + lane_rank64(m);
-                if (in && slot < kLastMax) s_val[slot] = cr[j];
+                if (in && slot < kLastMax) s_val[slot] = c;
             }
+        };
+#pragma unroll
+        for (int j = 0; j < kCandReg; ++j) put(j < ncr && cr[j] >= lo && cr[j] <= hi, cr[j]);
+        if (flat) {
+#pragma unroll
+            for (int r = 0; r < FPT; ++r) put(fi[r] >= 0 && fv[r] >= lo && fv[r] <= hi, fv[r]);
+        } else {
+            for (int u = 0; u < rounds; ++u)
+                visit_mem(u, [&](int c) {
+                    if (c >= lo && c <= hi) {
+                        const int slot = atomicAdd(&s_res[3], 1);
+                        if (slot < kLastMax) s_val[slot] = c;
+                    }
+                });
         }
-        for (int u = 0; u < rounds; ++u)
-            visit_mem(u, [&](int c) {
-                if (c >= lo && c <= hi) {
-                    const int slot = atomicAdd(&s_res[3], 1);
-                    if (slot < kLastMax) s_val[slot] = c;
-                }
-            });
         __syncthreads();
         narrow_to_value(tid < cnt ? s_val[tid] : -1, lo, hi, need, cnt, s_hist, s_res);
     }
@@ -604,12 +707,18 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
 
     // per tile: entries above T (above bin B1 or candidates > T) and at T; exclusive
     // prefix over this sequence's tiles, in tile order
+    if (flat) {
+#pragma unroll
+        for (int r = 0; r < FPT; ++r)
+            if (fi[r] >= 0 && fv[r] >= T) atomicAdd(&s_tc[fi[r]], fv[r] > T ? 1u : 0x10000u);
+        __syncthreads();
+    }
     int og = 0, oe = 0;
     for (int u = 0; u < rounds; ++u) {               // uniform
         const int i = tid + u * NT;
         int gl = 0, el = 0;
         if (i < st.ntiles) {
-            gl = u == 0 ? ta0 : w.tile_above[st.tile0 + i];
+            gl = u == 0 ? ta0 : g.tile_above[st.tile0 + i];
             if (u == 0) {
 #pragma unroll
                 for (int j = 0; j < kCandReg; ++j) {
@@ -617,36 +726,42 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
                     el += j < ncr && cr[j] == T;
                 }
             }
-            visit_mem(u, [&](int c) {
-                gl += c > T;
-                el += c == T;
-            });
+            if (flat) {
+                const uint32_t x = s_tc[i];
+                gl += (int)(x & 0xFFFFu);
+                el += (int)(x >> 16);
+            } else {
+                visit_mem(u, [&](int c) {
+                    gl += c > T;
+                    el += c == T;
+                });
+            }
         }
         int tg, te;
         const int pg = block_exclusive_scan<NT>(gl, s_tmp, tg);
         const int pe = block_exclusive_scan<NT>(el, s_tmp, te);
         if (i < st.ntiles) {
-            w.tile_off[2 * (st.tile0 + i)] = og + pg;
-            w.tile_off[2 * (st.tile0 + i) + 1] = oe + pe;
+            g.tile_off[2 * (st.tile0 + i)] = og + pg;
+            g.tile_off[2 * (st.tile0 + i) + 1] = oe + pe;
         }
         og += tg;
         oe += te;
     }
     if (tid == 0) {
-        w.st[b].T = T;
-        w.st[b].needT = needT;
+        g.st[b].T = T;
+        g.st[b].needT = needT;
     }
 }
 
-// ---- 5. write: ordered compaction of the pool ------------------------------------
-__global__ __launch_bounds__(kScanThreads) void full_write_kernel(int B, int P,
-                                                                  int* __restrict__ pool_pos,
-                                                                  int* __restrict__ pool_score,
-                                                                  int* __restrict__ pool_len,
+// ---- 5. write: ordered compaction of the pool (and of the top k) -----------------
+// blockIdx.y selects the target and its output.
+__global__ __launch_bounds__(kScanThreads) void full_write_kernel(int B, FullOut o0, FullOut o1,
                                                                   FullWs w) {
     __shared__ int s_b;
     __shared__ int s_tmp[kScanThreads / kWave];
     const int t = blockIdx.x;
+    const FullTarget g = w.tg[blockIdx.y];
+    const FullOut o = blockIdx.y ? o1 : o0;
     // the tile's scores and output offsets sit at t whatever its sequence: load first
     const int* sc = w.scores + (size_t)t * kTile;
     constexpr int PER = kTile / kScanThreads;   // contiguous positions per thread
@@ -654,17 +769,17 @@ __global__ __launch_bounds__(kScanThreads) void full_write_kernel(int B, int P,
     int v[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) v[j] = sc[i0 + j];
-    const int tile_gt = w.tile_off[2 * t], tile_eq = w.tile_off[2 * t + 1];
+    const int tile_gt = g.tile_off[2 * t], tile_eq = g.tile_off[2 * t + 1];
     FullState st;
-    const int b = tile_state(w.st, B, t, &s_b, st);
+    const int b = tile_state(g.st, B, t, &s_b, st);
     // tail fill of sequence t (each block handles at most one sequence's tail)
     if (t < B) {
-        const int Peff = B == 1 ? st.Peff : w.st[t].Peff;
-        for (int i = Peff + threadIdx.x; i < P; i += kScanThreads) {
-            pool_pos[(size_t)t * P + i] = -1;
-            pool_score[(size_t)t * P + i] = -1;
+        const int Peff = B == 1 ? st.Peff : g.st[t].Peff;
+        for (int i = Peff + threadIdx.x; i < o.stride; i += kScanThreads) {
+            o.pos[(size_t)t * o.stride + i] = -1;
+            if (o.score) o.score[(size_t)t * o.stride + i] = -1;
         }
-        if (threadIdx.x == 0) pool_len[t] = Peff;
+        if (threadIdx.x == 0) o.len[t] = Peff;
     }
     if (b < 0) return;
     const int p_tile = (t - st.tile0) * kTile;
@@ -693,14 +808,14 @@ __global__ __launch_bounds__(kScanThreads) void full_write_kernel(int B, int P,
     }
     int base = tile_gt + (tile_eq < st.needT ? tile_eq : st.needT);
     base += block_exclusive_scan<kScanThreads>(n_sel, s_tmp, tot);
-    int* out_p = pool_pos + (size_t)b * P;
-    int* out_s = pool_score + (size_t)b * P;
+    int* out_p = o.pos + (size_t)b * o.stride;
+    int* out_s = o.score ? o.score + (size_t)b * o.stride : nullptr;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if (take[j]) {
             if (base < st.Peff) {            // always true for consistent inputs
                 out_p[base] = p_tile + i0 + j;
-                out_s[base] = v[j];
+                if (out_s) out_s[base] = v[j];
             }
             ++base;
         }
@@ -754,22 +869,25 @@ extern "C" int csa2_index_full(const signed char* q, const signed char* w,
                                const signed char* keys, const long long* row_off,
                                const int* len, int B, long long max_len, long long total_len,
                                int H, int Dk, int window, int P, int* pool_pos,
-                               int* pool_score, int* pool_len, void* ws, size_t ws_bytes,
-                               void* stream) {
+                               int* pool_score, int* pool_len, int k, int* sel_pos,
+                               int* sel_len, void* ws, size_t ws_bytes, void* stream) {
     if (int e = check_scan_args("csa2_index_full", q, w, keys, row_off, len, B, max_len,
                                 total_len, H, Dk, window))
         return e;
     if (B == 0) return CSA2_OK;
-    if (!pool_pos || !pool_score || !pool_len)
-        return fail(CSA2_ERR_INVALID, "csa2_index_full: null pointer");
     if (P < 1) return fail(CSA2_ERR_INVALID, "csa2_index_full: P < 1");
-    const size_t need = index_full_ws_bytes(B, total_len, P);
+    if (k < 0 || k > P) return fail(CSA2_ERR_INVALID, "csa2_index_full: k must be in [0, P]");
+    if (!pool_pos || !pool_score || !pool_len || (k > 0 && (!sel_pos || !sel_len)))
+        return fail(CSA2_ERR_INVALID, "csa2_index_full: null pointer");
+    const size_t need = index_full_ws_bytes(B, total_len, P, k);
     if (!ws || ws_bytes < need || !aligned(ws, 256))
         return fail(CSA2_ERR_WORKSPACE, "csa2_index_full: workspace needs %zu bytes (256-aligned)",
                     need);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     FullWs fw;
-    full_ws_layout(B, total_len, reinterpret_cast<char*>(ws), &fw);
+    const int ntg = k > 0 ? 2 : 1;
+    full_ws_layout(B, total_len, ntg, reinterpret_cast<char*>(ws), &fw);
+    fw.k = k;
     const unsigned tiles = (unsigned)full_tile_bound(B, total_len);
     const dim3 blk(kScanThreads);
 
@@ -777,11 +895,12 @@ extern "C" int csa2_index_full(const signed char* q, const signed char* w,
                              -1))
         return e;
     hipLaunchKernelGGL(full_reduce_kernel, dim3(kKeyBins / kRedBins, B), blk, 0, s, fw);
-    hipLaunchKernelGGL(full_gather_kernel, dim3(tiles), blk, 0, s, B, fw);
-    hipLaunchKernelGGL(full_threshold_kernel, dim3(B), dim3(kThrThreads), 0, s, fw);
+    hipLaunchKernelGGL(full_gather_kernel, dim3(tiles, ntg), blk, 0, s, B, fw);
+    hipLaunchKernelGGL(full_threshold_kernel, dim3(B, ntg), dim3(kThrThreads), 0, s, fw);
     const unsigned wgrid = tiles > (unsigned)B ? tiles : (unsigned)B;
-    hipLaunchKernelGGL(full_write_kernel, dim3(wgrid), blk, 0, s, B, P, pool_pos, pool_score,
-                       pool_len, fw);
+    const FullOut o0 = {pool_pos, pool_score, pool_len, P};
+    const FullOut o1 = {sel_pos, nullptr, sel_len, k};
+    hipLaunchKernelGGL(full_write_kernel, dim3(wgrid, ntg), blk, 0, s, B, o0, o1, fw);
     return launch_status("csa2_index_full launch");
 }
 
@@ -795,12 +914,12 @@ extern "C" int csa2_index_score(const signed char* q, const signed char* w,
         return e;
     if (B == 0) return CSA2_OK;
     if (!score) return fail(CSA2_ERR_INVALID, "csa2_index_score: null pointer");
-    const size_t need = index_full_ws_bytes(B, total_len, 1);
+    const size_t need = index_full_ws_bytes(B, total_len, 1, 0);
     if (!ws || ws_bytes < need || !aligned(ws, 256))
         return fail(CSA2_ERR_WORKSPACE,
                     "csa2_index_score: workspace needs %zu bytes (256-aligned)", need);
     FullWs fw;
-    full_ws_layout(B, total_len, reinterpret_cast<char*>(ws), &fw);
+    full_ws_layout(B, total_len, 1, reinterpret_cast<char*>(ws), &fw);
     const unsigned tiles = (unsigned)full_tile_bound(B, total_len);
     return launch_score(H, tiles, reinterpret_cast<hipStream_t>(stream), q, w, keys, row_off, len,
                         B, window, 1, fw, score, max_len);

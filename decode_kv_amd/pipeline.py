@@ -45,7 +45,7 @@ class Engine:
         self.out = torch.zeros((wl.n_layers, B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
         self.lse = torch.zeros((wl.n_layers, B, wl.Hq), dtype=torch.float32, device=dev)
         self.ws_full = csa2.workspace(csa2.workspace_bytes(
-            csa2.OP_INDEX_FULL, B, self.max_len, self.total_len, wl.H, P), dev)
+            csa2.OP_INDEX_FULL, B, self.max_len, self.total_len, wl.H, P, wl.k), dev)
         self.ws_attn = csa2.workspace(csa2.workspace_bytes(
             csa2.OP_SPARSE_ATTN, B, self.max_len, 0, 0, 0, k, wl.Hq, wl.D, wl.window), dev)
 
@@ -117,9 +117,8 @@ class Engine:
             if kind == "F":
                 csa2.index_full(inp["idx_q"][l], inp["idx_w"][l], self.keys, self.row_off,
                                 self.lens, self.max_len, self.total_len, wl.window, wl.P,
-                                self.pool_pos, self.pool_score, self.pool_len, self.ws_full, s)
-                csa2.select_topk(self.pool_score, self.pool_pos, self.pool_len, wl.k,
-                                 self.sel_pos[l], self.sel_len[l], None, s)
+                                self.pool_pos, self.pool_score, self.pool_len, self.ws_full, s,
+                                k=wl.k, sel_pos=self.sel_pos[l], sel_len=self.sel_len[l])
                 src = l
             elif kind == "R":
                 csa2.index_reindex(inp["idx_q"][l], inp["idx_w"][l], self.keys, self.row_off,

@@ -115,17 +115,24 @@ int csa2_kv_append_fp4(const void* x_bf16, const long long* dst_row, int n, int 
  *   pool_pos [B][P] int32 out: pool positions, ascending, tail -1.
  *   pool_score [B][P] int32 out: score of each pool entry, tail -1.
  *   pool_len [B] int32 out: P_eff.
+ *   k        0, or the size of the Full layer's own selection (1 <= k <= P).
+ *   sel_pos  [B][k] int32 out when k > 0 (else ignored, may be NULL): the
+ *            first min(k, P_eff) positions under the same rank order,
+ *            ascending, tail -1 -- exactly what csa2_select_topk returns for
+ *            the pool and its scores, without a separate pass over them.
+ *   sel_len  [B] int32 out when k > 0: min(k, P_eff).
  *   ws, ws_bytes: workspace of csa2_workspace_bytes(CSA2_OP_INDEX_FULL, B,
- *            max_len, total_len, H, P, ...) bytes, 256-byte aligned.  Its
+ *            max_len, total_len, H, P, k, ...) bytes, 256-byte aligned.  Its
  *            contents need no initialisation and are not preserved.
- * Requires Dk == 64, 1 <= H <= 64, 1 <= P, window >= 0.  Scores are exact
- * int32 (at most 64 * 15 * 64 * 127^2 < 2^31).  Ties at the pool boundary go
- * to the lower position.
+ * Requires Dk == 64, 1 <= H <= 64, 1 <= P, 0 <= k <= P, window >= 0.  Scores
+ * are exact int32 (at most 64 * 15 * 64 * 127^2 < 2^31).  Ties at the pool
+ * and selection boundaries go to the lower position.
  */
 int csa2_index_full(const signed char* q, const signed char* w, const signed char* keys,
                     const long long* row_off, const int* len, int B, long long max_len,
                     long long total_len, int H, int Dk, int window, int P,
                     int* pool_pos, int* pool_score, int* pool_len,
+                    int k, int* sel_pos, int* sel_len,
                     void* ws, size_t ws_bytes, void* stream);
 
 /*

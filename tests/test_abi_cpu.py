@@ -35,6 +35,9 @@ def test_workspace_sizes(lib):
     w1 = csa2.workspace_bytes(csa2.OP_INDEX_FULL, 1, 1 << 20, 1 << 20, 64, 16384)
     w2 = csa2.workspace_bytes(csa2.OP_INDEX_FULL, 1, 1 << 21, 1 << 21, 64, 16384)
     assert w1 > 4 * (1 << 20) and w2 > w1 and w1 % 256 == 0
+    wk = csa2.workspace_bytes(csa2.OP_INDEX_FULL, 1, 1 << 20, 1 << 20, 64, 16384, 512)
+    assert wk > w1 and wk % 256 == 0                 # the selection's own candidate arrays
+    assert csa2.workspace_bytes(csa2.OP_INDEX_FULL, 1, 1 << 20, 1 << 20, 64, 16384, 16385) == 0
     assert csa2.workspace_bytes(csa2.OP_SELECT_TOPK, 4, 0, 0, 0, 16384, 512) == 0
     wa1 = csa2.workspace_bytes(csa2.OP_SPARSE_ATTN, 1, 0, 0, 0, 0, 512, 64, 512, 128)
     wa32 = csa2.workspace_bytes(csa2.OP_SPARSE_ATTN, 32, 0, 0, 0, 0, 512, 64, 512, 128)
@@ -58,12 +61,12 @@ def test_append_rejects_bad_arguments(lib):
 def _full(lib, **kw):
     a = dict(q=256, w=256, keys=256, row_off=256, len=256, B=1, max_len=4096, total_len=4096,
              H=64, Dk=64, window=128, P=1024, pool_pos=256, pool_score=256, pool_len=256,
-             ws=256, ws_bytes=1 << 40, stream=None)
+             k=0, sel_pos=None, sel_len=None, ws=256, ws_bytes=1 << 40, stream=None)
     a.update(kw)
     return lib.csa2_index_full(a["q"], a["w"], a["keys"], a["row_off"], a["len"], a["B"],
                                a["max_len"], a["total_len"], a["H"], a["Dk"], a["window"],
-                               a["P"], a["pool_pos"], a["pool_score"], a["pool_len"], a["ws"],
-                               a["ws_bytes"], a["stream"])
+                               a["P"], a["pool_pos"], a["pool_score"], a["pool_len"], a["k"],
+                               a["sel_pos"], a["sel_len"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 def test_index_full_rejects_bad_arguments(lib):
@@ -79,6 +82,11 @@ def test_index_full_rejects_bad_arguments(lib):
     assert _full(lib, ws_bytes=100) == csa2.CSA2_ERR_WORKSPACE
     assert "workspace" in csa2.last_error()
     assert _full(lib, max_len=1 << 31) == csa2.CSA2_ERR_UNSUPPORTED
+    assert _full(lib, k=-1) == csa2.CSA2_ERR_INVALID
+    assert _full(lib, k=1025) == csa2.CSA2_ERR_INVALID                      # k > P
+    assert _full(lib, k=64) == csa2.CSA2_ERR_INVALID                        # sel_pos NULL
+    assert "null" in csa2.last_error()
+    assert _full(lib, k=64, sel_pos=256, sel_len=None) == csa2.CSA2_ERR_INVALID
 
 
 def test_index_score_rejects_bad_arguments(lib):

@@ -132,7 +132,7 @@ def test_kv_append_wide_rows():
 # csa2_index_full
 # ---------------------------------------------------------------------------
 
-def run_full(keys_np, row_off, lens, q_np, w_np, window, P):
+def run_full(keys_np, row_off, lens, q_np, w_np, window, P, k=0):
     B = len(lens)
     keys = torch.from_numpy(keys_np).to(DEV)
     ro = torch.tensor(row_off, dtype=torch.int64, device=DEV)
@@ -142,15 +142,25 @@ def run_full(keys_np, row_off, lens, q_np, w_np, window, P):
     pos = torch.full((B, P), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
     scr = torch.full((B, P), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
     plen = torch.full((B,), -9, dtype=torch.int32, device=DEV)
+    sel = torch.full((B, max(k, 1)), 0x5A5A5A5A, dtype=torch.int32, device=DEV)
+    slen = torch.full((B,), -9, dtype=torch.int32, device=DEV)
     max_len, total_len = max(lens + [0]), keys_np.shape[0]
-    ws = csa2.workspace(csa2.workspace_bytes(csa2.OP_INDEX_FULL, B, max_len, total_len, q.shape[1], P))
-    csa2.index_full(q, w, keys, ro, ln, max_len, total_len, window, P, pos, scr, plen, ws)
+    ws = csa2.workspace(csa2.workspace_bytes(csa2.OP_INDEX_FULL, B, max_len, total_len, q.shape[1],
+                                             P, k))
+    csa2.index_full(q, w, keys, ro, ln, max_len, total_len, window, P, pos, scr, plen, ws,
+                    k=k, sel_pos=sel if k else None, sel_len=slen if k else None)
     torch.cuda.synchronize()
-    return pos.cpu().numpy(), scr.cpu().numpy(), plen.cpu().numpy()
+    return (pos.cpu().numpy(), scr.cpu().numpy(), plen.cpu().numpy(), sel.cpu().numpy(),
+            slen.cpu().numpy())
 
 
-def check_full(keys_np, row_off, lens, q_np, w_np, window, P, what=""):
-    pos, scr, plen = run_full(keys_np, row_off, lens, q_np, w_np, window, P)
+def check_full(keys_np, row_off, lens, q_np, w_np, window, P, what="", k=None):
+    """Pool (and, for k > 0, the Full layer's own top k, default P // 3 + 1)
+    against the oracle: the selection must be the oracle's top k of the
+    oracle's pool."""
+    if k is None:
+        k = P // 3 + 1
+    pos, scr, plen, sel, slen = run_full(keys_np, row_off, lens, q_np, w_np, window, P, k)
     for b, L in enumerate(lens):
         rp, rs = oracle.index_full(keys_np, row_off[b], L, q_np[b], w_np[b], window, P)
         n = len(rp)
@@ -158,6 +168,14 @@ def check_full(keys_np, row_off, lens, q_np, w_np, window, P, what=""):
         assert np.array_equal(pos[b, :n], rp), (what, b)
         assert np.array_equal(scr[b, :n], rs), (what, b)
         assert (pos[b, n:] == -1).all() and (scr[b, n:] == -1).all(), (what, b)
+        if k:
+            ref, _ = oracle.select_topk(rs, rp, k)
+            m = len(ref)
+            assert slen[b] == m, (what, b, "selection")
+            assert np.array_equal(sel[b, :m], ref), (what, b, "selection")
+            assert (sel[b, m:k] == -1).all(), (what, b, "selection")
+        else:
+            assert (slen == -9).all() and (sel == 0x5A5A5A5A).all(), (what, "k = 0 wrote")
 
 
 @pytest.mark.parametrize("seed", range(40))
@@ -165,8 +183,9 @@ def test_index_full_tiny_seeds(seed):
     case = W.Case(W.WORKLOADS["tiny_4k"], seed, "cpu")
     keys = case.keys_all().numpy()
     q, w = case.index_qw_batch(0, 0)
+    k = [0, 64, 1, 1024][seed % 4]                   # 0: the pool alone; 1024: k = P
     check_full(keys, list(case.row_off), case.lengths, q.numpy(), w.numpy(), 128, 1024,
-               "tiny seed %d" % seed)
+               "tiny seed %d" % seed, k=k)
 
 
 def test_index_full_tie_adversarial():
@@ -233,6 +252,33 @@ def test_index_full_crowded_sub_bin():
         check_full(keys, [0], [L], q, w, W_, P, "5,000 hot over 64 values, P %d" % P)
 
 
+def test_index_full_skewed_candidates():
+    """Candidates of the threshold bin crowded into a few tiles (recent
+    positions), and more of them than the threshold kernel's flat list holds
+    (its per-tile walk), for the pool and the selection."""
+    rng = np.random.default_rng(21)
+    L, W_ = 20000, 128
+    keys = np.zeros((L, 64), dtype=np.int8)
+    keys[:, 0] = 50
+    hot = L - W_ - 1 - rng.choice(900, 700, replace=False)       # 700 hot in the last tile
+    keys[hot, 0] = 127
+    keys[:, 1] = rng.integers(0, 64, size=L)
+    q = np.zeros((1, 64, 64), dtype=np.int8)
+    q[0, 1:, 0] = 127
+    q[0, 0, 1] = 1
+    w = np.full((1, 64), 15, dtype=np.int8)
+    w[0, 0] = 1
+    for P, k in [(4000, 512), (650, 100), (700, 700)]:
+        check_full(keys, [0], [L], q, w, W_, P, "700 hot in one tile, P %d k %d" % (P, k), k=k)
+    L2 = 40000
+    keys2 = np.zeros((L2, 64), dtype=np.int8)
+    keys2[:, 0] = 127
+    keys2[:, 1] = rng.integers(0, 64, size=L2)
+    keys2[rng.choice(L2, 5000, replace=False), 0] = 50
+    for P, k in [(10000, 512), (16384, 9000)]:
+        check_full(keys2, [0], [L2], q, w, W_, P, "35,000 in one bin, P %d k %d" % (P, k), k=k)
+
+
 def test_index_score_matches_oracle():
     rng = np.random.default_rng(13)
     lens = [0, 1, 1023, 1024, 1025, 70001, 3000]
@@ -282,7 +328,8 @@ def test_index_full_ragged_batch_and_edges():
     q = rng.integers(-127, 128, size=(B, 64, 64)).astype(np.int8)
     w = rng.integers(0, 16, size=(B, 64)).astype(np.int8)
     check_full(keys, row_off, lens, q, w, 0, 1, "window 0, P 1")
-    check_full(keys, row_off, lens, q, w, 128, 16384, "P 16384")
+    check_full(keys, row_off, lens, q, w, 128, 16384, "P 16384", k=512)
+    check_full(keys, row_off, lens, q, w, 128, 16384, "P 16384, pool only", k=0)
 
 
 def test_index_full_extreme_scores():

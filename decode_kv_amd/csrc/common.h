@@ -163,6 +163,37 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_tmp, int& tota
     return before + x - v;
 }
 
+// Two exclusive prefix sums at once (a and b, thread order), with the block
+// sums; the same two barriers as one scan.  s_tmp holds 2 * NT / 64 ints.
+template <int NT>
+__device__ __forceinline__ void block_exclusive_scan2(int a, int b, int* s_tmp, int& pa, int& pb,
+                                                      int& ta, int& tb) {
+    constexpr int NW = NT / kWave;
+    const int l = lane_id(), wv = threadIdx.x / kWave;
+    const int xa = wave_inclusive_scan(a), xb = wave_inclusive_scan(b);
+    if (l == kWave - 1) {
+        s_tmp[wv] = xa;
+        s_tmp[NW + wv] = xb;
+    }
+    __syncthreads();
+    int ba = 0, bb = 0;
+    ta = 0;
+    tb = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const int ca = s_tmp[i], cb = s_tmp[NW + i];
+        if (i < wv) {
+            ba += ca;
+            bb += cb;
+        }
+        ta += ca;
+        tb += cb;
+    }
+    __syncthreads();
+    pa = ba + xa - a;
+    pb = bb + xb - b;
+}
+
 // Rank of this lane among the set lanes of a wave mask (lanes below it).
 __device__ __forceinline__ int lane_rank64(uint64_t m) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),

@@ -50,7 +50,7 @@ constexpr int kThrThreads = 1024;
 constexpr int kMaxTilesPerSeq = 8192;    // LDS tile tables of the threshold kernel (8M positions)
 constexpr int kLastMax = kThrThreads;    // entries the last digits take, one per thread
 constexpr int kCandHead = 16;            // candidates per tile in the dense head array
-constexpr int kFlatMax = 8 * kThrThreads;  // threshold: candidates outside registers, loaded once
+constexpr int kListMax = 8 * kThrThreads;  // threshold: bin B1 candidates compacted into LDS
 constexpr int kMaxBatch = 4096;
 
 struct FullState {
@@ -531,92 +531,120 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
 // One workgroup per sequence and target.  Tile i belongs to thread i mod 1,024
 // (round u = i / 1,024).  Every thread loads its first tile's counts and the
 // tile's first kCandHead candidates (dense across tiles, so the threads' loads
-// are contiguous) with the sub-histogram.  The candidates not held that way
-// (a tile with more than kCandHead entries in bin B1, every tile of later
-// rounds) form one flat list in tile order: an exclusive prefix of the
-// per-tile counts gives every tile its start, each thread takes list entries
-// tid, tid + 1,024, ... and finds their tile by binary search over the starts,
-// so the list is loaded once, spread evenly over the threads however the
-// candidates cluster in a few tiles.  A list longer than kFlatMax is read
-// from global memory at each pass instead, each thread walking its own tiles.
+// are contiguous) with the sub-histogram.  All candidates of bin B1 are then
+// compacted into one list in LDS (value and tile): first every thread's
+// registers, then the rest (a tile with more than kCandHead, every tile of
+// later rounds) in tile order, where thread t takes entries t, t + 1,024, ...
+// and finds their tile by binary search over the per-tile starts.  Every
+// later pass reads the list, each thread a share of the same size however the
+// candidates cluster.  A list longer than kListMax is not built: the passes
+// then read the registers and global memory, each thread walking its tiles.
+template <bool ONE>   // ONE: a single sequence, whose first tile is 0
 __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
     constexpr int NT = kThrThreads;
     constexpr int HPT = kSubBins / NT;               // sub-bins per thread
     constexpr int kCandReg = kCandHead;              // candidates of the first tile in registers
-    constexpr int FPT = kFlatMax / NT;               // flat-list entries per thread
+    constexpr int LPT = kListMax / NT;               // list entries per thread at most
     __shared__ uint32_t s_hist[kSubBins];
-    __shared__ int s_tmp[NT / kWave];
+    __shared__ int s_tmp[2 * NT / kWave];
     __shared__ int s_res[4];
-    __shared__ int s_val[kLastMax];
-    __shared__ int s_start[kMaxTilesPerSeq];         // flat-list start of every tile
-    __shared__ uint32_t s_tc[kMaxTilesPerSeq];       // flat entries per tile: > T, == T << 16
+    __shared__ int s_val[kLastMax];                  // the last entries: scores ...
+    __shared__ uint16_t s_valt[kLastMax];            // ... and their tiles
+    __shared__ int s_tile[kMaxTilesPerSeq];          // list start of each tile's rest, then
+                                                     // per tile: candidates > T | == T << 16
+    __shared__ uint64_t s_list[kListMax];            // the list: score | tile << 32
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     const FullTarget g = w.tg[blockIdx.y];
-    // round trip 1: second-level histogram, state, first tile's counts and candidates
-    int h2[HPT];
-#pragma unroll
-    for (int i = 0; i < HPT; ++i)
-        h2[i] = (int)g.hist2[(size_t)b * kSubBins + (NT - 1 - tid) * HPT + i];
+    // round trip 1: the first tile's counts (needed first: loads complete in
+    // order), its first candidates, the second-level histogram and the state.
+    // Every load is unconditional (a thread past the last tile reads another
+    // tile and then counts nothing), so none of them waits for another; with
+    // one sequence (first tile 0) they need not wait for the state either
     const FullState st = g.st[b];
-    if (st.Peff == 0) return;                        // uniform
-    // every load is unconditional (a thread past the last tile reads tile 0 and
-    // then counts nothing), so none of them waits for another
-    const bool has0 = tid < st.ntiles;
-    const size_t tile0 = (size_t)st.tile0 + (has0 ? tid : 0);
+    const size_t tile0 = ONE ? (size_t)min(tid, w.tmax - 1)
+                             : (size_t)st.tile0 + (tid < st.ntiles ? tid : 0);
+    const int tc0 = g.tile_cnt[tile0];               // read for another tile too, then masked
+    const int ta0 = g.tile_above[tile0];
     // slot j of consecutive tiles is contiguous: each load is coalesced
     int cr[kCandReg];                                // slots past tc0 hold stale data, unused
 #pragma unroll
     for (int j = 0; j < kCandReg; ++j) cr[j] = g.cand_head[(size_t)j * w.tmax + tile0];
-    const int tc0 = g.tile_cnt[tile0];               // read for tile 0 too, then masked
-    const int ta0 = g.tile_above[tile0];
+    int h2[HPT];
+#pragma unroll
+    for (int i = 0; i < HPT; ++i)
+        h2[i] = (int)g.hist2[(size_t)b * kSubBins + (NT - 1 - tid) * HPT + i];
+    if (st.Peff == 0) {                              // uniform
+        // an empty use of the loads on this path too keeps the compiler from
+        // moving them below the branch, behind the state's round trip
+        int x = tc0 ^ ta0;
+#pragma unroll
+        for (int j = 0; j < kCandReg; ++j) x ^= cr[j];
+#pragma unroll
+        for (int i = 0; i < HPT; ++i) x ^= h2[i];
+        asm volatile("" ::"v"(x));
+        return;
+    }
+    const bool has0 = tid < st.ntiles;
     const int ncr = has0 ? min(tc0, kCandReg) : 0;   // candidates held in cr
     const int rounds = (st.ntiles + NT - 1) / NT;    // uniform
 
-    // the flat list: per tile, the candidates not in cr, in tile order
-    int nflat = 0;                                   // uniform
-    for (int u = 0; u < rounds; ++u) {
+    // list layout: the registers' candidates in thread order, then the rest
+    int reg_pre, rest_pre, nreg, nrest;
+    block_exclusive_scan2<NT>(ncr, has0 ? tc0 - ncr : 0, s_tmp, reg_pre, rest_pre, nreg, nrest);
+    if (has0) s_tile[tid] = rest_pre;
+    for (int u = 1; u < rounds; ++u) {               // uniform; later rounds: all in the rest
         const int i = tid + u * NT;
-        int m = 0;
-        if (i < st.ntiles) m = u == 0 ? tc0 - ncr : g.tile_cnt[st.tile0 + i];
+        const int m = i < st.ntiles ? g.tile_cnt[st.tile0 + i] : 0;
         int tot;
         const int pre = block_exclusive_scan<NT>(m, s_tmp, tot);
-        if (i < st.ntiles) {
-            s_start[i] = nflat + pre;
-            s_tc[i] = 0;
-        }
-        nflat += tot;
+        if (i < st.ntiles) s_tile[i] = nrest + pre;
+        nrest += tot;
     }
-    const bool flat = nflat <= kFlatMax;             // uniform
-    __syncthreads();
-    int fv[FPT], fi[FPT];                            // entry value and tile (-1: none)
+    const int nlist = nreg + nrest;                  // uniform
+    const bool inlds = nlist <= kListMax;            // uniform
+    if (inlds) {
 #pragma unroll
-    for (int r = 0; r < FPT; ++r) {
-        const int c = tid + r * NT;
-        fi[r] = -1;
-        if (flat && c < nflat) {
-            int lo_ = 0, hi_ = st.ntiles - 1;        // last tile whose start <= c
-            while (lo_ < hi_) {
-                const int mid = (lo_ + hi_ + 1) >> 1;
-                if (s_start[mid] <= c) lo_ = mid;
-                else hi_ = mid - 1;
+        for (int j = 0; j < kCandReg; ++j)
+            if (j < ncr) s_list[reg_pre + j] = (uint32_t)cr[j] | (uint64_t)tid << 32;
+    }
+    __syncthreads();                                 // the rest's starts are complete
+    if (inlds && nrest > 0) {                        // uniform
+        const int R = (nrest + NT - 1) / NT;         // uniform, <= LPT
+        int fi[LPT];                                 // last tile whose start <= entry
+#pragma unroll
+        for (int r = 0; r < LPT; ++r) fi[r] = 0;
+        for (int step = 1 << (31 - __clz(st.ntiles)); step > 0; step >>= 1) {
+#pragma unroll
+            for (int r = 0; r < LPT; ++r) {
+                if (r < R) {
+                    const int q = min(fi[r] + step, st.ntiles - 1);
+                    if (s_tile[q] <= tid + r * NT) fi[r] = q;
+                }
             }
-            fi[r] = lo_;
         }
-    }
+        int fv[LPT];
 #pragma unroll
-    for (int r = 0; r < FPT; ++r) {
-        fv[r] = -1;
-        if (fi[r] >= 0) {
-            const int i = fi[r];
-            const int slot = tid + r * NT - s_start[i] + (i < NT ? kCandReg : 0);
-            const size_t t = (size_t)st.tile0 + i;
-            fv[r] = slot < kCandHead ? g.cand_head[(size_t)slot * w.tmax + t]
-                                     : g.cand[t * kTile + slot];
+        for (int r = 0; r < LPT; ++r) {
+            const int c = tid + r * NT;
+            if (r < R && c < nrest) {
+                const int i = fi[r];
+                const int slot = c - s_tile[i] + (i < NT ? kCandReg : 0);
+                const size_t t = (size_t)st.tile0 + i;
+                fv[r] = slot < kCandHead ? g.cand_head[(size_t)slot * w.tmax + t]
+                                         : g.cand[t * kTile + slot];
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < LPT; ++r) {
+            const int c = tid + r * NT;
+            if (r < R && c < nrest) s_list[nreg + c] = (uint32_t)fv[r] | (uint64_t)fi[r] << 32;
         }
     }
-    // without the flat list: fn(score) for every candidate of this thread's
-    // tile in round u that is not held in cr, read from global memory
+    __syncthreads();                                 // list complete, starts no longer needed
+    for (int i = tid; i < st.ntiles; i += NT) s_tile[i] = 0;
+    // without the list: fn(score) for every candidate of this thread's tile in
+    // round u that is not held in cr, read from global memory
     auto visit_mem = [&](int u, auto&& fn) {
         const int i = tid + u * NT;
         if (i >= st.ntiles) return;
@@ -627,6 +655,24 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         } else {
             const int tc = g.tile_cnt[t];
             for (int j = 0; j < tc; ++j) fn(j < kCandHead ? g.cand_head[(size_t)j * w.tmax + t] : cg[j]);
+        }
+    };
+    // fn(score, tile) for every candidate of the sequence, each once
+    const int RL = (nlist + NT - 1) / NT;            // uniform
+    auto visit_all = [&](auto&& fn) {
+        if (inlds) {
+            for (int r = 0; r < RL; ++r) {
+                const int c = tid + r * NT;
+                if (c < nlist) {
+                    const uint64_t e = s_list[c];
+                    fn((int)(uint32_t)e, (int)(e >> 32));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < kCandReg; ++j)
+                if (j < ncr) fn(cr[j], tid);
+            for (int u = 0; u < rounds; ++u) visit_mem(u, [&](int c) { fn(c, tid + u * NT); });
         }
     };
 
@@ -648,19 +694,9 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         sub_digit(lo, hi, sh2, nb2);
         for (int i = tid; i < nb2; i += NT) s_hist[i] = 0;
         __syncthreads();
-        auto add = [&](int c) {
+        visit_all([&](int c, int) {
             if (c >= lo && c <= hi) atomicAdd(&s_hist[(unsigned)(c - lo) >> sh2], 1u);
-        };
-#pragma unroll
-        for (int j = 0; j < kCandReg; ++j)
-            if (j < ncr) add(cr[j]);
-        if (flat) {
-#pragma unroll
-            for (int r = 0; r < FPT; ++r)
-                if (fi[r] >= 0) add(fv[r]);
-        } else {
-            for (int u = 0; u < rounds; ++u) visit_mem(u, add);
-        }
+        });
         __syncthreads();
         find_bin<NT, kSubBins / NT>(s_hist, nb2, need, s_tmp, s_res, d, a, cnt);
         need -= a;
@@ -668,78 +704,53 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
         hi = sub_range_hi(nlo, sh2, hi);
         lo = nlo;
     }
-    if (lo < hi) {
-        // <= kLastMax entries in [lo, hi]: gather their scores, one per thread,
-        // and take the last digits on them; ties at the resulting value are
-        // taken in position order by the write kernel
-        if (tid == 0) s_res[3] = 0;
-        __syncthreads();
-        // values in registers: one LDS atomic per wave and register
-        const int lane = tid & (kWave - 1);
-        auto put = [&](bool in, int c) {
-            const uint64_t m = __ballot(in);
-            if (m) {                                 // uniform within the wave
-                int first = 0;
-                if (lane == 0) first = atomicAdd(&s_res[3], __popcll(m));
-                first = __builtin_amdgcn_readfirstlane(first);
-                const int slot = first + lane_rank64(m);
-                if (in && slot < kLastMax) s_val[slot] = c;
+    // T lies in [lo, hi]: one pass counts, per tile, the candidates above hi
+    // (all > T); those in [lo, hi] are the ties at T when lo == hi, else (<=
+    // kLastMax of them) they are gathered with their tiles, one per thread, the
+    // last digits narrow them to T, and each thread adds its entry to its
+    // tile's counts.  Ties at T are taken in position order by the write kernel.
+    if (tid == 0) s_res[3] = 0;
+    __syncthreads();
+    const bool single = lo == hi;                    // uniform
+    visit_all([&](int c, int i) {
+        uint32_t* ti = reinterpret_cast<uint32_t*>(&s_tile[i]);
+        if (c > hi) {
+            atomicAdd(ti, 1u);
+        } else if (c >= lo) {
+            if (single) {
+                atomicAdd(ti, 0x10000u);
+            } else {
+                const int slot = atomicAdd(&s_res[3], 1);
+                if (slot < kLastMax) {
+                    s_val[slot] = c;
+                    s_valt[slot] = (uint16_t)i;
+                }
             }
-        };
-#pragma unroll
-        for (int j = 0; j < kCandReg; ++j) put(j < ncr && cr[j] >= lo && cr[j] <= hi, cr[j]);
-        if (flat) {
-#pragma unroll
-            for (int r = 0; r < FPT; ++r) put(fi[r] >= 0 && fv[r] >= lo && fv[r] <= hi, fv[r]);
-        } else {
-            for (int u = 0; u < rounds; ++u)
-                visit_mem(u, [&](int c) {
-                    if (c >= lo && c <= hi) {
-                        const int slot = atomicAdd(&s_res[3], 1);
-                        if (slot < kLastMax) s_val[slot] = c;
-                    }
-                });
         }
-        __syncthreads();
-        narrow_to_value(tid < cnt ? s_val[tid] : -1, lo, hi, need, cnt, s_hist, s_res);
+    });
+    __syncthreads();
+    if (!single) {
+        const int x = tid < cnt ? s_val[tid] : -1;
+        const int xt = tid < cnt ? (int)s_valt[tid] : 0;
+        narrow_to_value(x, lo, hi, need, cnt, s_hist, s_res);   // lo = hi = T
+        if (x >= lo) atomicAdd(reinterpret_cast<uint32_t*>(&s_tile[xt]), x > lo ? 1u : 0x10000u);
     }
     const int T = lo, needT = need;
+    __syncthreads();
 
     // per tile: entries above T (above bin B1 or candidates > T) and at T; exclusive
     // prefix over this sequence's tiles, in tile order
-    if (flat) {
-#pragma unroll
-        for (int r = 0; r < FPT; ++r)
-            if (fi[r] >= 0 && fv[r] >= T) atomicAdd(&s_tc[fi[r]], fv[r] > T ? 1u : 0x10000u);
-        __syncthreads();
-    }
     int og = 0, oe = 0;
     for (int u = 0; u < rounds; ++u) {               // uniform
         const int i = tid + u * NT;
         int gl = 0, el = 0;
         if (i < st.ntiles) {
-            gl = u == 0 ? ta0 : g.tile_above[st.tile0 + i];
-            if (u == 0) {
-#pragma unroll
-                for (int j = 0; j < kCandReg; ++j) {
-                    gl += j < ncr && cr[j] > T;
-                    el += j < ncr && cr[j] == T;
-                }
-            }
-            if (flat) {
-                const uint32_t x = s_tc[i];
-                gl += (int)(x & 0xFFFFu);
-                el += (int)(x >> 16);
-            } else {
-                visit_mem(u, [&](int c) {
-                    gl += c > T;
-                    el += c == T;
-                });
-            }
+            const int x = s_tile[i];
+            gl = (u == 0 ? ta0 : g.tile_above[st.tile0 + i]) + (x & 0xFFFF);
+            el = (int)((unsigned)x >> 16);
         }
-        int tg, te;
-        const int pg = block_exclusive_scan<NT>(gl, s_tmp, tg);
-        const int pe = block_exclusive_scan<NT>(el, s_tmp, te);
+        int pg, pe, tg, te;
+        block_exclusive_scan2<NT>(gl, el, s_tmp, pg, pe, tg, te);
         if (i < st.ntiles) {
             g.tile_off[2 * (st.tile0 + i)] = og + pg;
             g.tile_off[2 * (st.tile0 + i) + 1] = oe + pe;
@@ -896,7 +907,10 @@ extern "C" int csa2_index_full(const signed char* q, const signed char* w,
         return e;
     hipLaunchKernelGGL(full_reduce_kernel, dim3(kKeyBins / kRedBins, B), blk, 0, s, fw);
     hipLaunchKernelGGL(full_gather_kernel, dim3(tiles, ntg), blk, 0, s, B, fw);
-    hipLaunchKernelGGL(full_threshold_kernel, dim3(B, ntg), dim3(kThrThreads), 0, s, fw);
+    if (B == 1)
+        hipLaunchKernelGGL(full_threshold_kernel<true>, dim3(B, ntg), dim3(kThrThreads), 0, s, fw);
+    else
+        hipLaunchKernelGGL(full_threshold_kernel<false>, dim3(B, ntg), dim3(kThrThreads), 0, s, fw);
     const unsigned wgrid = tiles > (unsigned)B ? tiles : (unsigned)B;
     const FullOut o0 = {pool_pos, pool_score, pool_len, P};
     const FullOut o1 = {sel_pos, nullptr, sel_len, k};

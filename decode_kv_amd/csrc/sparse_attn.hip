@@ -6,7 +6,10 @@
 // K = V = the dequantised 512-wide latent row.
 //
 // Workgroup = (split, sequence, group of 16 heads), four waves, up to four
-// 32-row tiles of attended rows.  All of a workgroup's global loads are issued
+// 32-row tiles of attended rows.  The launch is one-dimensional so that the
+// placement on the eight XCDs (workgroup i on XCD i mod 8) can be chosen: all
+// splits of a (sequence, head group) pair, and the combine workgroups of its
+// heads, run on one XCD.  All of a workgroup's global loads are issued
 // up front (sequence scalars and selection entries, then the raw FP4 rows of
 // every tile into registers, 32 bytes of codes per thread and the scale rows
 // by one wave, in 16-byte loads), so the gather latency is paid once.
@@ -83,7 +86,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     const int* __restrict__ len, const int* __restrict__ sel_pos,
     const int* __restrict__ sel_len, int Hq, int k, int window, float scale_log2,
     int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml,
-    float* __restrict__ out, float* __restrict__ lse) {
+    float* __restrict__ out, float* __restrict__ lse, int B) {
     __shared__ __attribute__((aligned(16))) uint16_t s_vjd[kAttnRows * kVjdLd];
     __shared__ __attribute__((aligned(16))) uint16_t s_vdj[kAttnD * kVdjLd];
     // one tile's raw rows as loaded: codes [32][264 B], then scales [32][16 B]
@@ -100,10 +103,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         return reinterpret_cast<f32x4*>(s_vjd + (q >> 4) * kVjdLd + 128 * w + 8 * (q & 15));
     };
 
-    const int split = blockIdx.x, b = blockIdx.y;
+    // workgroup i runs on XCD i mod 8: all splits of one (sequence, head group)
+    // pair go to the same XCD, where they share the query rows in L2 and the
+    // combine of that pair (placed the same way) finds their partials
+    const int HG = Hq / kHeadsPerWg, npairs = B * HG;
+    const int xid = blockIdx.x & 7, xslot = blockIdx.x >> 3;
+    const int xr = xslot / n_splits, split = xslot - xr * n_splits;
+    const int pair = xr * 8 + xid;
+    if (pair >= npairs) return;
+    const int b = pair / HG, hz = pair - b * HG;
     const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
     const int g = l >> 4, c16 = l & 15;
-    const int head = blockIdx.z * kHeadsPerWg + c16;      // this lane's head
+    const int head = hz * kHeadsPerWg + c16;      // this lane's head
     // dequantisation work split: thread owns rows 8rg..8rg+7 x elements 8dc..8dc+7
     const int dc = tid >> 2, rg = tid & 3;
     const int t_begin = split * TPW;
@@ -303,20 +314,28 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         return;
     }
     // split partial: unnormalised O, running max and sum.  Only the combine
-    // kernel reads them, so they are stored non-temporal (streamed past the
-    // caches instead of waiting in L2 for the end-of-kernel write-back).
+    // kernel reads them.  With at most one pair per XCD they stay in that
+    // XCD's L2 for it; with more, they are stored non-temporal (streamed past
+    // the caches instead of waiting in L2 for the end-of-kernel write-back).
     const size_t base = ((size_t)b * n_splits + split) * Hq + head;
     float* ob = part_o + base * kAttnD + d0;
+    const u32x2 ml = {__float_as_uint(m_run), __float_as_uint(l_run)};
+    if (npairs <= 8) {                                   // uniform
 #pragma unroll
-    for (int nb = 0; nb < kNb; ++nb)
-        __builtin_nontemporal_store(o[nb], reinterpret_cast<f32x4*>(ob + 16 * nb));
-    if (wave == 0 && g == 0)
-        __builtin_nontemporal_store(u32x2{__float_as_uint(m_run), __float_as_uint(l_run)},
-                                    reinterpret_cast<u32x2*>(part_ml + base * 2));
+        for (int nb = 0; nb < kNb; ++nb) *reinterpret_cast<f32x4*>(ob + 16 * nb) = o[nb];
+        if (wave == 0 && g == 0) *reinterpret_cast<u32x2*>(part_ml + base * 2) = ml;
+    } else {
+#pragma unroll
+        for (int nb = 0; nb < kNb; ++nb)
+            __builtin_nontemporal_store(o[nb], reinterpret_cast<f32x4*>(ob + 16 * nb));
+        if (wave == 0 && g == 0)
+            __builtin_nontemporal_store(ml, reinterpret_cast<u32x2*>(part_ml + base * 2));
+    }
 }
 
 // Log-sum-exp merge of the split partials: one workgroup per (head, sequence),
-// 128 threads x 4 output elements.  Each thread issues the loads of its
+// on the XCD of that head's attention workgroups (workgroup i runs on XCD
+// i mod 8), 128 threads x 4 output elements.  Each thread issues the loads of its
 // partial outputs of CH splits (indices past the last split reread it and get
 // weight 0) and, for split s = thread, that split's (m, l), all before any of
 // them is used, so the merge costs one memory round trip; splits beyond CH
@@ -331,10 +350,14 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* part_o,
                                                            const float* part_ml,
                                                            int Hq, int n_splits,
                                                            float* __restrict__ out,
-                                                           float* __restrict__ lse) {
+                                                           float* __restrict__ lse, int B) {
     __shared__ __attribute__((aligned(16))) float s_w[kAttnMaxSplits + 32];   // zero-padded to CH
     __shared__ float s_red[2][2];
-    const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+    const int HG = Hq / kHeadsPerWg, npairs = B * HG;
+    const int xid = blockIdx.x & 7, xslot = blockIdx.x >> 3;
+    const int pair = (xslot >> 4) * 8 + xid;
+    if (pair >= npairs) return;
+    const int b = pair / HG, h = (pair - b * HG) * kHeadsPerWg + (xslot & 15), tid = threadIdx.x;
     const size_t row0 = (size_t)b * n_splits * Hq + h;          // split s at row0 + s * Hq
     f32x4 os[CH];
 #pragma unroll
@@ -490,24 +513,25 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
     float* part_ml = nullptr;
     if (ns > 1) attn_ws_layout(B, Hq, ns, reinterpret_cast<char*>(ws), &part_o, &part_ml);
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-    const dim3 grid(ns, B, (Hq + kHeadsPerWg - 1) / kHeadsPerWg), blk(kAttnThreads);
+    const int npairs = B * (Hq / kHeadsPerWg), pr = (npairs + 7) / 8;
+    const dim3 grid(8 * pr * ns), blk(kAttnThreads);
     const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q_bf16);
     switch (tpw) {
-        case 1: hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse); break;
-        case 2: hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse); break;
-        default: hipLaunchKernelGGL(sparse_attn_kernel<4>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse); break;
+        case 1: hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse, B); break;
+        case 2: hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse, B); break;
+        default: hipLaunchKernelGGL(sparse_attn_kernel<4>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse, B); break;
     }
     if (int e = launch_status("csa2_sparse_attn_decode launch")) return e;
     if (ns > 1) {
-        const dim3 cg(Hq, B), cb(128);
+        const dim3 cg(8 * pr * kHeadsPerWg), cb(128);
         if (ns <= 8)
-            hipLaunchKernelGGL(attn_combine_kernel<8>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse);
+            hipLaunchKernelGGL(attn_combine_kernel<8>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B);
         else if (ns <= 16)
-            hipLaunchKernelGGL(attn_combine_kernel<16>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse);
+            hipLaunchKernelGGL(attn_combine_kernel<16>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B);
         else if (ns <= 24)
-            hipLaunchKernelGGL(attn_combine_kernel<24>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse);
+            hipLaunchKernelGGL(attn_combine_kernel<24>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B);
         else
-            hipLaunchKernelGGL(attn_combine_kernel<32>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse);
+            hipLaunchKernelGGL(attn_combine_kernel<32>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B);
         return launch_status("csa2_sparse_attn_decode combine launch");
     }
     return CSA2_OK;

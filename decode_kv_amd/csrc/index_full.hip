@@ -98,8 +98,12 @@ struct FullOut {
     int stride;
 };
 
+// Tiles of the scratch layout and of every per-tile grid: an upper bound on
+// the tiles of all sequences, rounded up to a multiple of 8 so that tile t of
+// every grid row lands on the same XCD (workgroup i runs on XCD i mod 8) as
+// the scoring workgroup that wrote its scores.
 static long long full_tile_bound(int B, long long total_len) {
-    return total_len / kTile + B + 1;
+    return (total_len / kTile + B + 1 + 7) / 8 * 8;
 }
 
 static size_t full_ws_layout(int B, long long total_len, int ntargets, char* base, FullWs* w) {

@@ -66,13 +66,8 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, int sb) {
     return r;
 }
 
-__device__ __forceinline__ uint16_t bf16_bits(float x) {
-    return __builtin_bit_cast(uint16_t, (__bf16)x);
-}
-
-__device__ __forceinline__ float bf16_value(uint16_t b) {
-    return __builtin_bit_cast(float, (uint32_t)b << 16);
-}
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // Attention of one workgroup over tiles [TPW * split, TPW * split + TPW) of
 // its sequence's attended rows.  Every global load the workgroup needs is
@@ -208,14 +203,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
             }
 #pragma unroll
             for (int c = 0; c < 8; ++c) {
-                const int half = (c & 1) * 16;
+                // element c of rows 2i and 2i+1 in one word: the low halves of
+                // word c/2 (c even) or the high halves (c odd), one byte permute
+                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
                 u32x4 tr;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t a = (v[2 * i][c >> 1] >> half) & 0xFFFFu;
-                    const uint32_t bb = (v[2 * i + 1][c >> 1] >> half) & 0xFFFFu;
-                    tr[i] = a | (bb << 16);
-                }
+                for (int i = 0; i < 4; ++i)
+                    tr[i] = __builtin_amdgcn_perm(v[2 * i + 1][c >> 1], v[2 * i][c >> 1], sel);
                 uint16_t* vw = s_vdj + (8 * dc + c) * kVdjLd + 8 * rg;
                 *reinterpret_cast<u32x2*>(vw) = u32x2{tr[0], tr[1]};
                 *reinterpret_cast<u32x2*>(vw + 4) = u32x2{tr[2], tr[3]};
@@ -268,14 +262,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         float p[8], psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            p[i] = exp2f(ts[i] - m_new);
+            p[i] = __builtin_amdgcn_exp2f(ts[i] - m_new);   // <= 0; -inf gives 0
             psum += p[i];
         }
         psum = rows4_sum(psum);
         if (t == 0) {                              // nothing accumulated yet
             l_run = psum;
         } else {
-            const float alpha = exp2f(m_run - m_new);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             l_run = l_run * alpha + psum;
 #pragma unroll
             for (int nb = 0; nb < kNb; ++nb) o[nb] *= alpha;   // this lane's head
@@ -285,11 +279,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         u32x4 ph_u, pl_u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint16_t h_a = bf16_bits(p[2 * i]), h_b = bf16_bits(p[2 * i + 1]);
-            const uint16_t l_a = bf16_bits(p[2 * i] - bf16_value(h_a));
-            const uint16_t l_b = bf16_bits(p[2 * i + 1] - bf16_value(h_b));
-            ph_u[i] = (uint32_t)h_a | ((uint32_t)h_b << 16);
-            pl_u[i] = (uint32_t)l_a | ((uint32_t)l_b << 16);
+            // two weights per conversion: the bf16 high parts, then the bf16
+            // residuals (each residual is exact in fp32 before rounding)
+            const f32x2 pp = {p[2 * i], p[2 * i + 1]};
+            const uint32_t hu = bitcast<uint32_t>(__builtin_convertvector(pp, bf16x2));
+            const f32x2 hf = {__uint_as_float(hu << 16), __uint_as_float(hu & 0xFFFF0000u)};
+            ph_u[i] = hu;
+            pl_u[i] = bitcast<uint32_t>(__builtin_convertvector(pp - hf, bf16x2));
         }
         const bf16x8 ph = bitcast<bf16x8>(ph_u), pl = bitcast<bf16x8>(pl_u);
 #pragma unroll

@@ -35,10 +35,13 @@ FLAGS = [
 
 # The scoring kernels read every int8 MFMA result straight into VALU
 # arithmetic (ReLU and head weight): keeping the results in VGPRs saves one
-# accumulator-register read per head and token.
+# accumulator-register read per head and token.  The attention kernel's P.V
+# accumulators likewise start from zero and leave in stores without copies
+# between accumulator and vector registers.
 EXTRA = {
     "index_full.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "index_reindex.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "sparse_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 

@@ -142,6 +142,48 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     const int S = nsel + win;
     const int ntile = (S + kAttnRows - 1) / kAttnRows;
     const int t_end = min(t_begin + TPW, ntile);
+    // p . v is split over the output dimension: wave w owns d-blocks [8w, 8w+8)
+    constexpr int kNb = kAttnD / 16 / (kAttnThreads / kWave);   // 8 blocks of 16
+    // the results: lane holds head `head`, latent elements 16 (8 wave + nb) + 4 g + (0..3)
+    const int d0 = 16 * kNb * wave + 4 * g;
+    auto emit = [&](const f32x4 (&oo)[kNb], float m_fin, float l_fin) {
+        if (n_splits == 1) {
+            float* ob = out + ((size_t)b * Hq + head) * kAttnD + d0;
+            const float inv = l_fin > 0.f ? 1.f / l_fin : 0.f;
+#pragma unroll
+            for (int nb = 0; nb < kNb; ++nb)
+                *reinterpret_cast<f32x4*>(ob + 16 * nb) = oo[nb] * inv;
+            if (lse && wave == 0 && g == 0)
+                lse[(size_t)b * Hq + head] =
+                    l_fin > 0.f ? (m_fin + log2f(l_fin)) * 0.69314718055994531f : -INFINITY;
+            return;
+        }
+        // split partial: unnormalised O, running max and sum.  Only the combine
+        // kernel reads them.  With at most one pair per XCD they stay in that
+        // XCD's L2 for it; with more, they are stored non-temporal (streamed past
+        // the caches instead of waiting in L2 for the end-of-kernel write-back).
+        const size_t base = ((size_t)b * n_splits + split) * Hq + head;
+        float* ob = part_o + base * kAttnD + d0;
+        const u32x2 ml = {__float_as_uint(m_fin), __float_as_uint(l_fin)};
+        if (npairs <= 8) {                                   // uniform
+#pragma unroll
+            for (int nb = 0; nb < kNb; ++nb) *reinterpret_cast<f32x4*>(ob + 16 * nb) = oo[nb];
+            if (wave == 0 && g == 0) *reinterpret_cast<u32x2*>(part_ml + base * 2) = ml;
+        } else {
+#pragma unroll
+            for (int nb = 0; nb < kNb; ++nb)
+                __builtin_nontemporal_store(oo[nb], reinterpret_cast<f32x4*>(ob + 16 * nb));
+            if (wave == 0 && g == 0)
+                __builtin_nontemporal_store(ml, reinterpret_cast<u32x2*>(part_ml + base * 2));
+        }
+    };
+    if (t_begin >= t_end) {                              // uniform: a split past the attended rows
+        f32x4 z[kNb];
+#pragma unroll
+        for (int nb = 0; nb < kNb; ++nb) z[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        emit(z, -INFINITY, 0.f);
+        return;
+    }
 
     // round trip 2: the raw rows of every tile, in 16-byte loads (a row of an
     // invalid position reads row 0 and is staged as zeros)
@@ -165,17 +207,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
             rsc[t] = *reinterpret_cast<const u32x4*>(kv_scale + (roff + (ps >= 0 ? ps : 0)) * (kAttnD / 32));
     }
 
-    // p . v is split over the output dimension: wave w owns d-blocks [8w, 8w+8)
-    constexpr int kNb = kAttnD / 16 / (kAttnThreads / kWave);   // 8 blocks of 16
-    f32x4 o[kNb];
-#pragma unroll
-    for (int nb = 0; nb < kNb; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 o[kNb];                                        // set by the first tile's P.V
     float m_run = -INFINITY, l_run = 0.f;
 
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int tile = t_begin + t;
-        if (tile >= t_end) break;                           // uniform
+        if (t > 0 && tile >= t_end) break;                  // uniform; tile t_begin exists
         if (t > 0) __syncthreads();                          // previous tile's LDS reads are done
         {
             // stage the raw tile (rows 8-byte aligned: 264-byte stride)
@@ -251,8 +289,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         float ts[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            ts[i] = (jt + 4 * g + i < S) ? s0[i] * scale_log2 : -INFINITY;
-            ts[4 + i] = (jt + 16 + 4 * g + i < S) ? s1[i] * scale_log2 : -INFINITY;
+            ts[i] = s0[i] * scale_log2;
+            ts[4 + i] = s1[i] * scale_log2;
+        }
+        if (jt + kAttnRows > S) {                        // uniform: rows past S weigh 0
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (jt + 4 * g + i >= S) ts[i] = -INFINITY;
+                if (jt + 16 + 4 * g + i >= S) ts[4 + i] = -INFINITY;
+            }
         }
         float tmax = ts[0];
 #pragma unroll
@@ -291,42 +336,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
 #pragma unroll
         for (int nb = 0; nb < kNb; ++nb) {
             // O^T[d][head]: A = V^T (M = latent dim), B = P^T (N = head)
-            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[nb], ph, o[nb], 0, 0, 0);
+            const f32x4 acc = t == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : o[nb];
+            o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[nb], ph, acc, 0, 0, 0);
             o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bv[nb], pl, o[nb], 0, 0, 0);
         }
     }
 
-    // lane holds head `head`, latent elements 16 (8 wave + nb) + 4 g + (0..3)
-    const int d0 = 16 * kNb * wave + 4 * g;
-    if (n_splits == 1) {
-        float* ob = out + ((size_t)b * Hq + head) * kAttnD + d0;
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-#pragma unroll
-        for (int nb = 0; nb < kNb; ++nb)
-            *reinterpret_cast<f32x4*>(ob + 16 * nb) = o[nb] * inv;
-        if (lse && wave == 0 && g == 0)
-            lse[(size_t)b * Hq + head] =
-                l_run > 0.f ? (m_run + log2f(l_run)) * 0.69314718055994531f : -INFINITY;
-        return;
-    }
-    // split partial: unnormalised O, running max and sum.  Only the combine
-    // kernel reads them.  With at most one pair per XCD they stay in that
-    // XCD's L2 for it; with more, they are stored non-temporal (streamed past
-    // the caches instead of waiting in L2 for the end-of-kernel write-back).
-    const size_t base = ((size_t)b * n_splits + split) * Hq + head;
-    float* ob = part_o + base * kAttnD + d0;
-    const u32x2 ml = {__float_as_uint(m_run), __float_as_uint(l_run)};
-    if (npairs <= 8) {                                   // uniform
-#pragma unroll
-        for (int nb = 0; nb < kNb; ++nb) *reinterpret_cast<f32x4*>(ob + 16 * nb) = o[nb];
-        if (wave == 0 && g == 0) *reinterpret_cast<u32x2*>(part_ml + base * 2) = ml;
-    } else {
-#pragma unroll
-        for (int nb = 0; nb < kNb; ++nb)
-            __builtin_nontemporal_store(o[nb], reinterpret_cast<f32x4*>(ob + 16 * nb));
-        if (wave == 0 && g == 0)
-            __builtin_nontemporal_store(ml, reinterpret_cast<u32x2*>(part_ml + base * 2));
-    }
+    emit(o, m_run, l_run);
 }
 
 // Log-sum-exp merge of the split partials: one workgroup per (head, sequence),

@@ -4,8 +4,10 @@
 // pool; "How DeepSeek V4.1 Flash Actually Works", item 2: up to 16,384
 // candidate positions).  csa2_index_score exposes the scoring stage alone.
 //
-// Five kernels, all sequences of the batch at once, tiles of 1,024 positions,
-// no returning device-wide atomics:
+// Five kernels, all sequences of the batch at once, tiles of 1,024 positions
+// (per-tile grids padded to a multiple of 8 tiles, so tile t of every grid
+// row runs on the XCD whose L2 holds its scores), no returning device-wide
+// atomics:
 //   1. score      stream the int8 keys once (each wave issues all of its tile
 //                 loads before scoring), int8 MFMA scoring, int32 scores to
 //                 scratch, and a per-tile histogram of a float-like key
@@ -19,13 +21,14 @@
 //                 slot-major across tiles) and adds them to a 4,096-bin
 //                 histogram of the next 12 bits inside B1 (atomics whose
 //                 result is not waited for)
-//   4. threshold  one workgroup per sequence, one tile per thread: the
-//                 second-level histogram narrows B1 to one sub-bin; its
-//                 scores (<= 1,024, else more 12-bit passes over the
-//                 candidates) are gathered one per thread and 8-bit digit
-//                 passes narrow them to the threshold T and the number of
-//                 ties at T to keep (taken in position order); per-tile
-//                 counts and an exclusive prefix give every tile its offsets
+//   4. threshold  one workgroup per sequence, one tile per thread: B1's
+//                 candidates are compacted into one LDS list (score, tile);
+//                 the second-level histogram narrows B1 to one sub-bin; its
+//                 scores (<= 1,024, else more 12-bit passes over the list)
+//                 are gathered one per thread and 8-bit digit passes narrow
+//                 them to the threshold T and the number of ties at T to
+//                 keep (taken in position order); per-tile counts and an
+//                 exclusive prefix give every tile its offsets
 //   5. write      ordered compaction: s > T, plus the first ties in position
 //                 order; ascending positions, tail -1
 // With k > 0 the Full layer's own top-k selection comes out of the same

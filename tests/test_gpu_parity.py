@@ -332,6 +332,50 @@ def test_index_full_ragged_batch_and_edges():
     check_full(keys, row_off, lens, q, w, 128, 16384, "P 16384, pool only", k=0)
 
 
+def test_index_full_long_sequences():
+    """Sequences longer than 1,024 tiles, up to the 8,388,608-position maximum:
+    the threshold kernel gives each thread several tiles (later rounds hold
+    every candidate in its list, their starts and offsets span rounds).  Four
+    index heads keep the oracle quick; 600 high keys just before the window
+    crowd the selection's threshold bin into a few tiles."""
+    rng = np.random.default_rng(23)
+    lens = [2_500_017, 8_388_608, 1_500]
+    row_off, cur = [], 0
+    for L in lens:
+        row_off.append(cur)
+        cur += L
+    keys = rng.integers(-127, 128, size=(cur, 64), dtype=np.int8)
+    q = rng.integers(-127, 128, size=(len(lens), 4, 64), dtype=np.int8)
+    w = rng.integers(0, 16, size=(len(lens), 4), dtype=np.int8)
+    for b, L in enumerate(lens):
+        if L > 10_000:
+            hot = row_off[b] + L - 128 - 1 - rng.choice(3000, 600, replace=False)
+            keys[hot] = np.clip(q[b, 0].astype(np.int32) + rng.integers(-3, 4, size=(600, 64)),
+                                -127, 127).astype(np.int8)
+    _say("long sequences", lens)
+    check_full(keys, row_off, lens, q, w, 128, 16384, "long sequences, k 512", k=512)
+
+
+def test_index_full_long_crowded():
+    """3,000,000 positions (three rounds of tiles per threshold thread) with
+    ~600,000 scores inside one first-level bin: far more candidates than the
+    threshold's LDS list holds, so every pass walks the tiles from global
+    memory."""
+    rng = np.random.default_rng(29)
+    L, W_ = 3_000_000, 128
+    keys = np.zeros((L, 64), dtype=np.int8)
+    keys[:, 0] = 50
+    keys[rng.random(L) < 0.2, 0] = 127
+    keys[:, 1] = rng.integers(0, 64, size=L)
+    q = np.zeros((1, 4, 64), dtype=np.int8)
+    q[0, 1:, 0] = 127
+    q[0, 0, 1] = 1
+    w = np.full((1, 4), 15, dtype=np.int8)
+    w[0, 0] = 1
+    # score = 5,715 * k0 + k1: 64 distinct values inside the hot bin
+    check_full(keys, [0], [L], q, w, W_, 16384, "3M, 600K in one bin, k 512", k=512)
+
+
 def test_index_full_extreme_scores():
     """Maximal scores (64 heads x 15 x 64 x 127^2) stay exact in int32."""
     L = 3000
@@ -431,7 +475,7 @@ def test_select_topk_clustered(top_span):
 
 def run_attention(codes, scales, row_off, lens, sel, sel_len, q_bits, k, window):
     """Two calls on one workspace: the second (into fresh NaN outputs) must be
-    bit-identical, which also shows the first left its split counters reset."""
+    bit-identical (nothing carries over between calls)."""
     B, Hq, D = q_bits.shape
     qt = torch.from_numpy(q_bits.view(np.int16)).to(DEV).view(torch.bfloat16)
     ws = csa2.workspace(csa2.workspace_bytes(csa2.OP_SPARSE_ATTN, B, 0, 0, 0, 0, k, Hq, D, window))
@@ -492,6 +536,11 @@ def test_attention_small_heads_and_short_contexts():
 def test_attention_many_splits():
     attention_case(15, [40000], 8192, 64)           # 260 tiles over 65 splits
     attention_case(16, [20000, 300, 9000], 2048, 32)
+
+
+def test_attention_maximum_rows_and_many_pairs():
+    attention_case(17, [20000], 16384 - 128, 16)    # k + window = 16,384: 512 tiles, 128 splits
+    attention_case(18, [700] * 12, 256, 64)         # 48 (sequence, head group) pairs > 8
 
 
 def test_attention_scale_ranges():

@@ -376,6 +376,24 @@ def test_index_full_long_crowded():
     check_full(keys, [0], [L], q, w, W_, 16384, "3M, 600K in one bin, k 512", k=512)
 
 
+def test_index_full_maximum_batch():
+    """4,096 sequences (the batch limit): every scoring thread maps eight of
+    them to tiles; lengths 0 .. 2,600 so that some sequences have no eligible
+    position and some span three tiles."""
+    rng = np.random.default_rng(31)
+    B = 4096
+    lens = [int(x) for x in rng.integers(0, 2600, size=B)]
+    lens[0], lens[1], lens[-1] = 0, 129, 2599
+    row_off, cur = [], 0
+    for L in lens:
+        row_off.append(cur)
+        cur += L
+    keys = rng.integers(-127, 128, size=(cur, 64), dtype=np.int8)
+    q = rng.integers(-127, 128, size=(B, 4, 64), dtype=np.int8)
+    w = rng.integers(0, 16, size=(B, 4), dtype=np.int8)
+    check_full(keys, row_off, lens, q, w, 128, 600, "4,096 sequences", k=100)
+
+
 def test_index_full_extreme_scores():
     """Maximal scores (64 heads x 15 x 64 x 127^2) stay exact in int32."""
     L = 3000
@@ -541,6 +559,8 @@ def test_attention_many_splits():
 def test_attention_maximum_rows_and_many_pairs():
     attention_case(17, [20000], 16384 - 128, 16)    # k + window = 16,384: 512 tiles, 128 splits
     attention_case(18, [700] * 12, 256, 64)         # 48 (sequence, head group) pairs > 8
+    attention_case(19, [int(x) for x in np.random.default_rng(19).integers(0, 900, size=200)],
+                   128, 16)                          # 200 sequences, some empty
 
 
 def test_attention_scale_ranges():

@@ -29,6 +29,9 @@ FLAGS = [
     "-Wno-unused-function",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # the first 64 bytes of every kernel's arguments arrive in SGPRs with the
+    # wave, instead of through a scalar load at its start
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-I" + os.path.join(ROOT, "include"),
 ]
 

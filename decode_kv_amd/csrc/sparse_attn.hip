@@ -74,14 +74,16 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 // issued before the first tile is processed: the per-sequence scalars and the
 // selection entries in one round trip, then the FP4 codes and scales of all
 // TPW tiles in a second one, held in registers until their tile's turn.
+// The arguments the first round trip needs (the sizes, then the pointers it
+// loads from) fill the 64 bytes that arrive in SGPRs with the wave.
 template <int TPW>
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
+    int B, int Hq, int k, int window, int n_splits, float scale_log2,
+    const long long* __restrict__ row_off, const int* __restrict__ len,
+    const int* __restrict__ sel_len, const int* __restrict__ sel_pos,
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_fp4,
-    const uint8_t* __restrict__ kv_scale, const long long* __restrict__ row_off,
-    const int* __restrict__ len, const int* __restrict__ sel_pos,
-    const int* __restrict__ sel_len, int Hq, int k, int window, float scale_log2,
-    int n_splits, float* __restrict__ part_o, float* __restrict__ part_ml,
-    float* __restrict__ out, float* __restrict__ lse, int B) {
+    const uint8_t* __restrict__ kv_scale, float* __restrict__ part_o,
+    float* __restrict__ part_ml, float* __restrict__ out, float* __restrict__ lse) {
     __shared__ __attribute__((aligned(16))) uint16_t s_vjd[kAttnRows * kVjdLd];
     __shared__ __attribute__((aligned(16))) uint16_t s_vdj[kAttnD * kVdjLd];
     // one tile's raw rows as loaded: codes [32][264 B], then scales [32][16 B]
@@ -529,9 +531,9 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
     const dim3 grid(8 * pr * ns), blk(kAttnThreads);
     const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q_bf16);
     switch (tpw) {
-        case 1: hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse, B); break;
-        case 2: hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse, B); break;
-        default: hipLaunchKernelGGL(sparse_attn_kernel<4>, grid, blk, 0, s, q16, kv_fp4, kv_scale, row_off, len, sel_pos, sel_len, Hq, k, window, scale_log2, ns, part_o, part_ml, out, lse, B); break;
+        case 1: hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, blk, 0, s, B, Hq, k, window, ns, scale_log2, row_off, len, sel_len, sel_pos, q16, kv_fp4, kv_scale, part_o, part_ml, out, lse); break;
+        case 2: hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, blk, 0, s, B, Hq, k, window, ns, scale_log2, row_off, len, sel_len, sel_pos, q16, kv_fp4, kv_scale, part_o, part_ml, out, lse); break;
+        default: hipLaunchKernelGGL(sparse_attn_kernel<4>, grid, blk, 0, s, B, Hq, k, window, ns, scale_log2, row_off, len, sel_len, sel_pos, q16, kv_fp4, kv_scale, part_o, part_ml, out, lse); break;
     }
     if (int e = launch_status("csa2_sparse_attn_decode launch")) return e;
     if (ns > 1) {

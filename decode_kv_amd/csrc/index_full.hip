@@ -83,14 +83,42 @@ struct FullTarget {
                           // the first kCandHead live in cand_head)
 };
 
+// The workspace as the kernels see it.  Each per-target array holds target
+// 0's block, then target 1's (used when k > 0), so a target's arrays are
+// these bases plus fixed strides: no kernel indexes its arguments by target.
+// The sizes and the arrays the gather and threshold kernels read first come
+// first: kernels that take FullWs as their first argument receive those 64
+// bytes in SGPRs with the wave.
 struct FullWs {
-    FullTarget tg[2];     // tg[1] is used when k > 0
+    int B;                // sequences
+    int tmax;             // Tmax: tiles of the layout, the slot stride of cand_head
+    int k;                // size of target 1, 0 when there is none
+    int pad;
+    int* scores;          // [Tmax][kTile]
+    FullState* st;        // [2][B]
+    uint32_t* hist2;      // [2][B][kSubBins]
+    int* tile_cnt;        // [2][Tmax]
+    int* tile_above;      // [2][Tmax]
+    int* cand_head;       // [2][kCandHead][Tmax]
+    int* tile_off;        // [2][Tmax][2]
+    int* cand;            // [2][Tmax][kTile]
     uint32_t* hist;       // [B][kKeyBins]
     uint16_t* tile_hist;  // [Tmax][kKeyBins]
-    int* scores;          // [Tmax][kTile]
-    int tmax;             // Tmax: the slot stride of cand_head
-    int k;                // size of target 1, 0 when there is none
 };
+
+// The arrays of target y.
+__device__ __forceinline__ FullTarget target(const FullWs& w, int y) {
+    const size_t T = (size_t)w.tmax;
+    FullTarget g;
+    g.st = w.st + (size_t)y * w.B;
+    g.hist2 = w.hist2 + (size_t)y * w.B * kSubBins;
+    g.tile_above = w.tile_above + y * T;
+    g.tile_cnt = w.tile_cnt + y * T;
+    g.tile_off = w.tile_off + y * T * 2;
+    g.cand_head = w.cand_head + y * T * kCandHead;
+    g.cand = w.cand + y * T * kTile;
+    return g;
+}
 
 // Where a target's result goes: pos (and score, when not null) [B][stride],
 // ascending positions, tail -1; len [B].
@@ -117,20 +145,19 @@ static size_t full_ws_layout(int B, long long total_len, int ntargets, char* bas
         off = round_up(off + bytes, 256);
         return base ? base + at : nullptr;
     };
+    const size_t n = (size_t)ntargets;
     FullWs x = {};
     x.hist = reinterpret_cast<uint32_t*>(take(4ull * B * kKeyBins));
     x.tile_hist = reinterpret_cast<uint16_t*>(take(2ull * (size_t)T * kKeyBins));
     x.scores = reinterpret_cast<int*>(take(4ull * (size_t)T * kTile));
-    for (int g = 0; g < ntargets; ++g) {
-        FullTarget& y = x.tg[g];
-        y.st = reinterpret_cast<FullState*>(take(sizeof(FullState) * (size_t)B));
-        y.hist2 = reinterpret_cast<uint32_t*>(take(4ull * B * kSubBins));
-        y.tile_above = reinterpret_cast<int*>(take(4ull * T));
-        y.tile_cnt = reinterpret_cast<int*>(take(4ull * T));
-        y.tile_off = reinterpret_cast<int*>(take(8ull * T));
-        y.cand_head = reinterpret_cast<int*>(take(4ull * (size_t)T * kCandHead));
-        y.cand = reinterpret_cast<int*>(take(4ull * (size_t)T * kTile));
-    }
+    x.st = reinterpret_cast<FullState*>(take(n * sizeof(FullState) * (size_t)B));
+    x.hist2 = reinterpret_cast<uint32_t*>(take(n * 4ull * B * kSubBins));
+    x.tile_above = reinterpret_cast<int*>(take(n * 4ull * T));
+    x.tile_cnt = reinterpret_cast<int*>(take(n * 4ull * T));
+    x.tile_off = reinterpret_cast<int*>(take(n * 8ull * T));
+    x.cand_head = reinterpret_cast<int*>(take(n * 4ull * (size_t)T * kCandHead));
+    x.cand = reinterpret_cast<int*>(take(n * 4ull * (size_t)T * kTile));
+    x.B = B;
     x.tmax = (int)T;
     x.k = 0;
     if (w) *w = x;
@@ -346,12 +373,11 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
     TileInfo ti;
     if (B == 1) {
         load_query(0);
-        ti = map_tile_one(len, row_off, window, P, w.k, t, w.tg[0].st,
-                          w.k > 0 ? w.tg[1].st : nullptr);
+        ti = map_tile_one(len, row_off, window, P, w.k, t, w.st, w.k > 0 ? w.st + B : nullptr);
         if (ti.b < 0) return;                              // past the last tile
     } else {
-        ti = map_tile<kScoreThreads>(len, row_off, B, window, P, w.k, t, w.tg[0].st,
-                                     w.k > 0 ? w.tg[1].st : nullptr);
+        ti = map_tile<kScoreThreads>(len, row_off, B, window, P, w.k, t, w.st,
+                                     w.k > 0 ? w.st + B : nullptr);
         if (ti.b < 0) return;
         load_query(ti.b);
     }
@@ -412,11 +438,11 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
 __global__ __launch_bounds__(kScanThreads) void full_reduce_kernel(FullWs w) {
     __shared__ uint32_t s_part[kScanThreads / 4][kRedBins + 1];
     const int c = blockIdx.x, b = blockIdx.y;
-    const FullState st = w.tg[0].st[b];                        // tile0, ntiles: both targets
+    const FullState st = w.st[b];                              // tile0, ntiles: both targets
     const int z = c * kScanThreads + threadIdx.x;              // clear the sub-bin histograms
     if (z < kSubBins) {
-        w.tg[0].hist2[(size_t)b * kSubBins + z] = 0;
-        if (w.k > 0) w.tg[1].hist2[(size_t)b * kSubBins + z] = 0;
+        w.hist2[(size_t)b * kSubBins + z] = 0;
+        if (w.k > 0) w.hist2[((size_t)w.B + b) * kSubBins + z] = 0;
     }
     const int r = threadIdx.x >> 2, k = threadIdx.x & 3;
     uint32_t acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -476,7 +502,8 @@ __device__ __forceinline__ int tile_state(const FullState* __restrict__ sts, int
 }
 
 // ---- 3. gather: entries above / inside bin B1 --------------------------------------
-__global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs w) {
+__global__ __launch_bounds__(kScanThreads) void full_gather_kernel(FullWs w) {
+    const int B = w.B;
     __shared__ int s_b;
     __shared__ int s_tmp[kScanThreads / kWave];
     __shared__ int s_res[3];
@@ -488,7 +515,7 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(int B, FullWs
     int v[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) v[j] = sc[i0 + j];
-    const FullTarget g = w.tg[blockIdx.y];
+    const FullTarget g = target(w, blockIdx.y);
     FullState st;
     const int b = tile_state(g.st, B, t, &s_b, st);
     if (b < 0) return;
@@ -562,7 +589,7 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
     __shared__ uint64_t s_list[kListMax];            // the list: score | tile << 32
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
-    const FullTarget g = w.tg[blockIdx.y];
+    const FullTarget g = target(w, blockIdx.y);
     // round trip 1: the first tile's counts (needed first: loads complete in
     // order), its first candidates, the second-level histogram and the state.
     // Every load is unconditional (a thread past the last tile reads another
@@ -773,12 +800,13 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
 
 // ---- 5. write: ordered compaction of the pool (and of the top k) -----------------
 // blockIdx.y selects the target and its output.
-__global__ __launch_bounds__(kScanThreads) void full_write_kernel(int B, FullOut o0, FullOut o1,
-                                                                  FullWs w) {
+__global__ __launch_bounds__(kScanThreads) void full_write_kernel(FullWs w, FullOut o0,
+                                                                  FullOut o1) {
+    const int B = w.B;
     __shared__ int s_b;
     __shared__ int s_tmp[kScanThreads / kWave];
     const int t = blockIdx.x;
-    const FullTarget g = w.tg[blockIdx.y];
+    const FullTarget g = target(w, blockIdx.y);
     const FullOut o = blockIdx.y ? o1 : o0;
     // the tile's scores and output offsets sit at t whatever its sequence: load first
     const int* sc = w.scores + (size_t)t * kTile;
@@ -913,7 +941,7 @@ extern "C" int csa2_index_full(const signed char* q, const signed char* w,
                              -1))
         return e;
     hipLaunchKernelGGL(full_reduce_kernel, dim3(kKeyBins / kRedBins, B), blk, 0, s, fw);
-    hipLaunchKernelGGL(full_gather_kernel, dim3(tiles, ntg), blk, 0, s, B, fw);
+    hipLaunchKernelGGL(full_gather_kernel, dim3(tiles, ntg), blk, 0, s, fw);
     if (B == 1)
         hipLaunchKernelGGL(full_threshold_kernel<true>, dim3(B, ntg), dim3(kThrThreads), 0, s, fw);
     else
@@ -921,7 +949,7 @@ extern "C" int csa2_index_full(const signed char* q, const signed char* w,
     const unsigned wgrid = tiles > (unsigned)B ? tiles : (unsigned)B;
     const FullOut o0 = {pool_pos, pool_score, pool_len, P};
     const FullOut o1 = {sel_pos, nullptr, sel_len, k};
-    hipLaunchKernelGGL(full_write_kernel, dim3(wgrid, ntg), blk, 0, s, B, o0, o1, fw);
+    hipLaunchKernelGGL(full_write_kernel, dim3(wgrid, ntg), blk, 0, s, fw, o0, o1);
     return launch_status("csa2_index_full launch");
 }
 

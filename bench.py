@@ -126,7 +126,7 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly (debug)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(got --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 

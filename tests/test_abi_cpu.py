@@ -26,6 +26,20 @@ def test_exports_every_header_function(lib):
         assert hasattr(lib, n), n
 
 
+def test_binding_matches_header_parameters(lib):
+    """Every declaration's parameter count equals the ctypes binding's."""
+    import re
+    src = re.sub(r"/\*.*?\*/", "", open(csa2.HEADER).read(), flags=re.S)
+    decls = dict(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", src))
+    assert "csa2_index_full" in decls and "csa2_sparse_attn_decode" in decls
+    for name, params in decls.items():
+        params = params.strip()
+        n = 0 if params in ("", "void") else len(params.split(","))
+        argtypes = getattr(lib, name).argtypes
+        assert argtypes is not None, name
+        assert len(argtypes) == n, (name, len(argtypes), n)
+
+
 def test_version_and_error_text(lib):
     assert csa2.version().startswith("csa2-gfx950")
     assert isinstance(csa2.last_error(), str)

@@ -11,18 +11,19 @@
 // splits of a (sequence, head group) pair, and the combine workgroups of its
 // heads, run on one XCD.  All of a workgroup's global loads are issued
 // up front (sequence scalars and selection entries, then the raw FP4 rows of
-// every tile into registers, 32 bytes of codes per thread and the scale rows
-// by one wave, in 16-byte loads), so the gather latency is paid once.
+// every tile into registers: 32 bytes of codes and their two scale bytes per
+// thread), so the gather latency is paid once.
 // Per tile:
-//   * stage the raw rows in LDS, then dequantise them exactly to bf16 and
-//     store them twice: row-major (for q.v) and d-major (for p.v), so both
-//     products read contiguous 16- or 8-byte operands;
+//   * every thread dequantises its 64 codes exactly to bf16 and stores them
+//     row-major in LDS;
 //   * S^T = V q^T on bf16 MFMA (16x16x32), fp32 accumulation, the latent
 //     dimension split over the four waves and the partial sums added in LDS;
 //   * online softmax in base 2, per head (every wave holds the full scores);
 //   * O^T += V^T P^T on bf16 MFMA, each wave owning a quarter of the output
 //     dimension, with P split into a bf16 high part and a bf16 residual so the
-//     weights carry ~16 significant bits.
+//     weights carry ~16 significant bits.  The V^T operand comes from the
+//     row-major tile through gfx950's transposing LDS read, so the tile is
+//     stored once.
 // The k-slots of P's MFMA operand are the rows the S^T result left in each
 // lane, and V's operand is read with the same row order, so P never moves.
 // Computing O^T (M = latent dim, N = head) leaves each lane four consecutive
@@ -42,8 +43,6 @@ constexpr int kAttnRows = 32;
 constexpr int kAttnD = 512;
 constexpr int kHeadsPerWg = 16;
 constexpr int kVjdLd = kAttnD + 8;      // bf16 per row-major row (padded)
-constexpr int kVdjLd = kAttnRows + 4;   // bf16 per d-major row (72 B: 8-B aligned)
-constexpr int kRawLd = kAttnD / 2 + 8;   // bytes per staged row of FP4 codes (66 words)
 constexpr int kAttnMaxTilesPerWg = 4;   // tiles whose loads one workgroup keeps in flight
 constexpr int kAttnMaxRows = 16384;     // k + window
 constexpr int kAttnMinWgs = 64;         // workgroups wanted per launch
@@ -68,6 +67,13 @@ __device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, int sb) {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16 at an LDS address (8-byte aligned)
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    return bitcast<u32x2>(__builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p)));
+}
 
 // Attention of one workgroup over tiles [TPW * split, TPW * split + TPW) of
 // its sequence's attended rows.  Every global load the workgroup needs is
@@ -84,21 +90,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_fp4,
     const uint8_t* __restrict__ kv_scale, float* __restrict__ part_o,
     float* __restrict__ part_ml, float* __restrict__ out, float* __restrict__ lse) {
+    // the tile's rows, dequantised, row-major (41.5 KB of LDS with the
+    // partial sums: three workgroups per CU)
     __shared__ __attribute__((aligned(16))) uint16_t s_vjd[kAttnRows * kVjdLd];
-    __shared__ __attribute__((aligned(16))) uint16_t s_vdj[kAttnD * kVdjLd];
-    // one tile's raw rows as loaded: codes [32][264 B], then scales [32][16 B]
-    __shared__ __attribute__((aligned(16))) uint8_t s_raw[kAttnRows * kRawLd + kAttnRows * 16];
-    uint8_t* const s_rsc = s_raw + kAttnRows * kRawLd;
-    // The S^T partial sums of wave w go to rows 0..7 of the latent columns
-    // [128w, 128w + 128) of s_vjd, which only wave w reads for its scores:
-    // each wave overwrites its own band once its reads are done, so this
-    // needs no extra barrier, and the workgroup stays under 80 KB of LDS
-    // (two per CU).  Slot q = 64 m + lane (m: 16-row tile) is row q >> 4,
-    // 16-byte column q & 15 of the band.
-    auto red_slot = [&](int w, int m, int lane) -> f32x4* {
-        const int q = 64 * m + lane;
-        return reinterpret_cast<f32x4*>(s_vjd + (q >> 4) * kVjdLd + 128 * w + 8 * (q & 15));
-    };
+    // S^T partial sums of each wave over its quarter of the latent dimension
+    __shared__ f32x4 s_red[kAttnThreads / kWave][2][kWave];
 
     // workgroup i runs on XCD i mod 8: all splits of one (sequence, head group)
     // pair go to the same XCD, where they share the query rows in L2 and the
@@ -119,15 +115,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     // round trip 1: sequence scalars, this thread's selection entries, q
     const int len_b = len[b], sel_b = sel_len[b];
     const long long roff = row_off[b];
-    // loads of a tile: thread t takes 32 bytes of codes of row t >> 3 (bytes
-    // 32 (t & 7) ..), wave 0 lane l the 16 scale bytes of row l & 31
-    const int crow = tid >> 3, srow = l & 31;
-    int spc[TPW], sps[TPW];
+    // loads of a tile: thread t takes the 32 bytes of codes of row t >> 3 at
+    // bytes 32 (t & 7) .. (latent elements 64 (t & 7) ..) and their two scales
+    const int crow = tid >> 3;
+    int spc[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-        const int jc = (t_begin + t) * kAttnRows + crow, js = (t_begin + t) * kAttnRows + srow;
+        const int jc = (t_begin + t) * kAttnRows + crow;
         spc[t] = jc < k ? sel_pos[(size_t)b * k + jc] : -1;
-        sps[t] = (wave == 0 && js < k) ? sel_pos[(size_t)b * k + js] : -1;
     }
     // q . v is split over the latent dimension: wave w owns d in [128w, 128w+128)
     constexpr int kKs = kAttnD / 32 / (kAttnThreads / kWave);   // 4 k-steps per wave
@@ -194,19 +189,18 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         if (j < S) return (long long)(L - win + (j - nsel));
         return -1;
     };
-    u32x4 rc0[TPW], rc1[TPW], rsc[TPW];
-    uint32_t cok = 0, sok = 0;                           // per tile: row valid
+    u32x4 rc0[TPW], rc1[TPW];
+    uint32_t rsb[TPW];                                   // scale bytes of elements 0..31, 32..63
+    uint32_t cok = 0;                                    // per tile: row valid
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const long long pc = pos_of((t_begin + t) * kAttnRows + crow, spc[t]);
-        const long long ps = pos_of((t_begin + t) * kAttnRows + srow, sps[t]);
         cok |= (uint32_t)(pc >= 0) << t;
-        sok |= (uint32_t)(ps >= 0) << t;
-        const uint8_t* cp = kv_fp4 + (roff + (pc >= 0 ? pc : 0)) * (kAttnD / 2) + 32 * (tid & 7);
+        const long long row = roff + (pc >= 0 ? pc : 0);
+        const uint8_t* cp = kv_fp4 + row * (kAttnD / 2) + 32 * (tid & 7);
         rc0[t] = *reinterpret_cast<const u32x4*>(cp);
         rc1[t] = *reinterpret_cast<const u32x4*>(cp + 16);
-        if (wave == 0)                                    // uniform
-            rsc[t] = *reinterpret_cast<const u32x4*>(kv_scale + (roff + (ps >= 0 ? ps : 0)) * (kAttnD / 32));
+        rsb[t] = *reinterpret_cast<const uint16_t*>(kv_scale + row * (kAttnD / 32) + 2 * (tid & 7));
     }
 
     f32x4 o[kNb];                                        // set by the first tile's P.V
@@ -218,41 +212,17 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         if (t > 0 && tile >= t_end) break;                  // uniform; tile t_begin exists
         if (t > 0) __syncthreads();                          // previous tile's LDS reads are done
         {
-            // stage the raw tile (rows 8-byte aligned: 264-byte stride)
+            // dequantise this thread's 64 elements of row crow straight from
+            // the loaded registers (an invalid row is zeros, scale byte 0)
             const u32x4 z = {0u, 0u, 0u, 0u};
-            const u32x4 a = ((cok >> t) & 1u) ? rc0[t] : z, bq = ((cok >> t) & 1u) ? rc1[t] : z;
-            uint8_t* sr = s_raw + crow * kRawLd + 32 * (tid & 7);
-            *reinterpret_cast<u32x2*>(sr) = u32x2{a[0], a[1]};
-            *reinterpret_cast<u32x2*>(sr + 8) = u32x2{a[2], a[3]};
-            *reinterpret_cast<u32x2*>(sr + 16) = u32x2{bq[0], bq[1]};
-            *reinterpret_cast<u32x2*>(sr + 24) = u32x2{bq[2], bq[3]};
-            if (wave == 0 && l < kAttnRows)
-                *reinterpret_cast<u32x4*>(s_rsc + 16 * l) = ((sok >> t) & 1u) ? rsc[t] : z;
-        }
-        __syncthreads();
-        {
-            // this thread's 8 rows x 8 dims: codes word dc of rows 8rg.., their scale
-            // bytes; a 66-word row stride puts the 4 row groups of a wave 16 banks apart
-            u32x4 v[8];
+            const bool ok = (cok >> t) & 1u;
+            const u32x4 a = ok ? rc0[t] : z, bq = ok ? rc1[t] : z;
+            const uint32_t sbp = ok ? rsb[t] : 0u;
+            uint16_t* vr = s_vjd + crow * kVjdLd + 64 * (tid & 7);
 #pragma unroll
-            for (int r = 0; r < 8; ++r) {
-                const uint32_t cw = *reinterpret_cast<const uint32_t*>(s_raw + (8 * rg + r) * kRawLd + 4 * dc);
-                const int sb = s_rsc[(8 * rg + r) * 16 + (dc >> 2)];
-                v[r] = fp4x8_to_bf16x8(cw, sb);
-                *reinterpret_cast<u32x4*>(s_vjd + (8 * rg + r) * kVjdLd + 8 * dc) = v[r];
-            }
-#pragma unroll
-            for (int c = 0; c < 8; ++c) {
-                // element c of rows 2i and 2i+1 in one word: the low halves of
-                // word c/2 (c even) or the high halves (c odd), one byte permute
-                const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
-                u32x4 tr;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    tr[i] = __builtin_amdgcn_perm(v[2 * i + 1][c >> 1], v[2 * i][c >> 1], sel);
-                uint16_t* vw = s_vdj + (8 * dc + c) * kVdjLd + 8 * rg;
-                *reinterpret_cast<u32x2*>(vw) = u32x2{tr[0], tr[1]};
-                *reinterpret_cast<u32x2*>(vw + 4) = u32x2{tr[2], tr[3]};
+            for (int j = 0; j < 4; ++j) {
+                *reinterpret_cast<u32x4*>(vr + 8 * j) = fp4x8_to_bf16x8(a[j], sbp & 0xFF);
+                *reinterpret_cast<u32x4*>(vr + 32 + 8 * j) = fp4x8_to_bf16x8(bq[j], sbp >> 8);
             }
         }
         __syncthreads();
@@ -270,21 +240,28 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[ks], s1, 0, 0, 0);
             }
         }
-        *red_slot(wave, 0, l) = s0;
-        *red_slot(wave, 1, l) = s1;
+        s_red[wave][0][l] = s0;
+        s_red[wave][1][l] = s1;
         __syncthreads();
-        // this wave's V^T operands of the P.V product, read before the softmax
-        // so their LDS latency overlaps it
+        // this wave's V^T operands of the P.V product (latent elements d0 + c16
+        // of rows 4g..4g+3 and 16+4g..16+4g+3, d0 = 16 (8 wave + nb)), read
+        // before the softmax so their LDS latency overlaps it.  The gfx950
+        // transposing LDS read works in groups of 16 lanes: lane 4a + c of a
+        // group receives, as element e, the 16-bit value at offset c of the
+        // 8 bytes addressed by lane a + 4e of the group.  So lane (g, 4a' + c')
+        // addresses row 4g + a' at elements d0 + 4c' .. d0 + 4c' + 3.
         bf16x8 bv[kNb];
+        {
+            const uint16_t* vt = s_vjd + (4 * g + (c16 >> 2)) * kVjdLd + 16 * kNb * wave + 4 * (c16 & 3);
 #pragma unroll
-        for (int nb = 0; nb < kNb; ++nb) {
-            const uint16_t* vd = s_vdj + (16 * (kNb * wave + nb) + c16) * kVdjLd + 4 * g;
-            const u32x2 lo = *reinterpret_cast<const u32x2*>(vd);
-            const u32x2 hi = *reinterpret_cast<const u32x2*>(vd + 16);
-            bv[nb] = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            for (int nb = 0; nb < kNb; ++nb) {
+                const u32x2 lo = lds_read_tr16(vt + 16 * nb);
+                const u32x2 hi = lds_read_tr16(vt + 16 * kVjdLd + 16 * nb);
+                bv[nb] = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
+            }
         }
-        s0 = *red_slot(0, 0, l) + *red_slot(1, 0, l) + *red_slot(2, 0, l) + *red_slot(3, 0, l);
-        s1 = *red_slot(0, 1, l) + *red_slot(1, 1, l) + *red_slot(2, 1, l) + *red_slot(3, 1, l);
+        s0 = s_red[0][0][l] + s_red[1][0][l] + s_red[2][0][l] + s_red[3][0][l];
+        s1 = s_red[0][1][l] + s_red[1][1][l] + s_red[2][1][l] + s_red[3][1][l];
 
         // every wave now holds the full scores: head c16, rows 4g+i and 16+4g+i
         const int jt = tile * kAttnRows;

@@ -42,10 +42,11 @@ constexpr int kAttnThreads = 256;
 constexpr int kAttnRows = 32;
 constexpr int kAttnD = 512;
 constexpr int kHeadsPerWg = 16;
-constexpr int kVjdLd = kAttnD + 8;      // bf16 per row-major row (padded)
+constexpr int kVjdLdMax = kAttnD + 16;  // bf16 per row-major row, at most (1,056 B)
 constexpr int kAttnMaxTilesPerWg = 4;   // tiles whose loads one workgroup keeps in flight
 constexpr int kAttnMaxRows = 16384;     // k + window
 constexpr int kAttnMinWgs = 64;         // workgroups wanted per launch
+constexpr int kAttnWideWgs = 256;       // above this many workgroups, the wide layout
 constexpr int kAttnMaxSplits = kAttnMaxRows / kAttnRows;   // one tile per split at most
 
 // Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
@@ -69,6 +70,32 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 
+// Two layouts of the dequantised tile in LDS.  LDS serves 128 bytes (32
+// banks) per cycle; a row is 64 pieces of 16 bytes (8 latent elements).  The
+// dequantised stores (eight lanes per cycle, one piece each), the score
+// operands (the same piece of rows r..r+7 per eight lanes) and the
+// transposing reads (two adjacent pieces of rows 4g..4g+3 per sixteen lanes)
+// must each hit eight different bank groups per cycle.
+//   * Narrow (few workgroups, latency-bound): thread t dequantises row t >> 3,
+//     pieces 8c..8c+7 with c = t & 7, so the loads of a row are contiguous
+//     lanes.  Rows are 1,040 bytes apart and piece p sits at position
+//     p ^ ((p >> 3) & 7), so thread c writes its j-th piece to position
+//     8c + (j ^ c).  The transposing reads meet two-way conflicts.
+//   * Wide (more workgroups than CUs, where each instruction counts): lane l
+//     of wave w dequantises row 8w + (l & 7), so eight consecutive lanes
+//     store to eight rows; rows are 1,056 bytes apart and rows 4..7 mod 8
+//     start 16 bytes later.  No conflicts, and every LDS address is a
+//     per-lane base plus a constant, with no swizzle arithmetic.
+// Both permutations keep pairs of pieces 2i, 2i+1 together, so every read
+// stays whole.
+template <bool WIDE> constexpr int kVjdLd = WIDE ? kAttnD + 16 : kAttnD + 8;
+template <bool WIDE> __device__ __forceinline__ int vjd_row(int r) {
+    return WIDE ? r * kVjdLd<WIDE> + 8 * ((r >> 2) & 1) : r * kVjdLd<WIDE>;
+}
+template <bool WIDE> __device__ __forceinline__ int vjd_piece(int p) {   // offset of piece p
+    return WIDE ? 8 * p : 8 * (p ^ ((p >> 3) & 7));
+}
+
 // ds_read_b64_tr_b16 at an LDS address (8-byte aligned)
 __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
     typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -82,7 +109,7 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 // TPW tiles in a second one, held in registers until their tile's turn.
 // The arguments the first round trip needs (the sizes, then the pointers it
 // loads from) fill the 64 bytes that arrive in SGPRs with the wave.
-template <int TPW>
+template <int TPW, bool WIDE>
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     int B, int Hq, int k, int window, int n_splits, float scale_log2,
     const long long* __restrict__ row_off, const int* __restrict__ len,
@@ -90,9 +117,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_fp4,
     const uint8_t* __restrict__ kv_scale, float* __restrict__ part_o,
     float* __restrict__ part_ml, float* __restrict__ out, float* __restrict__ lse) {
-    // the tile's rows, dequantised, row-major (41.5 KB of LDS with the
+    // the tile's rows, dequantised, row-major (41 KB of LDS with the
     // partial sums: three workgroups per CU)
-    __shared__ __attribute__((aligned(16))) uint16_t s_vjd[kAttnRows * kVjdLd];
+    __shared__ __attribute__((aligned(16))) uint16_t s_vjd[kAttnRows * kVjdLdMax];
+    constexpr int LD = kVjdLd<WIDE>;
     // S^T partial sums of each wave over its quarter of the latent dimension
     __shared__ f32x4 s_red[kAttnThreads / kWave][2][kWave];
 
@@ -115,9 +143,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     // round trip 1: sequence scalars, this thread's selection entries, q
     const int len_b = len[b], sel_b = sel_len[b];
     const long long roff = row_off[b];
-    // loads of a tile: thread t takes the 32 bytes of codes of row t >> 3 at
-    // bytes 32 (t & 7) .. (latent elements 64 (t & 7) ..) and their two scales
-    const int crow = tid >> 3;
+    // loads of a tile: thread t takes the 32 bytes of codes of row crow at
+    // bytes 32 c8 .. (latent elements 64 c8 ..) and their two scales; each
+    // wave takes 8 whole rows
+    const int crow = WIDE ? 8 * wave + (l & 7) : tid >> 3, c8 = WIDE ? l >> 3 : tid & 7;
     int spc[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -197,10 +226,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         const long long pc = pos_of((t_begin + t) * kAttnRows + crow, spc[t]);
         cok |= (uint32_t)(pc >= 0) << t;
         const long long row = roff + (pc >= 0 ? pc : 0);
-        const uint8_t* cp = kv_fp4 + row * (kAttnD / 2) + 32 * (tid & 7);
+        const uint8_t* cp = kv_fp4 + row * (kAttnD / 2) + 32 * c8;
         rc0[t] = *reinterpret_cast<const u32x4*>(cp);
         rc1[t] = *reinterpret_cast<const u32x4*>(cp + 16);
-        rsb[t] = *reinterpret_cast<const uint16_t*>(kv_scale + row * (kAttnD / 32) + 2 * (tid & 7));
+        rsb[t] = *reinterpret_cast<const uint16_t*>(kv_scale + row * (kAttnD / 32) + 2 * c8);
     }
 
     f32x4 o[kNb];                                        // set by the first tile's P.V
@@ -218,11 +247,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
             const bool ok = (cok >> t) & 1u;
             const u32x4 a = ok ? rc0[t] : z, bq = ok ? rc1[t] : z;
             const uint32_t sbp = ok ? rsb[t] : 0u;
-            uint16_t* vr = s_vjd + crow * kVjdLd + 64 * (tid & 7);
+            // pieces 8 c8 + j and 8 c8 + 4 + j (narrow: positions 8 c8 + (j ^ c8) ..)
+            uint16_t* vr = s_vjd + vjd_row<WIDE>(crow) + 64 * c8;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                *reinterpret_cast<u32x4*>(vr + 8 * j) = fp4x8_to_bf16x8(a[j], sbp & 0xFF);
-                *reinterpret_cast<u32x4*>(vr + 32 + 8 * j) = fp4x8_to_bf16x8(bq[j], sbp >> 8);
+                const int p0 = WIDE ? 8 * j : 8 * (j ^ c8);
+                const int p1 = WIDE ? 32 + 8 * j : 8 * ((4 + j) ^ c8);
+                *reinterpret_cast<u32x4*>(vr + p0) = fp4x8_to_bf16x8(a[j], sbp & 0xFF);
+                *reinterpret_cast<u32x4*>(vr + p1) = fp4x8_to_bf16x8(bq[j], sbp >> 8);
             }
         }
         __syncthreads();
@@ -230,12 +262,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         // partial S^T[row][head] over this wave's quarter of the latent dimension
         f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
         {
-            const uint16_t* r0 = s_vjd + c16 * kVjdLd + 32 * kKs * wave + 8 * g;
-            const uint16_t* r1 = r0 + 16 * kVjdLd;
+            // rows c16 and 16 + c16 (the same offset of 16 rows further on)
+            // latent elements 128 wave + 32 ks + 8 g .. (piece 16 wave + 4 ks + g)
+            const uint16_t* r0 = s_vjd + vjd_row<WIDE>(c16) + (WIDE ? 32 * kKs * wave + 8 * g : 0);
+            const uint16_t* r1 = r0 + 16 * LD;
 #pragma unroll
             for (int ks = 0; ks < kKs; ++ks) {
-                const bf16x8 a0 = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(r0 + 32 * ks));
-                const bf16x8 a1 = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(r1 + 32 * ks));
+                const int pc = WIDE ? 32 * ks : vjd_piece<WIDE>(4 * kKs * wave + 4 * ks + g);
+                const bf16x8 a0 = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(r0 + pc));
+                const bf16x8 a1 = bitcast<bf16x8>(*reinterpret_cast<const u32x4*>(r1 + pc));
                 s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qb[ks], s0, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qb[ks], s1, 0, 0, 0);
             }
@@ -252,11 +287,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         // addresses row 4g + a' at elements d0 + 4c' .. d0 + 4c' + 3.
         bf16x8 bv[kNb];
         {
-            const uint16_t* vt = s_vjd + (4 * g + (c16 >> 2)) * kVjdLd + 16 * kNb * wave + 4 * (c16 & 3);
+            // latent elements d0 + 4 (c16 & 3) ..: half c16 & 1 of piece d0 / 8 + (c16 & 3) / 2
+            const uint16_t* vt = s_vjd + vjd_row<WIDE>(4 * g + (c16 >> 2)) +
+                                 (WIDE ? 16 * kNb * wave + 4 * (c16 & 3) : 4 * (c16 & 1));
 #pragma unroll
             for (int nb = 0; nb < kNb; ++nb) {
-                const u32x2 lo = lds_read_tr16(vt + 16 * nb);
-                const u32x2 hi = lds_read_tr16(vt + 16 * kVjdLd + 16 * nb);
+                const int pc = WIDE ? 16 * nb : vjd_piece<WIDE>(2 * kNb * wave + 2 * nb + ((c16 & 3) >> 1));
+                const u32x2 lo = lds_read_tr16(vt + pc);
+                const u32x2 hi = lds_read_tr16(vt + 16 * LD + pc);
                 bv[nb] = bitcast<bf16x8>(u32x4{lo[0], lo[1], hi[0], hi[1]});
             }
         }
@@ -507,10 +545,15 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
     const int npairs = B * (Hq / kHeadsPerWg), pr = (npairs + 7) / 8;
     const dim3 grid(8 * pr * ns), blk(kAttnThreads);
     const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q_bf16);
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, blk, 0, s, B, Hq, k, window, ns, scale_log2, row_off, len,
+                           sel_len, sel_pos, q16, kv_fp4, kv_scale, part_o, part_ml, out, lse);
+    };
+    const bool wide = (long long)npairs * ns > kAttnWideWgs;
     switch (tpw) {
-        case 1: hipLaunchKernelGGL(sparse_attn_kernel<1>, grid, blk, 0, s, B, Hq, k, window, ns, scale_log2, row_off, len, sel_len, sel_pos, q16, kv_fp4, kv_scale, part_o, part_ml, out, lse); break;
-        case 2: hipLaunchKernelGGL(sparse_attn_kernel<2>, grid, blk, 0, s, B, Hq, k, window, ns, scale_log2, row_off, len, sel_len, sel_pos, q16, kv_fp4, kv_scale, part_o, part_ml, out, lse); break;
-        default: hipLaunchKernelGGL(sparse_attn_kernel<4>, grid, blk, 0, s, B, Hq, k, window, ns, scale_log2, row_off, len, sel_len, sel_pos, q16, kv_fp4, kv_scale, part_o, part_ml, out, lse); break;
+        case 1: wide ? launch(sparse_attn_kernel<1, true>) : launch(sparse_attn_kernel<1, false>); break;
+        case 2: wide ? launch(sparse_attn_kernel<2, true>) : launch(sparse_attn_kernel<2, false>); break;
+        default: wide ? launch(sparse_attn_kernel<4, true>) : launch(sparse_attn_kernel<4, false>); break;
     }
     if (int e = launch_status("csa2_sparse_attn_decode launch")) return e;
     if (ns > 1) {

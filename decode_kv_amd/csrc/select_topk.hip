@@ -50,10 +50,15 @@ __device__ __forceinline__ void sel_find_bin(const uint32_t* s_hist, int nb, int
                                              int* s_tmp, int* s_res) {
     const int per = (nb + kSelThreads - 1) / kSelThreads;
     const int r = kSelThreads - 1 - threadIdx.x;            // thread 0 owns the top bins
+    // four bins per thread (the first pass): one 16-byte read each, so the
+    // lanes of a wave read consecutive words instead of every fourth word
+    // (a four-way LDS bank conflict); at most bin 4095 of the 8,192 is read
+    u32x4 h4 = {0u, 0u, 0u, 0u};
+    if (per == 4) h4 = *reinterpret_cast<const u32x4*>(s_hist + 4 * r);
     int mysum = 0;
     for (int i = 0; i < per; ++i) {
         const int bin = r * per + i;
-        mysum += bin < nb ? (int)s_hist[bin] : 0;
+        mysum += bin < nb ? (int)(per == 4 ? h4[i & 3] : s_hist[bin]) : 0;
     }
     int tot;
     const int above = block_exclusive_scan<kSelThreads>(mysum, s_tmp, tot);
@@ -61,7 +66,7 @@ __device__ __forceinline__ void sel_find_bin(const uint32_t* s_hist, int nb, int
         int acc = above;
         for (int i = per - 1; i >= 0; --i) {
             const int bin = r * per + i;
-            const int c = bin < nb ? (int)s_hist[bin] : 0;
+            const int c = bin < nb ? (int)(per == 4 ? h4[i & 3] : s_hist[bin]) : 0;
             if (acc + c >= need) {
                 s_res[0] = bin;
                 s_res[1] = acc;
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(kSelThreads) void select_topk_kernel(
     int* __restrict__ sel_len) {
     constexpr int PER = kSelMaxP / kSelThreads;   // 16
     static_assert(PER * kSelWaves == 4 * kWave, "slot_wave_scan covers 256 entries");
-    __shared__ uint32_t s_hist[kSelRefBins];
+    __shared__ __attribute__((aligned(16))) uint32_t s_hist[kSelRefBins];
     __shared__ int s_tmp[kSelWaves];
     __shared__ int s_res[4];
     static_assert(PER == 16 && kSelWaves == 16, "slot prefixes are 16 x 16");

@@ -548,11 +548,11 @@ def test_attention_small_heads_and_short_contexts():
     attention_case(11, [50, 128, 129, 0, 300], 64, 16)
     attention_case(12, [5000] * 3, 64, 128)
     attention_case(13, [100000], 512, 64, window=0)
-    attention_case(14, [3000] * 32, 512, 64)
+    attention_case(14, [3000] * 32, 512, 64)         # 640 workgroups: the wide tile layout
 
 
 def test_attention_many_splits():
-    attention_case(15, [40000], 8192, 64)           # 260 tiles over 65 splits
+    attention_case(15, [40000], 8192, 64)           # 260 tiles over 65 splits (wide layout)
     attention_case(16, [20000, 300, 9000], 2048, 32)
 
 
@@ -560,7 +560,7 @@ def test_attention_maximum_rows_and_many_pairs():
     attention_case(17, [20000], 16384 - 128, 16)    # k + window = 16,384: 512 tiles, 128 splits
     attention_case(18, [700] * 12, 256, 64)         # 48 (sequence, head group) pairs > 8
     attention_case(19, [int(x) for x in np.random.default_rng(19).integers(0, 900, size=200)],
-                   128, 16)                          # 200 sequences, some empty
+                   128, 16)                          # 200 sequences, some empty (wide layout)
 
 
 def test_attention_scale_ranges():

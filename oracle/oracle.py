@@ -56,14 +56,21 @@ def build(force: bool = True) -> str:
 
 _lib = None
 
+# A test may point the loader at another build of the same source (for
+# example one compiled with the address and undefined-behaviour sanitizers).
+_LIB_ENV = "CSA2_ORACLE_LIB"
+
 
 def load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB_PATH) or \
-                os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-            build(force=True)
-        lib = ctypes.CDLL(_LIB_PATH)
+        path = os.environ.get(_LIB_ENV)
+        if not path:
+            path = _LIB_PATH
+            if not os.path.exists(_LIB_PATH) or \
+                    os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build(force=True)
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
         lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
@@ -167,7 +174,7 @@ def topk(score: np.ndarray, pos: np.ndarray, k: int):
     s(p) > s(p') or (s(p) == s(p') and p < p'), returned ascending by
     position together with their scores.
 
-    [HOW] item 2 and [AGAIN]: keep the 512 most relevant / up to 512 positions;
+    [HOW] item 2 and [AGAIN]: a layer keeps a selection of 512 positions;
     ties go to the lower position (this path's reading).
     """
     s = np.ascontiguousarray(score, dtype=np.int64)
@@ -190,7 +197,7 @@ def topk(score: np.ndarray, pos: np.ndarray, k: int):
 def eligible_count(L: int, window: int) -> int:
     """Positions eligible for global selection: [0, L - W).  The window rows
     [L - W, L) are attended anyway and are never selected twice ([HOW] item 2:
-    512 selected entries plus a local 128-token window)."""
+    the selection and the newest 128 tokens are attended side by side)."""
     return max(0, int(L) - int(window))
 
 
@@ -201,9 +208,8 @@ def window_positions(L: int, window: int) -> np.ndarray:
 def index_full(keys, row_off: int, L: int, q, w, window: int, P: int):
     """Full mode: score every eligible position of the context and keep the
     first min(P, E) under the rank order as the candidate pool, ascending by
-    position ([CED] "Act 2": the first full-mode indexing layer searches the
-    whole context and builds a candidate pool; [HOW] item 2: up to 16,384
-    candidate positions)."""
+    position ([CED] "Act 2": one Full pass over the context yields the pool
+    the later layers work from; [HOW] item 2: at most 16,384 positions)."""
     E = eligible_count(L, window)
     pos = np.arange(E, dtype=np.int64)
     s = index_scores(keys, row_off + pos, q, w)
@@ -212,16 +218,15 @@ def index_full(keys, row_off: int, L: int, q, w, window: int, P: int):
 
 def index_reindex(keys, row_off: int, cand_pos, q, w) -> np.ndarray:
     """Reindex mode: re-score only the pool with this layer's own index query
-    and weights and the same index keys ([CED] "Act 2": later layers search
-    only the much smaller pool; [HOW] item 2: later layers search within that
-    shortlist)."""
+    and weights and the same index keys ([CED] "Act 2" and [HOW] item 2: a
+    Reindex layer ranks the Full layer's pool again, not the context)."""
     cand_pos = np.asarray(cand_pos, dtype=np.int64)
     return index_scores(keys, row_off + cand_pos, q, w)
 
 
 def select_topk(score, cand_pos, k: int):
-    """Top-k global positions of a scored candidate list ([HOW] item 2: the 512
-    most relevant entries), ascending by position."""
+    """Top-k global positions of a scored candidate list, ascending by position
+    ([HOW] item 2: a layer's selection of 512 positions)."""
     return topk(score, cand_pos, k)
 
 
@@ -275,7 +280,8 @@ def decode_step(pattern: str, keys, row_off: int, L: int, window: int, P: int, k
     here with the oracle's own FP4 rule).
     Returns per-layer dicts with pool, selection, out and lse.
     Reuse takes the most recent layer's selection; Reindex re-scores the most
-    recent Full layer's pool ([CED] "Act 2"; [HOW] item 2: selection reuse).
+    recent Full layer's pool ([CED] "Act 2"; [HOW] item 2: Reuse layers keep
+    the selection of the layer before).
     """
     results = []
     pool = None

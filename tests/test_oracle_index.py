@@ -2,6 +2,7 @@
 and window rule against a hand-worked example, closed forms, plain-Python
 brute force and exhaustive rank counting."""
 import itertools
+import math
 import os
 
 import numpy as np
@@ -206,6 +207,66 @@ def test_reindex_with_whole_context_equals_full():
     a, _ = oracle.select_topk(rs, pool, k)
     b, _ = oracle.index_full(keys, 0, L, q, w, W, k)
     assert np.array_equal(a, b)
+
+
+def _distinct_sequences(rng, lens, gap=7):
+    """Index keys of several sequences in one cache, each sequence drawn from
+    its own range so that reading the wrong rows changes every score."""
+    row_off, parts, cur = [], [], 0
+    for b, L in enumerate(lens):
+        pad = rng.integers(-127, 128, size=(gap, 64))
+        parts.append(pad)
+        cur += gap
+        row_off.append(cur)
+        lo = -127 + 40 * b
+        parts.append(rng.integers(lo, lo + 60, size=(L, 64)))
+        cur += L
+    return np.concatenate(parts).astype(np.int8), row_off
+
+
+def test_reindex_row_offset_matches_brute_force():
+    """Reindex reads sequence b's keys at row_off[b] + position: scores of the
+    pool of a sequence placed after others in the cache equal plain-Python
+    scores of exactly those rows (and differ from the rows at offset 0)."""
+    rng = np.random.default_rng(12)
+    keys, row_off = _distinct_sequences(rng, [300, 500, 200])
+    q = rng.integers(-127, 128, size=(5, 64)).astype(np.int8)
+    w = rng.integers(1, 16, size=5).astype(np.int8)
+    for b, L in enumerate([300, 500, 200]):
+        cand = np.sort(rng.choice(L, 60, replace=False))
+        got = oracle.index_reindex(keys, row_off[b], cand, q, w)
+        assert list(got) == _brute_scores(keys, row_off[b] + cand, q, w)
+        if b:
+            assert list(got) != _brute_scores(keys, cand, q, w)
+
+
+def test_decode_step_row_offset():
+    """A whole decode step of a sequence stored at a non-zero row offset:
+    the Full pool and selection are the exhaustive ranking of plain-Python
+    scores of rows row_off + p, and each Reindex score is the plain-Python
+    score of row row_off + pool position with that layer's query."""
+    rng = np.random.default_rng(13)
+    lens = [400, 700]
+    keys, row_off = _distinct_sequences(rng, lens)
+    W, P, k, H, D = 128, 90, 20, 3, 512
+    b, L = 1, lens[1]
+    off = row_off[b]
+    qs = {l: rng.integers(-127, 128, size=(H, 64)).astype(np.int8) for l in (0, 1, 4)}
+    ws = {l: rng.integers(0, 16, size=H).astype(np.int8) for l in (0, 1, 4)}
+    attn_q = [np.zeros((16, D), dtype=np.uint16) for _ in range(5)]
+    kv = np.zeros((L, D), dtype=np.uint16)
+    res = oracle.decode_step("FRUUR", keys, off, L, W, P, k, qs, ws, attn_q,
+                             lambda l, S: kv[S], 1 / math.sqrt(D))
+    E = L - W
+    s0 = _brute_scores(keys, off + np.arange(E), qs[0], ws[0])
+    assert list(res[0]["pool_pos"]) == _rank_count_topk(s0, np.arange(E), P)
+    assert list(res[0]["sel"]) == _rank_count_topk(s0, np.arange(E), k)
+    pool = res[0]["pool_pos"]
+    for l in (1, 4):
+        want = _brute_scores(keys, off + pool, qs[l], ws[l])
+        assert list(res[l]["reindex_score"]) == want
+        assert list(res[l]["sel"]) == _rank_count_topk(want, pool, k)
+    assert np.array_equal(res[2]["sel"], res[1]["sel"]) and np.array_equal(res[3]["sel"], res[1]["sel"])
 
 
 def test_window_and_eligibility():

@@ -1,9 +1,9 @@
 // csa2_sparse_attn_decode: attention of every query head over the selected
-// global positions plus the recent window, reading the FP4 latent cache
-// ("How DeepSeek V4.1 Flash Actually Works", item 2: the 512 most relevant KV
-// entries plus a local 128-token window; "DeepSeek Has Done It Again...": up
-// to 512 global positions alongside the 128 most recent tokens).  MQA with
-// K = V = the dequantised 512-wide latent row.
+// global positions plus the recent window, reading the FP4 latent cache.
+// ("How DeepSeek V4.1 Flash Actually Works", item 2, and "DeepSeek Has Done
+// It Again...", "Architecture and inference efficiency": a layer attends to
+// 512 positions chosen from the whole history together with the newest 128
+// tokens.)  MQA with K = V = the dequantised 512-wide latent row.
 //
 // Workgroup = (split, sequence, group of 16 heads), four waves, up to four
 // 32-row tiles of attended rows.  The launch is one-dimensional so that the
@@ -50,14 +50,18 @@ constexpr int kAttnWideWgs = 256;       // above this many workgroups, the wide 
 constexpr int kAttnMaxSplits = kAttnMaxRows / kAttnRows;   // one tile per split at most
 
 // Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
-// times 2^(sb - 127), to eight bf16 (element 2i in the low half of word i).
-// v_cvt_scalef32_pk_bf16_fp4 converts the two codes of one byte and applies
-// the fp32 scale; the scale 2^(sb-127) is built from its bits (sb = 0 gives
-// the subnormal 2^-127).  Exact for every code and every scale byte <= 252:
-// the results have at most two significant bits and bf16 has fp32's exponent
-// range, subnormals included.
-__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, int sb) {
-    const float scale = __builtin_bit_cast(float, sb ? (uint32_t)sb << 23 : 0x00400000u);
+// times 2^d, d <= 0, to eight bf16 (element 2i in the low half of word i).
+// The kernel dequantises relative to the largest scale byte of the rows a wave
+// holds: d = (scale byte of the block) - (that maximum), so the values stay
+// between 2^-1 * 2^d and 6 and the absolute power of two is applied to the
+// scores and carried with the outputs.  v_cvt_scalef32_pk_bf16_fp4 converts the
+// two codes of one byte and applies the fp32 scale 2^d, built from its bits
+// (subnormal below 2^-126, zero below 2^-149).  Exact whenever d >= -126:
+// the results have at most two significant bits.
+__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t codes, int d) {
+    const int eb = d + 127;
+    const uint32_t bits = eb > 0 ? (uint32_t)eb << 23 : (eb > -23 ? 0x00400000u >> (-eb) : 0u);
+    const float scale = __builtin_bit_cast(float, bits);
     u32x4 r;
     r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
     r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
@@ -123,6 +127,8 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     constexpr int LD = kVjdLd<WIDE>;
     // S^T partial sums of each wave over its quarter of the latent dimension
     __shared__ f32x4 s_red[kAttnThreads / kWave][2][kWave];
+    // per wave: the largest scale byte of the rows it dequantises (all tiles)
+    __shared__ int s_e[kAttnThreads / kWave];
 
     // workgroup i runs on XCD i mod 8: all splits of one (sequence, head group)
     // pair go to the same XCD, where they share the query rows in L2 and the
@@ -172,13 +178,20 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     constexpr int kNb = kAttnD / 16 / (kAttnThreads / kWave);   // 8 blocks of 16
     // the results: lane holds head `head`, latent elements 16 (8 wave + nb) + 4 g + (0..3)
     const int d0 = 16 * kNb * wave + 4 * g;
-    auto emit = [&](const f32x4 (&oo)[kNb], float m_fin, float l_fin) {
+    // oo is in units of 2^(e_fin - 127) (e_fin: the largest scale byte of the
+    // workgroup's rows), m_fin and l_fin are the running max and sum of the
+    // base-2 scores
+    auto emit = [&](const f32x4 (&oo)[kNb], float m_fin, float l_fin, int e_fin) {
         if (n_splits == 1) {
             float* ob = out + ((size_t)b * Hq + head) * kAttnD + d0;
             const float inv = l_fin > 0.f ? 1.f / l_fin : 0.f;
 #pragma unroll
-            for (int nb = 0; nb < kNb; ++nb)
-                *reinterpret_cast<f32x4*>(ob + 16 * nb) = oo[nb] * inv;
+            for (int nb = 0; nb < kNb; ++nb) {
+                f32x4 r = oo[nb] * inv;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) r[i] = ldexpf(r[i], e_fin - 127);
+                *reinterpret_cast<f32x4*>(ob + 16 * nb) = r;
+            }
             if (lse && wave == 0 && g == 0)
                 lse[(size_t)b * Hq + head] =
                     l_fin > 0.f ? (m_fin + log2f(l_fin)) * 0.69314718055994531f : -INFINITY;
@@ -190,24 +203,24 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         // the caches instead of waiting in L2 for the end-of-kernel write-back).
         const size_t base = ((size_t)b * n_splits + split) * Hq + head;
         float* ob = part_o + base * kAttnD + d0;
-        const u32x2 ml = {__float_as_uint(m_fin), __float_as_uint(l_fin)};
+        const f32x4 ml = {m_fin, l_fin, (float)e_fin, 0.f};
         if (npairs <= 8) {                                   // uniform
 #pragma unroll
             for (int nb = 0; nb < kNb; ++nb) *reinterpret_cast<f32x4*>(ob + 16 * nb) = oo[nb];
-            if (wave == 0 && g == 0) *reinterpret_cast<u32x2*>(part_ml + base * 2) = ml;
+            if (wave == 0 && g == 0) *reinterpret_cast<f32x4*>(part_ml + base * 4) = ml;
         } else {
 #pragma unroll
             for (int nb = 0; nb < kNb; ++nb)
                 __builtin_nontemporal_store(oo[nb], reinterpret_cast<f32x4*>(ob + 16 * nb));
             if (wave == 0 && g == 0)
-                __builtin_nontemporal_store(ml, reinterpret_cast<u32x2*>(part_ml + base * 2));
+                __builtin_nontemporal_store(ml, reinterpret_cast<f32x4*>(part_ml + base * 4));
         }
     };
     if (t_begin >= t_end) {                              // uniform: a split past the attended rows
         f32x4 z[kNb];
 #pragma unroll
         for (int nb = 0; nb < kNb; ++nb) z[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        emit(z, -INFINITY, 0.f);
+        emit(z, -INFINITY, 0.f, 0);
         return;
     }
 
@@ -221,19 +234,32 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     u32x4 rc0[TPW], rc1[TPW];
     uint32_t rsb[TPW];                                   // scale bytes of elements 0..31, 32..63
     uint32_t cok = 0;                                    // per tile: row valid
+    long long rrow[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {                      // the scale bytes first: the wave's
+        const long long pc = pos_of((t_begin + t) * kAttnRows + crow, spc[t]);   // exponent
+        cok |= (uint32_t)(pc >= 0) << t;                 // needs them before any tile
+        rrow[t] = roff + (pc >= 0 ? pc : 0);
+        rsb[t] = *reinterpret_cast<const uint16_t*>(kv_scale + rrow[t] * (kAttnD / 32) + 2 * c8);
+    }
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
-        const long long pc = pos_of((t_begin + t) * kAttnRows + crow, spc[t]);
-        cok |= (uint32_t)(pc >= 0) << t;
-        const long long row = roff + (pc >= 0 ? pc : 0);
-        const uint8_t* cp = kv_fp4 + row * (kAttnD / 2) + 32 * c8;
+        const uint8_t* cp = kv_fp4 + rrow[t] * (kAttnD / 2) + 32 * c8;
         rc0[t] = *reinterpret_cast<const u32x4*>(cp);
         rc1[t] = *reinterpret_cast<const u32x4*>(cp + 16);
-        rsb[t] = *reinterpret_cast<const uint16_t*>(kv_scale + row * (kAttnD / 32) + 2 * c8);
     }
+    // the wave's exponent: the largest scale byte of its valid rows in all of
+    // the workgroup's tiles (a wave holds the same 8 rows of every tile)
+    int ew = 0;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+        if ((cok >> t) & 1u) ew = max(ew, (int)max(rsb[t] & 0xFFu, rsb[t] >> 8));
+    ew = __builtin_amdgcn_readfirstlane((int)wave_max((float)ew));
+    if (l == 0) s_e[wave] = ew;
 
     f32x4 o[kNb];                                        // set by the first tile's P.V
     float m_run = -INFINITY, l_run = 0.f;
+    int ea = 0, eb = 0, etop = 0;                        // exponents, read after the first barrier
 
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -246,15 +272,15 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
             const u32x4 z = {0u, 0u, 0u, 0u};
             const bool ok = (cok >> t) & 1u;
             const u32x4 a = ok ? rc0[t] : z, bq = ok ? rc1[t] : z;
-            const uint32_t sbp = ok ? rsb[t] : 0u;
+            const int sbp = ok ? (int)rsb[t] : 0;
             // pieces 8 c8 + j and 8 c8 + 4 + j (narrow: positions 8 c8 + (j ^ c8) ..)
             uint16_t* vr = s_vjd + vjd_row<WIDE>(crow) + 64 * c8;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int p0 = WIDE ? 8 * j : 8 * (j ^ c8);
                 const int p1 = WIDE ? 32 + 8 * j : 8 * ((4 + j) ^ c8);
-                *reinterpret_cast<u32x4*>(vr + p0) = fp4x8_to_bf16x8(a[j], sbp & 0xFF);
-                *reinterpret_cast<u32x4*>(vr + p1) = fp4x8_to_bf16x8(bq[j], sbp >> 8);
+                *reinterpret_cast<u32x4*>(vr + p0) = fp4x8_to_bf16x8(a[j], (sbp & 0xFF) - ew);
+                *reinterpret_cast<u32x4*>(vr + p1) = fp4x8_to_bf16x8(bq[j], (sbp >> 8) - ew);
             }
         }
         __syncthreads();
@@ -300,14 +326,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         }
         s0 = s_red[0][0][l] + s_red[1][0][l] + s_red[2][0][l] + s_red[3][0][l];
         s1 = s_red[0][1][l] + s_red[1][1][l] + s_red[2][1][l] + s_red[3][1][l];
+        if (t == 0) {
+            // rows 4g..4g+3 were dequantised by wave g >> 1, rows 16+4g.. by
+            // wave 2 + (g >> 1); etop is the workgroup's largest exponent
+            ea = s_e[g >> 1];
+            eb = s_e[2 + (g >> 1)];
+            etop = max(max(s_e[0], s_e[1]), max(s_e[2], s_e[3]));
+        }
 
         // every wave now holds the full scores: head c16, rows 4g+i and 16+4g+i
+        // (the scores of the relative values times their wave's 2^(e - 127))
         const int jt = tile * kAttnRows;
         float ts[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            ts[i] = s0[i] * scale_log2;
-            ts[4 + i] = s1[i] * scale_log2;
+            ts[i] = ldexpf(s0[i] * scale_log2, ea - 127);
+            ts[4 + i] = ldexpf(s1[i] * scale_log2, eb - 127);
         }
         if (jt + kAttnRows > S) {                        // uniform: rows past S weigh 0
 #pragma unroll
@@ -342,8 +376,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             // two weights per conversion: the bf16 high parts, then the bf16
-            // residuals (each residual is exact in fp32 before rounding)
-            const f32x2 pp = {p[2 * i], p[2 * i + 1]};
+            // residuals (each residual is exact in fp32 before rounding).  A
+            // row's weight times 2^(its wave's exponent - etop) puts every row's
+            // relative values on the workgroup's common scale 2^(etop - 127).
+            const int sh = (i < 2 ? ea : eb) - etop;
+            const f32x2 pp = {ldexpf(p[2 * i], sh), ldexpf(p[2 * i + 1], sh)};
             const uint32_t hu = bitcast<uint32_t>(__builtin_convertvector(pp, bf16x2));
             const f32x2 hf = {__uint_as_float(hu << 16), __uint_as_float(hu & 0xFFFF0000u)};
             ph_u[i] = hu;
@@ -359,14 +396,14 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         }
     }
 
-    emit(o, m_run, l_run);
+    emit(o, m_run, l_run, etop);
 }
 
 // Log-sum-exp merge of the split partials: one workgroup per (head, sequence),
 // on the XCD of that head's attention workgroups (workgroup i runs on XCD
 // i mod 8), 128 threads x 4 output elements.  Each thread issues the loads of its
 // partial outputs of CH splits (indices past the last split reread it and get
-// weight 0) and, for split s = thread, that split's (m, l), all before any of
+// weight 0) and, for split s = thread, that split's (m, l, e), all before any of
 // them is used, so the merge costs one memory round trip; splits beyond CH
 // follow in further chunks.  CH is the smallest of 8, 16, 24, 32 that covers
 // the splits when it can.
@@ -381,7 +418,7 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* part_o,
                                                            float* __restrict__ out,
                                                            float* __restrict__ lse, int B) {
     __shared__ __attribute__((aligned(16))) float s_w[kAttnMaxSplits + 32];   // zero-padded to CH
-    __shared__ float s_red[2][2];
+    __shared__ float s_red[3][2];
     const int HG = Hq / kHeadsPerWg, npairs = B * HG;
     const int xid = blockIdx.x & 7, xslot = blockIdx.x >> 3;
     const int pair = (xslot >> 4) * 8 + xid;
@@ -394,48 +431,62 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* part_o,
         const int s = min(u, n_splits - 1);
         os[u] = *reinterpret_cast<const f32x4*>(part_o + (row0 + (size_t)s * Hq) * kAttnD + 4 * tid);
     }
-    const float2 ml = *reinterpret_cast<const float2*>(
-        part_ml + (row0 + (size_t)min(tid, n_splits - 1) * Hq) * 2);   // used for tid < n_splits
+    const f32x4 ml = *reinterpret_cast<const f32x4*>(
+        part_ml + (row0 + (size_t)min(tid, n_splits - 1) * Hq) * 4);   // used for tid < n_splits
     asm volatile("" ::: "memory");
-    // M = max over splits of m_s; weights w_s = 2^(m_s - M) (0 for an empty
-    // split and zero-padded to a multiple of CH); lsum = sum w_s l_s
+    // A split's partial is (m_s, l_s, e_s) and O_s in units of 2^(e_s - 127).
+    // M = max m_s and Ex = max e_s over the splits; w_s = 2^(m_s - M) (0 for an
+    // empty split); lsum = sum w_s l_s; split s enters the output sum with
+    // w_s 2^(e_s - Ex) (kept in LDS, zero-padded to a multiple of CH) and the
+    // sum is scaled by 2^(Ex - 127) at the end
     const int n_pad = (n_splits + CH - 1) / CH * CH;
     float M, lsum;
+    int Ex;
     if (n_pad <= kWave) {                                       // uniform: wave 0 alone
         if (tid < kWave) {
             const bool in = tid < n_splits;
             const float m = in ? ml.x : -INFINITY;
             const float Mw = wave_max(m);
+            const float Ew = wave_max(in ? ml.z : 0.f);
             const float w = (in && Mw != -INFINITY) ? exp2f(m - Mw) : 0.f;
             const float ls = wave_sum(w * (in ? ml.y : 0.f));
-            s_w[tid] = w;
+            s_w[tid] = in ? ldexpf(w, (int)(ml.z - Ew)) : 0.f;
             if (tid == 0) {
                 s_red[0][0] = Mw;
                 s_red[1][0] = ls;
+                s_red[2][0] = Ew;
             }
         }
         __syncthreads();
         M = s_red[0][0];
         lsum = s_red[1][0];
+        Ex = (int)s_red[2][0];
     } else {
         float mloc = tid < n_splits ? ml.x : -INFINITY;
-        for (int s = tid + 128; s < n_splits; s += 128)
-            mloc = fmaxf(mloc, part_ml[(row0 + (size_t)s * Hq) * 2]);
+        float eloc = tid < n_splits ? ml.z : 0.f;
+        for (int s = tid + 128; s < n_splits; s += 128) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(part_ml + (row0 + (size_t)s * Hq) * 4);
+            mloc = fmaxf(mloc, v.x);
+            eloc = fmaxf(eloc, v.z);
+        }
         mloc = wave_max(mloc);
-        if ((tid & (kWave - 1)) == 0) s_red[0][tid / kWave] = mloc;
+        eloc = wave_max(eloc);
+        if ((tid & (kWave - 1)) == 0) {
+            s_red[0][tid / kWave] = mloc;
+            s_red[2][tid / kWave] = eloc;
+        }
         __syncthreads();
         M = fmaxf(s_red[0][0], s_red[0][1]);
+        Ex = (int)fmaxf(s_red[2][0], s_red[2][1]);
         float lpart = 0.f;
         for (int s = tid; s < n_pad; s += 128) {
             float w = 0.f;
             if (s < n_splits && M != -INFINITY) {
-                float ms = ml.x, ls = ml.y;
-                if (s >= 128) {
-                    ms = part_ml[(row0 + (size_t)s * Hq) * 2];
-                    ls = part_ml[(row0 + (size_t)s * Hq) * 2 + 1];
-                }
-                w = exp2f(ms - M);
-                lpart += w * ls;
+                f32x4 v = ml;
+                if (s >= 128) v = *reinterpret_cast<const f32x4*>(part_ml + (row0 + (size_t)s * Hq) * 4);
+                const float ws = exp2f(v.x - M);
+                lpart += ws * v.y;
+                w = ldexpf(ws, (int)v.z - Ex);
             }
             s_w[s] = w;
         }
@@ -466,7 +517,10 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* part_o,
             for (int i = 0; i < 4; ++i) acc += w[i] * os[u4 + i];
         }
     }
-    *reinterpret_cast<f32x4*>(o) = acc / lsum;
+    f32x4 r = acc / lsum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = ldexpf(r[i], Ex - 127);
+    *reinterpret_cast<f32x4*>(o) = r;
     if (lse && tid == 0) lse[(size_t)b * Hq + h] = (M + log2f(lsum)) * 0.69314718055994531f;
 }
 
@@ -488,7 +542,7 @@ int sparse_attn_splits(int B, int Hq, int k, int window) {
     return ns < 1 ? 1 : ns;
 }
 
-// Workspace: the partial O, then (m, l), of every (sequence, split, head).
+// Workspace: the partial O, then (m, l, e, -), of every (sequence, split, head).
 static size_t attn_ws_layout(int B, int Hq, int ns, char* base, float** part_o,
                              float** part_ml) {
     const size_t n = (size_t)B * ns * Hq;
@@ -497,7 +551,7 @@ static size_t attn_ws_layout(int B, int Hq, int ns, char* base, float** part_o,
         *part_o = reinterpret_cast<float*>(base);
         *part_ml = reinterpret_cast<float*>(base + o_bytes);
     }
-    return o_bytes + round_up(n * 2 * 4, 256);
+    return o_bytes + round_up(n * 4 * 4, 256);
 }
 
 size_t sparse_attn_ws_bytes(int B, int Hq, int D, int k, int window) {
@@ -527,7 +581,11 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
     if (Hq < 16 || Hq % 16 != 0)
         return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: Hq must be a positive multiple of 16");
     if (B > 65535 || Hq > 1024) return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: B or Hq too large");
-    if (!aligned(q_bf16, 16) || !aligned(kv_fp4, 4) || !aligned(out, 16) || !aligned(row_off, 8))
+    // the kernel reads a row's codes in 16-byte pieces and its scale bytes in
+    // pairs, and stores the outputs in 16-byte pieces
+    if (!aligned(q_bf16, 16) || !aligned(kv_fp4, 16) || !aligned(kv_scale, 2) ||
+        !aligned(out, 16) || !aligned(row_off, 8) || !aligned(len, 4) || !aligned(sel_len, 4) ||
+        !aligned(sel_pos, 4) || !aligned(lse, 4))
         return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: misaligned pointer");
     if ((long long)k + window > kAttnMaxRows)
         return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: k + window > %d", kAttnMaxRows);

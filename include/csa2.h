@@ -4,15 +4,15 @@
  *
  * What the path computes (page title, section):
  *  - "DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 2: CSA2 &
- *    Hierarchical Sparse Indexing": a Full indexing layer searches the whole
- *    context and builds a candidate pool; later layers search only the pool
- *    (Reindex) or reuse what is already known (Reuse).
+ *    Hierarchical Sparse Indexing": one Full pass ranks the whole context
+ *    into a candidate pool; Reindex layers rank that pool again, and Reuse
+ *    layers keep the previous selection.
  *  - "How DeepSeek V4.1 Flash Actually Works", "The three KV-cache
- *    optimizations", item 2: attention reads the 512 most relevant KV entries
- *    plus a local 128-token window; one indexing layer yields up to 16,384
- *    candidate positions; KV values are stored in FP4.
+ *    optimizations", item 2: each layer attends to 512 selected positions and
+ *    the newest 128 tokens; the Full pass keeps at most 16,384 candidates;
+ *    the KV cache holds 4-bit floating-point values.
  *  - "DeepSeek Has Done It Again...", "Architecture and inference efficiency":
- *    up to 512 global positions alongside the 128 most recent tokens.
+ *    at most 512 positions from the history, next to the newest 128 tokens.
  * Readings this library fixes where the pages are silent: int8 index keys
  * (one 64-byte key per token, shared by all index heads) and int8 queries;
  * score(p) = sum_h w_h * max(0, q_h . K[p]) exact in int32; rank order =
@@ -81,9 +81,9 @@ size_t csa2_workspace_bytes(int op, int B, long long max_len, long long total_le
 
 /*
  * csa2_kv_append_fp4 -- quantise n bf16 latent rows into the FP4 cache.
- * ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 3": FP4 main KV
- * caching; "How DeepSeek V4.1 Flash Actually Works", item 2: KV compressed
- * from FP8 to FP4.)
+ * ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 3", and "How
+ * DeepSeek V4.1 Flash Actually Works", item 2: the KV cache is stored at 4
+ * bits per value, down from 8.)
  *   x_bf16   [n][D] bf16, row-major, 16-byte aligned.
  *   dst_row  [n] int64: destination row of each input row (any row of the
  *            arrays below; rows must be distinct within one call).
@@ -104,10 +104,10 @@ int csa2_kv_append_fp4(const void* x_bf16, const long long* dst_row, int n, int 
  * csa2_index_full -- Full mode: score every eligible position of each
  * sequence and keep the first P_eff = min(P, E_b) positions under the rank
  * order as the candidate pool.
- * ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 2": the first
- * full-mode indexing layer searches the large context and builds a candidate
- * pool; "How DeepSeek V4.1 Flash Actually Works", item 2: up to 16,384
- * candidate positions.)
+ * ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 2": one Full pass
+ * over the context yields the pool the later indexing layers work from; "How
+ * DeepSeek V4.1 Flash Actually Works", item 2: the pool holds at most 16,384
+ * positions.)
  *   q        [B][H][Dk] int8 index queries (one per sequence), 16-byte aligned.
  *   w        [B][H] int8 per-head weights in [0, 15].
  *   keys     index-key cache, row r at keys + r*Dk (int8), 16-byte aligned.
@@ -157,9 +157,9 @@ int csa2_index_score(const signed char* q, const signed char* w, const signed ch
 /*
  * csa2_index_reindex -- Reindex mode: re-score only the candidate list with
  * this layer's own index query and weights, reading the same index keys.
- * ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 2": later layers
- * search only that much smaller pool; "How DeepSeek V4.1 Flash Actually
- * Works", item 2: later layers search within that shortlist.)
+ * ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 2", and "How
+ * DeepSeek V4.1 Flash Actually Works", item 2: a Reindex layer ranks the Full
+ * layer's pool again rather than the whole context.)
  *   q, w, keys, row_off: as csa2_index_full.
  *   cand_pos [B][P] int32 positions (the Full layer's pool), cand_len [B].
  *   score    [B][P] int32 out: score of cand_pos[b][i] for i < cand_len[b],
@@ -174,8 +174,9 @@ int csa2_index_reindex(const signed char* q, const signed char* w, const signed 
  * csa2_select_topk -- keep the first k_eff = min(k, cand_len[b]) candidates
  * under the rank order (score descending, then lower position), output
  * ascending by position.
- * ("How DeepSeek V4.1 Flash Actually Works", item 2: the 512 most relevant
- * KV entries; "DeepSeek Has Done It Again...": up to 512 global positions.)
+ * ("How DeepSeek V4.1 Flash Actually Works", item 2, and "DeepSeek Has Done
+ * It Again...", "Architecture and inference efficiency": a layer attends to a
+ * selection of 512 positions from the history.)
  *   score    [B][P] int32 (values >= 0 for valid entries).
  *   cand_pos [B][P] int32 positions, strictly ascending over the valid
  *            entries (as produced by csa2_index_full).
@@ -193,11 +194,13 @@ int csa2_select_topk(const int* score, const int* cand_pos, const int* cand_len,
  * reading the FP4 latent cache of one layer (MQA, K = V = latent):
  *   out[b][h][:] = sum_j softmax_j(sm_scale * q[b][h] . v_j) v_j
  *   lse[b][h]    = ln sum_j exp(sm_scale * q[b][h] . v_j)
- * ("How DeepSeek V4.1 Flash Actually Works", item 2: the 512 selected
- * entries plus a local 128-token window; "DeepSeek Has Done It Again...":
- * up to 512 global positions alongside the most recent 128 tokens.)
+ * ("How DeepSeek V4.1 Flash Actually Works", item 2, and "DeepSeek Has Done
+ * It Again...", "Architecture and inference efficiency": a layer attends to
+ * its 512 selected positions together with the newest 128 tokens.)
  *   q_bf16   [B][Hq][D] bf16, 16-byte aligned.
- *   kv_fp4, kv_scale: this layer's cache (layout as csa2_kv_append_fp4).
+ *   kv_fp4, kv_scale: this layer's cache (layout as csa2_kv_append_fp4);
+ *            kv_fp4 16-byte aligned (rows are read in 16-byte pieces),
+ *            kv_scale 2-byte aligned.
  *   row_off, len, max_len: as csa2_index_full.
  *   sel_pos  [B][k] int32 selected positions (all < L_b - window), sel_len [B].
  *   out      [B][Hq][D] fp32;  lse [B][Hq] fp32 or NULL.
@@ -209,6 +212,17 @@ int csa2_select_topk(const int* score, const int* cand_pos, const int* cand_len,
  * for a given (B, Hq, k, window).  A sequence with L_b == 0 gets out = 0 and
  * lse = -inf.  Requires D == 512, Hq a positive multiple of 16 (<= 1024), k >= 0,
  * k + window <= 16384.
+ * Numeric range: every E8M0 scale byte 0..254 is read exactly (the rows are
+ * dequantised relative to the largest scale byte among the rows a wave
+ * holds, and that power of two is applied to the scores and outputs).  The
+ * results meet 1e-3 * max|out| whenever every score sm_scale * q . v is
+ * finite in fp32; blocks more than 126 octaves below the largest scale of
+ * their workgroup's rows are taken as zero (their contribution is below
+ * 2^-126 of the largest value).  Scale byte 255 (NaN in E8M0) is not valid
+ * input; csa2_kv_append_fp4 never writes it.
+ * Errors: INVALID for null pointers, negative sizes, Hq not a multiple of 16
+ * or a misaligned pointer; UNSUPPORTED for D != 512 or k + window > 16384;
+ * WORKSPACE for a missing or small workspace.
  */
 int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* kv_fp4,
                             const unsigned char* kv_scale, const long long* row_off,

@@ -143,3 +143,22 @@ def test_reindex_select_attention_reject_bad_arguments(lib):
     no_ws = list(args)
     no_ws[16] = None
     assert a(*no_ws) == csa2.CSA2_ERR_WORKSPACE
+
+
+def test_attention_rejects_misaligned_cache_and_outputs(lib):
+    """The FP4 codes are read in 16-byte pieces and the scale bytes in pairs:
+    csa2_sparse_attn_decode rejects a code array that is not 16-byte aligned
+    and a scale array that is not 2-byte aligned, before launching anything."""
+    a = lib.csa2_sparse_attn_decode
+    args = [256, 256, 256, 256, 256, 4096, 256, 256, 1, 64, 512, 512, 128, 0.04, 256, 256,
+            256, 1 << 40, None]
+    for i, addr in [(1, 264), (1, 260), (1, 257), (2, 257), (0, 264), (14, 264), (3, 260),
+                    (4, 258), (6, 258), (7, 258), (15, 258)]:
+        bad = list(args)
+        bad[i] = addr
+        assert a(*bad) == csa2.CSA2_ERR_INVALID, (i, addr)
+        assert "misaligned" in csa2.last_error()
+    ok = list(args)
+    ok[2] = 258                                      # scale bytes: 2-byte alignment suffices
+    ok[16] = None                                    # ...so the call gets as far as the workspace
+    assert a(*ok) == csa2.CSA2_ERR_WORKSPACE

@@ -1,6 +1,7 @@
 """GPU parity: every C-ABI entry point against the CPU oracle on the same
 seeded inputs.  Bar: bit-exact pool / selection / scores / FP4 bytes;
-attention within 1e-3 * max|out| per (sequence, layer) and lse within 1e-3."""
+attention within 1e-3 * max|out| per (sequence, layer) and lse within
+1e-3 + 1e-6 |lse| (a few fp32 spacings once |lse| is large)."""
 import math
 import sys
 
@@ -514,7 +515,11 @@ def run_attention(codes, scales, row_off, lens, sel, sel_len, q_bits, k, window)
     return res[0]
 
 
-def attention_case(seed, lens, k, Hq, scale_lo=118, scale_hi=130, window=128):
+def attention_case(seed, lens, k, Hq, scale_lo=118, scale_hi=130, window=128, q_exp=None):
+    """Random FP4 rows (every code, scale bytes uniform in [scale_lo, scale_hi])
+    and bf16 queries: N(0,1), or with q_exp, magnitudes in [0.25, 4) times
+    2^q_exp (all normal bf16), so that caches with huge scales keep every
+    score finite in fp32."""
     rng = np.random.default_rng(seed)
     B = len(lens)
     row_off = list(np.cumsum([0] + lens[:-1]))
@@ -529,7 +534,10 @@ def attention_case(seed, lens, k, Hq, scale_lo=118, scale_hi=130, window=128):
         if m:
             sel[b, :m] = np.sort(rng.choice(E, m, replace=False))
         sel_len.append(m)
-    q = (rng.standard_normal((B, Hq, 512)).astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    qf = rng.standard_normal((B, Hq, 512))
+    if q_exp is not None:
+        qf = np.sign(qf) * np.clip(np.abs(qf), 0.25, 3.99) * 2.0 ** q_exp
+    q = (qf.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
     out, lse = run_attention(codes, scales, row_off, lens, sel, sel_len, q, k, window)
     for b, L in enumerate(lens):
         S = oracle.attention_positions(L, sel[b, :sel_len[b]], window)
@@ -566,6 +574,31 @@ def test_attention_maximum_rows_and_many_pairs():
 def test_attention_scale_ranges():
     attention_case(20, [4096, 2000], 512, 64, scale_lo=100, scale_hi=150)
     attention_case(21, [4096, 2000], 512, 64, scale_lo=1, scale_hi=1)
+
+
+def test_attention_smallest_scale_byte():
+    """Scale byte 0 (2^-127) on every block with non-zero codes: every value
+    is at most 6 * 2^-127, many are bf16 subnormals, and the outputs are fp32
+    subnormals; one sequence alone (single split) and a batch (split-K)."""
+    attention_case(22, [4096, 2000], 512, 64, scale_lo=0, scale_hi=0)
+    attention_case(23, [3000], 512, 64, scale_lo=0, scale_hi=2)
+    attention_case(24, [2500] * 16, 512, 64, scale_lo=0, scale_hi=0)     # wide layout
+
+
+def test_attention_largest_scale_bytes():
+    """Scale bytes 240..252 (the largest the append produces for finite bf16):
+    values up to 6 * 2^125, whose unnormalised softmax sums would overflow
+    fp32; the queries are small enough that the scores stay finite."""
+    attention_case(25, [4096, 2000], 512, 64, scale_lo=240, scale_hi=252, q_exp=-121)
+    attention_case(26, [4096, 2000], 512, 64, scale_lo=250, scale_hi=252, q_exp=-124)
+    attention_case(27, [2500] * 16, 512, 64, scale_lo=240, scale_hi=252, q_exp=-124)
+
+
+def test_attention_full_scale_range():
+    """Scale bytes drawn from the whole finite range 0..252 block by block, so
+    the rows of one workgroup span 252 octaves."""
+    attention_case(28, [4096, 2000], 512, 64, scale_lo=0, scale_hi=252, q_exp=-124)
+    attention_case(29, [40000], 8192, 64, scale_lo=0, scale_hi=252, q_exp=-124)
 
 
 def test_attention_empty_sequence():

@@ -1,8 +1,9 @@
-// csa2_index_full: Full-mode index scan and candidate pool
-// ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 2": the first
-// full-mode indexing layer searches the whole context and builds a candidate
-// pool; "How DeepSeek V4.1 Flash Actually Works", item 2: up to 16,384
-// candidate positions).  csa2_index_score exposes the scoring stage alone.
+// csa2_index_full: Full-mode index scan and candidate pool.
+// ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 2": one pass over
+// every cached position ranks the context once and yields the pool that the
+// later indexing layers work from; "How DeepSeek V4.1 Flash Actually Works",
+// item 2: that pool holds at most 16,384 positions.)  csa2_index_score
+// exposes the scoring stage alone.
 //
 // Five kernels, all sequences of the batch at once, tiles of 1,024 positions
 // (per-tile grids padded to a multiple of 8 tiles, so tile t of every grid

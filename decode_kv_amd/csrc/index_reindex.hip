@@ -1,8 +1,7 @@
 // csa2_index_reindex: Reindex mode, re-scoring only the candidate pool with
-// the layer's own index query ("DeepSeek V4.1-Flash 552B runs like 16B
-// (CED)", "Act 2": later layers search only that much smaller pool; "How
-// DeepSeek V4.1 Flash Actually Works", item 2: later layers search within the
-// shortlist).
+// the layer's own index query.  ("DeepSeek V4.1-Flash 552B runs like 16B
+// (CED)", "Act 2", and "How DeepSeek V4.1 Flash Actually Works", item 2: a
+// Reindex layer ranks the Full layer's pool again instead of the context.)
 //
 // Same int8 MFMA scoring as the Full scan, with the key operand gathered:
 // each lane loads 16 bytes of the 64-byte key row of its candidate, four lanes

@@ -1,6 +1,7 @@
 // csa2_kv_append_fp4: quantise bf16 latent rows into the FP4 E2M1 cache with
-// one E8M0 scale per 32 elements ("DeepSeek V4.1-Flash 552B runs like 16B
-// (CED)", "Act 3": FP4 main KV caching; block rule of OCP MX v1.0).
+// one E8M0 scale per 32 elements.  ("DeepSeek V4.1-Flash 552B runs like 16B
+// (CED)", "Act 3": the main KV cache is kept in 4-bit floating point; the
+// block rule is that of OCP MX v1.0.)
 //
 // One wavefront per row: lane l owns elements [8l, 8l+8) of a 512-wide chunk
 // (one 16-byte load), four lanes own one 32-element block.  The block amax is

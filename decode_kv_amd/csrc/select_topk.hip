@@ -1,7 +1,8 @@
 // csa2_select_topk: the k highest-ranked candidates of a scored list, ties
-// to the lower position, output ascending ("How DeepSeek V4.1 Flash Actually
-// Works", item 2: the 512 most relevant KV entries; "DeepSeek Has Done It
-// Again...": up to 512 global positions).
+// to the lower position, output ascending.  ("How DeepSeek V4.1 Flash Actually
+// Works", item 2, and "DeepSeek Has Done It Again...", "Architecture and
+// inference efficiency": each layer attends to a selection of 512 positions
+// from the history.)
 //
 // One workgroup (1,024 threads) per sequence.  The candidate scores and
 // positions (<= 16,384 each) are loaded with all of a thread's loads in

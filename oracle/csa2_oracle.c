@@ -12,14 +12,14 @@
  *
  * Sources (page titles as they appear in the collected pages):
  *  - "DeepSeek V4.1-Flash 552B runs like 16B (CED)", section "Act 2: CSA2 &
- *    Hierarchical Sparse Indexing": the Full layer scans the context and builds
- *    a candidate pool; later layers search only that pool.
+ *    Hierarchical Sparse Indexing": one Full pass ranks the context into a
+ *    candidate pool, which the later indexing layers rank again.
  *  - "How DeepSeek V4.1 Flash Actually Works", section "The three KV-cache
- *    optimizations", item 2 (Compress Sparse Attention): 512 selected entries
- *    plus a local 128-token window; an indexing layer produces up to 16,384
- *    candidate positions; FP4 KV values.
+ *    optimizations", item 2 (Compress Sparse Attention): a layer attends to
+ *    512 selected positions and the newest 128 tokens; the pool holds at most
+ *    16,384 positions; the KV cache stores 4-bit values.
  *  - "DeepSeek Has Done It Again...", section "Architecture and inference
- *    efficiency": up to 512 global positions alongside the 128 most recent.
+ *    efficiency": at most 512 history positions next to the newest 128.
  *  - Where the pages leave the arithmetic open, this path fixes it: int8
  *    index keys and queries with exact integer scores,
  *    score = sum_h w_h*max(0, q_h.k), ties broken by lower position, KV stored

@@ -16,6 +16,7 @@ import torch
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libcsa2.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "csa2.h")
+HEADERS = [HEADER, os.path.join(os.path.dirname(HERE), "include", "csa2_measure.h")]
 
 CSA2_OK = 0
 CSA2_ERR_INVALID = -1
@@ -53,6 +54,8 @@ def lib():
         L.csa2_workspace_bytes.argtypes = [I, I, LL, LL, I, I, I, I, I, I]
         L.csa2_kv_append_fp4.restype = I
         L.csa2_kv_append_fp4.argtypes = [V, V, I, I, V, V, V]
+        L.csa2_append_token.restype = I
+        L.csa2_append_token.argtypes = [V, V, V, V, I, I, LL, I, I, V, V, V, V]
         L.csa2_index_full.restype = I
         L.csa2_index_full.argtypes = [V, V, V, V, V, I, LL, LL, I, I, I, I, V, V, V, I, V, V, V, SZ,
                                        V]
@@ -62,6 +65,10 @@ def lib():
         L.csa2_index_reindex.argtypes = [V, V, V, V, V, V, I, I, I, I, V, V]
         L.csa2_select_topk.restype = I
         L.csa2_select_topk.argtypes = [V, V, V, I, I, I, V, V, V, SZ, V]
+        L.csa2_stream_read_sink_words.restype = SZ
+        L.csa2_stream_read_sink_words.argtypes = [SZ]
+        L.csa2_stream_read.restype = I
+        L.csa2_stream_read.argtypes = [V, SZ, V, SZ, V]
         L.csa2_sparse_attn_decode.restype = I
         L.csa2_sparse_attn_decode.argtypes = [V, V, V, V, V, LL, V, V, I, I, I, I, I, F, V, V,
                                               V, SZ, V]
@@ -69,11 +76,15 @@ def lib():
     return _lib
 
 
+def header_source() -> str:
+    """The declarations of include/csa2.h and include/csa2_measure.h, comments removed."""
+    src = "".join(open(h).read() for h in HEADERS)
+    return re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+
+
 def header_functions() -> list:
-    """Names of the functions include/csa2.h declares."""
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", src)))
+    """Names of the functions the headers declare."""
+    return sorted(set(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(", header_source())))
 
 
 def last_error() -> str:
@@ -124,6 +135,18 @@ def kv_append_fp4(x_bf16, dst_row, kv_fp4, kv_scale, stream=None):
                                     _s(stream)))
 
 
+def append_token(x_bf16, key_rows, row_off, lens, kv_fp4, kv_scale, keys, stream=None):
+    """x_bf16 [n_layers][B][D]; kv_fp4 [n_layers][rows][D/2]; kv_scale
+    [n_layers][rows][D/32]; key_rows [B][Dk]; keys [rows][Dk]."""
+    n_layers, B, D = x_bf16.shape
+    layer_rows = kv_fp4.shape[1]
+    assert kv_fp4.shape[0] == n_layers and kv_scale.shape[:2] == kv_fp4.shape[:2]
+    _check("csa2_append_token",
+           lib().csa2_append_token(_p(x_bf16), _p(key_rows), _p(row_off), _p(lens), B, n_layers,
+                                   layer_rows, D, key_rows.shape[1], _p(kv_fp4), _p(kv_scale),
+                                   _p(keys), _s(stream)))
+
+
 def index_full(q, w, keys, row_off, lens, max_len, total_len, window, P, pool_pos, pool_score,
                pool_len, ws, stream=None, k=0, sel_pos=None, sel_len=None):
     B, H, Dk = q.shape
@@ -158,6 +181,18 @@ def select_topk(score, cand_pos, cand_len, k, sel_pos, sel_len, ws=None, stream=
     _check("csa2_select_topk",
            lib().csa2_select_topk(_p(score), _p(cand_pos), _p(cand_len), B, P, k, _p(sel_pos),
                                   _p(sel_len), _p(ws), nbytes, _s(stream)))
+
+
+def stream_read(src, sink, stream=None):
+    """Read the bytes of tensor `src` once (measurement helper; see
+    include/csa2_measure.h)."""
+    nbytes = src.numel() * src.element_size()
+    _check("csa2_stream_read",
+           lib().csa2_stream_read(_p(src), nbytes, _p(sink), sink.numel(), _s(stream)))
+
+
+def stream_read_sink_words(nbytes: int) -> int:
+    return int(lib().csa2_stream_read_sink_words(nbytes))
 
 
 def sparse_attn_decode(q, kv_fp4, kv_scale, row_off, lens, max_len, sel_pos, sel_len, k, window,

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "csa2.h"
+#include "csa2_measure.h"
 
 namespace csa2 {
 

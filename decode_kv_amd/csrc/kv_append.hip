@@ -52,17 +52,13 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t mag, int b) {
     return c;
 }
 
-__global__ __launch_bounds__(kAppendThreads) void kv_append_fp4_kernel(
-    const uint16_t* __restrict__ x, const long long* __restrict__ dst_row, int n, int D,
-    uint8_t* __restrict__ kv_fp4, uint8_t* __restrict__ kv_scale) {
-    const int wave = threadIdx.x / kWave;
+// Quantise one row of D bf16 values (D % 32 == 0) with one wavefront: lane l
+// owns elements [8l, 8l+8) of each 512-wide chunk (one 16-byte load), four
+// lanes one 32-element block.
+__device__ __forceinline__ void quantise_row_fp4(const uint16_t* __restrict__ xr, int D,
+                                                 uint8_t* __restrict__ codes_row,
+                                                 uint8_t* __restrict__ scale_row) {
     const int l = lane_id();
-    const long long r = (long long)blockIdx.x * (kAppendThreads / kWave) + wave;
-    if (r >= n) return;
-    const long long dst = dst_row[r];
-    const uint16_t* xr = x + r * (long long)D;
-    uint8_t* codes_row = kv_fp4 + dst * (long long)(D / 2);
-    uint8_t* scale_row = kv_scale + dst * (long long)(D / 32);
     for (int base = 0; base < D; base += 512) {
         const int e0 = base + 8 * l;
         const bool active = e0 < D;  // D % 32 == 0: whole 4-lane groups
@@ -96,6 +92,42 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_fp4_kernel(
     }
 }
 
+__global__ __launch_bounds__(kAppendThreads) void kv_append_fp4_kernel(
+    const uint16_t* __restrict__ x, const long long* __restrict__ dst_row, int n, int D,
+    uint8_t* __restrict__ kv_fp4, uint8_t* __restrict__ kv_scale) {
+    const int wave = threadIdx.x / kWave;
+    const long long r = (long long)blockIdx.x * (kAppendThreads / kWave) + wave;
+    if (r >= n) return;
+    const long long dst = dst_row[r];
+    quantise_row_fp4(x + r * (long long)D, D, kv_fp4 + dst * (long long)(D / 2),
+                     kv_scale + dst * (long long)(D / 32));
+}
+
+// One workgroup per sequence b: the token's FP4 row of every layer (wave w
+// takes layers w, w + 4, ...) and its index key go to row row_off[b] + len[b];
+// after a barrier, thread 0 advances len[b].  Only this workgroup reads or
+// writes len[b], so the old length is read before the new one is stored.
+__global__ __launch_bounds__(kAppendThreads) void append_token_kernel(
+    const uint16_t* __restrict__ x, const int8_t* __restrict__ key_rows,
+    const long long* __restrict__ row_off, int* __restrict__ len, int B, int n_layers,
+    long long layer_rows, int D, uint8_t* __restrict__ kv_fp4, uint8_t* __restrict__ kv_scale,
+    int8_t* __restrict__ keys) {
+    const int b = blockIdx.x;
+    const int wave = threadIdx.x / kWave;
+    const int L = len[b];
+    const long long row = row_off[b] + L;
+    if (threadIdx.x < kDk / 16)                       // the 64-byte index key, 16 bytes a thread
+        *reinterpret_cast<u32x4*>(keys + row * kDk + 16 * threadIdx.x) =
+            *reinterpret_cast<const u32x4*>(key_rows + (size_t)b * kDk + 16 * threadIdx.x);
+    for (int layer = wave; layer < n_layers; layer += kAppendThreads / kWave) {
+        const long long dst = layer * layer_rows + row;
+        quantise_row_fp4(x + ((size_t)layer * B + b) * D, D, kv_fp4 + dst * (long long)(D / 2),
+                         kv_scale + dst * (long long)(D / 32));
+    }
+    __syncthreads();                                  // every thread has read len[b]
+    if (threadIdx.x == 0) len[b] = L + 1;
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -116,4 +148,27 @@ extern "C" int csa2_kv_append_fp4(const void* x_bf16, const long long* dst_row, 
                        reinterpret_cast<const uint16_t*>(x_bf16), dst_row, n, D, kv_fp4,
                        kv_scale);
     return launch_status("csa2_kv_append_fp4 launch");
+}
+
+extern "C" int csa2_append_token(const void* x_bf16, const signed char* key_rows,
+                                 const long long* row_off, int* len, int B, int n_layers,
+                                 long long layer_rows, int D, int Dk, unsigned char* kv_fp4,
+                                 unsigned char* kv_scale, signed char* keys, void* stream) {
+    if (B < 0 || n_layers < 0 || layer_rows < 0)
+        return fail(CSA2_ERR_INVALID, "csa2_append_token: negative size");
+    if (B == 0) return CSA2_OK;
+    if (!key_rows || !row_off || !len || !keys || (n_layers > 0 && (!x_bf16 || !kv_fp4 || !kv_scale)))
+        return fail(CSA2_ERR_INVALID, "csa2_append_token: null pointer");
+    if (Dk != kDk) return fail(CSA2_ERR_UNSUPPORTED, "csa2_append_token: Dk must be 64");
+    if (D <= 0 || D % 32 != 0) return fail(CSA2_ERR_INVALID, "csa2_append_token: D %% 32 != 0");
+    if (B > 65535) return fail(CSA2_ERR_UNSUPPORTED, "csa2_append_token: B > 65535");
+    if (!aligned(x_bf16, 16) || !aligned(key_rows, 16) || !aligned(keys, 16) ||
+        !aligned(kv_fp4, 4) || !aligned(row_off, 8) || !aligned(len, 4))
+        return fail(CSA2_ERR_INVALID, "csa2_append_token: misaligned pointer");
+    hipLaunchKernelGGL(append_token_kernel, dim3(B), dim3(kAppendThreads), 0,
+                       reinterpret_cast<hipStream_t>(stream),
+                       reinterpret_cast<const uint16_t*>(x_bf16),
+                       reinterpret_cast<const int8_t*>(key_rows), row_off, len, B, n_layers,
+                       layer_rows, D, kv_fp4, kv_scale, reinterpret_cast<int8_t*>(keys));
+    return launch_status("csa2_append_token launch");
 }

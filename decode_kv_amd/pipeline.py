@@ -6,8 +6,9 @@ V4.1-Flash 552B runs like 16B (CED)", "Act 2"): a Full layer scores the whole
 context into a pool and selects from it, a Reindex layer re-scores the most
 recent Full layer's pool, a Reuse layer attends with the most recent
 selection.  Every layer then attends over its selection plus the window.
-With appends, the new token's FP4 rows (every layer) and index key are written
-first and the lengths advance, so the token attends to itself.
+With appends, one library call first writes the new token's FP4 rows (every
+layer) and index key at the device-side length and advances it, so the token
+attends to itself.
 """
 from __future__ import annotations
 
@@ -15,6 +16,27 @@ import torch
 
 from . import csa2
 from .workloads import KV_POOL_ROWS, Case
+
+
+def copy_inputs(dst: dict, src: dict, stream=None):
+    """Copy one step's inputs (as returned by Engine.step_inputs) into the
+    buffers of another, e.g. the static inputs of a captured step."""
+    ctx = torch.cuda.stream(stream) if stream is not None else None
+    if ctx is not None:
+        ctx.__enter__()
+    try:
+        for key, v in src.items():
+            if isinstance(v, dict):
+                for l, t in v.items():
+                    dst[key][l].copy_(t, non_blocking=True)
+            elif isinstance(v, list):
+                for a, t in zip(dst[key], v):
+                    a.copy_(t, non_blocking=True)
+            else:
+                dst[key].copy_(v, non_blocking=True)
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
 
 
 class Engine:
@@ -90,28 +112,29 @@ class Engine:
                 inp["idx_q"][l], inp["idx_w"][l] = q.to(self.device), w.to(self.device)
             inp["attn_q"].append(case.attn_q_batch(step, l).to(self.device))
         if wl.append:
+            # the token of step `step` sits at position L0 + step; the library
+            # writes it at the device-side length, which equals that position
+            # when the steps run in order
             pos = [L + step for L in case.lengths]
-            xs, dst = [], []
-            for l in range(wl.n_layers):
-                for b in range(wl.B):
-                    xs.append(case.kv_bf16(l, b, [pos[b]]))
-                    dst.append(l * self.rows + int(case.row_off[b]) + pos[b])
-            inp["app_x"] = torch.cat(xs).to(self.device).contiguous()
-            inp["app_dst"] = torch.tensor(dst, dtype=torch.int64, device=self.device)
-            krow = [int(case.row_off[b]) + pos[b] for b in range(wl.B)]
-            inp["key_idx"] = torch.tensor(krow, dtype=torch.int64, device=self.device)
-            inp["key_rows"] = torch.stack([case.key_row(b, pos[b]) for b in range(wl.B)]).to(self.device)
+            xs = [case.kv_bf16(l, b, [pos[b]]) for l in range(wl.n_layers) for b in range(wl.B)]
+            inp["app_x"] = torch.cat(xs).view(wl.n_layers, wl.B, wl.D).to(self.device).contiguous()
+            inp["key_rows"] = torch.stack([case.key_row(b, pos[b]) for b in range(wl.B)]) \
+                .to(self.device).contiguous()
         return inp
 
     # ---- one step -------------------------------------------------------------
-    def run_step(self, inp: dict, stream=None):
+    def run_step(self, inp: dict, stream=None, mark=None):
+        """Enqueue one decode step on `stream` (torch's current stream if None).
+        mark(name), when given, is called after each library call with the
+        call's kind ("append", "full", "reindex", "select", "attn"); the
+        benchmark records an event there to time the calls one by one."""
         wl = self.wl
         s = stream
+        note = mark if mark is not None else (lambda name: None)
         if wl.append:
-            csa2.kv_append_fp4(inp["app_x"], inp["app_dst"], self.kv_fp4.view(-1, wl.D // 2),
-                               self.kv_scale.view(-1, wl.D // 32), s)
-            self.keys.index_copy_(0, inp["key_idx"], inp["key_rows"])
-            self.lens += 1
+            csa2.append_token(inp["app_x"], inp["key_rows"], self.row_off, self.lens,
+                              self.kv_fp4, self.kv_scale, self.keys, s)
+            note("append")
         src = None
         for l, kind in enumerate(self.pattern):
             if kind == "F":
@@ -119,17 +142,21 @@ class Engine:
                                 self.lens, self.max_len, self.total_len, wl.window, wl.P,
                                 self.pool_pos, self.pool_score, self.pool_len, self.ws_full, s,
                                 k=wl.k, sel_pos=self.sel_pos[l], sel_len=self.sel_len[l])
+                note("full")
                 src = l
             elif kind == "R":
                 csa2.index_reindex(inp["idx_q"][l], inp["idx_w"][l], self.keys, self.row_off,
                                    self.pool_pos, self.pool_len, self.rscore[l], s)
+                note("reindex")
                 csa2.select_topk(self.rscore[l], self.pool_pos, self.pool_len, wl.k,
                                  self.sel_pos[l], self.sel_len[l], None, s)
+                note("select")
                 src = l
             csa2.sparse_attn_decode(inp["attn_q"][l], self.kv_fp4[l], self.kv_scale[l],
                                     self.row_off, self.lens, self.max_len, self.sel_pos[src],
                                     self.sel_len[src], wl.k, wl.window, wl.sm_scale,
                                     self.out[l], self.lse[l], self.ws_attn, s)
+            note("attn")
         return src
 
     def selection_layer(self, l: int) -> int:

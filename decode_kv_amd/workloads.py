@@ -211,11 +211,17 @@ class Case:
         if not log_distance:
             h = I.hash_stream(key, torch.arange(E, dtype=torch.int64))
             return torch.argsort(h, stable=True)[:n].numpy().astype(np.int64)
+        if n == E:
+            # every eligible position is planted (a short sequence); the draw
+            # below never reaches distance L, i.e. position 0
+            return np.arange(E, dtype=np.int64)
         W = self.wl.window
         L = E + W
         out, seen, i = [], set(), 0
         lo, hi = math.log(W + 1), math.log(L)
         while len(out) < n:
+            if i > 4 * n * 100_000:
+                raise RuntimeError("planted positions: draw did not finish")
             u = I.uniform01(key, torch.arange(i, i + 4 * n, dtype=torch.int64)).numpy()
             i += 4 * n
             d = np.floor(np.exp(lo + u * (hi - lo))).astype(np.int64)

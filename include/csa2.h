@@ -101,6 +101,40 @@ int csa2_kv_append_fp4(const void* x_bf16, const long long* dst_row, int n, int 
                        unsigned char* kv_fp4, unsigned char* kv_scale, void* stream);
 
 /*
+ * csa2_append_token -- one decode step's cache update: each sequence's new
+ * token is written into the index-key cache and into every layer's FP4 KV
+ * cache, and the sequence's length advances by one.  For sequence b, with
+ * L = len[b] as stored on the device and row r = row_off[b] + L:
+ *   keys[r][:]                      = key_rows[b][:]
+ *   FP4 row l * layer_rows + r      = quantise(x_bf16[l][b][:])  for each layer l
+ *   len[b]                          = L + 1
+ * The quantisation is exactly that of csa2_kv_append_fp4.  The token is the
+ * newest position of the sequence, so the layers that run afterwards attend
+ * to it as part of the window.  Because the row follows from len on the
+ * device, a captured step appends at the next position on every replay.
+ * ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 3": the main KV cache
+ * is kept in 4-bit floating point; the order "write, then attend" is this
+ * library's reading.)
+ *   x_bf16   [n_layers][B][D] bf16, 16-byte aligned (may be NULL when n_layers == 0).
+ *   key_rows [B][Dk] int8, 16-byte aligned.
+ *   row_off  [B] int64 (device); len [B] int32 (device, read and advanced).
+ *   layer_rows  rows per layer of kv_fp4 / kv_scale (layer l's row r is row
+ *            l * layer_rows + r of the arrays).
+ *   kv_fp4   [n_layers * layer_rows][D/2] uint8, 4-byte aligned;
+ *   kv_scale [n_layers * layer_rows][D/32] uint8.
+ *   keys     index-key cache [rows][Dk] int8, 16-byte aligned.
+ * The caller guarantees that row row_off[b] + len[b] belongs to sequence b
+ * (its reserved rows are not exhausted); the library does not check it.
+ * Errors: INVALID for null pointers, negative sizes, D % 32 != 0 or a
+ * misaligned pointer; UNSUPPORTED for Dk != 64 or B > 65535.  B == 0 is a
+ * no-op.
+ */
+int csa2_append_token(const void* x_bf16, const signed char* key_rows,
+                      const long long* row_off, int* len, int B, int n_layers,
+                      long long layer_rows, int D, int Dk, unsigned char* kv_fp4,
+                      unsigned char* kv_scale, signed char* keys, void* stream);
+
+/*
  * csa2_index_full -- Full mode: score every eligible position of each
  * sequence and keep the first P_eff = min(P, E_b) positions under the rank
  * order as the candidate pool.

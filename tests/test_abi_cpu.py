@@ -1,6 +1,7 @@
 """Host-side checks of the C-ABI library without a GPU: it loads, exports
 every function the header declares, sizes workspaces, and rejects invalid
-arguments before launching anything."""
+arguments before launching anything.  Every call here fails validation (the
+addresses are fake), so nothing is ever launched, also on a machine with a GPU."""
 import ctypes
 import os
 
@@ -19,8 +20,8 @@ def lib():
 
 def test_exports_every_header_function(lib):
     names = csa2.header_functions()
-    assert {"csa2_kv_append_fp4", "csa2_index_full", "csa2_index_score", "csa2_index_reindex",
-            "csa2_select_topk",
+    assert {"csa2_kv_append_fp4", "csa2_append_token", "csa2_index_full", "csa2_index_score",
+            "csa2_index_reindex", "csa2_select_topk",
             "csa2_sparse_attn_decode", "csa2_workspace_bytes", "csa2_last_error"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
@@ -29,8 +30,7 @@ def test_exports_every_header_function(lib):
 def test_binding_matches_header_parameters(lib):
     """Every declaration's parameter count equals the ctypes binding's."""
     import re
-    src = re.sub(r"/\*.*?\*/", "", open(csa2.HEADER).read(), flags=re.S)
-    decls = dict(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", src))
+    decls = dict(re.findall(r"\b(csa2_[a-z0-9_]+)\s*\(([^)]*)\)\s*;", csa2.header_source()))
     assert "csa2_index_full" in decls and "csa2_sparse_attn_decode" in decls
     for name, params in decls.items():
         params = params.strip()
@@ -38,6 +38,18 @@ def test_binding_matches_header_parameters(lib):
         argtypes = getattr(lib, name).argtypes
         assert argtypes is not None, name
         assert len(argtypes) == n, (name, len(argtypes), n)
+
+
+def test_stream_read_rejects_bad_arguments(lib):
+    f = lib.csa2_stream_read
+    assert lib.csa2_stream_read_sink_words(0) == 0
+    assert lib.csa2_stream_read_sink_words(1 << 16) == 1
+    assert lib.csa2_stream_read_sink_words((1 << 26) + 16) == 1025
+    assert f(None, 0, None, 0, None) == csa2.CSA2_OK                   # nothing to read
+    assert f(None, 1 << 16, 256, 1, None) == csa2.CSA2_ERR_INVALID
+    assert f(264, 1 << 16, 256, 1, None) == csa2.CSA2_ERR_INVALID      # src not 16-aligned
+    assert f(256, (1 << 16) + 4, 256, 2, None) == csa2.CSA2_ERR_INVALID
+    assert f(256, 1 << 20, 256, 15, None) == csa2.CSA2_ERR_WORKSPACE   # needs 16 words
 
 
 def test_version_and_error_text(lib):
@@ -70,6 +82,36 @@ def test_append_rejects_bad_arguments(lib):
     assert f(16, 16, 4, 500, 16, 16, None) == csa2.CSA2_ERR_INVALID        # D % 32
     assert f(18, 16, 4, 512, 16, 16, None) == csa2.CSA2_ERR_INVALID        # misaligned
     assert f(16, 16, -1, 512, 16, 16, None) == csa2.CSA2_ERR_INVALID
+
+
+def test_append_token_rejects_bad_arguments(lib):
+    f = lib.csa2_append_token
+    #      x    keys_in row_off len  B  nl  layer_rows D   Dk  kv   sc   keys stream
+    ok = [256, 256, 256, 256, 2, 20, 1 << 20, 512, 64, 256, 256, 256, None]
+    assert f(*ok[:4], 0, *ok[5:]) == csa2.CSA2_OK                       # B == 0: no-op
+    for i in (1, 2, 3, 11):                                             # always needed
+        bad = list(ok)
+        bad[i] = None
+        assert f(*bad) == csa2.CSA2_ERR_INVALID and "null" in csa2.last_error(), i
+    for i in (0, 9, 10):                                                # needed for layers
+        bad = list(ok)
+        bad[i] = None
+        assert f(*bad) == csa2.CSA2_ERR_INVALID, i
+    # no layers: the bf16 rows and the FP4 arrays may be NULL (the call then
+    # stops at the next check, Dk, so nothing is launched with these fake addresses)
+    bad = list(ok)
+    bad[0], bad[9], bad[10], bad[5], bad[8] = None, None, None, 0, 32
+    assert f(*bad) == csa2.CSA2_ERR_UNSUPPORTED
+    for i, v, code in [(4, -1, csa2.CSA2_ERR_INVALID), (5, -1, csa2.CSA2_ERR_INVALID),
+                       (6, -1, csa2.CSA2_ERR_INVALID), (7, 500, csa2.CSA2_ERR_INVALID),
+                       (8, 32, csa2.CSA2_ERR_UNSUPPORTED), (4, 70000, csa2.CSA2_ERR_UNSUPPORTED),
+                       (0, 264, csa2.CSA2_ERR_INVALID), (1, 264, csa2.CSA2_ERR_INVALID),
+                       (11, 264, csa2.CSA2_ERR_INVALID), (9, 258, csa2.CSA2_ERR_INVALID),
+                       (2, 260, csa2.CSA2_ERR_INVALID), (3, 258, csa2.CSA2_ERR_INVALID)]:
+        bad = list(ok)
+        bad[i] = v
+        assert f(*bad) == code, (i, v)
+        assert "csa2_append_token" in csa2.last_error()
 
 
 def _full(lib, **kw):

@@ -129,6 +129,48 @@ def test_kv_append_wide_rows():
         assert np.array_equal(kv.cpu().numpy(), c) and np.array_equal(sc.cpu().numpy(), s)
 
 
+@pytest.mark.parametrize("D", [512, 96])
+def test_append_token_bitexact(D):
+    """Three decode-step appends into a batch with ragged lengths (0 to 1,000,
+    gaps between the sequences' rows): every layer's FP4 row and the index key
+    land at row_off[b] + len[b], quantised exactly as the oracle does, nothing
+    else changes, and each length advances by one per call."""
+    rng = np.random.default_rng(41 + D)
+    B, nl = 5, 3
+    lens0 = [0, 7, 129, 1000, 3]
+    caps = [L + 4 for L in lens0]
+    row_off, cur = [], 0
+    for c in caps:
+        cur += 2
+        row_off.append(cur)
+        cur += c
+    rows = cur + 2
+    kv = torch.full((nl, rows, D // 2), 0xEE, dtype=torch.uint8, device=DEV)
+    sc = torch.full((nl, rows, D // 32), 0xEE, dtype=torch.uint8, device=DEV)
+    keys = torch.full((rows, 64), 85, dtype=torch.int8, device=DEV)
+    lens = torch.tensor(lens0, dtype=torch.int32, device=DEV)
+    ro = torch.tensor(row_off, dtype=torch.int64, device=DEV)
+    want_kv, want_sc, want_keys = kv.cpu().numpy(), sc.cpu().numpy(), keys.cpu().numpy()
+    for step in range(3):
+        g = rng.standard_normal((nl, B, D)) * 2.0 ** rng.integers(-40, 40, size=(nl, B, 1))
+        x = (g.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+        kr = rng.integers(-127, 128, size=(B, 64)).astype(np.int8)
+        csa2.append_token(torch.from_numpy(x.view(np.int16)).to(DEV).view(torch.bfloat16),
+                          torch.from_numpy(kr).to(DEV), ro, lens, kv, sc, keys)
+        codes, scales = oracle.fp4_quantize(x.reshape(nl * B, D))
+        for b in range(B):
+            r = row_off[b] + lens0[b] + step
+            want_keys[r] = kr[b]
+            for l in range(nl):
+                want_kv[l, r] = codes[l * B + b]
+                want_sc[l, r] = scales[l * B + b]
+    torch.cuda.synchronize()
+    assert np.array_equal(lens.cpu().numpy(), np.array(lens0) + 3)
+    assert np.array_equal(keys.cpu().numpy(), want_keys)
+    assert np.array_equal(kv.cpu().numpy(), want_kv)
+    assert np.array_equal(sc.cpu().numpy(), want_sc)
+
+
 # ---------------------------------------------------------------------------
 # csa2_index_full
 # ---------------------------------------------------------------------------
@@ -676,6 +718,41 @@ def test_workload_ctx_1m():
     eng.run_step(eng.step_inputs(0))
     torch.cuda.synchronize()
     assert torch.equal(out1, eng.out) and torch.equal(pool1, eng.pool_pos)
+
+
+def test_append_steps_side_stream_and_graph_replay():
+    """Decode steps with appends run three ways give identical bits: eagerly
+    on torch's current stream, eagerly on a stream that is not current (every
+    call, the append included, is enqueued on the stream it is given), and as
+    one captured step replayed with fresh inputs, the lengths advancing on the
+    device.  The last step is also checked against the oracle."""
+    wl = W.WORKLOADS["ragged32_1m"].scaled(B=4, len_range=(300, 30000), n_layers=5, steps=4)
+    engs = [pipeline.Engine(W.Case(wl, 3, DEV), DEV) for _ in range(3)]
+    keys_np = engs[0].keys.cpu().numpy()
+    for step in range(wl.steps):
+        engs[0].run_step(engs[0].step_inputs(step))
+    side = torch.cuda.Stream()
+    for step in range(wl.steps):
+        inp = engs[1].step_inputs(step)
+        side.wait_stream(torch.cuda.current_stream())
+        engs[1].run_step(inp, stream=side)
+        torch.cuda.current_stream().wait_stream(side)
+    static = engs[2].step_inputs(0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        engs[2].run_step(static)
+    for step in range(wl.steps):
+        pipeline.copy_inputs(static, engs[2].step_inputs(step))
+        graph.replay()
+    torch.cuda.synchronize()
+    names = ["lens", "keys", "kv_fp4", "kv_scale", "pool_pos", "pool_score", "pool_len",
+             "rscore", "sel_pos", "sel_len", "out", "lse"]
+    for e in engs[1:]:
+        for n in names:
+            assert torch.equal(getattr(engs[0], n), getattr(e, n)), n
+    assert engs[0].lens.cpu().tolist() == W.Case(wl, 3, "cpu").lengths_at(wl.steps - 1)
+    check_engine_step(engs[0], W.Case(wl, 3, "cpu"), wl.steps - 1, [0, 3], keys_np)
 
 
 def test_workload_ragged32_sampled():

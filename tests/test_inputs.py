@@ -79,3 +79,19 @@ def test_log_distance_planting():
     assert d.min() >= 129
     # log-uniform distances: roughly equal counts per decade
     assert (d < 1000).sum() > 200 and (d > 10000).sum() > 200
+
+
+def test_planted_positions_of_short_sequences():
+    """Sequences with fewer eligible positions than planted keys plant every
+    eligible position (the log-distance draw cannot reach position 0), and
+    one more eligible position than planted keys still finishes."""
+    wl = W.WORKLOADS["ragged32_1m"].scaled(B=2, len_range=(200, 400), n_layers=1)
+    c = W.Case(wl, 3, "cpu")
+    for b in range(wl.B):
+        E = max(0, c.lengths[b] - wl.window)
+        pos, rows = c.planted(b)
+        assert sorted(pos.tolist()) == list(range(min(E, wl.n_planted)))
+        assert rows.shape == (len(pos), wl.Dk)
+    wl2 = W.WORKLOADS["ctx_1m"].scaled(L=wl.n_planted + 1 + wl.window, n_planted=wl.n_planted)
+    pos, _ = W.Case(wl2, 0, "cpu").planted(0)
+    assert len(set(pos.tolist())) == wl.n_planted and pos.max() <= wl.n_planted

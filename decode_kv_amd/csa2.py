@@ -69,6 +69,9 @@ def lib():
         L.csa2_stream_read_sink_words.argtypes = [SZ]
         L.csa2_stream_read.restype = I
         L.csa2_stream_read.argtypes = [V, SZ, V, SZ, V]
+        L.csa2_sparse_attn_decode_static.restype = I
+        L.csa2_sparse_attn_decode_static.argtypes = [V, V, V, V, V, LL, V, V, I, I, I, I, I, F,
+                                                     V, V, V]
         L.csa2_sparse_attn_decode.restype = I
         L.csa2_sparse_attn_decode.argtypes = [V, V, V, V, V, LL, V, V, I, I, I, I, I, F, V, V,
                                               V, SZ, V]
@@ -204,3 +207,18 @@ def sparse_attn_decode(q, kv_fp4, kv_scale, row_off, lens, max_len, sel_pos, sel
                                          int(max_len), _p(sel_pos), _p(sel_len), B, Hq, D, k,
                                          window, float(sm_scale), _p(out), _p(lse), _p(ws),
                                          nbytes, _s(stream)))
+
+
+ATTN_STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def sparse_attn_decode_static(q, kv_fp4, kv_scale, row_off, lens, max_len, sel_pos, sel_len, k,
+                              window, sm_scale, out, lse, stream=None):
+    """csa2_sparse_attn_decode_static: no workspace argument (the library's
+    per-GPU static scratch holds the split partials)."""
+    B, Hq, D = q.shape
+    _check("csa2_sparse_attn_decode_static",
+           lib().csa2_sparse_attn_decode_static(_p(q), _p(kv_fp4), _p(kv_scale), _p(row_off),
+                                                _p(lens), int(max_len), _p(sel_pos),
+                                                _p(sel_len), B, Hq, D, k, window,
+                                                float(sm_scale), _p(out), _p(lse), _s(stream)))

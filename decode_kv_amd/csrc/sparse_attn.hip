@@ -33,6 +33,8 @@
 // log-sum-exp combine.
 #include <math.h>
 
+#include <mutex>
+
 #include "abi_common.h"
 #include "common.h"
 
@@ -561,40 +563,38 @@ size_t sparse_attn_ws_bytes(int B, int Hq, int D, int k, int window) {
     return attn_ws_layout(B, Hq, ns, nullptr, nullptr, nullptr);
 }
 
-}  // namespace csa2
-
-using namespace csa2;
-
-extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* kv_fp4,
-                                       const unsigned char* kv_scale, const long long* row_off,
-                                       const int* len, long long max_len, const int* sel_pos,
-                                       const int* sel_len, int B, int Hq, int D, int k,
-                                       int window, float sm_scale, float* out, float* lse,
-                                       void* ws, size_t ws_bytes, void* stream) {
+// The entry points' shared body: argument checks, then the attention and
+// combine launches with the split partials in the scratch that get_ws(need,
+// &ptr) supplies once the sizes are known to be valid.  fn names the entry
+// point in error messages.
+template <typename GetWs>
+static int attn_decode(const char* fn, const void* q_bf16, const unsigned char* kv_fp4,
+                       const unsigned char* kv_scale, const long long* row_off, const int* len,
+                       long long max_len, const int* sel_pos, const int* sel_len, int B, int Hq,
+                       int D, int k, int window, float sm_scale, float* out, float* lse,
+                       GetWs get_ws, void* stream) {
     if (B < 0 || max_len < 0 || k < 0 || window < 0)
-        return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: negative size");
+        return fail(CSA2_ERR_INVALID, "%s: negative size", fn);
     if (B == 0) return CSA2_OK;
     if (!q_bf16 || !kv_fp4 || !kv_scale || !row_off || !len || !sel_len || !out ||
         (k > 0 && !sel_pos))
-        return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: null pointer");
-    if (D != kAttnD) return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: D must be 512");
+        return fail(CSA2_ERR_INVALID, "%s: null pointer", fn);
+    if (D != kAttnD) return fail(CSA2_ERR_UNSUPPORTED, "%s: D must be 512", fn);
     if (Hq < 16 || Hq % 16 != 0)
-        return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: Hq must be a positive multiple of 16");
-    if (B > 65535 || Hq > 1024) return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: B or Hq too large");
+        return fail(CSA2_ERR_INVALID, "%s: Hq must be a positive multiple of 16", fn);
+    if (B > 65535 || Hq > 1024) return fail(CSA2_ERR_UNSUPPORTED, "%s: B or Hq too large", fn);
     // the kernel reads a row's codes in 16-byte pieces and its scale bytes in
     // pairs, and stores the outputs in 16-byte pieces
     if (!aligned(q_bf16, 16) || !aligned(kv_fp4, 16) || !aligned(kv_scale, 2) ||
         !aligned(out, 16) || !aligned(row_off, 8) || !aligned(len, 4) || !aligned(sel_len, 4) ||
         !aligned(sel_pos, 4) || !aligned(lse, 4))
-        return fail(CSA2_ERR_INVALID, "csa2_sparse_attn_decode: misaligned pointer");
+        return fail(CSA2_ERR_INVALID, "%s: misaligned pointer", fn);
     if ((long long)k + window > kAttnMaxRows)
-        return fail(CSA2_ERR_UNSUPPORTED, "csa2_sparse_attn_decode: k + window > %d", kAttnMaxRows);
+        return fail(CSA2_ERR_UNSUPPORTED, "%s: k + window > %d", fn, kAttnMaxRows);
     const int tpw = sparse_attn_tiles_per_wg(B, Hq, k, window);
     const int ns = sparse_attn_splits(B, Hq, k, window);
-    const size_t need = sparse_attn_ws_bytes(B, Hq, D, k, window);
-    if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
-        return fail(CSA2_ERR_WORKSPACE,
-                    "csa2_sparse_attn_decode: workspace needs %zu bytes (256-aligned)", need);
+    void* ws = nullptr;
+    if (int e = get_ws(sparse_attn_ws_bytes(B, Hq, D, k, window), &ws)) return e;
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
     float* part_o = nullptr;
     float* part_ml = nullptr;
@@ -613,7 +613,7 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
         case 2: wide ? launch(sparse_attn_kernel<2, true>) : launch(sparse_attn_kernel<2, false>); break;
         default: wide ? launch(sparse_attn_kernel<4, true>) : launch(sparse_attn_kernel<4, false>); break;
     }
-    if (int e = launch_status("csa2_sparse_attn_decode launch")) return e;
+    if (int e = launch_status(fn)) return e;
     if (ns > 1) {
         const dim3 cg(8 * pr * kHeadsPerWg), cb(128);
         if (ns <= 8)
@@ -624,7 +624,96 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
             hipLaunchKernelGGL(attn_combine_kernel<24>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B);
         else
             hipLaunchKernelGGL(attn_combine_kernel<32>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B);
-        return launch_status("csa2_sparse_attn_decode combine launch");
+        return launch_status(fn);
     }
     return CSA2_OK;
+}
+
+// ---- the allocation-free variant ------------------------------------------------
+// The split partials live in a file-scope device array of kAttnStaticScratch
+// bytes.  In host code the array's name is only a stand-in: its device
+// address is looked up once per device, with that device current, and that
+// address is what the kernels receive.
+constexpr size_t kAttnStaticScratch = CSA2_ATTN_STATIC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+
+}  // namespace csa2
+
+static __device__ __align__(256) unsigned char scratch[csa2::kAttnStaticScratch];
+
+namespace csa2 {
+
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (the device `stream`
+// runs on must be the current one).
+static int static_scratch(const char* fn, hipStream_t stream, void** out) {
+    int dev = 0;
+    if (int e = hip_status(hipGetDevice(&dev), "hipGetDevice")) return e;
+    if (stream) {
+        hipDevice_t sdev = 0;
+        if (int e = hip_status(hipStreamGetDevice(stream, &sdev), "hipStreamGetDevice")) return e;
+        if ((int)sdev != dev)
+            return fail(CSA2_ERR_INVALID,
+                        "%s: the stream belongs to device %d, not to the current device %d", fn,
+                        (int)sdev, dev);
+    }
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(CSA2_ERR_UNSUPPORTED, "%s: device id %d >= %d", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (int e = hip_status(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)),
+                               "hipGetSymbolAddress(scratch)"))
+            return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return CSA2_OK;
+}
+
+}  // namespace csa2
+
+using namespace csa2;
+
+extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* kv_fp4,
+                                       const unsigned char* kv_scale, const long long* row_off,
+                                       const int* len, long long max_len, const int* sel_pos,
+                                       const int* sel_len, int B, int Hq, int D, int k,
+                                       int window, float sm_scale, float* out, float* lse,
+                                       void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "csa2_sparse_attn_decode";
+    auto caller_ws = [&](size_t need, void** p) -> int {
+        if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+            return fail(CSA2_ERR_WORKSPACE, "%s: workspace needs %zu bytes (256-aligned)", fn,
+                        need);
+        *p = ws;
+        return CSA2_OK;
+    };
+    return attn_decode(fn, q_bf16, kv_fp4, kv_scale, row_off, len, max_len, sel_pos, sel_len, B,
+                       Hq, D, k, window, sm_scale, out, lse, caller_ws, stream);
+}
+
+extern "C" int csa2_sparse_attn_decode_static(const void* q_bf16, const unsigned char* kv_fp4,
+                                              const unsigned char* kv_scale,
+                                              const long long* row_off, const int* len,
+                                              long long max_len, const int* sel_pos,
+                                              const int* sel_len, int B, int Hq, int D, int k,
+                                              int window, float sm_scale, float* out, float* lse,
+                                              void* stream) {
+    const char* fn = "csa2_sparse_attn_decode_static";
+    auto static_ws = [&](size_t need, void** p) -> int {
+        if (need > kAttnStaticScratch)
+            return fail(CSA2_ERR_UNSUPPORTED,
+                        "%s: these sizes need %zu bytes of scratch; the static scratch holds %zu",
+                        fn, need, kAttnStaticScratch);
+        if (need == 0) {
+            *p = nullptr;
+            return CSA2_OK;
+        }
+        return static_scratch(fn, reinterpret_cast<hipStream_t>(stream), p);
+    };
+    return attn_decode(fn, q_bf16, kv_fp4, kv_scale, row_off, len, max_len, sel_pos, sel_len, B,
+                       Hq, D, k, window, sm_scale, out, lse, static_ws, stream);
 }

@@ -265,6 +265,34 @@ int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* kv_fp4,
                             float sm_scale, float* out, float* lse,
                             void* ws, size_t ws_bytes, void* stream);
 
+/* Bytes of device scratch behind csa2_sparse_attn_decode_static (per GPU). */
+#define CSA2_ATTN_STATIC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * csa2_sparse_attn_decode_static -- csa2_sparse_attn_decode for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  The arguments and results are those
+ * of csa2_sparse_attn_decode without ws / ws_bytes (the same kernels run); the
+ * split-K partials go to a scratch array of CSA2_ATTN_STATIC_SCRATCH_BYTES
+ * (32 MiB) that the library keeps in device memory, one per GPU, from the
+ * library's first use on that GPU until the process ends.  The call allocates
+ * nothing (no hipMalloc, no allocating library routine).
+ *  - Sizes whose partials need more than that
+ *    (csa2_workspace_bytes(CSA2_OP_SPARSE_ATTN, ...) > 32 MiB, e.g. more than
+ *    about 50 sequences of 64 heads with k = 512 and window 128) are rejected
+ *    with CSA2_ERR_UNSUPPORTED and nothing is launched.
+ *  - `stream` must belong to the current device (else CSA2_ERR_INVALID).
+ *  - Every call on one GPU uses that GPU's one scratch array: calls that
+ *    overlap in time on one GPU (streams not ordered with each other) race and
+ *    their results are undefined.  Calls ordered on one stream are safe.  The
+ *    scratch needs no initialisation; it keeps the last call's partials.
+ */
+int csa2_sparse_attn_decode_static(const void* q_bf16, const unsigned char* kv_fp4,
+                                   const unsigned char* kv_scale, const long long* row_off,
+                                   const int* len, long long max_len, const int* sel_pos,
+                                   const int* sel_len, int B, int Hq, int D, int k, int window,
+                                   float sm_scale, float* out, float* lse, void* stream);
+
 
 #ifdef __cplusplus
 }

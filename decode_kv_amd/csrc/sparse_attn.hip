@@ -115,9 +115,35 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 // TPW tiles in a second one, held in registers until their tile's turn.
 // The arguments the first round trip needs (the sizes, then the pointers it
 // loads from) fill the 64 bytes that arrive in SGPRs with the wave.
+// Placement flags of the attention and combine launches.
+constexpr int kPlaceSeq = 1;     // sequence b (all head groups and splits) on XCD b mod 8
+constexpr int kPlacePlain = 2;   // split partials stored with plain stores (they fit in L2)
+
+// Workgroup i runs on XCD i mod 8.  Pair-major placement puts (sequence, head
+// group) pair p on XCD p mod 8: at one sequence its four head groups use four
+// XCDs.  Sequence-major placement puts every workgroup of sequence b on XCD
+// b mod 8, so that XCD's L2 fetches each FP4 row once for all head groups and
+// holds the split partials for the combine.  Returns false past the last pair.
+__device__ __forceinline__ bool attn_place(int flags, int B, int HG, int n_splits, int& b,
+                                           int& hz, int& split) {
+    const int xid = blockIdx.x & 7, xslot = blockIdx.x >> 3;
+    const int lp = xslot / n_splits;
+    split = xslot - lp * n_splits;
+    if (flags & kPlaceSeq) {
+        const int bi = lp / HG;
+        hz = lp - bi * HG;
+        b = bi * 8 + xid;
+        return b < B;
+    }
+    const int pair = lp * 8 + xid;
+    b = pair / HG;
+    hz = pair - b * HG;
+    return pair < B * HG;
+}
+
 template <int TPW, bool WIDE>
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
-    int B, int Hq, int k, int window, int n_splits, float scale_log2,
+    int B, int Hq, int k, int window, int n_splits, float scale_log2, int flags,
     const long long* __restrict__ row_off, const int* __restrict__ len,
     const int* __restrict__ sel_len, const int* __restrict__ sel_pos,
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ kv_fp4,
@@ -132,15 +158,12 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     // per wave: the largest scale byte of the rows it dequantises (all tiles)
     __shared__ int s_e[kAttnThreads / kWave];
 
-    // workgroup i runs on XCD i mod 8: all splits of one (sequence, head group)
-    // pair go to the same XCD, where they share the query rows in L2 and the
-    // combine of that pair (placed the same way) finds their partials
-    const int HG = Hq / kHeadsPerWg, npairs = B * HG;
-    const int xid = blockIdx.x & 7, xslot = blockIdx.x >> 3;
-    const int xr = xslot / n_splits, split = xslot - xr * n_splits;
-    const int pair = xr * 8 + xid;
-    if (pair >= npairs) return;
-    const int b = pair / HG, hz = pair - b * HG;
+    // all splits of one (sequence, head group) pair run on one XCD, where they
+    // share the query rows in L2 and the combine of that pair (placed the same
+    // way) finds their partials
+    const int HG = Hq / kHeadsPerWg;
+    int b, hz, split;
+    if (!attn_place(flags, B, HG, n_splits, b, hz, split)) return;
     const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
     const int g = l >> 4, c16 = l & 15;
     const int head = hz * kHeadsPerWg + c16;      // this lane's head
@@ -200,13 +223,13 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
             return;
         }
         // split partial: unnormalised O, running max and sum.  Only the combine
-        // kernel reads them.  With at most one pair per XCD they stay in that
-        // XCD's L2 for it; with more, they are stored non-temporal (streamed past
-        // the caches instead of waiting in L2 for the end-of-kernel write-back).
+        // kernel reads them.  When they fit in the XCD's L2 they stay there for
+        // it; otherwise they are stored non-temporal (streamed past the caches
+        // instead of waiting in L2 for the end-of-kernel write-back).
         const size_t base = ((size_t)b * n_splits + split) * Hq + head;
         float* ob = part_o + base * kAttnD + d0;
         const f32x4 ml = {m_fin, l_fin, (float)e_fin, 0.f};
-        if (npairs <= 8) {                                   // uniform
+        if (flags & kPlacePlain) {                           // uniform
 #pragma unroll
             for (int nb = 0; nb < kNb; ++nb) *reinterpret_cast<f32x4*>(ob + 16 * nb) = oo[nb];
             if (wave == 0 && g == 0) *reinterpret_cast<f32x4*>(part_ml + base * 4) = ml;
@@ -418,14 +441,16 @@ __global__ __launch_bounds__(128) void attn_combine_kernel(const float* part_o,
                                                            const float* part_ml,
                                                            int Hq, int n_splits,
                                                            float* __restrict__ out,
-                                                           float* __restrict__ lse, int B) {
+                                                           float* __restrict__ lse, int B,
+                                                           int flags) {
     __shared__ __attribute__((aligned(16))) float s_w[kAttnMaxSplits + 32];   // zero-padded to CH
     __shared__ float s_red[3][2];
-    const int HG = Hq / kHeadsPerWg, npairs = B * HG;
-    const int xid = blockIdx.x & 7, xslot = blockIdx.x >> 3;
-    const int pair = (xslot >> 4) * 8 + xid;
-    if (pair >= npairs) return;
-    const int b = pair / HG, h = (pair - b * HG) * kHeadsPerWg + (xslot & 15), tid = threadIdx.x;
+    // the combine of head h of a pair runs on the pair's XCD (attn_place with
+    // one "split" per head of the pair)
+    const int HG = Hq / kHeadsPerWg;
+    int b, hz, hl;
+    if (!attn_place(flags, B, HG, kHeadsPerWg, b, hz, hl)) return;
+    const int h = hz * kHeadsPerWg + hl, tid = threadIdx.x;
     const size_t row0 = (size_t)b * n_splits * Hq + h;          // split s at row0 + s * Hq
     f32x4 os[CH];
 #pragma unroll
@@ -600,12 +625,20 @@ static int attn_decode(const char* fn, const void* q_bf16, const unsigned char* 
     float* part_ml = nullptr;
     if (ns > 1) attn_ws_layout(B, Hq, ns, reinterpret_cast<char*>(ws), &part_o, &part_ml);
     const float scale_log2 = sm_scale * 1.4426950408889634f;
-    const int npairs = B * (Hq / kHeadsPerWg), pr = (npairs + 7) / 8;
+    const int HG = Hq / kHeadsPerWg, npairs = B * HG;
+    // sequence-major placement from 8 sequences on; plain partial stores when
+    // one XCD's share of the partials fits in 3 of its 4 MB of L2
+    const bool seq = B >= 8;
+    const long long per_xcd = seq ? (long long)((B + 7) / 8) * HG : (npairs + 7) / 8;
+    const bool plain = per_xcd * ns * kHeadsPerWg * (kAttnD * 4 + 16) <= (3ll << 20);
+    const int flags = (seq ? kPlaceSeq : 0) | (plain ? kPlacePlain : 0);
+    const int pr = seq ? (int)((B + 7) / 8) * HG : (npairs + 7) / 8;   // slots per XCD / splits
     const dim3 grid(8 * pr * ns), blk(kAttnThreads);
     const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q_bf16);
     auto launch = [&](auto kernel) {
-        hipLaunchKernelGGL(kernel, grid, blk, 0, s, B, Hq, k, window, ns, scale_log2, row_off, len,
-                           sel_len, sel_pos, q16, kv_fp4, kv_scale, part_o, part_ml, out, lse);
+        hipLaunchKernelGGL(kernel, grid, blk, 0, s, B, Hq, k, window, ns, scale_log2, flags,
+                           row_off, len, sel_len, sel_pos, q16, kv_fp4, kv_scale, part_o, part_ml,
+                           out, lse);
     };
     const bool wide = (long long)npairs * ns > kAttnWideWgs;
     switch (tpw) {
@@ -617,13 +650,13 @@ static int attn_decode(const char* fn, const void* q_bf16, const unsigned char* 
     if (ns > 1) {
         const dim3 cg(8 * pr * kHeadsPerWg), cb(128);
         if (ns <= 8)
-            hipLaunchKernelGGL(attn_combine_kernel<8>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B);
+            hipLaunchKernelGGL(attn_combine_kernel<8>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B, flags);
         else if (ns <= 16)
-            hipLaunchKernelGGL(attn_combine_kernel<16>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B);
+            hipLaunchKernelGGL(attn_combine_kernel<16>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B, flags);
         else if (ns <= 24)
-            hipLaunchKernelGGL(attn_combine_kernel<24>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B);
+            hipLaunchKernelGGL(attn_combine_kernel<24>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B, flags);
         else
-            hipLaunchKernelGGL(attn_combine_kernel<32>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B);
+            hipLaunchKernelGGL(attn_combine_kernel<32>, cg, cb, 0, s, part_o, part_ml, Hq, ns, out, lse, B, flags);
         return launch_status(fn);
     }
     return CSA2_OK;

@@ -613,6 +613,16 @@ def test_attention_maximum_rows_and_many_pairs():
                    128, 16)                          # 200 sequences, some empty (wide layout)
 
 
+def test_attention_batched_shapes():
+    """Batches placed sequence-major (8 sequences and more): 65 splits per
+    sequence merged in chunks of 32 by the combine (8 sequences, k = 8,192),
+    12 sequences of 48 heads, ragged lengths with empty sequences and
+    sequences shorter than the window."""
+    attention_case(30, [20000] * 8, 8192, 16)
+    attention_case(31, [700] * 12, 256, 48)
+    attention_case(32, [0, 50, 129, 3000, 0, 640, 12000, 77, 4096, 1], 512, 64)
+
+
 def test_attention_scale_ranges():
     attention_case(20, [4096, 2000], 512, 64, scale_lo=100, scale_hi=150)
     attention_case(21, [4096, 2000], 512, 64, scale_lo=1, scale_hi=1)

@@ -52,18 +52,23 @@ __device__ __forceinline__ uint32_t e2m1_code(uint32_t mag, int b) {
     return c;
 }
 
-// Quantise one row of D bf16 values (D % 32 == 0) with one wavefront: lane l
-// owns elements [8l, 8l+8) of each 512-wide chunk (one 16-byte load), four
-// lanes one 32-element block.
-__device__ __forceinline__ void quantise_row_fp4(const uint16_t* __restrict__ xr, int D,
-                                                 uint8_t* __restrict__ codes_row,
-                                                 uint8_t* __restrict__ scale_row) {
+// Lane l's 16-byte piece of the 512-wide chunk at `base` of a row of D bf16
+// values (elements base + 8l .. + 7; zeros past D, D % 32 == 0).
+__device__ __forceinline__ u32x4 load_chunk(const uint16_t* __restrict__ xr, int D, int base) {
+    const int e0 = base + 8 * lane_id();
+    return e0 < D ? *reinterpret_cast<const u32x4*>(xr + e0) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Quantise and store one 512-wide chunk of a row with one wavefront: lane l
+// owns elements [8l, 8l+8) of the chunk (its piece v), four lanes one
+// 32-element block.
+__device__ __forceinline__ void quantise_chunk(u32x4 v, int D, int base,
+                                               uint8_t* __restrict__ codes_row,
+                                               uint8_t* __restrict__ scale_row) {
     const int l = lane_id();
-    for (int base = 0; base < D; base += 512) {
+    {
         const int e0 = base + 8 * l;
         const bool active = e0 < D;  // D % 32 == 0: whole 4-lane groups
-        u32x4 v = {0, 0, 0, 0};
-        if (active) v = *reinterpret_cast<const u32x4*>(xr + e0);
         uint32_t h[8];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -92,6 +97,14 @@ __device__ __forceinline__ void quantise_row_fp4(const uint16_t* __restrict__ xr
     }
 }
 
+// Quantise one row of D bf16 values with one wavefront, chunk by chunk.
+__device__ __forceinline__ void quantise_row_fp4(const uint16_t* __restrict__ xr, int D,
+                                                 uint8_t* __restrict__ codes_row,
+                                                 uint8_t* __restrict__ scale_row) {
+    for (int base = 0; base < D; base += 512)
+        quantise_chunk(load_chunk(xr, D, base), D, base, codes_row, scale_row);
+}
+
 __global__ __launch_bounds__(kAppendThreads) void kv_append_fp4_kernel(
     const uint16_t* __restrict__ x, const long long* __restrict__ dst_row, int n, int D,
     uint8_t* __restrict__ kv_fp4, uint8_t* __restrict__ kv_scale) {
@@ -103,11 +116,15 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_fp4_kernel(
                      kv_scale + dst * (long long)(D / 32));
 }
 
-// One workgroup per sequence b: the token's FP4 row of every layer (wave w
-// takes layers w, w + 4, ...) and its index key go to row row_off[b] + len[b];
-// after a barrier, thread 0 advances len[b].  Only this workgroup reads or
-// writes len[b], so the old length is read before the new one is stored.
-__global__ __launch_bounds__(kAppendThreads) void append_token_kernel(
+// One workgroup of 16 waves per sequence b: the token's FP4 row of every
+// layer (wave w takes layers w, w + 16, ...) and its index key go to row
+// row_off[b] + len[b]; after a barrier, thread 0 advances len[b].  Only this
+// workgroup reads or writes len[b], so the old length is read before the new
+// one is stored.  A wave issues the loads of its first two rows before it
+// quantises either, so the step pays one load round trip.
+constexpr int kTokenThreads = 1024;
+
+__global__ __launch_bounds__(kTokenThreads) void append_token_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ key_rows,
     const long long* __restrict__ row_off, int* __restrict__ len, int B, int n_layers,
     long long layer_rows, int D, uint8_t* __restrict__ kv_fp4, uint8_t* __restrict__ kv_scale,
@@ -119,11 +136,25 @@ __global__ __launch_bounds__(kAppendThreads) void append_token_kernel(
     if (threadIdx.x < kDk / 16)                       // the 64-byte index key, 16 bytes a thread
         *reinterpret_cast<u32x4*>(keys + row * kDk + 16 * threadIdx.x) =
             *reinterpret_cast<const u32x4*>(key_rows + (size_t)b * kDk + 16 * threadIdx.x);
-    for (int layer = wave; layer < n_layers; layer += kAppendThreads / kWave) {
+    constexpr int NW = kTokenThreads / kWave;
+    const int l0 = wave, l1 = wave + NW;
+    const uint16_t* x0 = x + ((size_t)l0 * B + b) * D;
+    const uint16_t* x1 = x + ((size_t)l1 * B + b) * D;
+    const u32x4 v0 = l0 < n_layers ? load_chunk(x0, D, 0) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 v1 = l1 < n_layers ? load_chunk(x1, D, 0) : u32x4{0u, 0u, 0u, 0u};
+    auto finish = [&](int layer, const uint16_t* xr, u32x4 v) {
         const long long dst = layer * layer_rows + row;
-        quantise_row_fp4(x + ((size_t)layer * B + b) * D, D, kv_fp4 + dst * (long long)(D / 2),
-                         kv_scale + dst * (long long)(D / 32));
-    }
+        uint8_t* cr = kv_fp4 + dst * (long long)(D / 2);
+        uint8_t* sr = kv_scale + dst * (long long)(D / 32);
+        quantise_chunk(v, D, 0, cr, sr);
+        for (int base = 512; base < D; base += 512)
+            quantise_chunk(load_chunk(xr, D, base), D, base, cr, sr);
+    };
+    if (l0 < n_layers) finish(l0, x0, v0);
+    if (l1 < n_layers) finish(l1, x1, v1);
+    for (int layer = wave + 2 * NW; layer < n_layers; layer += NW)
+        quantise_row_fp4(x + ((size_t)layer * B + b) * D, D, kv_fp4 + (layer * layer_rows + row) * (long long)(D / 2),
+                         kv_scale + (layer * layer_rows + row) * (long long)(D / 32));
     __syncthreads();                                  // every thread has read len[b]
     if (threadIdx.x == 0) len[b] = L + 1;
 }
@@ -165,7 +196,7 @@ extern "C" int csa2_append_token(const void* x_bf16, const signed char* key_rows
     if (!aligned(x_bf16, 16) || !aligned(key_rows, 16) || !aligned(keys, 16) ||
         !aligned(kv_fp4, 4) || !aligned(row_off, 8) || !aligned(len, 4))
         return fail(CSA2_ERR_INVALID, "csa2_append_token: misaligned pointer");
-    hipLaunchKernelGGL(append_token_kernel, dim3(B), dim3(kAppendThreads), 0,
+    hipLaunchKernelGGL(append_token_kernel, dim3(B), dim3(kTokenThreads), 0,
                        reinterpret_cast<hipStream_t>(stream),
                        reinterpret_cast<const uint16_t*>(x_bf16),
                        reinterpret_cast<const int8_t*>(key_rows), row_off, len, B, n_layers,

@@ -129,14 +129,15 @@ def test_kv_append_wide_rows():
         assert np.array_equal(kv.cpu().numpy(), c) and np.array_equal(sc.cpu().numpy(), s)
 
 
-@pytest.mark.parametrize("D", [512, 96])
-def test_append_token_bitexact(D):
+@pytest.mark.parametrize("D,nl", [(512, 3), (96, 3), (512, 20), (1024, 40)])
+def test_append_token_bitexact(D, nl):
     """Three decode-step appends into a batch with ragged lengths (0 to 1,000,
-    gaps between the sequences' rows): every layer's FP4 row and the index key
+    gaps between the sequences' rows), 3 to 40 layers (a wave of the kernel
+    takes one, two or three of them): every layer's FP4 row and the index key
     land at row_off[b] + len[b], quantised exactly as the oracle does, nothing
     else changes, and each length advances by one per call."""
-    rng = np.random.default_rng(41 + D)
-    B, nl = 5, 3
+    rng = np.random.default_rng(41 + D + nl)
+    B = 5
     lens0 = [0, 7, 129, 1000, 3]
     caps = [L + 4 for L in lens0]
     row_off, cur = [], 0
@@ -763,6 +764,16 @@ def test_append_steps_side_stream_and_graph_replay():
             assert torch.equal(getattr(engs[0], n), getattr(e, n)), n
     assert engs[0].lens.cpu().tolist() == W.Case(wl, 3, "cpu").lengths_at(wl.steps - 1)
     check_engine_step(engs[0], W.Case(wl, 3, "cpu"), wl.steps - 1, [0, 3], keys_np)
+
+
+def test_workload_ctx_1m_shared_kv():
+    run_workload("ctx_1m_shared", 1)
+
+
+def test_workload_ragged32_shared_kv_sampled():
+    case = W.Case(W.WORKLOADS["ragged32_1m_shared"], 0, "cpu")
+    order = np.argsort(case.lengths)
+    run_workload("ragged32_1m_shared", 2, sorted({int(order[0]), int(order[-1]), 9}))
 
 
 def test_workload_ragged32_sampled():

@@ -66,9 +66,9 @@ def algorithmic_bytes(wl, lengths) -> dict:
         tot["attn"] += wl.n_layers * (272 * (keff + W) + 6 * wl.Hq * wl.D + 4 * keff)
         tot["scan_kernel"] += 64 * E + 65 * wl.H
         if wl.append:
-            # per layer: the bf16 row in, its FP4 codes and scales out; the
-            # 64-byte index key in and out
-            tot["append"] += wl.n_layers * (2 * wl.D + wl.D // 2 + wl.D // 32) + 2 * wl.Dk
+            # per cache (one per layer, or one shared by all): the bf16 row in,
+            # its FP4 codes and scales out; the 64-byte index key in and out
+            tot["append"] += wl.n_kv * (2 * wl.D + wl.D // 2 + wl.D // 32) + 2 * wl.Dk
     tot["step"] = tot["append"] + tot["full"] + tot["select"] + tot["reindex"] + tot["attn"]
     return tot
 

@@ -49,8 +49,8 @@ class Engine:
         self.pattern = wl.pattern
         self.keys = case.keys_all(dev)
         R = self.rows = case.total_rows
-        self.kv_fp4 = torch.empty((wl.n_layers, R, wl.D // 2), dtype=torch.uint8, device=dev)
-        self.kv_scale = torch.empty((wl.n_layers, R, wl.D // 32), dtype=torch.uint8, device=dev)
+        self.kv_fp4 = torch.empty((wl.n_kv, R, wl.D // 2), dtype=torch.uint8, device=dev)
+        self.kv_scale = torch.empty((wl.n_kv, R, wl.D // 32), dtype=torch.uint8, device=dev)
         self.row_off = torch.tensor(case.row_off, dtype=torch.int64, device=dev)
         self.lens = torch.tensor(case.lengths, dtype=torch.int32, device=dev)
         self.max_len = max(case.caps)
@@ -76,7 +76,7 @@ class Engine:
         case, wl = self.case, self.wl
         fp4 = self.kv_fp4.view(-1, wl.D // 2)
         sc = self.kv_scale.view(-1, wl.D // 32)
-        n_needed = wl.n_layers * sum(case.lengths)
+        n_needed = wl.n_kv * sum(case.lengths)
         direct = n_needed < KV_POOL_ROWS // 4
         if not direct:   # quantise the whole pool once, then gather rows
             pool_fp4 = torch.empty((KV_POOL_ROWS, wl.D // 2), dtype=torch.uint8, device=self.device)
@@ -86,7 +86,7 @@ class Engine:
                 x = case.kv_pool_range(first, n, self.device)
                 dst = torch.arange(first, first + n, dtype=torch.int64, device=self.device)
                 csa2.kv_append_fp4(x, dst, pool_fp4, pool_sc)
-        for layer in range(wl.n_layers):
+        for layer in range(wl.n_kv):
             for b in range(wl.B):
                 L0 = case.lengths[b]
                 base = layer * self.rows + int(case.row_off[b])
@@ -116,8 +116,8 @@ class Engine:
             # writes it at the device-side length, which equals that position
             # when the steps run in order
             pos = [L + step for L in case.lengths]
-            xs = [case.kv_bf16(l, b, [pos[b]]) for l in range(wl.n_layers) for b in range(wl.B)]
-            inp["app_x"] = torch.cat(xs).view(wl.n_layers, wl.B, wl.D).to(self.device).contiguous()
+            xs = [case.kv_bf16(l, b, [pos[b]]) for l in range(wl.n_kv) for b in range(wl.B)]
+            inp["app_x"] = torch.cat(xs).view(wl.n_kv, wl.B, wl.D).to(self.device).contiguous()
             inp["key_rows"] = torch.stack([case.key_row(b, pos[b]) for b in range(wl.B)]) \
                 .to(self.device).contiguous()
         return inp
@@ -152,7 +152,8 @@ class Engine:
                                  self.sel_pos[l], self.sel_len[l], None, s)
                 note("select")
                 src = l
-            csa2.sparse_attn_decode(inp["attn_q"][l], self.kv_fp4[l], self.kv_scale[l],
+            kl = wl.kv_layer(l)
+            csa2.sparse_attn_decode(inp["attn_q"][l], self.kv_fp4[kl], self.kv_scale[kl],
                                     self.row_off, self.lens, self.max_len, self.sel_pos[src],
                                     self.sel_len[src], wl.k, wl.window, wl.sm_scale,
                                     self.out[l], self.lse[l], self.ws_attn, s)

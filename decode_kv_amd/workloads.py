@@ -15,6 +15,9 @@ Five workloads, named by what they are:
   ragged32_1m   32 sequences, lengths log-uniform in [4,096, 1,048,576], the
                 20-layer pattern, one append per sequence and layer per step,
                 64 steps, queries re-drawn every step.
+  ctx_1m_shared, ragged32_1m_shared
+                the same with one FP4 latent cache shared by all 20 layers
+                (one append per sequence per step).
 
 Everywhere: window 128, index key dim 64, latent dim 512, softmax scale
 1/sqrt(512).  Nothing here computes any part of the method; the only
@@ -50,6 +53,7 @@ class Workload:
     steps: int
     append: bool
     redraw_queries: bool
+    shared_kv: bool = False                # one FP4 latent cache read by every layer
     Dk: int = 64
     D: int = 512
 
@@ -60,6 +64,15 @@ class Workload:
     @property
     def pattern(self) -> str:
         return "".join(layer_kind(l) for l in range(self.n_layers))
+
+    @property
+    def n_kv(self) -> int:
+        """FP4 latent caches: one per layer, or one for all layers."""
+        return 1 if self.shared_kv else self.n_layers
+
+    def kv_layer(self, l: int) -> int:
+        """Cache that layer l attends to."""
+        return 0 if self.shared_kv else l
 
     def scaled(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -88,6 +101,12 @@ WORKLOADS = {
                             keys="planted", n_planted=1024, steps=64, append=True,
                             redraw_queries=True),
 }
+# The shared-KV variants: every decoder layer attends to one FP4 latent cache
+# (the pages' setting in which only some layers build global KV and the
+# others reuse it), so a decode step appends one FP4 row per sequence.
+WORKLOADS["ctx_1m_shared"] = WORKLOADS["ctx_1m"].scaled(name="ctx_1m_shared", shared_kv=True)
+WORKLOADS["ragged32_1m_shared"] = WORKLOADS["ragged32_1m"].scaled(name="ragged32_1m_shared",
+                                                                  shared_kv=True)
 
 
 KV_POOL_ROWS = 1 << 20
@@ -160,7 +179,7 @@ class Case:
     # a pool of 2^20 rows keeps repeats inside one attended set rare.
     def kv_row_id(self, layer: int, b: int, positions) -> torch.Tensor:
         pos = torch.as_tensor(positions, dtype=torch.int64, device=self.device).reshape(-1)
-        key = I.stream_key(self.seed, I.TAG_KV, layer, b)
+        key = I.stream_key(self.seed, I.TAG_KV, self.wl.kv_layer(layer), b)
         return I._srl(I.hash_stream(key, pos), 44)           # top 20 bits
 
     def kv_pool_rows(self, row_ids, device=None) -> torch.Tensor:

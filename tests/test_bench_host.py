@@ -35,6 +35,14 @@ def test_small_and_batched_bytes():
         32 * 1296 + 8 * 128
 
 
+def test_shared_kv_appends_one_row():
+    per_layer = bench.algorithmic_bytes(W.WORKLOADS["ragged32_1m"], [5000])
+    shared = bench.algorithmic_bytes(W.WORKLOADS["ragged32_1m_shared"], [5000])
+    assert per_layer["append"] == 20 * 1296 + 128 and shared["append"] == 1296 + 128
+    assert {k: v for k, v in per_layer.items() if k not in ("append", "step")} == \
+        {k: v for k, v in shared.items() if k not in ("append", "step")}
+
+
 def test_short_sequences_clamp():
     wl = W.WORKLOADS["ragged32_1m"]
     ab = bench.algorithmic_bytes(wl, [100])            # L <= W: no eligible position

@@ -89,6 +89,28 @@ def test_empty_row_set():
     assert not out.any() and np.isneginf(lse).all()
 
 
+def test_decode_step_shared_kv():
+    """One latent cache for every layer: two Reuse layers that attend with the
+    same query see the same rows and give identical outputs, which layers with
+    caches of their own do not."""
+    rng = np.random.default_rng(6)
+    L, W, P, k, H, Hq, D = 1200, 128, 200, 30, 4, 4, 512
+    keys = rng.integers(-127, 128, size=(L, 64)).astype(np.int8)
+    q0 = rng.integers(-127, 128, size=(H, 64)).astype(np.int8)
+    w0 = rng.integers(0, 16, size=H).astype(np.int8)
+    attn_q = [_bf16(rng.standard_normal((Hq, D))) for _ in range(4)]
+    attn_q[3] = attn_q[2]
+    kv0 = _bf16(rng.standard_normal((L, D)))
+    kv_own = [_bf16(rng.standard_normal((L, D))) for _ in range(4)]
+    args = ("FRUU", keys, 0, L, W, P, k, {0: q0, 1: q0}, {0: w0, 1: w0}, attn_q)
+    shared = oracle.decode_step(*args, lambda l, S: kv0[S], 1 / math.sqrt(D))
+    own = oracle.decode_step(*args, lambda l, S: kv_own[l][S], 1 / math.sqrt(D))
+    assert np.array_equal(shared[2]["S"], shared[3]["S"])
+    assert np.array_equal(shared[2]["out"], shared[3]["out"])
+    assert np.array_equal(shared[2]["lse"], shared[3]["lse"])
+    assert not np.allclose(own[2]["out"], own[3]["out"])
+
+
 def test_decode_step_modes():
     """Full -> Reindex -> Reuse: a Reindex layer with the Full layer's own query
     selects the same positions; Reuse layers repeat the previous selection."""

@@ -21,6 +21,9 @@ tie order, FP4 E2M1 + E8M0 per 32, K = V = latent, 1/sqrt(512)) are listed with
 each function.
 
 Parity status: all functions are pinned by the CPU tests; none is unpinned.
+The multi-token block functions at the end are pinned against the single-
+token step (T = 1), plain-Python scores with exhaustive ranking, causality
+and dense causal softmax attention.
 """
 from __future__ import annotations
 
@@ -39,7 +42,8 @@ __all__ = [
     "build", "load", "bf16_to_f64", "fp4_quantize", "fp4_dequantize", "fp4_value",
     "index_scores", "topk", "eligible_count", "window_positions", "index_full",
     "index_reindex", "select_topk", "attention_positions", "attention",
-    "layer_kind", "layer_pattern", "decode_step",
+    "layer_kind", "layer_pattern", "decode_step", "block_lengths", "index_full_block",
+    "index_reindex_block", "decode_block",
 ]
 
 
@@ -305,5 +309,109 @@ def decode_step(pattern: str, keys, row_off: int, L: int, window: int, P: int, k
         codes, scales = fp4_quantize(x)
         out, lse = attention(attn_q[l], codes, scales, sm_scale)
         rec.update(sel=sel, out=out, lse=lse, S=S)
+        results.append(rec)
+    return results
+
+
+# --------------------------------------------------------------------------
+# Multi-token decode: a block of T tokens verified in one step ("DeepSeek Has
+# Done It Again...", "Architecture and inference efficiency", bullet on
+# DSpark: drafted tokens are checked by the main model together, in blocks
+# of five; "DeepSeek V4.1-Flash 552B runs like 16B (CED)", "DSpark, Engram &
+# Single-Pass mHC").  Readings of this path, where the pages are silent:
+#  * the block's T tokens are the last T cached positions; token t sits at
+#    position L - T + t and sees positions 0 .. L - T + t only (causal), so
+#    its own window is the 128 positions ending at itself;
+#  * per-token selection: every token ranks its own eligible positions with
+#    its own index query, exactly as a single decoding token would;
+#  * shared selection: one pool and one selection for the block, ranking the
+#    positions eligible for every token of the block (those of token 0) by the
+#    best score any of the block's tokens gives them, max_t s_t(p); the
+#    maximum stays an exact int32 (a sum of five scores would not).
+# --------------------------------------------------------------------------
+
+def block_lengths(L: int, T: int):
+    """Cached positions seen by each token of a block of T tokens at the end
+    of a context of L positions (the block included)."""
+    assert 1 <= T <= L
+    return [int(L) - int(T) + 1 + t for t in range(int(T))]
+
+
+def _block_scores(keys, row_off: int, pos, q, w):
+    """max over the block's tokens of each token's score at `pos`."""
+    s = None
+    for t in range(len(q)):
+        st = index_scores(keys, row_off + np.asarray(pos, dtype=np.int64), q[t], w[t])
+        s = st if s is None else np.maximum(s, st)
+    return s
+
+
+def index_full_block(keys, row_off: int, L: int, T: int, q, w, window: int, P: int, shared: bool):
+    """Full mode for a block.  q: [T][H][Dk] int8, w: [T][H].  Per token: a list
+    of T (pool_pos, pool_score), token t's pool over its own eligible positions.
+    Shared: one (pool_pos, pool_score) over token 0's eligible positions,
+    ranked by max_t s_t(p)."""
+    Ls = block_lengths(L, T)
+    if not shared:
+        return [index_full(keys, row_off, Ls[t], q[t], w[t], window, P) for t in range(T)]
+    E0 = eligible_count(Ls[0], window)
+    pos = np.arange(E0, dtype=np.int64)
+    return topk(_block_scores(keys, row_off, pos, q, w), pos, min(int(P), E0))
+
+
+def index_reindex_block(keys, row_off: int, cand_pos, q, w, shared: bool):
+    """Reindex for a block: per token, token t's own pool re-scored with its
+    own query (cand_pos is then a list of T pools); shared, the block's pool
+    re-scored with max_t s_t(p)."""
+    if not shared:
+        return [index_reindex(keys, row_off, cand_pos[t], q[t], w[t]) for t in range(len(q))]
+    return _block_scores(keys, row_off, cand_pos, q, w)
+
+
+def decode_block(pattern: str, keys, row_off: int, L: int, T: int, window: int, P: int, k: int,
+                 idx_q, idx_w, attn_q, kv_rows, sm_scale: float, shared: bool):
+    """One verify step of a block of T tokens of one sequence over the layers
+    of ``pattern`` (Full, Reindex, Reuse as in decode_step).
+
+    idx_q[l], idx_w[l]: [T][H][Dk] / [T][H] int8 of F and R layers.
+    attn_q[l]: [T][Hq][D] bf16 bit patterns.  kv_rows(l, positions) as in
+    decode_step.  Returns per layer a dict with the pool(s), the selection(s)
+    (a list of T, or one shared), and per token out, lse and S.
+    """
+    Ls = block_lengths(L, T)
+    results = []
+    pool = None
+    sel = None
+    for l, kind in enumerate(pattern):
+        rec = {"kind": kind}
+        if kind == "F":
+            res = index_full_block(keys, row_off, L, T, idx_q[l], idx_w[l], window, P, shared)
+            if shared:
+                pool, pool_score = res
+                sel, _ = select_topk(pool_score, pool, k)
+            else:
+                pool = [r[0] for r in res]
+                pool_score = [r[1] for r in res]
+                sel = [select_topk(pool_score[t], pool[t], k)[0] for t in range(T)]
+            rec.update(pool_pos=pool, pool_score=pool_score)
+        elif kind == "R":
+            assert pool is not None, "Reindex needs an earlier Full layer"
+            sc = index_reindex_block(keys, row_off, pool, idx_q[l], idx_w[l], shared)
+            if shared:
+                sel, _ = select_topk(sc, pool, k)
+            else:
+                sel = [select_topk(sc[t], pool[t], k)[0] for t in range(T)]
+            rec.update(reindex_score=sc)
+        else:
+            assert sel is not None, "Reuse needs an earlier selection"
+        outs, lses, Ss = [], [], []
+        for t in range(T):
+            S = attention_positions(Ls[t], sel if shared else sel[t], window)
+            codes, scales = fp4_quantize(kv_rows(l, S))
+            out, lse = attention(attn_q[l][t], codes, scales, sm_scale)
+            outs.append(out)
+            lses.append(lse)
+            Ss.append(S)
+        rec.update(sel=sel, out=outs, lse=lses, S=Ss)
         results.append(rec)
     return results

@@ -49,28 +49,67 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "decode steps/s at 1M ctx (index+sparse attn) + achieved HBM GB/s vs peak"
 
 
-def algorithmic_bytes(wl, lengths) -> dict:
+def algorithmic_bytes(wl, lengths, sel_union=None) -> dict:
     """Bytes the method must move per step (every buffer crossing the C ABI
-    once, plus the index keys and KV rows it reads), summed over sequences."""
+    once, plus the index keys and KV rows it reads), summed over sequences.
+
+    A verify block of T tokens reads the index keys once for all tokens (the
+    positions the last token may rank, or with a shared selection those of the
+    first token) and the union of the tokens' windows (window + T - 1 rows).
+    sel_union[b][l], when given, is the number of distinct positions in the T
+    per-token selections layer l attends with; without it each token's
+    selection is counted on its own."""
     pat = wl.pattern
     nF, nR = pat.count("F"), pat.count("R")
+    T, shared = wl.block, wl.block_shared or wl.block == 1
     tot = {"append": 0, "full": 0, "select": 0, "reindex": 0, "attn": 0, "scan_kernel": 0}
-    for L in lengths:
-        E = max(0, L - wl.window)
-        Peff = min(wl.P, E)
-        keff = min(wl.k, Peff)
-        W = min(wl.window, L)
-        tot["full"] += nF * (64 * E + 65 * wl.H + 8 * Peff)
-        tot["select"] += (nF + nR) * (8 * Peff + 4 * keff)
-        tot["reindex"] += nR * (72 * Peff + 65 * wl.H)
-        tot["attn"] += wl.n_layers * (272 * (keff + W) + 6 * wl.Hq * wl.D + 4 * keff)
-        tot["scan_kernel"] += 64 * E + 65 * wl.H
+    for b, L in enumerate(lengths):
+        Ls = [L - (T - 1 - t) for t in range(T)]
+        Es = [max(0, x - wl.window) for x in Ls]
+        E_scan = Es[0] if shared else Es[-1]
+        lists = [Es[0]] if shared else Es                      # eligible count of each list
+        peff = [min(wl.P, e) for e in lists]
+        keff = [min(wl.k, p) for p in peff]
+        q_idx = T * 65 * wl.H                                  # int8 query + weights per token
+        tot["full"] += nF * (64 * E_scan + q_idx + 8 * sum(peff))
+        tot["select"] += (nF + nR) * sum(8 * p + 4 * kk for p, kk in zip(peff, keff))
+        tot["reindex"] += nR * (72 * sum(peff) + q_idx)
+        win_rows = min(wl.window + T - 1, max(0, L))
+        for l in range(wl.n_layers):
+            if shared:
+                sel_rows = keff[0]
+            elif sel_union is not None:
+                sel_rows = sel_union[b][l]
+            else:
+                sel_rows = sum(keff)
+            tot["attn"] += 272 * (sel_rows + win_rows) + T * 6 * wl.Hq * wl.D + 4 * sum(keff)
+        tot["scan_kernel"] += 64 * E_scan + q_idx
         if wl.append:
-            # per cache (one per layer, or one shared by all): the bf16 row in,
-            # its FP4 codes and scales out; the 64-byte index key in and out
-            tot["append"] += wl.n_kv * (2 * wl.D + wl.D // 2 + wl.D // 32) + 2 * wl.Dk
+            # per token and cache (one per layer, or one shared by all): the
+            # bf16 row in, its FP4 codes and scales out; the 64-byte index key
+            # in and out
+            tot["append"] += T * (wl.n_kv * (2 * wl.D + wl.D // 2 + wl.D // 32) + 2 * wl.Dk)
     tot["step"] = tot["append"] + tot["full"] + tot["select"] + tot["reindex"] + tot["attn"]
     return tot
+
+
+def selection_unions(eng) -> list:
+    """Per sequence and layer: distinct positions in the block's per-token
+    selections that the layer attends with (from the engine's last step)."""
+    import numpy as np
+    wl = eng.wl
+    T = wl.block
+    sel = eng.sel_pos.cpu().numpy()
+    sl = eng.sel_len.cpu().numpy()
+    out = []
+    for b in range(wl.B):
+        row = []
+        for l in range(wl.n_layers):
+            src = eng.selection_layer(l)
+            parts = [sel[src, b * T + t, :sl[src, b * T + t]] for t in range(T)]
+            row.append(len(np.unique(np.concatenate(parts))) if parts else 0)
+        out.append(row)
+    return out
 
 
 SCAN_SOURCES = ("decode_kv_amd/csrc/index_full.hip", "decode_kv_amd/csrc/common.h")
@@ -113,10 +152,18 @@ def cpu_baseline(wl, seed: int, step: int, keys_np, seconds_target: float = 12.0
     lens = case.lengths_at(step)
     u16 = lambda t: t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
+    T = wl.block
+    FR = [l for l, c in enumerate(wl.pattern) if c in "FR"]
+
+    def per_token(fn, conv, l, b):
+        if T == 1:
+            return conv(fn(step, l, b))
+        return np.stack([conv(fn(step, l, b, t)) for t in range(T)])
+
     def seq_inputs(b):
-        idx_q = {l: case.index_q(step, l, b).numpy() for l, c in enumerate(wl.pattern) if c in "FR"}
-        idx_w = {l: case.index_w(step, l, b).numpy() for l, c in enumerate(wl.pattern) if c in "FR"}
-        attn_q = [u16(case.attn_q(step, l, b)) for l in range(wl.n_layers)]
+        idx_q = {l: per_token(case.index_q, lambda x: x.numpy(), l, b) for l in FR}
+        idx_w = {l: per_token(case.index_w, lambda x: x.numpy(), l, b) for l in FR}
+        attn_q = [per_token(case.attn_q, u16, l, b) for l in range(wl.n_layers)]
         off = int(case.row_off[b])
         return keys_np[off:off + case.caps[b]], idx_q, idx_w, attn_q, \
             (lambda l, S, b=b: u16(case.kv_bf16(l, b, S)))
@@ -124,8 +171,12 @@ def cpu_baseline(wl, seed: int, step: int, keys_np, seconds_target: float = 12.0
     def run(b, inputs):
         kb, idx_q, idx_w, attn_q, kv_rows = inputs
         t0 = time.perf_counter()
-        oracle.decode_step(wl.pattern, kb, 0, lens[b], wl.window, wl.P, wl.k, idx_q, idx_w,
-                           attn_q, kv_rows, wl.sm_scale)
+        if T == 1:
+            oracle.decode_step(wl.pattern, kb, 0, lens[b], wl.window, wl.P, wl.k, idx_q, idx_w,
+                               attn_q, kv_rows, wl.sm_scale)
+        else:
+            oracle.decode_block(wl.pattern, kb, 0, lens[b], T, wl.window, wl.P, wl.k, idx_q,
+                                idx_w, attn_q, kv_rows, wl.sm_scale, wl.block_shared)
         return time.perf_counter() - t0
 
     cores = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or len(os.sched_getaffinity(0))
@@ -237,14 +288,21 @@ def main():
     R = max(2, -(-(300 << 20) // key_bytes) + 1)
     key_copies = [eng.keys] + [eng.keys.clone() for _ in range(R - 1)]
     q0, w0 = static["idx_q"][0], static["idx_w"][0]
-    scores = torch.empty((wl.B, eng.max_len), dtype=torch.int32, device=dev)
+    blk = wl.block > 1
+    n_lists = wl.B if (not blk or wl.block_shared) else wl.B * wl.block
+    scores = torch.empty((n_lists, eng.max_len), dtype=torch.int32, device=dev)
     sink = torch.empty(csa2.stream_read_sink_words(key_bytes), dtype=torch.int32, device=dev)
     n_scan = max(50, 4 * R)
 
     def scan_all():
         for i in range(n_scan):
-            csa2.index_score(q0, w0, key_copies[i % R], eng.row_off, eng.lens, eng.max_len,
-                             eng.total_len, wl.window, scores, eng.ws_full, stream)
+            if blk:
+                csa2.index_score_block(q0, w0, key_copies[i % R], eng.row_off, eng.lens,
+                                       eng.max_len, eng.total_len, wl.window, wl.block_shared,
+                                       scores, eng.ws_full, stream)
+            else:
+                csa2.index_score(q0, w0, key_copies[i % R], eng.row_off, eng.lens, eng.max_len,
+                                 eng.total_len, wl.window, scores, eng.ws_full, stream)
 
     def read_all():
         for i in range(n_scan):
@@ -339,11 +397,12 @@ def main():
         results[mode] = [a.elapsed_time(b) for a, b in ev]
         say("%s: %d steps, mean %.2f us" % (mode, K, statistics.mean(results[mode]) * 1e3))
     if wl.append:
-        want = [L + next_step[0] for L in case.lengths]
+        want = [L + next_step[0] * wl.block for L in case.lengths]
         assert eng.lens.cpu().tolist() == want, "lengths did not advance once per step"
 
     lengths = case.lengths_at(first_timed_step if wl.append else 0)
-    ab = algorithmic_bytes(wl, lengths)
+    unions = selection_unions(eng) if blk and not wl.block_shared else None
+    ab = algorithmic_bytes(wl, lengths, unions)
     step_bytes = ab["step"]
 
     def summary(ms_list):
@@ -375,7 +434,9 @@ def main():
                    "pattern": wl.pattern, "P": wl.P, "k": wl.k, "window": wl.window,
                    "index_heads": wl.H, "query_heads": wl.Hq, "latent": wl.D,
                    "append": wl.append, "mode": "cold (Infinity Cache evicted before each step)",
-                   "graph": True},
+                   "graph": True, "block": wl.block,
+                   "block_selection": ("shared" if wl.block_shared else "per-token")
+                   if blk else None},
         "step_ms_p10_p50_p90": [round(x, 5) for x in statistics.quantiles(results["cold"], n=10)[0::4]]
         if K >= 10 else None,
         "algorithmic_MB_per_step": round(step_bytes / 1e6, 3),
@@ -383,7 +444,9 @@ def main():
                                    if k in ("append", "full", "select", "reindex", "attn")},
         "step_GBps": round(step_gbs, 1),
         "step_frac_of_hbm_peak": round(step_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": "full_score_kernel (Full-mode index scan)", "bound": "hbm",
+        "roofline": {"kernel": ("full_score_block_kernel (Full-mode index scan, %d tokens)"
+                                % wl.block) if blk else "full_score_kernel (Full-mode index scan)",
+                     "bound": "hbm",
                      "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches_timed": n_scan,
@@ -400,8 +463,9 @@ def main():
                          "library calls (kernel time plus the gaps between launches)",
         "timed_region_wall_s": round(wall, 4),
     }
-    if wl.append:
-        res["tokens_per_s"] = round(wl.B * 1000.0 / ms, 1)
+    if wl.append or blk:
+        # tokens decoded (or verified, for a block) per second
+        res["tokens_per_s"] = round(wl.B * wl.block * 1000.0 / ms, 1)
     if "warm" in results:
         wms, wgbs = summary(results["warm"])
         res["warm"] = {"ms_per_step": round(wms, 5), "steps_per_s": round(1000.0 / wms, 2),

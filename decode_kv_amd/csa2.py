@@ -75,6 +75,18 @@ def lib():
         L.csa2_sparse_attn_decode.restype = I
         L.csa2_sparse_attn_decode.argtypes = [V, V, V, V, V, LL, V, V, I, I, I, I, I, F, V, V,
                                               V, SZ, V]
+        L.csa2_block_workspace_bytes.restype = SZ
+        L.csa2_block_workspace_bytes.argtypes = [I, I, I, I, LL, LL, I, I, I, I, I, I]
+        L.csa2_index_full_block.restype = I
+        L.csa2_index_full_block.argtypes = [V, V, V, V, V, I, I, I, LL, LL, I, I, I, I, V, V, V,
+                                            I, V, V, V, SZ, V]
+        L.csa2_index_score_block.restype = I
+        L.csa2_index_score_block.argtypes = [V, V, V, V, V, I, I, I, LL, LL, I, I, I, V, V, SZ, V]
+        L.csa2_index_reindex_block.restype = I
+        L.csa2_index_reindex_block.argtypes = [V, V, V, V, V, V, I, I, I, I, I, I, V, V]
+        L.csa2_sparse_attn_decode_block.restype = I
+        L.csa2_sparse_attn_decode_block.argtypes = [V, V, V, V, V, LL, V, V, I, I, I, I, I, I, I,
+                                                    F, V, V, V, SZ, V]
         _lib = L
     return _lib
 
@@ -222,3 +234,58 @@ def sparse_attn_decode_static(q, kv_fp4, kv_scale, row_off, lens, max_len, sel_p
                                                 _p(lens), int(max_len), _p(sel_pos),
                                                 _p(sel_len), B, Hq, D, k, window,
                                                 float(sm_scale), _p(out), _p(lse), _s(stream)))
+
+
+# ---- verify blocks: T tokens per sequence (per-token or shared selection) ----
+
+def block_workspace_bytes(op: int, B: int, T: int, shared: bool, max_len: int = 0,
+                          total_len: int = 0, H: int = 0, P: int = 0, k: int = 0, Hq: int = 0,
+                          D: int = 0, window: int = 0) -> int:
+    return int(lib().csa2_block_workspace_bytes(op, B, T, int(shared), max_len, total_len, H, P,
+                                                k, Hq, D, window))
+
+
+def index_full_block(q, w, keys, row_off, lens, max_len, total_len, window, P, shared, pool_pos,
+                     pool_score, pool_len, ws, stream=None, k=0, sel_pos=None, sel_len=None):
+    """q [B][T][H][Dk]; w [B][T][H]."""
+    B, T, H, Dk = q.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("csa2_index_full_block",
+           lib().csa2_index_full_block(_p(q), _p(w), _p(keys), _p(row_off), _p(lens), B, T,
+                                       int(shared), int(max_len), int(total_len), H, Dk, window,
+                                       P, _p(pool_pos), _p(pool_score), _p(pool_len), int(k),
+                                       _p(sel_pos), _p(sel_len), _p(ws), nbytes, _s(stream)))
+
+
+def index_score_block(q, w, keys, row_off, lens, max_len, total_len, window, shared, score, ws,
+                      stream=None):
+    """q [B][T][H][Dk]; score [B][T][max_len] (per token) or [B][max_len] (shared)."""
+    B, T, H, Dk = q.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("csa2_index_score_block",
+           lib().csa2_index_score_block(_p(q), _p(w), _p(keys), _p(row_off), _p(lens), B, T,
+                                        int(shared), int(max_len), int(total_len), H, Dk, window,
+                                        _p(score), _p(ws), nbytes, _s(stream)))
+
+
+def index_reindex_block(q, w, keys, row_off, cand_pos, cand_len, shared, score, stream=None):
+    """q [B][T][H][Dk]; cand_pos / score [lists][P] with lists = B (shared) or B*T."""
+    B, T, H, Dk = q.shape
+    P = cand_pos.shape[-1]
+    _check("csa2_index_reindex_block",
+           lib().csa2_index_reindex_block(_p(q), _p(w), _p(keys), _p(row_off), _p(cand_pos),
+                                          _p(cand_len), B, T, int(shared), H, Dk, P, _p(score),
+                                          _s(stream)))
+
+
+def sparse_attn_decode_block(q, kv_fp4, kv_scale, row_off, lens, max_len, sel_pos, sel_len, k,
+                             window, shared, sm_scale, out, lse, ws, stream=None):
+    """q / out [B][T][Hq][D]; sel_pos [B][k] (shared) or [B][T][k]."""
+    B, T, Hq, D = q.shape
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("csa2_sparse_attn_decode_block",
+           lib().csa2_sparse_attn_decode_block(_p(q), _p(kv_fp4), _p(kv_scale), _p(row_off),
+                                               _p(lens), int(max_len), _p(sel_pos), _p(sel_len),
+                                               B, T, int(shared), Hq, D, k, window,
+                                               float(sm_scale), _p(out), _p(lse), _p(ws), nbytes,
+                                               _s(stream)))

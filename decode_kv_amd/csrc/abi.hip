@@ -60,3 +60,28 @@ extern "C" size_t csa2_workspace_bytes(int op, int B, long long max_len, long lo
             return 0;
     }
 }
+
+extern "C" size_t csa2_block_workspace_bytes(int op, int B, int T, int shared, long long max_len,
+                                             long long total_len, int H, int P, int k, int Hq,
+                                             int D, int window) {
+    if (B < 0 || T < 1 || shared < 0 || shared > 1) {
+        fail(CSA2_ERR_INVALID, "csa2_block_workspace_bytes: B < 0, T < 1 or shared not 0/1");
+        return 0;
+    }
+    switch (op) {
+        case CSA2_OP_INDEX_FULL:
+            if (total_len < 0 || P < 1 || k < 0 || k > P) {
+                fail(CSA2_ERR_INVALID,
+                     "csa2_block_workspace_bytes: total_len < 0, P < 1 or k outside [0, P]");
+                return 0;
+            }
+            return index_full_block_ws_bytes(B, T, shared, total_len, k);
+        case CSA2_OP_SELECT_TOPK:
+        case CSA2_OP_SPARSE_ATTN:
+            return csa2_workspace_bytes(op, (int)((long long)B * T > 0x7FFFFFFF ? 0x7FFFFFFF : (long long)B * T),
+                                        max_len, total_len, H, P, k, Hq, D, window);
+        default:
+            fail(CSA2_ERR_INVALID, "csa2_block_workspace_bytes: unknown op %d", op);
+            return 0;
+    }
+}

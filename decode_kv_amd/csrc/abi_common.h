@@ -25,8 +25,8 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace sizes (bytes) of the ops that need one.
 size_t index_full_ws_bytes(int B, long long total_len, int P, int k);
+size_t index_full_block_ws_bytes(int B, int T, int shared, long long total_len, int k);
 size_t sparse_attn_ws_bytes(int B, int Hq, int D, int k, int window);
 int sparse_attn_splits(int B, int Hq, int k, int window);
-int sparse_attn_tiles_per_wg(int B, int Hq, int k, int window);
 
 }  // namespace csa2

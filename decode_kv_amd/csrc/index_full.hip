@@ -38,6 +38,11 @@
 // P_eff = min(k, E) side by side with the pool (grid dimension y, separate
 // candidate arrays) and no separate selection pass reads the pool back.
 // The result is exact and independent of the launch shape.
+//
+// Verify blocks (csa2_index_full_block, csa2_index_score_block): kernel 1b
+// scores all T tokens of a block from one load of the keys, and kernels 2-5
+// run unchanged over the block's lists, T per sequence (one per token, each
+// over its own eligible positions) or one (the best score over the block).
 #include "abi_common.h"
 #include "common.h"
 
@@ -138,8 +143,8 @@ static long long full_tile_bound(int B, long long total_len) {
     return (total_len / kTile + B + 1 + 7) / 8 * 8;
 }
 
-static size_t full_ws_layout(int B, long long total_len, int ntargets, char* base, FullWs* w) {
-    const long long T = full_tile_bound(B, total_len);
+// Workspace of B score lists laid out over T tiles.
+static size_t full_ws_layout(int B, long long T, int ntargets, char* base, FullWs* w) {
     size_t off = 0;
     auto take = [&](size_t bytes) {
         const size_t at = off;
@@ -167,7 +172,21 @@ static size_t full_ws_layout(int B, long long total_len, int ntargets, char* bas
 
 size_t index_full_ws_bytes(int B, long long total_len, int P, int k) {
     (void)P;
-    return full_ws_layout(B, total_len, k > 0 ? 2 : 1, nullptr, nullptr);
+    return full_ws_layout(B, full_tile_bound(B, total_len), k > 0 ? 2 : 1, nullptr, nullptr);
+}
+
+// A verify block of T tokens per sequence.  Per-token selection ranks T lists
+// per sequence (list b * T + t, token t's own eligible positions); their
+// tiles lie in T planes of full_tile_bound(B, total_len) tiles each, list
+// (b, t) at the tiles of sequence b in plane t, so tile g of every plane sits
+// on the XCD of the scoring workgroup g that wrote it.  Shared selection ranks
+// one list per sequence (the best score over the block) in one plane.
+static int block_planes(int T, int shared) { return shared ? 1 : T; }
+
+size_t index_full_block_ws_bytes(int B, int T, int shared, long long total_len, int k) {
+    const int planes = block_planes(T, shared);
+    return full_ws_layout(B * planes, planes * full_tile_bound(B, total_len), k > 0 ? 2 : 1,
+                          nullptr, nullptr);
 }
 
 // Monotone key of a score: exact below 32, otherwise the exponent and the 5
@@ -244,10 +263,10 @@ __device__ __forceinline__ void find_bin(const H* h, int nb, int need, int* s_tm
     find_bin_counts<NT, PER>(c, need, s_tmp, s_res, bin_out, above_out, cnt_out);
 }
 
-// Tile t -> sequence, from the lengths (up to kMaxBatch sequences, 16 per
+// Tile t -> sequence, from the lengths (up to kMaxBatch sequences, 8 per
 // thread).  Returns the sequence (or -1 past the last tile) and the layout of
-// that sequence.  Workgroup 0 also writes every sequence's state: st0 gets
-// P_eff = min(P, E) and st1 (when not null) min(k, E).
+// that sequence.  Workgroup 0 also writes every list's state (write_states):
+// st0 gets P_eff = min(P, E) and st1 (when not null) min(k, E).
 struct TileInfo {
     int b, tile0, E;
     long long roff;
@@ -266,19 +285,31 @@ __device__ __forceinline__ FullState initial_state(int E, int P, int tile0, int 
     return s;
 }
 
+// States of sequence b's lists: one per plane.  The list of plane i ranks
+// E - (planes - 1 - i) positions (a verify block's token i sees one position
+// fewer than token i + 1) over the tiles of the sequence in plane i.  With one
+// plane that is the sequence's own list.
+__device__ __forceinline__ void write_states(FullState* st0, FullState* st1, int b, int E, int P,
+                                             int k, int tile0, int planes, int TB) {
+    for (int i = 0; i < planes; ++i) {
+        const int Ei = max(0, E - (planes - 1 - i));
+        const int nt = (Ei + kTile - 1) / kTile;
+        st0[b * planes + i] = initial_state(Ei, P, i * TB + tile0, nt);
+        if (st1) st1[b * planes + i] = initial_state(Ei, k, i * TB + tile0, nt);
+    }
+}
+
 // One sequence: no scan, no LDS, no barrier.
 __device__ __forceinline__ TileInfo map_tile_one(const int* __restrict__ len,
                                                  const long long* __restrict__ row_off,
                                                  int window, int P, int k, int t,
-                                                 FullState* st0, FullState* st1) {
+                                                 FullState* st0, FullState* st1, int planes = 1,
+                                                 int TB = 0) {
     const int L = len[0];
     const long long roff = row_off[0];
     const int E = L > window ? L - window : 0;
     const int nt = (E + kTile - 1) / kTile;
-    if (t == 0 && threadIdx.x == 0) {
-        st0[0] = initial_state(E, P, 0, nt);
-        if (st1) st1[0] = initial_state(E, k, 0, nt);
-    }
+    if (t == 0 && threadIdx.x == 0) write_states(st0, st1, 0, E, P, k, 0, planes, TB);
     TileInfo r;
     r.b = t < nt ? 0 : -1;
     r.tile0 = 0;
@@ -291,7 +322,7 @@ template <int NT>
 __device__ __noinline__ TileInfo map_tile(const int* __restrict__ len,
                                           const long long* __restrict__ row_off, int B,
                                           int window, int P, int k, int t, FullState* st0,
-                                          FullState* st1) {
+                                          FullState* st1, int planes = 1, int TB = 0) {
     __shared__ int s_tmp[NT / kWave];
     __shared__ int s_b, s_tile0, s_E;
     __shared__ long long s_roff;
@@ -325,10 +356,7 @@ __device__ __noinline__ TileInfo map_tile(const int* __restrict__ len,
                 s_E = Ev[i];
                 s_roff = row_off[b];
             }
-            if (t == 0) {
-                st0[b] = initial_state(Ev[i], P, pre_t, nt[i]);
-                if (st1) st1[b] = initial_state(Ev[i], k, pre_t, nt[i]);
-            }
+            if (t == 0) write_states(st0, st1, b, Ev[i], P, k, pre_t, planes, TB);
         }
         pre_t += nt[i];
     }
@@ -431,6 +459,134 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
     uint32_t* th = reinterpret_cast<uint32_t*>(w.tile_hist + (size_t)t * kKeyBins);
     for (int i = threadIdx.x; i < kKeyBins / 2; i += kScoreThreads)
         th[i] = s_hist[2 * i] | (s_hist[2 * i + 1] << 16);
+}
+
+// ---- 1b. score a verify block of T tokens ------------------------------------------
+// The same tiles and MFMA scoring, with the key operands loaded once and
+// scored against every token of the block in turn: each wave holds its 128
+// key rows in registers while the tokens' queries and weights come from LDS.
+// planes == T (per-token lists): token t's scores of the positions it may
+// rank (p < E - (T - 1 - t), E the last token's count) go to tile g of plane
+// t, each plane with its own histogram.  planes == 1 (shared list): the best
+// score over the block of each position every token may rank (E is then the
+// first token's count) goes to tile g.  Scores go to score_out in that tile
+// layout (seq_stride < 0) or to list (b, plane) at (b * planes + plane) *
+// seq_stride + p.
+constexpr int kMaxBlockT = 8;
+
+// Dynamic LDS of the block kernel: queries [T][16 NB][64] (heads past H are
+// zero), weights [T][64] bytes (zero past H), histograms [planes][kKeyBins].
+static size_t block_score_lds(int T, int NB, int planes) {
+    return (size_t)T * NB * 16 * kDk + (size_t)T * 64 + (size_t)planes * kKeyBins * 4;
+}
+
+template <int NB>
+__global__ __launch_bounds__(kScoreThreads) void full_score_block_kernel(
+    const int8_t* __restrict__ q, const int8_t* __restrict__ wts,
+    const int8_t* __restrict__ keys, const long long* __restrict__ row_off,
+    const int* __restrict__ len, int B, int H, int window, int P, FullWs w, int T, int planes,
+    int TB, int* __restrict__ score_out, long long seq_stride) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
+    i32x4* s_q = reinterpret_cast<i32x4*>(s_dyn);
+    uint32_t* s_w = reinterpret_cast<uint32_t*>(s_dyn + (size_t)T * NB * 16 * kDk);
+    uint32_t* s_hist = s_w + T * 16;
+    const int g = blockIdx.x;
+    const int l = lane_id();
+    const int wave = threadIdx.x / kWave;
+    FullState* st1 = w.k > 0 ? w.st + w.B : nullptr;
+    const TileInfo ti = B == 1 ? map_tile_one(len, row_off, window, P, w.k, g, w.st, st1, planes, TB)
+                               : map_tile<kScoreThreads>(len, row_off, B, window, P, w.k, g, w.st,
+                                                         st1, planes, TB);
+    if (ti.b < 0) return;                                      // past the last tile
+    const int b = ti.b;
+    const int p_tile = (g - ti.tile0) * kTile;
+    const int8_t* kbase = keys + ((size_t)ti.roff + p_tile) * kDk + (l >> 4) * 16;
+    const int nvalid = min(kTile, ti.E - p_tile);
+    constexpr int kWaves = kScoreThreads / kWave;
+    constexpr int kGroups = kTile / (kWaves * 16);
+    const int t0 = (kTile / kWaves) * wave;
+    i32x4 kop[kGroups];
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+        int tok = t0 + 16 * u + (l & 15);
+        tok = tok < nvalid ? tok : 0;
+        kop[u] = *reinterpret_cast<const i32x4*>(kbase + (size_t)tok * kDk);
+    }
+    asm volatile("" ::: "memory");                             // keys are in flight first
+    {
+        const int8_t* qb = q + (size_t)b * T * H * kDk;
+        const int pieces = T * NB * 16 * 4;                    // 16-byte pieces, zero past H
+        for (int i = threadIdx.x; i < pieces; i += kScoreThreads) {
+            const int tk = i / (NB * 64), h = (i >> 2) % (NB * 16);
+            s_q[i] = h < H ? *reinterpret_cast<const i32x4*>(qb + ((size_t)tk * H + h) * kDk +
+                                                             (i & 3) * 16)
+                           : i32x4{0, 0, 0, 0};
+        }
+        uint8_t* sw8 = reinterpret_cast<uint8_t*>(s_w);
+        for (int i = threadIdx.x; i < T * 64; i += kScoreThreads) {
+            const int tk = i >> 6, h = i & 63;
+            sw8[i] = h < H ? (uint8_t)wts[((size_t)b * T + tk) * H + h] : (uint8_t)0;
+        }
+        for (int i = threadIdx.x; i < planes * kKeyBins; i += kScoreThreads) s_hist[i] = 0;
+    }
+    __syncthreads();
+    int best[kGroups / 4];
+#pragma unroll
+    for (int it = 0; it < kGroups / 4; ++it) best[it] = 0;
+    for (int tk = 0; tk < T; ++tk) {
+        i32x4 qa[NB];
+        uint32_t wr[NB][4];
+#pragma unroll
+        for (int mb = 0; mb < NB; ++mb) {
+            qa[mb] = s_q[((tk * NB + mb) * 16 + (l & 15)) * 4 + (l >> 4)];
+            const uint32_t word = s_w[tk * 16 + 4 * mb + (l >> 4)];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) wr[mb][i] = (word >> (8 * i)) & 0xFFu;
+        }
+        // per-token lists: this token's plane and its own count of positions
+        const int nv = planes == 1 ? nvalid : min(kTile, ti.E - (T - 1 - tk) - p_tile);
+        int* sc_out = seq_stride < 0
+                          ? score_out + (size_t)(planes == 1 ? g : tk * TB + g) * kTile
+                          : score_out + ((size_t)b * planes + (planes == 1 ? 0 : tk)) *
+                                            (size_t)seq_stride + p_tile;
+        uint32_t* hist = s_hist + (planes == 1 ? 0 : tk * kKeyBins);
+#pragma unroll
+        for (int it = 0; it < kGroups / 4; ++it) {
+            if (t0 + 64 * it >= nvalid) break;                 // wave-uniform
+            uint32_t part[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) part[u] = score_partial16<NB>(qa, wr, kop[4 * it + u]);
+            const int mine = (int)reduce_rows4(part);          // token t0 + 64 it + l
+            const int pos = t0 + 64 * it + l;
+            if (planes == 1) {
+                best[it] = tk == 0 ? mine : max(best[it], mine);
+            } else if (pos < nv) {
+                sc_out[pos] = mine;
+                atomicAdd(&hist[score_key(mine)], 1u);
+            }
+        }
+    }
+    if (planes == 1) {
+        int* sc_out = seq_stride < 0 ? score_out + (size_t)g * kTile
+                                     : score_out + (size_t)b * seq_stride + p_tile;
+#pragma unroll
+        for (int it = 0; it < kGroups / 4; ++it) {
+            const int pos = t0 + 64 * it + l;
+            if (pos < nvalid) {
+                sc_out[pos] = best[it];
+                atomicAdd(&s_hist[score_key(best[it])], 1u);
+            }
+        }
+    }
+    __syncthreads();
+    // per-tile histograms of the planes whose list reaches this tile
+    for (int pl = 0; pl < planes; ++pl) {
+        if (planes > 1 && ti.E - (T - 1 - pl) <= p_tile) continue;   // uniform
+        uint32_t* th = reinterpret_cast<uint32_t*>(w.tile_hist + (size_t)(pl * TB + g) * kKeyBins);
+        const uint32_t* sh = s_hist + pl * kKeyBins;
+        for (int i = threadIdx.x; i < kKeyBins / 2; i += kScoreThreads)
+            th[i] = sh[2 * i] | (sh[2 * i + 1] << 16);
+    }
 }
 
 // ---- 2. reduce the per-tile histograms ---------------------------------------------
@@ -908,6 +1064,73 @@ static int launch_score(int H, unsigned tiles, hipStream_t s, const signed char*
     return launch_status("full_score");
 }
 
+static int launch_score_block(int H, int T, int shared, unsigned TB, hipStream_t s,
+                              const signed char* q, const signed char* w, const signed char* keys,
+                              const long long* row_off, const int* len, int B, int window, int P,
+                              const FullWs& fw, int* out, long long seq_stride) {
+    const int planes = block_planes(T, shared);
+    // per-token lists: tiles over the last token's positions (it sees the
+    // most); shared list: over the first token's, the ones every token sees
+    const int win = shared ? window + T - 1 : window;
+    const int8_t* q8 = reinterpret_cast<const int8_t*>(q);
+    const int8_t* w8 = reinterpret_cast<const int8_t*>(w);
+    const int8_t* k8 = reinterpret_cast<const int8_t*>(keys);
+    const dim3 grid(TB), blk(kScoreThreads);
+    const int NB = (H + 15) / 16;
+    const size_t lds = block_score_lds(T, NB, planes);
+    const int tb = (int)TB;
+    switch (NB) {
+        case 1: hipLaunchKernelGGL(full_score_block_kernel<1>, grid, blk, lds, s, q8, w8, k8, row_off, len, B, H, win, P, fw, T, planes, tb, out, seq_stride); break;
+        case 2: hipLaunchKernelGGL(full_score_block_kernel<2>, grid, blk, lds, s, q8, w8, k8, row_off, len, B, H, win, P, fw, T, planes, tb, out, seq_stride); break;
+        case 3: hipLaunchKernelGGL(full_score_block_kernel<3>, grid, blk, lds, s, q8, w8, k8, row_off, len, B, H, win, P, fw, T, planes, tb, out, seq_stride); break;
+        default: hipLaunchKernelGGL(full_score_block_kernel<4>, grid, blk, lds, s, q8, w8, k8, row_off, len, B, H, win, P, fw, T, planes, tb, out, seq_stride); break;
+    }
+    return launch_status("full_score_block");
+}
+
+// Checks of the verify-block arguments: CSA2_OK or an error code.
+static int check_block_args(const char* fn, int B, int T, int shared, int window) {
+    if (T < 1 || shared < 0 || shared > 1)
+        return fail(CSA2_ERR_INVALID, "%s: T < 1 or shared not 0/1", fn);
+    if (T > kMaxBlockT) return fail(CSA2_ERR_UNSUPPORTED, "%s: T > %d", fn, kMaxBlockT);
+    if (window > (1 << 30)) return fail(CSA2_ERR_UNSUPPORTED, "%s: window > 2^30", fn);
+    if ((long long)B * block_planes(T, shared) > 65535)
+        return fail(CSA2_ERR_UNSUPPORTED, "%s: more than 65535 lists", fn);
+    return CSA2_OK;
+}
+
+// Kernels 2-5 over the lists of fw (fw.B lists, `tiles` tiles), whose
+// scores, per-tile histograms and initial states kernel 1 has written.
+static int launch_chain(const FullWs& fw, unsigned tiles, int P, int k, int* pool_pos,
+                        int* pool_score, int* pool_len, int* sel_pos, int* sel_len,
+                        hipStream_t s, const char* fn) {
+    const int ntg = k > 0 ? 2 : 1;
+    const int nl = fw.B;
+    const dim3 blk(kScanThreads);
+    hipLaunchKernelGGL(full_reduce_kernel, dim3(kKeyBins / kRedBins, nl), blk, 0, s, fw);
+    hipLaunchKernelGGL(full_gather_kernel, dim3(tiles, ntg), blk, 0, s, fw);
+    if (nl == 1)
+        hipLaunchKernelGGL(full_threshold_kernel<true>, dim3(nl, ntg), dim3(kThrThreads), 0, s, fw);
+    else
+        hipLaunchKernelGGL(full_threshold_kernel<false>, dim3(nl, ntg), dim3(kThrThreads), 0, s, fw);
+    const unsigned wgrid = tiles > (unsigned)nl ? tiles : (unsigned)nl;
+    const FullOut o0 = {pool_pos, pool_score, pool_len, P};
+    const FullOut o1 = {sel_pos, nullptr, sel_len, k};
+    hipLaunchKernelGGL(full_write_kernel, dim3(wgrid, ntg), blk, 0, s, fw, o0, o1);
+    return launch_status(fn);
+}
+
+// Checks of the pool and selection arguments shared by the Full entry points.
+static int check_pool_args(const char* fn, int P, int k, const int* pool_pos,
+                           const int* pool_score, const int* pool_len, const int* sel_pos,
+                           const int* sel_len) {
+    if (P < 1) return fail(CSA2_ERR_INVALID, "%s: P < 1", fn);
+    if (k < 0 || k > P) return fail(CSA2_ERR_INVALID, "%s: k must be in [0, P]", fn);
+    if (!pool_pos || !pool_score || !pool_len || (k > 0 && (!sel_pos || !sel_len)))
+        return fail(CSA2_ERR_INVALID, "%s: null pointer", fn);
+    return CSA2_OK;
+}
+
 }  // namespace csa2
 
 using namespace csa2;
@@ -918,40 +1141,59 @@ extern "C" int csa2_index_full(const signed char* q, const signed char* w,
                                int H, int Dk, int window, int P, int* pool_pos,
                                int* pool_score, int* pool_len, int k, int* sel_pos,
                                int* sel_len, void* ws, size_t ws_bytes, void* stream) {
-    if (int e = check_scan_args("csa2_index_full", q, w, keys, row_off, len, B, max_len,
-                                total_len, H, Dk, window))
+    const char* fn = "csa2_index_full";
+    if (int e = check_scan_args(fn, q, w, keys, row_off, len, B, max_len, total_len, H, Dk,
+                                window))
         return e;
     if (B == 0) return CSA2_OK;
-    if (P < 1) return fail(CSA2_ERR_INVALID, "csa2_index_full: P < 1");
-    if (k < 0 || k > P) return fail(CSA2_ERR_INVALID, "csa2_index_full: k must be in [0, P]");
-    if (!pool_pos || !pool_score || !pool_len || (k > 0 && (!sel_pos || !sel_len)))
-        return fail(CSA2_ERR_INVALID, "csa2_index_full: null pointer");
+    if (int e = check_pool_args(fn, P, k, pool_pos, pool_score, pool_len, sel_pos, sel_len))
+        return e;
     const size_t need = index_full_ws_bytes(B, total_len, P, k);
     if (!ws || ws_bytes < need || !aligned(ws, 256))
-        return fail(CSA2_ERR_WORKSPACE, "csa2_index_full: workspace needs %zu bytes (256-aligned)",
-                    need);
+        return fail(CSA2_ERR_WORKSPACE, "%s: workspace needs %zu bytes (256-aligned)", fn, need);
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const long long tiles = full_tile_bound(B, total_len);
     FullWs fw;
-    const int ntg = k > 0 ? 2 : 1;
-    full_ws_layout(B, total_len, ntg, reinterpret_cast<char*>(ws), &fw);
+    full_ws_layout(B, tiles, k > 0 ? 2 : 1, reinterpret_cast<char*>(ws), &fw);
     fw.k = k;
-    const unsigned tiles = (unsigned)full_tile_bound(B, total_len);
-    const dim3 blk(kScanThreads);
-
-    if (int e = launch_score(H, tiles, s, q, w, keys, row_off, len, B, window, P, fw, fw.scores,
-                             -1))
+    if (int e = launch_score(H, (unsigned)tiles, s, q, w, keys, row_off, len, B, window, P, fw,
+                             fw.scores, -1))
         return e;
-    hipLaunchKernelGGL(full_reduce_kernel, dim3(kKeyBins / kRedBins, B), blk, 0, s, fw);
-    hipLaunchKernelGGL(full_gather_kernel, dim3(tiles, ntg), blk, 0, s, fw);
-    if (B == 1)
-        hipLaunchKernelGGL(full_threshold_kernel<true>, dim3(B, ntg), dim3(kThrThreads), 0, s, fw);
-    else
-        hipLaunchKernelGGL(full_threshold_kernel<false>, dim3(B, ntg), dim3(kThrThreads), 0, s, fw);
-    const unsigned wgrid = tiles > (unsigned)B ? tiles : (unsigned)B;
-    const FullOut o0 = {pool_pos, pool_score, pool_len, P};
-    const FullOut o1 = {sel_pos, nullptr, sel_len, k};
-    hipLaunchKernelGGL(full_write_kernel, dim3(wgrid, ntg), blk, 0, s, fw, o0, o1);
-    return launch_status("csa2_index_full launch");
+    return launch_chain(fw, (unsigned)tiles, P, k, pool_pos, pool_score, pool_len, sel_pos,
+                        sel_len, s, "csa2_index_full launch");
+}
+
+extern "C" int csa2_index_full_block(const signed char* q, const signed char* w,
+                                     const signed char* keys, const long long* row_off,
+                                     const int* len, int B, int T, int shared, long long max_len,
+                                     long long total_len, int H, int Dk, int window, int P,
+                                     int* pool_pos, int* pool_score, int* pool_len, int k,
+                                     int* sel_pos, int* sel_len, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    const char* fn = "csa2_index_full_block";
+    if (int e = check_scan_args(fn, q, w, keys, row_off, len, B, max_len, total_len, H, Dk,
+                                window))
+        return e;
+    if (int e = check_block_args(fn, B, T, shared, window)) return e;
+    if (B == 0) return CSA2_OK;
+    if (int e = check_pool_args(fn, P, k, pool_pos, pool_score, pool_len, sel_pos, sel_len))
+        return e;
+    const int planes = block_planes(T, shared);
+    const size_t need = index_full_block_ws_bytes(B, T, shared, total_len, k);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+        return fail(CSA2_ERR_WORKSPACE, "%s: workspace needs %zu bytes (256-aligned)", fn, need);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const long long TB = full_tile_bound(B, total_len);
+    FullWs fw;
+    full_ws_layout(B * planes, planes * TB, k > 0 ? 2 : 1, reinterpret_cast<char*>(ws), &fw);
+    fw.k = k;
+    // per-token lists: tiles over the last token's positions (it sees the
+    // most); shared list: over the first token's, the ones every token sees
+    if (int e = launch_score_block(H, T, shared, (unsigned)TB, s, q, w, keys, row_off, len, B,
+                                   window, P, fw, fw.scores, -1))
+        return e;
+    return launch_chain(fw, (unsigned)(planes * TB), P, k, pool_pos, pool_score, pool_len,
+                        sel_pos, sel_len, s, "csa2_index_full_block launch");
 }
 
 extern "C" int csa2_index_score(const signed char* q, const signed char* w,
@@ -969,8 +1211,31 @@ extern "C" int csa2_index_score(const signed char* q, const signed char* w,
         return fail(CSA2_ERR_WORKSPACE,
                     "csa2_index_score: workspace needs %zu bytes (256-aligned)", need);
     FullWs fw;
-    full_ws_layout(B, total_len, 1, reinterpret_cast<char*>(ws), &fw);
+    full_ws_layout(B, full_tile_bound(B, total_len), 1, reinterpret_cast<char*>(ws), &fw);
     const unsigned tiles = (unsigned)full_tile_bound(B, total_len);
     return launch_score(H, tiles, reinterpret_cast<hipStream_t>(stream), q, w, keys, row_off, len,
                         B, window, 1, fw, score, max_len);
+}
+
+extern "C" int csa2_index_score_block(const signed char* q, const signed char* w,
+                                      const signed char* keys, const long long* row_off,
+                                      const int* len, int B, int T, int shared, long long max_len,
+                                      long long total_len, int H, int Dk, int window, int* score,
+                                      void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "csa2_index_score_block";
+    if (int e = check_scan_args(fn, q, w, keys, row_off, len, B, max_len, total_len, H, Dk,
+                                window))
+        return e;
+    if (int e = check_block_args(fn, B, T, shared, window)) return e;
+    if (B == 0) return CSA2_OK;
+    if (!score) return fail(CSA2_ERR_INVALID, "%s: null pointer", fn);
+    const size_t need = index_full_block_ws_bytes(B, T, shared, total_len, 0);
+    if (!ws || ws_bytes < need || !aligned(ws, 256))
+        return fail(CSA2_ERR_WORKSPACE, "%s: workspace needs %zu bytes (256-aligned)", fn, need);
+    const int planes = block_planes(T, shared);
+    const long long TB = full_tile_bound(B, total_len);
+    FullWs fw;
+    full_ws_layout(B * planes, planes * TB, 1, reinterpret_cast<char*>(ws), &fw);
+    return launch_score_block(H, T, shared, (unsigned)TB, reinterpret_cast<hipStream_t>(stream), q,
+                              w, keys, row_off, len, B, window, 1, fw, score, max_len);
 }

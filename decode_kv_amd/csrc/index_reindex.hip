@@ -13,28 +13,36 @@ namespace csa2 {
 
 constexpr int kReThreads = 256;  // 4 waves x 64 candidates
 
+// List y of a verify block of T tokens per sequence: shared (one list per
+// sequence, scored with the best score over the block's tokens) or per token
+// (list y = b * T + t, scored with token t's query).  T == 1 is the plain
+// one-token step.
 template <int NB>
 __global__ __launch_bounds__(kReThreads) void reindex_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ wts,
     const int8_t* __restrict__ keys, const long long* __restrict__ row_off,
     const int* __restrict__ cand_pos, const int* __restrict__ cand_len, int H, int P,
-    int* __restrict__ score) {
-    const int b = blockIdx.y;
+    int* __restrict__ score, int T, int shared) {
+    const int y = blockIdx.y;
+    const int b = shared || T == 1 ? y : y / T;         // sequence: its keys
+    const int tk0 = shared ? 0 : y - b * T;              // tokens tk0 .. tk1 - 1 score the list
+    const int tk1 = shared ? T : tk0 + 1;
     const int l = lane_id();
     const int base = blockIdx.x * kReThreads + (threadIdx.x / kWave) * kWave;
     if (base >= P) return;
-    const int* cp = cand_pos + (size_t)b * P;
-    int* out = score + (size_t)b * P;
+    const int* cp = cand_pos + (size_t)y * P;
+    int* out = score + (size_t)y * P;
     // round trip 1: the list length, this wave's four groups of candidate
     // positions (indices clamped into the row, so every load is unconditional),
     // the index query and the row offset
     int pos[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) pos[u] = cp[min(base + 16 * u + (l & 15), P - 1)];
-    const int n = min(cand_len[b], P);
+    const int n = min(cand_len[y], P);
     i32x4 qa[NB];
     uint32_t wr[NB][4];
-    load_index_query<NB>(q + (size_t)b * H * kDk, wts + (size_t)b * H, H, qa, wr);
+    const size_t qrow = (size_t)b * T + tk0;             // the first token's query
+    load_index_query<NB>(q + qrow * H * kDk, wts + qrow * H, H, qa, wr);
     const long long roff = row_off[b];
     if (base >= n) {
         if (base + l < P) out[base + l] = -1;
@@ -54,9 +62,47 @@ __global__ __launch_bounds__(kReThreads) void reindex_kernel(
     uint32_t part[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) part[u] = score_partial16<NB>(qa, wr, kop[u]);
-    const int mine = (int)reduce_rows4(part);          // candidate base + l
+    int mine = (int)reduce_rows4(part);                // candidate base + l
+    for (int tk = tk0 + 1; tk < tk1; ++tk) {             // shared list: best over the block
+        const size_t r = (size_t)b * T + tk;
+        load_index_query<NB>(q + r * H * kDk, wts + r * H, H, qa, wr);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) part[u] = score_partial16<NB>(qa, wr, kop[u]);
+        mine = max(mine, (int)reduce_rows4(part));
+    }
     const int i = base + l;
     if (i < P) out[i] = i < n ? mine : -1;
+}
+
+static int reindex(const char* fn, const signed char* q, const signed char* w,
+                   const signed char* keys, const long long* row_off, const int* cand_pos,
+                   const int* cand_len, int B, int T, int shared, int H, int Dk, int P,
+                   int* score, void* stream) {
+    if (B < 0) return fail(CSA2_ERR_INVALID, "%s: B < 0", fn);
+    if (T < 1 || shared < 0 || shared > 1)
+        return fail(CSA2_ERR_INVALID, "%s: T < 1 or shared not 0/1", fn);
+    if (B == 0) return CSA2_OK;
+    if (!q || !w || !keys || !row_off || !cand_pos || !cand_len || !score)
+        return fail(CSA2_ERR_INVALID, "%s: null pointer", fn);
+    if (Dk != kDk) return fail(CSA2_ERR_UNSUPPORTED, "%s: Dk must be 64", fn);
+    if (H < 1 || H > 64) return fail(CSA2_ERR_INVALID, "%s: H must be in [1, 64]", fn);
+    if (P < 1) return fail(CSA2_ERR_INVALID, "%s: P < 1", fn);
+    const long long lists = shared ? (long long)B : (long long)B * T;
+    if (lists > 65535) return fail(CSA2_ERR_UNSUPPORTED, "%s: more than 65535 lists", fn);
+    if (!aligned(q, 16) || !aligned(keys, 16) || !aligned(row_off, 8))
+        return fail(CSA2_ERR_INVALID, "%s: misaligned pointer", fn);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const dim3 grid((P + kReThreads - 1) / kReThreads, (unsigned)lists);
+    const int8_t* q8 = reinterpret_cast<const int8_t*>(q);
+    const int8_t* w8 = reinterpret_cast<const int8_t*>(w);
+    const int8_t* k8 = reinterpret_cast<const int8_t*>(keys);
+    switch ((H + 15) / 16) {
+        case 1: hipLaunchKernelGGL(reindex_kernel<1>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T, shared); break;
+        case 2: hipLaunchKernelGGL(reindex_kernel<2>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T, shared); break;
+        case 3: hipLaunchKernelGGL(reindex_kernel<3>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T, shared); break;
+        default: hipLaunchKernelGGL(reindex_kernel<4>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T, shared); break;
+    }
+    return launch_status(fn);
 }
 
 }  // namespace csa2
@@ -67,26 +113,15 @@ extern "C" int csa2_index_reindex(const signed char* q, const signed char* w,
                                   const signed char* keys, const long long* row_off,
                                   const int* cand_pos, const int* cand_len, int B, int H,
                                   int Dk, int P, int* score, void* stream) {
-    if (B < 0) return fail(CSA2_ERR_INVALID, "csa2_index_reindex: B < 0");
-    if (B == 0) return CSA2_OK;
-    if (!q || !w || !keys || !row_off || !cand_pos || !cand_len || !score)
-        return fail(CSA2_ERR_INVALID, "csa2_index_reindex: null pointer");
-    if (Dk != kDk) return fail(CSA2_ERR_UNSUPPORTED, "csa2_index_reindex: Dk must be 64");
-    if (H < 1 || H > 64) return fail(CSA2_ERR_INVALID, "csa2_index_reindex: H must be in [1, 64]");
-    if (P < 1) return fail(CSA2_ERR_INVALID, "csa2_index_reindex: P < 1");
-    if (B > 65535) return fail(CSA2_ERR_UNSUPPORTED, "csa2_index_reindex: B > 65535");
-    if (!aligned(q, 16) || !aligned(keys, 16) || !aligned(row_off, 8))
-        return fail(CSA2_ERR_INVALID, "csa2_index_reindex: misaligned pointer");
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    const dim3 grid((P + kReThreads - 1) / kReThreads, B);
-    const int8_t* q8 = reinterpret_cast<const int8_t*>(q);
-    const int8_t* w8 = reinterpret_cast<const int8_t*>(w);
-    const int8_t* k8 = reinterpret_cast<const int8_t*>(keys);
-    switch ((H + 15) / 16) {
-        case 1: hipLaunchKernelGGL(reindex_kernel<1>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score); break;
-        case 2: hipLaunchKernelGGL(reindex_kernel<2>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score); break;
-        case 3: hipLaunchKernelGGL(reindex_kernel<3>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score); break;
-        default: hipLaunchKernelGGL(reindex_kernel<4>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score); break;
-    }
-    return launch_status("csa2_index_reindex launch");
+    return reindex("csa2_index_reindex", q, w, keys, row_off, cand_pos, cand_len, B, 1, 0, H, Dk,
+                   P, score, stream);
+}
+
+extern "C" int csa2_index_reindex_block(const signed char* q, const signed char* w,
+                                        const signed char* keys, const long long* row_off,
+                                        const int* cand_pos, const int* cand_len, int B, int T,
+                                        int shared, int H, int Dk, int P, int* score,
+                                        void* stream) {
+    return reindex("csa2_index_reindex_block", q, w, keys, row_off, cand_pos, cand_len, B, T,
+                   shared, H, Dk, P, score, stream);
 }

@@ -118,6 +118,12 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 // Placement flags of the attention and combine launches.
 constexpr int kPlaceSeq = 1;     // sequence b (all head groups and splits) on XCD b mod 8
 constexpr int kPlacePlain = 2;   // split partials stored with plain stores (they fit in L2)
+// A verify block of T tokens per sequence (flags bits 8-15 hold T, 0 meaning
+// 1): query row b of the launch is token t = b mod T of sequence b / T, which
+// sees the positions before len - (T - 1 - t).  With kBlockShared every token
+// of a sequence attends to the sequence's one selection, else row b has its own.
+constexpr int kBlockShared = 16;
+constexpr int kBlockShift = 8;
 
 // Workgroup i runs on XCD i mod 8.  Pair-major placement puts (sequence, head
 // group) pair p on XCD p mod 8: at one sequence its four head groups use four
@@ -172,8 +178,11 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     const int t_begin = split * TPW;
 
     // round trip 1: sequence scalars, this thread's selection entries, q
-    const int len_b = len[b], sel_b = sel_len[b];
-    const long long roff = row_off[b];
+    const int bt = flags >> kBlockShift;
+    const int bs = bt > 1 ? b / bt : b;                        // the sequence of query row b
+    const int bsel = bt > 1 && (flags & kBlockShared) ? bs : b;   // the row of its selection
+    const int len_b = len[bs] - (bt > 1 ? bt - 1 - (b - bs * bt) : 0), sel_b = sel_len[bsel];
+    const long long roff = row_off[bs];
     // loads of a tile: thread t takes the 32 bytes of codes of row crow at
     // bytes 32 c8 .. (latent elements 64 c8 ..) and their two scales; each
     // wave takes 8 whole rows
@@ -182,7 +191,7 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         const int jc = (t_begin + t) * kAttnRows + crow;
-        spc[t] = jc < k ? sel_pos[(size_t)b * k + jc] : -1;
+        spc[t] = jc < k ? sel_pos[(size_t)bsel * k + jc] : -1;
     }
     // q . v is split over the latent dimension: wave w owns d in [128w, 128w+128)
     constexpr int kKs = kAttnD / 32 / (kAttnThreads / kWave);   // 4 k-steps per wave
@@ -592,15 +601,22 @@ size_t sparse_attn_ws_bytes(int B, int Hq, int D, int k, int window) {
 // combine launches with the split partials in the scratch that get_ws(need,
 // &ptr) supplies once the sizes are known to be valid.  fn names the entry
 // point in error messages.
+// T and shared describe a verify block (T == 1: one token per sequence); the
+// launch then has B * T query rows.
 template <typename GetWs>
 static int attn_decode(const char* fn, const void* q_bf16, const unsigned char* kv_fp4,
                        const unsigned char* kv_scale, const long long* row_off, const int* len,
-                       long long max_len, const int* sel_pos, const int* sel_len, int B, int Hq,
-                       int D, int k, int window, float sm_scale, float* out, float* lse,
-                       GetWs get_ws, void* stream) {
+                       long long max_len, const int* sel_pos, const int* sel_len, int B, int T,
+                       int shared, int Hq, int D, int k, int window, float sm_scale, float* out,
+                       float* lse, GetWs get_ws, void* stream) {
     if (B < 0 || max_len < 0 || k < 0 || window < 0)
         return fail(CSA2_ERR_INVALID, "%s: negative size", fn);
+    if (T < 1 || shared < 0 || shared > 1)
+        return fail(CSA2_ERR_INVALID, "%s: T < 1 or shared not 0/1", fn);
+    if (T > 255) return fail(CSA2_ERR_UNSUPPORTED, "%s: T > 255", fn);
     if (B == 0) return CSA2_OK;
+    if ((long long)B * T > 65535) return fail(CSA2_ERR_UNSUPPORTED, "%s: B * T > 65535", fn);
+    B *= T;                                              // query rows of the launch
     if (!q_bf16 || !kv_fp4 || !kv_scale || !row_off || !len || !sel_len || !out ||
         (k > 0 && !sel_pos))
         return fail(CSA2_ERR_INVALID, "%s: null pointer", fn);
@@ -631,7 +647,8 @@ static int attn_decode(const char* fn, const void* q_bf16, const unsigned char* 
     const bool seq = B >= 8;
     const long long per_xcd = seq ? (long long)((B + 7) / 8) * HG : (npairs + 7) / 8;
     const bool plain = per_xcd * ns * kHeadsPerWg * (kAttnD * 4 + 16) <= (3ll << 20);
-    const int flags = (seq ? kPlaceSeq : 0) | (plain ? kPlacePlain : 0);
+    const int flags = (seq ? kPlaceSeq : 0) | (plain ? kPlacePlain : 0) |
+                      (T > 1 && shared ? kBlockShared : 0) | (T > 1 ? T << kBlockShift : 0);
     const int pr = seq ? (int)((B + 7) / 8) * HG : (npairs + 7) / 8;   // slots per XCD / splits
     const dim3 grid(8 * pr * ns), blk(kAttnThreads);
     const uint16_t* q16 = reinterpret_cast<const uint16_t*>(q_bf16);
@@ -725,7 +742,7 @@ extern "C" int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* 
         return CSA2_OK;
     };
     return attn_decode(fn, q_bf16, kv_fp4, kv_scale, row_off, len, max_len, sel_pos, sel_len, B,
-                       Hq, D, k, window, sm_scale, out, lse, caller_ws, stream);
+                       1, 0, Hq, D, k, window, sm_scale, out, lse, caller_ws, stream);
 }
 
 extern "C" int csa2_sparse_attn_decode_static(const void* q_bf16, const unsigned char* kv_fp4,
@@ -748,5 +765,24 @@ extern "C" int csa2_sparse_attn_decode_static(const void* q_bf16, const unsigned
         return static_scratch(fn, reinterpret_cast<hipStream_t>(stream), p);
     };
     return attn_decode(fn, q_bf16, kv_fp4, kv_scale, row_off, len, max_len, sel_pos, sel_len, B,
-                       Hq, D, k, window, sm_scale, out, lse, static_ws, stream);
+                       1, 0, Hq, D, k, window, sm_scale, out, lse, static_ws, stream);
+}
+
+extern "C" int csa2_sparse_attn_decode_block(const void* q_bf16, const unsigned char* kv_fp4,
+                                             const unsigned char* kv_scale,
+                                             const long long* row_off, const int* len,
+                                             long long max_len, const int* sel_pos,
+                                             const int* sel_len, int B, int T, int shared, int Hq,
+                                             int D, int k, int window, float sm_scale, float* out,
+                                             float* lse, void* ws, size_t ws_bytes, void* stream) {
+    const char* fn = "csa2_sparse_attn_decode_block";
+    auto caller_ws = [&](size_t need, void** p) -> int {
+        if (need > 0 && (!ws || ws_bytes < need || !aligned(ws, 256)))
+            return fail(CSA2_ERR_WORKSPACE, "%s: workspace needs %zu bytes (256-aligned)", fn,
+                        need);
+        *p = ws;
+        return CSA2_OK;
+    };
+    return attn_decode(fn, q_bf16, kv_fp4, kv_scale, row_off, len, max_len, sel_pos, sel_len, B,
+                       T, shared, Hq, D, k, window, sm_scale, out, lse, caller_ws, stream);
 }

@@ -8,7 +8,9 @@ recent Full layer's pool, a Reuse layer attends with the most recent
 selection.  Every layer then attends over its selection plus the window.
 With appends, one library call first writes the new token's FP4 rows (every
 layer) and index key at the device-side length and advances it, so the token
-attends to itself.
+attends to itself.  A verify block of T drafted tokens per sequence appends
+its T tokens (one call each) and runs the block variants of the calls, which
+score, select and attend for all T tokens at once.
 """
 from __future__ import annotations
 
@@ -56,20 +58,23 @@ class Engine:
         self.max_len = max(case.caps)
         self.total_len = sum(case.caps)
         self._fill_kv()
-        B, P, k = wl.B, wl.P, wl.k
+        B, P, k, T = wl.B, wl.P, wl.k, wl.block
+        nl = wl.n_lists                      # pools / selections: per sequence or per token
         i32 = dict(dtype=torch.int32, device=dev)
-        self.pool_pos = torch.full((B, P), -7, **i32)
-        self.pool_score = torch.full((B, P), -7, **i32)
-        self.pool_len = torch.zeros(B, **i32)
-        self.rscore = torch.full((wl.n_layers, B, P), -7, **i32)
-        self.sel_pos = torch.full((wl.n_layers, B, k), -7, **i32)
-        self.sel_len = torch.zeros((wl.n_layers, B), **i32)
-        self.out = torch.zeros((wl.n_layers, B, wl.Hq, wl.D), dtype=torch.float32, device=dev)
-        self.lse = torch.zeros((wl.n_layers, B, wl.Hq), dtype=torch.float32, device=dev)
-        self.ws_full = csa2.workspace(csa2.workspace_bytes(
-            csa2.OP_INDEX_FULL, B, self.max_len, self.total_len, wl.H, P, wl.k), dev)
-        self.ws_attn = csa2.workspace(csa2.workspace_bytes(
-            csa2.OP_SPARSE_ATTN, B, self.max_len, 0, 0, 0, k, wl.Hq, wl.D, wl.window), dev)
+        self.pool_pos = torch.full((nl, P), -7, **i32)
+        self.pool_score = torch.full((nl, P), -7, **i32)
+        self.pool_len = torch.zeros(nl, **i32)
+        self.rscore = torch.full((wl.n_layers, nl, P), -7, **i32)
+        self.sel_pos = torch.full((wl.n_layers, nl, k), -7, **i32)
+        self.sel_len = torch.zeros((wl.n_layers, nl), **i32)
+        rows = (B,) if T == 1 else (B, T)   # query rows: a token per sequence, or a block
+        self.out = torch.zeros((wl.n_layers, *rows, wl.Hq, wl.D), dtype=torch.float32, device=dev)
+        self.lse = torch.zeros((wl.n_layers, *rows, wl.Hq), dtype=torch.float32, device=dev)
+        sh = wl.block_shared
+        self.ws_full = csa2.workspace(csa2.block_workspace_bytes(
+            csa2.OP_INDEX_FULL, B, T, sh, self.max_len, self.total_len, wl.H, P, wl.k), dev)
+        self.ws_attn = csa2.workspace(csa2.block_workspace_bytes(
+            csa2.OP_SPARSE_ATTN, B, T, sh, self.max_len, 0, 0, 0, k, wl.Hq, wl.D, wl.window), dev)
 
     # ---- cache fill (set-up, not part of a step) --------------------------
     def _fill_kv(self, chunk_rows: int = 1 << 16):
@@ -112,14 +117,17 @@ class Engine:
                 inp["idx_q"][l], inp["idx_w"][l] = q.to(self.device), w.to(self.device)
             inp["attn_q"].append(case.attn_q_batch(step, l).to(self.device))
         if wl.append:
-            # the token of step `step` sits at position L0 + step; the library
-            # writes it at the device-side length, which equals that position
-            # when the steps run in order
-            pos = [L + step for L in case.lengths]
-            xs = [case.kv_bf16(l, b, [pos[b]]) for l in range(wl.n_kv) for b in range(wl.B)]
-            inp["app_x"] = torch.cat(xs).view(wl.n_kv, wl.B, wl.D).to(self.device).contiguous()
-            inp["key_rows"] = torch.stack([case.key_row(b, pos[b]) for b in range(wl.B)]) \
-                .to(self.device).contiguous()
+            # token j of step `step` sits at position L0 + step * T + j; the
+            # library writes it at the device-side length, which equals that
+            # position when the steps run in order
+            T = wl.block
+            xs, ks = [], []
+            for j in range(T):
+                pos = [L + step * T + j for L in case.lengths]
+                xs += [case.kv_bf16(l, b, [pos[b]]) for l in range(wl.n_kv) for b in range(wl.B)]
+                ks += [case.key_row(b, pos[b]) for b in range(wl.B)]
+            inp["app_x"] = torch.cat(xs).view(T, wl.n_kv, wl.B, wl.D).to(self.device).contiguous()
+            inp["key_rows"] = torch.stack(ks).view(T, wl.B, wl.Dk).to(self.device).contiguous()
         return inp
 
     # ---- one step -------------------------------------------------------------
@@ -132,31 +140,45 @@ class Engine:
         s = stream
         note = mark if mark is not None else (lambda name: None)
         if wl.append:
-            csa2.append_token(inp["app_x"], inp["key_rows"], self.row_off, self.lens,
-                              self.kv_fp4, self.kv_scale, self.keys, s)
+            for j in range(wl.block):        # a block's tokens in order, each advancing len
+                csa2.append_token(inp["app_x"][j], inp["key_rows"][j], self.row_off, self.lens,
+                                  self.kv_fp4, self.kv_scale, self.keys, s)
             note("append")
+        blk = wl.block > 1
+        sh = wl.block_shared
         src = None
         for l, kind in enumerate(self.pattern):
             if kind == "F":
-                csa2.index_full(inp["idx_q"][l], inp["idx_w"][l], self.keys, self.row_off,
-                                self.lens, self.max_len, self.total_len, wl.window, wl.P,
-                                self.pool_pos, self.pool_score, self.pool_len, self.ws_full, s,
-                                k=wl.k, sel_pos=self.sel_pos[l], sel_len=self.sel_len[l])
+                full = csa2.index_full_block if blk else csa2.index_full
+                extra = (sh,) if blk else ()
+                full(inp["idx_q"][l], inp["idx_w"][l], self.keys, self.row_off, self.lens,
+                     self.max_len, self.total_len, wl.window, wl.P, *extra, self.pool_pos,
+                     self.pool_score, self.pool_len, self.ws_full, s, k=wl.k,
+                     sel_pos=self.sel_pos[l], sel_len=self.sel_len[l])
                 note("full")
                 src = l
             elif kind == "R":
-                csa2.index_reindex(inp["idx_q"][l], inp["idx_w"][l], self.keys, self.row_off,
-                                   self.pool_pos, self.pool_len, self.rscore[l], s)
+                if blk:
+                    csa2.index_reindex_block(inp["idx_q"][l], inp["idx_w"][l], self.keys,
+                                             self.row_off, self.pool_pos, self.pool_len, sh,
+                                             self.rscore[l], s)
+                else:
+                    csa2.index_reindex(inp["idx_q"][l], inp["idx_w"][l], self.keys, self.row_off,
+                                       self.pool_pos, self.pool_len, self.rscore[l], s)
                 note("reindex")
                 csa2.select_topk(self.rscore[l], self.pool_pos, self.pool_len, wl.k,
                                  self.sel_pos[l], self.sel_len[l], None, s)
                 note("select")
                 src = l
             kl = wl.kv_layer(l)
-            csa2.sparse_attn_decode(inp["attn_q"][l], self.kv_fp4[kl], self.kv_scale[kl],
-                                    self.row_off, self.lens, self.max_len, self.sel_pos[src],
-                                    self.sel_len[src], wl.k, wl.window, wl.sm_scale,
-                                    self.out[l], self.lse[l], self.ws_attn, s)
+            args = (self.kv_fp4[kl], self.kv_scale[kl], self.row_off, self.lens, self.max_len,
+                    self.sel_pos[src], self.sel_len[src], wl.k, wl.window)
+            if blk:
+                csa2.sparse_attn_decode_block(inp["attn_q"][l], *args, sh, wl.sm_scale,
+                                              self.out[l], self.lse[l], self.ws_attn, s)
+            else:
+                csa2.sparse_attn_decode(inp["attn_q"][l], *args, wl.sm_scale, self.out[l],
+                                        self.lse[l], self.ws_attn, s)
             note("attn")
         return src
 

@@ -1,6 +1,6 @@
 """The synthetic decode workloads and their seeded inputs.
 
-Five workloads, named by what they are:
+The workloads, named by what they are:
 
   tiny_4k       L=4,096, 1 sequence, one Full layer (P=1,024, k=64), 4 index
                 heads, 16 query heads; uniform int8 keys + 8 planted keys.
@@ -18,6 +18,10 @@ Five workloads, named by what they are:
   ctx_1m_shared, ragged32_1m_shared
                 the same with one FP4 latent cache shared by all 20 layers
                 (one append per sequence per step).
+  ctx_1m_block5, batch8_256k_block5 (and *_shared)
+                verify blocks of 5 tokens per sequence: ctx_1m verifying its
+                last 5 cached positions, batch8_256k appending and verifying 5
+                tokens per sequence and step; per-token or shared selection.
 
 Everywhere: window 128, index key dim 64, latent dim 512, softmax scale
 1/sqrt(512).  Nothing here computes any part of the method; the only
@@ -54,6 +58,8 @@ class Workload:
     append: bool
     redraw_queries: bool
     shared_kv: bool = False                # one FP4 latent cache read by every layer
+    block: int = 1                         # tokens verified per step (a drafted block)
+    block_shared: bool = False             # the block's tokens share one pool / selection
     Dk: int = 64
     D: int = 512
 
@@ -73,6 +79,12 @@ class Workload:
     def kv_layer(self, l: int) -> int:
         """Cache that layer l attends to."""
         return 0 if self.shared_kv else l
+
+    @property
+    def n_lists(self) -> int:
+        """Pools / selections per step: one per sequence, or one per token
+        of a block whose tokens select on their own."""
+        return self.B if self.block == 1 or self.block_shared else self.B * self.block
 
     def scaled(self, **kw) -> "Workload":
         return dataclasses.replace(self, **kw)
@@ -107,6 +119,18 @@ WORKLOADS = {
 WORKLOADS["ctx_1m_shared"] = WORKLOADS["ctx_1m"].scaled(name="ctx_1m_shared", shared_kv=True)
 WORKLOADS["ragged32_1m_shared"] = WORKLOADS["ragged32_1m"].scaled(name="ragged32_1m_shared",
                                                                   shared_kv=True)
+# Verify blocks: five drafted tokens checked in one step, each token with its
+# own pool and selection, or one shared by the block (the pages give the block
+# size, not how its tokens share the selection).  The block's tokens are the
+# last five cached positions; the batched variant appends five tokens per
+# sequence and step before verifying them.
+WORKLOADS["ctx_1m_block5"] = WORKLOADS["ctx_1m"].scaled(name="ctx_1m_block5", block=5)
+WORKLOADS["ctx_1m_block5_shared"] = WORKLOADS["ctx_1m"].scaled(name="ctx_1m_block5_shared",
+                                                               block=5, block_shared=True)
+WORKLOADS["batch8_256k_block5"] = WORKLOADS["batch8_256k"].scaled(name="batch8_256k_block5",
+                                                                  block=5)
+WORKLOADS["batch8_256k_block5_shared"] = WORKLOADS["batch8_256k"].scaled(
+    name="batch8_256k_block5_shared", block=5, block_shared=True)
 
 
 KV_POOL_ROWS = 1 << 20
@@ -121,7 +145,7 @@ class Case:
         self.seed = int(seed)
         self.device = torch.device(device)
         self.lengths = self._lengths()
-        extra = wl.steps if wl.append else 0
+        extra = wl.steps * wl.block if wl.append else 0
         self.caps = [L + extra for L in self.lengths]
         offs = np.zeros(wl.B, dtype=np.int64)
         if wl.B > 1:
@@ -140,37 +164,55 @@ class Case:
         return [int(min(hi, max(lo, x))) for x in L.tolist()]
 
     def lengths_at(self, step: int):
-        """Cached lengths seen by the layers of decode step `step` (an append
-        happens before the layers run)."""
-        return [L + (step + 1 if self.wl.append else 0) for L in self.lengths]
+        """Cached lengths seen by the layers of decode step `step` (the step's
+        appends, one token or a block of them, happen before the layers run)."""
+        wl = self.wl
+        return [L + ((step + 1) * wl.block if wl.append else 0) for L in self.lengths]
 
-    # ---- index queries / weights ---------------------------------------
-    def index_q(self, step: int, layer: int, b: int) -> torch.Tensor:
+    def _qkey(self, tag: int, step: int, layer: int, b: int, t: int) -> int:
         wl = self.wl
         st = step if wl.redraw_queries else 0
-        key = I.stream_key(self.seed, I.TAG_IDXQ, st, layer, b)
+        if wl.block == 1:
+            return I.stream_key(self.seed, tag, st, layer, b)
+        return I.stream_key(self.seed, tag, st, layer, b, t)
+
+    # ---- index queries / weights (token t of a block) ----------------------
+    def index_q(self, step: int, layer: int, b: int, t: int = 0) -> torch.Tensor:
+        wl = self.wl
+        key = self._qkey(I.TAG_IDXQ, step, layer, b, t)
         return I.int8_uniform(key, 0, wl.H * wl.Dk, self.device).view(wl.H, wl.Dk)
 
-    def index_w(self, step: int, layer: int, b: int) -> torch.Tensor:
+    def index_w(self, step: int, layer: int, b: int, t: int = 0) -> torch.Tensor:
         wl = self.wl
-        st = step if wl.redraw_queries else 0
-        key = I.stream_key(self.seed, I.TAG_IDXW, st, layer, b)
+        key = self._qkey(I.TAG_IDXW, step, layer, b, t)
         return I.int8_uniform(key, 0, wl.H, self.device, 0, 15)
 
     def index_qw_batch(self, step: int, layer: int):
-        q = torch.stack([self.index_q(step, layer, b) for b in range(self.wl.B)])
-        w = torch.stack([self.index_w(step, layer, b) for b in range(self.wl.B)])
+        """[B][H][Dk] and [B][H]; with blocks [B][T][H][Dk] and [B][T][H]."""
+        wl = self.wl
+        if wl.block == 1:
+            q = torch.stack([self.index_q(step, layer, b) for b in range(wl.B)])
+            w = torch.stack([self.index_w(step, layer, b) for b in range(wl.B)])
+        else:
+            q = torch.stack([torch.stack([self.index_q(step, layer, b, t) for t in range(wl.block)])
+                             for b in range(wl.B)])
+            w = torch.stack([torch.stack([self.index_w(step, layer, b, t) for t in range(wl.block)])
+                             for b in range(wl.B)])
         return q.contiguous(), w.contiguous()
 
     # ---- attention queries ---------------------------------------------
-    def attn_q(self, step: int, layer: int, b: int) -> torch.Tensor:
+    def attn_q(self, step: int, layer: int, b: int, t: int = 0) -> torch.Tensor:
         wl = self.wl
-        st = step if wl.redraw_queries else 0
-        key = I.stream_key(self.seed, I.TAG_ATTQ, st, layer, b)
+        key = self._qkey(I.TAG_ATTQ, step, layer, b, t)
         return I.bf16_normal(key, 0, wl.Hq * wl.D, self.device).view(wl.Hq, wl.D)
 
     def attn_q_batch(self, step: int, layer: int) -> torch.Tensor:
-        return torch.stack([self.attn_q(step, layer, b) for b in range(self.wl.B)]).contiguous()
+        """[B][Hq][D]; with blocks [B][T][Hq][D]."""
+        wl = self.wl
+        if wl.block == 1:
+            return torch.stack([self.attn_q(step, layer, b) for b in range(wl.B)]).contiguous()
+        return torch.stack([torch.stack([self.attn_q(step, layer, b, t) for t in range(wl.block)])
+                            for b in range(wl.B)]).contiguous()
 
     # ---- latent KV rows (bf16, before quantisation) ----------------------
     # The latent row of (layer, sequence, position) is row `kv_row_id` of a

@@ -265,6 +265,108 @@ int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* kv_fp4,
                             float sm_scale, float* out, float* lse,
                             void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * Verify blocks.  A decode step may check several drafted tokens at once: the
+ * T newest cached positions of a sequence (the last T tokens appended, all
+ * counted in len[b]) form its block, and token t = 0 .. T-1 sits at position
+ * L_t - 1 with L_t = len[b] - (T - 1 - t).  Token t sees positions 0 .. L_t - 1
+ * only: its window is [L_t - min(window, L_t), L_t) and its eligible positions
+ * are [0, E_t), E_t = max(0, L_t - window).  Two selection modes:
+ *  - per-token (shared == 0): every token has its own pool and selection,
+ *    ranked by its own scores over its own eligible positions; list b * T + t
+ *    of every [B][T][...] array below belongs to token t of sequence b;
+ *  - shared (shared == 1): one pool and one selection per sequence,
+ *    ranked by the best score over the block's tokens, max_t score_t(p), over
+ *    the positions every token may rank, [0, E_0).  Each token still attends
+ *    to its own window.
+ * With T == 1 both modes are the one-token calls above.
+ * ("DeepSeek Has Done It Again...", "Architecture and inference efficiency",
+ * the DSpark bullet: the main model checks several drafted tokens together,
+ * in blocks of five in the described set-up; "DeepSeek V4.1-Flash 552B runs
+ * like 16B (CED)", "DSpark, Engram & Single-Pass mHC": several tokens can be
+ * accepted in one step.  The pages do not say how the block's tokens share
+ * the sparse selection; both readings are provided.)
+ */
+
+/* Workspace of a verify-block call: csa2_workspace_bytes with the sizes of a
+ * block of T tokens per sequence.  CSA2_OP_SPARSE_ATTN and CSA2_OP_SELECT_TOPK
+ * need what the one-token op needs for B * T query rows. */
+size_t csa2_block_workspace_bytes(int op, int B, int T, int shared, long long max_len,
+                                  long long total_len, int H, int P, int k, int Hq, int D,
+                                  int window);
+
+/*
+ * csa2_index_full_block -- csa2_index_full for a verify block of T tokens per
+ * sequence.  The index keys are read once for all T tokens.
+ *   q        [B][T][H][Dk] int8 (token t's index query), 16-byte aligned.
+ *   w        [B][T][H] int8 head weights in [0, 15].
+ *   keys, row_off, len, max_len, total_len, H, Dk, window, P, k: as
+ *            csa2_index_full (len counts every token of the block).
+ *   shared   0: per-token lists; pool_pos / pool_score [B][T][P], pool_len
+ *            [B][T], sel_pos [B][T][k], sel_len [B][T].
+ *            1: one list per sequence; pool_pos / pool_score [B][P], pool_len
+ *            [B], sel_pos [B][k], sel_len [B]; the scores are the block's best.
+ *   ws, ws_bytes: csa2_block_workspace_bytes(CSA2_OP_INDEX_FULL, B, T, shared,
+ *            max_len, total_len, H, P, k, ...) bytes, 256-byte aligned.
+ * Requires 1 <= T <= 8 (else UNSUPPORTED) and the csa2_index_full limits;
+ * UNSUPPORTED when the call has more than 65535 lists.
+ */
+int csa2_index_full_block(const signed char* q, const signed char* w, const signed char* keys,
+                          const long long* row_off, const int* len, int B, int T, int shared,
+                          long long max_len, long long total_len, int H, int Dk, int window,
+                          int P, int* pool_pos, int* pool_score, int* pool_len, int k,
+                          int* sel_pos, int* sel_len, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_index_score_block -- the scoring stage of csa2_index_full_block alone.
+ *   q, w, keys, row_off, len, B, T, shared, max_len, total_len, H, Dk,
+ *            window: as csa2_index_full_block.
+ *   score    shared == 0: [B][T][max_len] int32 out, score[b][t][p] = token
+ *            t's score of position p for p < E_t (later entries not written);
+ *            shared == 1: [B][max_len], the best score over the block's tokens
+ *            for p < E_0.
+ *   ws, ws_bytes: as csa2_index_full_block with k = 0.
+ */
+int csa2_index_score_block(const signed char* q, const signed char* w, const signed char* keys,
+                           const long long* row_off, const int* len, int B, int T, int shared,
+                           long long max_len, long long total_len, int H, int Dk, int window,
+                           int* score, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * csa2_index_reindex_block -- csa2_index_reindex for a verify block.
+ *   q [B][T][H][Dk], w [B][T][H]: as csa2_index_full_block.
+ *   shared   0: cand_pos / score [B][T][P], cand_len [B][T]; list b * T + t
+ *            is scored with token t's query.
+ *            1: cand_pos / score [B][P], cand_len [B]; each candidate gets the
+ *            best score over the block's tokens.
+ * Requires T >= 1 and the csa2_index_reindex limits; UNSUPPORTED when the call
+ * has more than 65535 lists.  No workspace.
+ */
+int csa2_index_reindex_block(const signed char* q, const signed char* w, const signed char* keys,
+                             const long long* row_off, const int* cand_pos, const int* cand_len,
+                             int B, int T, int shared, int H, int Dk, int P, int* score,
+                             void* stream);
+
+/*
+ * csa2_sparse_attn_decode_block -- csa2_sparse_attn_decode for a verify
+ * block: token t of sequence b attends to its selection and to its own
+ * window [L_t - min(window, L_t), L_t).
+ *   q_bf16   [B][T][Hq][D] bf16;  out [B][T][Hq][D] fp32;  lse [B][T][Hq] or NULL.
+ *   shared   0: sel_pos [B][T][k], sel_len [B][T] (token t's own selection);
+ *            1: sel_pos [B][k], sel_len [B] (one selection for the block; its
+ *            positions must be < E_0 so that no token attends a position twice).
+ *   ws, ws_bytes: csa2_block_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, T, shared,
+ *            max_len, 0, 0, 0, k, Hq, D, window) bytes.
+ * Same numerics, limits and errors as csa2_sparse_attn_decode, with B * T
+ * query rows (UNSUPPORTED for T > 255 or B * T > 65535).
+ */
+int csa2_sparse_attn_decode_block(const void* q_bf16, const unsigned char* kv_fp4,
+                                  const unsigned char* kv_scale, const long long* row_off,
+                                  const int* len, long long max_len, const int* sel_pos,
+                                  const int* sel_len, int B, int T, int shared, int Hq, int D,
+                                  int k, int window, float sm_scale, float* out, float* lse,
+                                  void* ws, size_t ws_bytes, void* stream);
+
 /* Bytes of device scratch behind csa2_sparse_attn_decode_static (per GPU). */
 #define CSA2_ATTN_STATIC_SCRATCH_BYTES (32u << 20)
 

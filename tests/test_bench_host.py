@@ -48,3 +48,29 @@ def test_short_sequences_clamp():
     ab = bench.algorithmic_bytes(wl, [100])            # L <= W: no eligible position
     assert ab["full"] == 65 * wl.H and ab["reindex"] == 5 * 65 * wl.H
     assert ab["attn"] == 20 * (272 * 100 + 6 * 64 * 512)
+
+
+def test_verify_block_bytes():
+    """Five tokens at L = 2^20: the keys are read once (the last token's
+    positions, or with a shared selection the first token's), each token
+    brings its query, pool and selection, and the windows' union is 132 rows."""
+    L, T, E4, E0 = 1 << 20, 5, (1 << 20) - 128, (1 << 20) - 132
+    per = bench.algorithmic_bytes(W.WORKLOADS["ctx_1m_block5"], [L])
+    sh = bench.algorithmic_bytes(W.WORKLOADS["ctx_1m_block5_shared"], [L])
+    one = bench.algorithmic_bytes(W.WORKLOADS["ctx_1m"], [L])
+    assert per["scan_kernel"] == 64 * E4 + T * 65 * 64
+    assert sh["scan_kernel"] == 64 * E0 + T * 65 * 64
+    assert per["full"] == 64 * E4 + T * 65 * 64 + T * 8 * 16384
+    assert sh["full"] == 64 * E0 + T * 65 * 64 + 8 * 16384
+    assert per["select"] == T * one["select"] and sh["select"] == one["select"]
+    assert sh["attn"] == 20 * (272 * (512 + 132) + T * 6 * 64 * 512 + 4 * 512)
+    # per-token selections counted once each, or by their union when given
+    assert per["attn"] == 20 * (272 * (T * 512 + 132) + T * 6 * 64 * 512 + T * 4 * 512)
+    uni = bench.algorithmic_bytes(W.WORKLOADS["ctx_1m_block5"], [L], [[600] * 20])
+    assert uni["attn"] == 20 * (272 * (600 + 132) + T * 6 * 64 * 512 + T * 4 * 512)
+
+
+def test_verify_block_appends_every_token():
+    one = bench.algorithmic_bytes(W.WORKLOADS["batch8_256k"], [262144])
+    blk = bench.algorithmic_bytes(W.WORKLOADS["batch8_256k_block5"], [262144])
+    assert blk["append"] == 5 * one["append"]

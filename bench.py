@@ -46,6 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA, MI355X
 METRIC = "decode steps/s at 1M ctx (index+sparse attn) + achieved HBM GB/s vs peak"
 
 
@@ -84,11 +85,16 @@ def algorithmic_bytes(wl, lengths, sel_union=None) -> dict:
                 sel_rows = sum(keff)
             tot["attn"] += 272 * (sel_rows + win_rows) + T * 6 * wl.Hq * wl.D + 4 * sum(keff)
         tot["scan_kernel"] += 64 * E_scan + q_idx
+        # int8 multiply-adds of the scan (two operations each): every token of
+        # the block against the positions it ranks
+        scan_E = Es[0] * T if shared else sum(Es)
+        tot["scan_ops"] = tot.get("scan_ops", 0) + 2 * wl.Dk * wl.H * scan_E
         if wl.append:
             # per token and cache (one per layer, or one shared by all): the
             # bf16 row in, its FP4 codes and scales out; the 64-byte index key
             # in and out
             tot["append"] += T * (wl.n_kv * (2 * wl.D + wl.D // 2 + wl.D // 32) + 2 * wl.Dk)
+    tot.setdefault("scan_ops", 0)
     tot["step"] = tot["append"] + tot["full"] + tot["select"] + tot["reindex"] + tot["attn"]
     return tot
 
@@ -412,9 +418,32 @@ def main():
 
     ms, step_gbs = summary(results["cold"])
     scan_gbs = ab["scan_kernel"] / (scan_avg_ms * 1e-3) / 1e9
+    scan_tops = ab["scan_ops"] / (scan_avg_ms * 1e-3) / 1e12
+    # the scan's bound: HBM (its key bytes at 8 TB/s) or the int8 matrix cores
+    # (its multiply-adds at 5.0 POP/s), whichever takes longer at peak; a long
+    # block of query tokens (a prefill chunk) is bound by the matrix cores
+    mfma_bound = ab["scan_ops"] / (INT8_PEAK_TOPS * 1e12) > ab["scan_kernel"] / (HBM_PEAK_GBS * 1e9)
+    scan_roofline = {
+        "kernel": ("full_score_block_kernel (Full-mode index scan, %d tokens)" % wl.block)
+        if blk else "full_score_kernel (Full-mode index scan)",
+        "bound": "mfma" if mfma_bound else "hbm",
+        "achieved": round(scan_tops if mfma_bound else scan_gbs, 1),
+        "peak": INT8_PEAK_TOPS if mfma_bound else HBM_PEAK_GBS,
+        "unit": "TOP/s" if mfma_bound else "GB/s",
+        "frac": round(scan_tops / INT8_PEAK_TOPS if mfma_bound else scan_gbs / HBM_PEAK_GBS, 4),
+        "traffic": None,
+        "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches_timed": n_scan,
+        "algorithmic_bytes_per_launch": ab["scan_kernel"],
+        "algorithmic_int8_ops_per_launch": ab["scan_ops"],
+        "other_bound": ({"unit": "GB/s", "achieved": round(scan_gbs, 1),
+                         "frac": round(scan_gbs / HBM_PEAK_GBS, 4)} if mfma_bound else
+                        {"unit": "TOP/s", "achieved": round(scan_tops, 1),
+                         "frac": round(scan_tops / INT8_PEAK_TOPS, 4)}),
+    }
     read_gbs = key_bytes / (read_avg_ms * 1e-3) / 1e9
-    traffic = (stale_traffic(os.path.join(ROOT, "profiles", "full_score_ctx_1m_counters.json"))
-               if wl.name == "ctx_1m" else None)
+    scan_roofline["traffic"] = (
+        stale_traffic(os.path.join(ROOT, "profiles", "full_score_ctx_1m_counters.json"))
+        if wl.name == "ctx_1m" else None)
     res = {
         "metric": METRIC,
         "value": round(1000.0 / ms, 2),
@@ -444,13 +473,7 @@ def main():
                                    if k in ("append", "full", "select", "reindex", "attn")},
         "step_GBps": round(step_gbs, 1),
         "step_frac_of_hbm_peak": round(step_gbs / HBM_PEAK_GBS, 4),
-        "roofline": {"kernel": ("full_score_block_kernel (Full-mode index scan, %d tokens)"
-                                % wl.block) if blk else "full_score_kernel (Full-mode index scan)",
-                     "bound": "hbm",
-                     "achieved": round(scan_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(scan_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches_timed": n_scan,
-                     "algorithmic_bytes_per_launch": ab["scan_kernel"]},
+        "roofline": scan_roofline,
         "read_ceiling": {"kernel": "csa2_stream_read (plain read of the key cache, scoring "
                                    "kernel's launch shape)",
                          "achieved": round(read_gbs, 1), "unit": "GB/s",

@@ -289,14 +289,17 @@ __device__ __forceinline__ FullState initial_state(int E, int P, int tile0, int 
 // E - (planes - 1 - i) positions (a verify block's token i sees one position
 // fewer than token i + 1) over the tiles of the sequence in plane i.  With one
 // plane that is the sequence's own list.
+__device__ __forceinline__ void write_state(FullState* st0, FullState* st1, int b, int E, int P,
+                                            int k, int tile0, int planes, int TB, int i) {
+    const int Ei = max(0, E - (planes - 1 - i));
+    const int nt = (Ei + kTile - 1) / kTile;
+    st0[(size_t)b * planes + i] = initial_state(Ei, P, i * TB + tile0, nt);
+    if (st1) st1[(size_t)b * planes + i] = initial_state(Ei, k, i * TB + tile0, nt);
+}
+
 __device__ __forceinline__ void write_states(FullState* st0, FullState* st1, int b, int E, int P,
                                              int k, int tile0, int planes, int TB) {
-    for (int i = 0; i < planes; ++i) {
-        const int Ei = max(0, E - (planes - 1 - i));
-        const int nt = (Ei + kTile - 1) / kTile;
-        st0[b * planes + i] = initial_state(Ei, P, i * TB + tile0, nt);
-        if (st1) st1[b * planes + i] = initial_state(Ei, k, i * TB + tile0, nt);
-    }
+    for (int i = 0; i < planes; ++i) write_state(st0, st1, b, E, P, k, tile0, planes, TB, i);
 }
 
 // One sequence: no scan, no LDS, no barrier.
@@ -309,7 +312,9 @@ __device__ __forceinline__ TileInfo map_tile_one(const int* __restrict__ len,
     const long long roff = row_off[0];
     const int E = L > window ? L - window : 0;
     const int nt = (E + kTile - 1) / kTile;
-    if (t == 0 && threadIdx.x == 0) write_states(st0, st1, 0, E, P, k, 0, planes, TB);
+    if (t == 0 && st0)                                   // the lists' states, a thread each
+        for (int i = threadIdx.x; i < planes; i += blockDim.x)
+            write_state(st0, st1, 0, E, P, k, 0, planes, TB, i);
     TileInfo r;
     r.b = t < nt ? 0 : -1;
     r.tile0 = 0;
@@ -356,7 +361,7 @@ __device__ __noinline__ TileInfo map_tile(const int* __restrict__ len,
                 s_E = Ev[i];
                 s_roff = row_off[b];
             }
-            if (t == 0) write_states(st0, st1, b, Ev[i], P, k, pre_t, planes, TB);
+            if (t == 0 && st0) write_states(st0, st1, b, Ev[i], P, k, pre_t, planes, TB);
         }
         pre_t += nt[i];
     }
@@ -461,23 +466,34 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
         th[i] = s_hist[2 * i] | (s_hist[2 * i + 1] << 16);
 }
 
-// ---- 1b. score a verify block of T tokens ------------------------------------------
+// ---- 1b. score a block of T query tokens -------------------------------------------
 // The same tiles and MFMA scoring, with the key operands loaded once and
-// scored against every token of the block in turn: each wave holds its 128
-// key rows in registers while the tokens' queries and weights come from LDS.
+// scored against many query tokens in turn: each wave holds its 128 key rows
+// in registers while the tokens' queries and weights come from LDS, eight
+// tokens at a time.
 // planes == T (per-token lists): token t's scores of the positions it may
 // rank (p < E - (T - 1 - t), E the last token's count) go to tile g of plane
-// t, each plane with its own histogram.  planes == 1 (shared list): the best
-// score over the block of each position every token may rank (E is then the
-// first token's count) goes to tile g.  Scores go to score_out in that tile
-// layout (seq_stride < 0) or to list (b, plane) at (b * planes + plane) *
-// seq_stride + p.
-constexpr int kMaxBlockT = 8;
+// t, each plane with its own histogram; the tokens are split over grid rows
+// of kBlockGroup tokens (a long block, e.g. a prefill chunk, then keeps the
+// chip busy; each row reloads the tile's keys).  planes == 1 (shared list):
+// one grid row; the best score over all T tokens of each position every token
+// may rank (E is then the first token's count) goes to tile g.  Scores go to
+// score_out in that tile layout (seq_stride < 0) or to list (b, plane) at
+// (b * planes + plane) * seq_stride + p.
+constexpr int kMaxBlockT = 1024;
+constexpr int kBlockChunk = 8;            // tokens whose queries sit in LDS at once
+constexpr int kBlockGroup = 32;           // per-token lists: tokens per grid row
 
-// Dynamic LDS of the block kernel: queries [T][16 NB][64] (heads past H are
-// zero), weights [T][64] bytes (zero past H), histograms [planes][kKeyBins].
-static size_t block_score_lds(int T, int NB, int planes) {
-    return (size_t)T * NB * 16 * kDk + (size_t)T * 64 + (size_t)planes * kKeyBins * 4;
+// Dynamic LDS of the block kernel: queries [kBlockChunk][16 NB][64] (heads
+// past H are zero), weights [kBlockChunk][64] bytes (zero past H),
+// histograms [kBlockChunk or 1][kKeyBins].
+static size_t block_score_lds(int NB, int planes) {
+    return (size_t)kBlockChunk * NB * 16 * kDk + (size_t)kBlockChunk * 64 +
+           (size_t)(planes == 1 ? 1 : kBlockChunk) * kKeyBins * 4;
+}
+
+static int block_groups(int T, int planes) {
+    return planes == 1 ? 1 : (T + kBlockGroup - 1) / kBlockGroup;
 }
 
 template <int NB>
@@ -488,14 +504,16 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_block_kernel(
     int TB, int* __restrict__ score_out, long long seq_stride) {
     extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
     i32x4* s_q = reinterpret_cast<i32x4*>(s_dyn);
-    uint32_t* s_w = reinterpret_cast<uint32_t*>(s_dyn + (size_t)T * NB * 16 * kDk);
-    uint32_t* s_hist = s_w + T * 16;
+    uint32_t* s_w = reinterpret_cast<uint32_t*>(s_dyn + (size_t)kBlockChunk * NB * 16 * kDk);
+    uint32_t* s_hist = s_w + kBlockChunk * 16;
     const int g = blockIdx.x;
     const int l = lane_id();
     const int wave = threadIdx.x / kWave;
-    FullState* st1 = w.k > 0 ? w.st + w.B : nullptr;
-    const TileInfo ti = B == 1 ? map_tile_one(len, row_off, window, P, w.k, g, w.st, st1, planes, TB)
-                               : map_tile<kScoreThreads>(len, row_off, B, window, P, w.k, g, w.st,
+    // grid row 0 writes the lists' states
+    FullState* st0 = blockIdx.y == 0 ? w.st : nullptr;
+    FullState* st1 = blockIdx.y == 0 && w.k > 0 ? w.st + w.B : nullptr;
+    const TileInfo ti = B == 1 ? map_tile_one(len, row_off, window, P, w.k, g, st0, st1, planes, TB)
+                               : map_tile<kScoreThreads>(len, row_off, B, window, P, w.k, g, st0,
                                                          st1, planes, TB);
     if (ti.b < 0) return;                                      // past the last tile
     const int b = ti.b;
@@ -513,56 +531,78 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_block_kernel(
         kop[u] = *reinterpret_cast<const i32x4*>(kbase + (size_t)tok * kDk);
     }
     asm volatile("" ::: "memory");                             // keys are in flight first
-    {
-        const int8_t* qb = q + (size_t)b * T * H * kDk;
-        const int pieces = T * NB * 16 * 4;                    // 16-byte pieces, zero past H
-        for (int i = threadIdx.x; i < pieces; i += kScoreThreads) {
-            const int tk = i / (NB * 64), h = (i >> 2) % (NB * 16);
-            s_q[i] = h < H ? *reinterpret_cast<const i32x4*>(qb + ((size_t)tk * H + h) * kDk +
-                                                             (i & 3) * 16)
-                           : i32x4{0, 0, 0, 0};
-        }
-        uint8_t* sw8 = reinterpret_cast<uint8_t*>(s_w);
-        for (int i = threadIdx.x; i < T * 64; i += kScoreThreads) {
-            const int tk = i >> 6, h = i & 63;
-            sw8[i] = h < H ? (uint8_t)wts[((size_t)b * T + tk) * H + h] : (uint8_t)0;
-        }
-        for (int i = threadIdx.x; i < planes * kKeyBins; i += kScoreThreads) s_hist[i] = 0;
-    }
-    __syncthreads();
+    const int tk_begin = planes == 1 ? 0 : blockIdx.y * kBlockGroup;
+    const int tk_end = planes == 1 ? T : min(T, tk_begin + kBlockGroup);
     int best[kGroups / 4];
 #pragma unroll
     for (int it = 0; it < kGroups / 4; ++it) best[it] = 0;
-    for (int tk = 0; tk < T; ++tk) {
-        i32x4 qa[NB];
-        uint32_t wr[NB][4];
-#pragma unroll
-        for (int mb = 0; mb < NB; ++mb) {
-            qa[mb] = s_q[((tk * NB + mb) * 16 + (l & 15)) * 4 + (l >> 4)];
-            const uint32_t word = s_w[tk * 16 + 4 * mb + (l >> 4)];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) wr[mb][i] = (word >> (8 * i)) & 0xFFu;
+    for (int c0 = tk_begin; c0 < tk_end; c0 += kBlockChunk) {
+        const int nc = min(kBlockChunk, tk_end - c0);          // uniform
+        if (c0 > tk_begin) __syncthreads();                    // the last chunk's LDS is read
+        {
+            const int8_t* qb = q + ((size_t)b * T + c0) * H * kDk;
+            const int pieces = nc * NB * 16 * 4;               // 16-byte pieces, zero past H
+            for (int i = threadIdx.x; i < pieces; i += kScoreThreads) {
+                const int tk = i / (NB * 64), h = (i >> 2) % (NB * 16);
+                s_q[i] = h < H ? *reinterpret_cast<const i32x4*>(qb + ((size_t)tk * H + h) * kDk +
+                                                                 (i & 3) * 16)
+                               : i32x4{0, 0, 0, 0};
+            }
+            uint8_t* sw8 = reinterpret_cast<uint8_t*>(s_w);
+            for (int i = threadIdx.x; i < nc * 64; i += kScoreThreads) {
+                const int tk = i >> 6, h = i & 63;
+                sw8[i] = h < H ? (uint8_t)wts[((size_t)b * T + c0 + tk) * H + h] : (uint8_t)0;
+            }
+            if (planes > 1 || c0 == 0)
+                for (int i = threadIdx.x; i < (planes == 1 ? 1 : nc) * kKeyBins; i += kScoreThreads)
+                    s_hist[i] = 0;
         }
-        // per-token lists: this token's plane and its own count of positions
-        const int nv = planes == 1 ? nvalid : min(kTile, ti.E - (T - 1 - tk) - p_tile);
-        int* sc_out = seq_stride < 0
-                          ? score_out + (size_t)(planes == 1 ? g : tk * TB + g) * kTile
-                          : score_out + ((size_t)b * planes + (planes == 1 ? 0 : tk)) *
-                                            (size_t)seq_stride + p_tile;
-        uint32_t* hist = s_hist + (planes == 1 ? 0 : tk * kKeyBins);
+        __syncthreads();
+        for (int tc = 0; tc < nc; ++tc) {
+            const int tk = c0 + tc;                            // the token of the block
+            i32x4 qa[NB];
+            uint32_t wr[NB][4];
 #pragma unroll
-        for (int it = 0; it < kGroups / 4; ++it) {
-            if (t0 + 64 * it >= nvalid) break;                 // wave-uniform
-            uint32_t part[4];
+            for (int mb = 0; mb < NB; ++mb) {
+                qa[mb] = s_q[((tc * NB + mb) * 16 + (l & 15)) * 4 + (l >> 4)];
+                const uint32_t word = s_w[tc * 16 + 4 * mb + (l >> 4)];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) part[u] = score_partial16<NB>(qa, wr, kop[4 * it + u]);
-            const int mine = (int)reduce_rows4(part);          // token t0 + 64 it + l
-            const int pos = t0 + 64 * it + l;
-            if (planes == 1) {
-                best[it] = tk == 0 ? mine : max(best[it], mine);
-            } else if (pos < nv) {
-                sc_out[pos] = mine;
-                atomicAdd(&hist[score_key(mine)], 1u);
+                for (int i = 0; i < 4; ++i) wr[mb][i] = (word >> (8 * i)) & 0xFFu;
+            }
+            // per-token lists: this token's plane and its own count of positions
+            const int nv = planes == 1 ? nvalid : min(kTile, ti.E - (T - 1 - tk) - p_tile);
+            int* sc_out = seq_stride < 0
+                              ? score_out + (size_t)(planes == 1 ? g : tk * TB + g) * kTile
+                              : score_out + ((size_t)b * planes + (planes == 1 ? 0 : tk)) *
+                                                (size_t)seq_stride + p_tile;
+            uint32_t* hist = s_hist + (planes == 1 ? 0 : tc * kKeyBins);
+#pragma unroll
+            for (int it = 0; it < kGroups / 4; ++it) {
+                if (t0 + 64 * it >= nvalid) break;             // wave-uniform
+                uint32_t part[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) part[u] = score_partial16<NB>(qa, wr, kop[4 * it + u]);
+                const int mine = (int)reduce_rows4(part);      // token t0 + 64 it + l
+                const int pos = t0 + 64 * it + l;
+                if (planes == 1) {
+                    best[it] = tk == 0 ? mine : max(best[it], mine);
+                } else if (pos < nv) {
+                    sc_out[pos] = mine;
+                    atomicAdd(&hist[score_key(mine)], 1u);
+                }
+            }
+        }
+        if (planes > 1) {
+            __syncthreads();
+            // per-tile histograms of the chunk's planes whose list reaches this tile
+            for (int tc = 0; tc < nc; ++tc) {
+                const int tk = c0 + tc;
+                if (ti.E - (T - 1 - tk) <= p_tile) continue;   // uniform
+                uint32_t* th =
+                    reinterpret_cast<uint32_t*>(w.tile_hist + (size_t)(tk * TB + g) * kKeyBins);
+                const uint32_t* sh = s_hist + tc * kKeyBins;
+                for (int i = threadIdx.x; i < kKeyBins / 2; i += kScoreThreads)
+                    th[i] = sh[2 * i] | (sh[2 * i + 1] << 16);
             }
         }
     }
@@ -577,15 +617,10 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_block_kernel(
                 atomicAdd(&s_hist[score_key(best[it])], 1u);
             }
         }
-    }
-    __syncthreads();
-    // per-tile histograms of the planes whose list reaches this tile
-    for (int pl = 0; pl < planes; ++pl) {
-        if (planes > 1 && ti.E - (T - 1 - pl) <= p_tile) continue;   // uniform
-        uint32_t* th = reinterpret_cast<uint32_t*>(w.tile_hist + (size_t)(pl * TB + g) * kKeyBins);
-        const uint32_t* sh = s_hist + pl * kKeyBins;
+        __syncthreads();
+        uint32_t* th = reinterpret_cast<uint32_t*>(w.tile_hist + (size_t)g * kKeyBins);
         for (int i = threadIdx.x; i < kKeyBins / 2; i += kScoreThreads)
-            th[i] = sh[2 * i] | (sh[2 * i + 1] << 16);
+            th[i] = s_hist[2 * i] | (s_hist[2 * i + 1] << 16);
     }
 }
 
@@ -1075,9 +1110,9 @@ static int launch_score_block(int H, int T, int shared, unsigned TB, hipStream_t
     const int8_t* q8 = reinterpret_cast<const int8_t*>(q);
     const int8_t* w8 = reinterpret_cast<const int8_t*>(w);
     const int8_t* k8 = reinterpret_cast<const int8_t*>(keys);
-    const dim3 grid(TB), blk(kScoreThreads);
+    const dim3 grid(TB, block_groups(T, planes)), blk(kScoreThreads);
     const int NB = (H + 15) / 16;
-    const size_t lds = block_score_lds(T, NB, planes);
+    const size_t lds = block_score_lds(NB, planes);
     const int tb = (int)TB;
     switch (NB) {
         case 1: hipLaunchKernelGGL(full_score_block_kernel<1>, grid, blk, lds, s, q8, w8, k8, row_off, len, B, H, win, P, fw, T, planes, tb, out, seq_stride); break;

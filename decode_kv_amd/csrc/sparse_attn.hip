@@ -118,8 +118,8 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
 // Placement flags of the attention and combine launches.
 constexpr int kPlaceSeq = 1;     // sequence b (all head groups and splits) on XCD b mod 8
 constexpr int kPlacePlain = 2;   // split partials stored with plain stores (they fit in L2)
-// A verify block of T tokens per sequence (flags bits 8-15 hold T, 0 meaning
-// 1): query row b of the launch is token t = b mod T of sequence b / T, which
+// A verify block of T tokens per sequence (flags bits 8 and up hold T, 0
+// meaning 1): query row b of the launch is token t = b mod T of sequence b / T, which
 // sees the positions before len - (T - 1 - t).  With kBlockShared every token
 // of a sequence attends to the sequence's one selection, else row b has its own.
 constexpr int kBlockShared = 16;
@@ -613,7 +613,7 @@ static int attn_decode(const char* fn, const void* q_bf16, const unsigned char* 
         return fail(CSA2_ERR_INVALID, "%s: negative size", fn);
     if (T < 1 || shared < 0 || shared > 1)
         return fail(CSA2_ERR_INVALID, "%s: T < 1 or shared not 0/1", fn);
-    if (T > 255) return fail(CSA2_ERR_UNSUPPORTED, "%s: T > 255", fn);
+    if (T > 1024) return fail(CSA2_ERR_UNSUPPORTED, "%s: T > 1024", fn);
     if (B == 0) return CSA2_OK;
     if ((long long)B * T > 65535) return fail(CSA2_ERR_UNSUPPORTED, "%s: B * T > 65535", fn);
     B *= T;                                              // query rows of the launch

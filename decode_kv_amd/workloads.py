@@ -22,6 +22,10 @@ The workloads, named by what they are:
                 verify blocks of 5 tokens per sequence: ctx_1m verifying its
                 last 5 cached positions, batch8_256k appending and verifying 5
                 tokens per sequence and step; per-token or shared selection.
+  prefill_128k_chunk256
+                chunked prefill indexing: the last 256 positions of a 131,072
+                token prompt score their own causal prefixes (one Full layer,
+                per-token pools and selections, then attention).
 
 Everywhere: window 128, index key dim 64, latent dim 512, softmax scale
 1/sqrt(512).  Nothing here computes any part of the method; the only
@@ -131,6 +135,13 @@ WORKLOADS["batch8_256k_block5"] = WORKLOADS["batch8_256k"].scaled(name="batch8_2
                                                                   block=5)
 WORKLOADS["batch8_256k_block5_shared"] = WORKLOADS["batch8_256k"].scaled(
     name="batch8_256k_block5_shared", block=5, block_shared=True)
+# Chunked prefill indexing: the last 256 tokens of a 131,072-token prompt,
+# already in the cache, each rank their own causal prefix (per-token pool and
+# selection) in one Full layer, then attend.
+WORKLOADS["prefill_128k_chunk256"] = Workload(
+    "prefill_128k_chunk256", B=1, L=131072, len_range=None, n_layers=1, P=16384, k=512,
+    window=128, H=64, Hq=64, keys="planted", n_planted=1024, steps=1, append=False,
+    redraw_queries=False, block=256)
 
 
 KV_POOL_ROWS = 1 << 20

@@ -308,8 +308,15 @@ size_t csa2_block_workspace_bytes(int op, int B, int T, int shared, long long ma
  *            [B], sel_pos [B][k], sel_len [B]; the scores are the block's best.
  *   ws, ws_bytes: csa2_block_workspace_bytes(CSA2_OP_INDEX_FULL, B, T, shared,
  *            max_len, total_len, H, P, k, ...) bytes, 256-byte aligned.
- * Requires 1 <= T <= 8 (else UNSUPPORTED) and the csa2_index_full limits;
- * UNSUPPORTED when the call has more than 65535 lists.
+ * Requires 1 <= T <= 1024 (else UNSUPPORTED) and the csa2_index_full limits;
+ * UNSUPPORTED when the call has more than 65535 lists.  A long block with
+ * per-token lists is also the chunked form of prefill indexing: the C tokens
+ * of a prompt chunk, appended to the cache, each rank their own causal prefix
+ * in one call.
+ * ("DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 1: Causal
+ * Encoder-Decoder", and "How DeepSeek V4.1 Flash Actually Works", item 1:
+ * prompt tokens go through the lower layers to build the global cache, so a
+ * prompt is indexed many query tokens at a time.)
  */
 int csa2_index_full_block(const signed char* q, const signed char* w, const signed char* keys,
                           const long long* row_off, const int* len, int B, int T, int shared,
@@ -358,7 +365,7 @@ int csa2_index_reindex_block(const signed char* q, const signed char* w, const s
  *   ws, ws_bytes: csa2_block_workspace_bytes(CSA2_OP_SPARSE_ATTN, B, T, shared,
  *            max_len, 0, 0, 0, k, Hq, D, window) bytes.
  * Same numerics, limits and errors as csa2_sparse_attn_decode, with B * T
- * query rows (UNSUPPORTED for T > 255 or B * T > 65535).
+ * query rows (UNSUPPORTED for T > 1024 or B * T > 65535).
  */
 int csa2_sparse_attn_decode_block(const void* q_bf16, const unsigned char* kv_fp4,
                                   const unsigned char* kv_scale, const long long* row_off,

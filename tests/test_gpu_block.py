@@ -304,3 +304,59 @@ def test_workload_batch_block5_appends(name):
     """Two verify steps, each appending its five tokens first, on a
     shortened batch (ragged lengths around the window)."""
     run_block_workload(name, 2, None, B=3, L=None, len_range=(130, 40000), steps=2)
+
+
+# ---------------------------------------------------------------------------
+# long blocks: chunked prefill indexing
+# ---------------------------------------------------------------------------
+
+def test_index_full_block_long_per_token():
+    """100 tokens per sequence (four grid rows of 32 tokens, the last partial;
+    chunks of 8 with a partial last chunk), ragged lengths."""
+    lens = [5000, 1300, 3000]
+    keys, row_off, q, w = _block_case(11, lens, 100, H=48)
+    check_full_block(keys, row_off, lens, q, w, 128, 700, 40, False, "T=100")
+
+
+def test_index_full_block_long_shared():
+    """A shared list over 20 tokens (three chunks of 8 in one grid row)."""
+    lens = [9000, 2500]
+    keys, row_off, q, w = _block_case(12, lens, 20)
+    check_full_block(keys, row_off, lens, q, w, 128, 1000, 64, True, "T=20 shared")
+
+
+def test_workload_prefill_chunk_sampled():
+    """prefill_128k_chunk256 at full size: 256 per-token pools and selections
+    in one call, sampled tokens checked against the oracle (pool, scores,
+    selection and attention), every token's pool length and list order
+    checked."""
+    wl = W.WORKLOADS["prefill_128k_chunk256"]
+    T = wl.block
+    eng = pipeline.Engine(W.Case(wl, 0, DEV), DEV)
+    eng.run_step(eng.step_inputs(0))
+    torch.cuda.synchronize()
+    keys_np = eng.keys.cpu().numpy()
+    case = W.Case(wl, 0, "cpu")
+    L = case.lengths_at(0)[0]
+    Ls = oracle.block_lengths(L, T)
+    plen = eng.pool_len.cpu().numpy()
+    assert plen.tolist() == [min(wl.P, x - wl.window) for x in Ls]
+    pools = eng.pool_pos.cpu().numpy()
+    for t in range(T):
+        p = pools[t, :plen[t]]
+        assert (np.diff(p) > 0).all() and p[-1] < Ls[t] - wl.window
+    for t in (0, 1, 100, 255):
+        q = case.index_q(0, 0, 0, t).numpy()
+        w = case.index_w(0, 0, 0, t).numpy()
+        rp, rs = oracle.index_full(keys_np, 0, Ls[t], q, w, wl.window, wl.P)
+        assert np.array_equal(pools[t, :plen[t]], rp), t
+        assert np.array_equal(eng.pool_score[t].cpu().numpy()[:plen[t]], rs), t
+        sel, _ = oracle.select_topk(rs, rp, wl.k)
+        assert int(eng.sel_len[0, t]) == len(sel), t
+        assert np.array_equal(eng.sel_pos[0, t].cpu().numpy()[:len(sel)], sel), t
+        S = oracle.attention_positions(Ls[t], sel, wl.window)
+        codes, scales = oracle.fp4_quantize(u16(case.kv_bf16(0, 0, S)))
+        ro, rl = oracle.attention(u16(case.attn_q(0, 0, 0, t)), codes, scales, wl.sm_scale)
+        check_attention(eng.out[0, 0, t].cpu().numpy(), eng.lse[0, 0, t].cpu().numpy(), ro, rl,
+                        "prefill token %d" % t)
+        _say("  checked prefill token", t)

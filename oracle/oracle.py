@@ -43,7 +43,8 @@ __all__ = [
     "index_scores", "topk", "eligible_count", "window_positions", "index_full",
     "index_reindex", "select_topk", "attention_positions", "attention",
     "layer_kind", "layer_pattern", "decode_step", "block_lengths", "index_full_block",
-    "index_reindex_block", "decode_block",
+    "index_reindex_block", "decode_block", "session_saved_length", "session_export",
+    "session_import", "replay_append",
 ]
 
 
@@ -415,3 +416,53 @@ def decode_block(pattern: str, keys, row_off: int, L: int, T: int, window: int, 
         rec.update(sel=sel, out=outs, lse=lses, S=Ss)
         results.append(rec)
     return results
+
+
+# --------------------------------------------------------------------------
+# Sessions and bounded replay ("How DeepSeek V4.1 Flash Actually Works", "The
+# three KV-cache optimizations", item 3; "DeepSeek V4.1-Flash 552B runs like
+# 16B (CED)", "Act 3: FP4 KV & SWA Bounded Replay").  Reading: a sequence's
+# state is its index keys and the FP4 rows of every layer; what outlives a
+# session is positions [0, L - min(R, L)) with R = 128 (the local window);
+# the newest min(R, L) positions are dropped and come back by appending the
+# replayed tokens, which the model recomputes.
+# --------------------------------------------------------------------------
+
+def session_saved_length(L: int, replay: int) -> int:
+    """Positions of a sequence of length L that outlive its session."""
+    return max(0, int(L) - min(int(replay), max(int(L), 0)))
+
+
+def session_export(keys, fp4, scales, row_off: int, L: int, replay: int):
+    """The saved state of one sequence: (n, keys[:n], [fp4_l[:n]], [scale_l[:n]])
+    with n = session_saved_length(L, replay).  fp4 / scales: one array of rows
+    per layer."""
+    n = session_saved_length(L, replay)
+    r = slice(int(row_off), int(row_off) + n)
+    return n, keys[r].copy(), [f[r].copy() for f in fp4], [c[r].copy() for c in scales]
+
+
+def session_import(saved, keys, fp4, scales, row_off: int) -> int:
+    """Write a saved state into the caches at row_off; returns the new length."""
+    n, k, f, c = saved
+    r = slice(int(row_off), int(row_off) + n)
+    keys[r] = k
+    for dst, src in zip(fp4, f):
+        dst[r] = src
+    for dst, src in zip(scales, c):
+        dst[r] = src
+    return n
+
+
+def replay_append(keys, fp4, scales, row_off: int, L: int, key_rows, x_bf16_rows):
+    """Append replayed tokens at positions L, L + 1, ...: their index keys
+    ([n][Dk]) and, per layer, their latent rows ([n][D] bf16, quantised with
+    the FP4 rule).  Returns the new length."""
+    n = len(key_rows)
+    r = slice(int(row_off) + int(L), int(row_off) + int(L) + n)
+    keys[r] = key_rows
+    for l in range(len(fp4)):
+        codes, sc = fp4_quantize(np.asarray(x_bf16_rows[l]))
+        fp4[l][r] = codes
+        scales[l][r] = sc
+    return int(L) + n

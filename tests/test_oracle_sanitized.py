@@ -15,7 +15,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "csa2_oracle.c")
 PINS = ["tests/test_oracle_index.py", "tests/test_oracle_attention.py",
-        "tests/test_oracle_fp4.py", "tests/test_oracle_block.py"]
+        "tests/test_oracle_fp4.py", "tests/test_oracle_block.py", "tests/test_oracle_session.py"]
 
 
 def _runtime(gcc: str, name: str) -> str:

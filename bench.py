@@ -213,6 +213,73 @@ def cpu_baseline(wl, seed: int, step: int, keys_np, seconds_target: float = 12.0
             "kind": "oracle", "sample": sample}
 
 
+def session_measure(eng, case, stream, reps: int = 10) -> dict:
+    """Bounded-replay bookkeeping on the engine's caches: save every
+    sequence's state (all but the newest `window` positions), restore it in
+    place, and replay the dropped window with one multi-token append (the
+    rows the model would recompute come from the generator).  HIP events
+    around each call on `stream`; the caches end as they began."""
+    import torch
+
+    from decode_kv_amd import csa2
+    wl = eng.wl
+    R = wl.window
+    dev = eng.keys.device
+    lens = eng.lens.cpu().tolist()
+    if min(lens) < R:
+        return {"skipped": "a sequence is shorter than the replay window"}
+    saved = [L - R for L in lens]
+    cap, nl = max(saved), wl.n_kv
+    s_keys = torch.empty((wl.B, cap, wl.Dk), dtype=torch.int8, device=dev)
+    s_fp4 = torch.empty((nl, wl.B, cap, wl.D // 2), dtype=torch.uint8, device=dev)
+    s_sc = torch.empty((nl, wl.B, cap, wl.D // 32), dtype=torch.uint8, device=dev)
+    s_len = torch.empty((wl.B,), dtype=torch.int32, device=dev)
+    # replay inputs: token j of sequence b is position L_b - R + j
+    x = torch.stack([torch.stack([case.kv_bf16(l, b, list(range(L - R, L)))
+                                  for b, L in enumerate(lens)]) for l in range(nl)])
+    x = x.permute(2, 0, 1, 3).contiguous()                       # [R][n_kv][B][D]
+    kr = torch.stack([eng.keys[int(eng.row_off[b]) + L - R:int(eng.row_off[b]) + L]
+                      for b, L in enumerate(lens)]).transpose(0, 1).contiguous()
+    keys0 = eng.keys.clone()
+    fp40, sc0 = eng.kv_fp4.clone(), eng.kv_scale.clone()
+    t = {"export": [], "import": [], "replay": []}
+    for _ in range(reps):
+        with torch.cuda.stream(stream):
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record()
+            csa2.session_export(eng.row_off, eng.lens, R, eng.kv_fp4, eng.kv_scale, eng.keys,
+                                s_fp4, s_sc, s_keys, s_len, stream)
+            ev[1].record()
+            csa2.session_import(eng.row_off, eng.lens, s_len, s_fp4, s_sc, s_keys, eng.kv_fp4,
+                                eng.kv_scale, eng.keys, stream)
+            ev[2].record()
+            csa2.append_tokens(x, kr, eng.row_off, eng.lens, eng.kv_fp4, eng.kv_scale, eng.keys,
+                               stream)
+            ev[3].record()
+        torch.cuda.synchronize()
+        for i, k in enumerate(("export", "import", "replay")):
+            t[k].append(ev[i].elapsed_time(ev[i + 1]) * 1e3)
+    assert eng.lens.cpu().tolist() == lens, "replay did not restore the lengths"
+    assert torch.equal(eng.keys, keys0) and torch.equal(eng.kv_fp4, fp40) and \
+        torch.equal(eng.kv_scale, sc0), "save, restore and replay changed the caches"
+    row = wl.Dk + nl * (wl.D // 2 + wl.D // 32)                # bytes per saved position
+    moved = 2 * sum(saved) * row                               # read once, written once
+    replay_bytes = wl.B * R * (nl * (2 * wl.D + wl.D // 2 + wl.D // 32) + 2 * wl.Dk)
+    med = {k: statistics.median(v) for k, v in t.items()}
+    return {
+        "replay_window": R, "saved_positions": sum(saved), "bytes_per_position": row,
+        "saved_MB": round(sum(saved) * row / 1e6, 1),
+        "dropped_MB": round(wl.B * R * row / 1e6, 3),
+        "export_us": round(med["export"], 1), "import_us": round(med["import"], 1),
+        "replay_append_us": round(med["replay"], 1),
+        "export_GBps": round(moved / (med["export"] * 1e-6) / 1e9, 1),
+        "import_GBps": round(moved / (med["import"] * 1e-6) / 1e9, 1),
+        "replay_GBps": round(replay_bytes / (med["replay"] * 1e-6) / 1e9, 1),
+        "note": "device-to-device copies (HBM read + write counted); replay appends the "
+                "dropped window's rows in one csa2_append_tokens call; median of %d" % reps,
+    }
+
+
 def say(msg: str):
     """Progress line on stderr (the JSON result is the only stdout line)."""
     print(msg, file=sys.stderr, flush=True)
@@ -228,6 +295,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-only", action="store_true", help="skip the warm-mode timing")
+    ap.add_argument("--no-session", action="store_true",
+                    help="skip the session save / restore / replay measurement")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -494,6 +563,9 @@ def main():
         res["warm"] = {"ms_per_step": round(wms, 5), "steps_per_s": round(1000.0 / wms, 2),
                        "step_GBps": round(wgbs, 1),
                        "step_frac_of_hbm_peak": round(wgbs / HBM_PEAK_GBS, 4)}
+    if not args.no_session:
+        say("session save / restore / replay")
+        res["session"] = session_measure(eng, case, stream)
     if not args.no_cpu_baseline:
         say("oracle baseline")
         keys_np = eng.keys.cpu().numpy()

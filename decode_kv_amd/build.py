@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libcsa2.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "obj")
 
 SOURCES = ["abi.hip", "kv_append.hip", "index_full.hip", "index_reindex.hip",
-           "select_topk.hip", "sparse_attn.hip", "measure.hip"]
+           "select_topk.hip", "sparse_attn.hip", "measure.hip", "session.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -75,6 +75,12 @@ def lib():
         L.csa2_sparse_attn_decode.restype = I
         L.csa2_sparse_attn_decode.argtypes = [V, V, V, V, V, LL, V, V, I, I, I, I, I, F, V, V,
                                               V, SZ, V]
+        L.csa2_append_tokens.restype = I
+        L.csa2_append_tokens.argtypes = [V, V, V, V, I, I, I, LL, I, I, V, V, V, V]
+        L.csa2_session_export.restype = I
+        L.csa2_session_export.argtypes = [V, V, I, I, LL, I, LL, I, I, V, V, V, V, V, V, V, V]
+        L.csa2_session_import.restype = I
+        L.csa2_session_import.argtypes = [V, V, V, I, LL, I, LL, I, I, V, V, V, V, V, V, V]
         L.csa2_block_workspace_bytes.restype = SZ
         L.csa2_block_workspace_bytes.argtypes = [I, I, I, I, LL, LL, I, I, I, I, I, I]
         L.csa2_index_full_block.restype = I
@@ -160,6 +166,41 @@ def append_token(x_bf16, key_rows, row_off, lens, kv_fp4, kv_scale, keys, stream
            lib().csa2_append_token(_p(x_bf16), _p(key_rows), _p(row_off), _p(lens), B, n_layers,
                                    layer_rows, D, key_rows.shape[1], _p(kv_fp4), _p(kv_scale),
                                    _p(keys), _s(stream)))
+
+
+def append_tokens(x_bf16, key_rows, row_off, lens, kv_fp4, kv_scale, keys, stream=None):
+    """x_bf16 [n][n_layers][B][D]; key_rows [n][B][Dk]; caches as append_token."""
+    n, n_layers, B, D = x_bf16.shape
+    layer_rows = kv_fp4.shape[1]
+    assert kv_fp4.shape[0] == n_layers and kv_scale.shape[:2] == kv_fp4.shape[:2]
+    _check("csa2_append_tokens",
+           lib().csa2_append_tokens(_p(x_bf16), _p(key_rows), _p(row_off), _p(lens), B, n,
+                                    n_layers, layer_rows, D, key_rows.shape[2], _p(kv_fp4),
+                                    _p(kv_scale), _p(keys), _s(stream)))
+
+
+def session_export(row_off, lens, replay, kv_fp4, kv_scale, keys, saved_fp4, saved_scale,
+                   saved_keys, saved_len, stream=None):
+    """Caches kv_fp4 [n_layers][rows][D/2], kv_scale [n_layers][rows][D/32],
+    keys [rows][Dk]; saved arrays [n_layers][B][cap][...] and [B][cap][Dk]."""
+    n_layers, layer_rows, half = kv_fp4.shape
+    B, cap, Dk = saved_keys.shape
+    _check("csa2_session_export",
+           lib().csa2_session_export(_p(row_off), _p(lens), B, int(replay), cap, n_layers,
+                                     layer_rows, 2 * half, Dk, _p(kv_fp4), _p(kv_scale), _p(keys),
+                                     _p(saved_fp4), _p(saved_scale), _p(saved_keys),
+                                     _p(saved_len), _s(stream)))
+
+
+def session_import(row_off, lens, saved_len, saved_fp4, saved_scale, saved_keys, kv_fp4,
+                   kv_scale, keys, stream=None):
+    n_layers, layer_rows, half = kv_fp4.shape
+    B, cap, Dk = saved_keys.shape
+    _check("csa2_session_import",
+           lib().csa2_session_import(_p(row_off), _p(lens), _p(saved_len), B, cap, n_layers,
+                                     layer_rows, 2 * half, Dk, _p(saved_fp4), _p(saved_scale),
+                                     _p(saved_keys), _p(kv_fp4), _p(kv_scale), _p(keys),
+                                     _s(stream)))
 
 
 def index_full(q, w, keys, row_off, lens, max_len, total_len, window, P, pool_pos, pool_score,

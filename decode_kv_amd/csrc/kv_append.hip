@@ -116,47 +116,105 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_fp4_kernel(
                      kv_scale + dst * (long long)(D / 32));
 }
 
-// One workgroup of 16 waves per sequence b: the token's FP4 row of every
-// layer (wave w takes layers w, w + 16, ...) and its index key go to row
-// row_off[b] + len[b]; after a barrier, thread 0 advances len[b].  Only this
-// workgroup reads or writes len[b], so the old length is read before the new
-// one is stored.  A wave issues the loads of its first two rows before it
-// quantises either, so the step pays one load round trip.
+// One workgroup of 16 waves per sequence b appends its n tokens: token j's
+// FP4 row of every layer (items (j, layer), wave w taking items w, w + 16,
+// ...) and its index key go to row row_off[b] + len[b] + j; after a barrier,
+// thread 0 advances len[b] by n.  Only this workgroup reads or writes len[b],
+// so the old length is read before the new one is stored.  A wave issues the
+// loads of two rows before it quantises either, so a one-token step pays one
+// load round trip.
 constexpr int kTokenThreads = 1024;
 
 __global__ __launch_bounds__(kTokenThreads) void append_token_kernel(
     const uint16_t* __restrict__ x, const int8_t* __restrict__ key_rows,
-    const long long* __restrict__ row_off, int* __restrict__ len, int B, int n_layers,
+    const long long* __restrict__ row_off, int* __restrict__ len, int B, int n, int n_layers,
     long long layer_rows, int D, uint8_t* __restrict__ kv_fp4, uint8_t* __restrict__ kv_scale,
     int8_t* __restrict__ keys) {
     const int b = blockIdx.x;
     const int wave = threadIdx.x / kWave;
     const int L = len[b];
-    const long long row = row_off[b] + L;
-    if (threadIdx.x < kDk / 16)                       // the 64-byte index key, 16 bytes a thread
-        *reinterpret_cast<u32x4*>(keys + row * kDk + 16 * threadIdx.x) =
-            *reinterpret_cast<const u32x4*>(key_rows + (size_t)b * kDk + 16 * threadIdx.x);
+    const long long row0 = row_off[b] + L;
+    for (int i = threadIdx.x; i < n * (kDk / 16); i += kTokenThreads) {   // 16 key bytes a thread
+        const int j = i / (kDk / 16), c = i % (kDk / 16);
+        *reinterpret_cast<u32x4*>(keys + (row0 + j) * kDk + 16 * c) =
+            *reinterpret_cast<const u32x4*>(key_rows + ((size_t)j * B + b) * kDk + 16 * c);
+    }
     constexpr int NW = kTokenThreads / kWave;
-    const int l0 = wave, l1 = wave + NW;
-    const uint16_t* x0 = x + ((size_t)l0 * B + b) * D;
-    const uint16_t* x1 = x + ((size_t)l1 * B + b) * D;
-    const u32x4 v0 = l0 < n_layers ? load_chunk(x0, D, 0) : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 v1 = l1 < n_layers ? load_chunk(x1, D, 0) : u32x4{0u, 0u, 0u, 0u};
-    auto finish = [&](int layer, const uint16_t* xr, u32x4 v) {
-        const long long dst = layer * layer_rows + row;
+    const int items = n * n_layers;                   // (token, layer) rows of this sequence
+    auto src = [&](int i) {                           // x is [n][n_layers][B][D]
+        return x + ((size_t)i * B + b) * D;
+    };
+    auto finish = [&](int i, u32x4 v) {
+        const int j = i / n_layers, layer = i - j * n_layers;
+        const long long dst = layer * layer_rows + row0 + j;
         uint8_t* cr = kv_fp4 + dst * (long long)(D / 2);
         uint8_t* sr = kv_scale + dst * (long long)(D / 32);
         quantise_chunk(v, D, 0, cr, sr);
         for (int base = 512; base < D; base += 512)
-            quantise_chunk(load_chunk(xr, D, base), D, base, cr, sr);
+            quantise_chunk(load_chunk(src(i), D, base), D, base, cr, sr);
     };
-    if (l0 < n_layers) finish(l0, x0, v0);
-    if (l1 < n_layers) finish(l1, x1, v1);
-    for (int layer = wave + 2 * NW; layer < n_layers; layer += NW)
-        quantise_row_fp4(x + ((size_t)layer * B + b) * D, D, kv_fp4 + (layer * layer_rows + row) * (long long)(D / 2),
-                         kv_scale + (layer * layer_rows + row) * (long long)(D / 32));
+    for (int i0 = wave; i0 < items; i0 += 2 * NW) {  // two rows' loads in flight
+        const int i1 = i0 + NW;
+        const u32x4 v0 = load_chunk(src(i0), D, 0);
+        const u32x4 v1 = i1 < items ? load_chunk(src(i1), D, 0) : u32x4{0u, 0u, 0u, 0u};
+        finish(i0, v0);
+        if (i1 < items) finish(i1, v1);
+    }
     __syncthreads();                                  // every thread has read len[b]
-    if (threadIdx.x == 0) len[b] = L + 1;
+    if (threadIdx.x == 0) len[b] = L + n;
+}
+
+// Many rows per sequence (a replayed window: n tokens times every layer):
+// the rows are spread over workgroups (x, b) of kWideItems (token, layer)
+// items each, which all read len[b]; the index keys and the length advance
+// follow in append_keys_len_kernel, launched after it on the same stream.
+constexpr int kWideItems = 64;
+constexpr int kWideThreads = 1024;    // 16 waves x 4 items, every load issued first
+
+__global__ __launch_bounds__(kWideThreads) void append_rows_wide_kernel(
+    const uint16_t* __restrict__ x, const long long* __restrict__ row_off,
+    const int* __restrict__ len, int B, int n, int n_layers, long long layer_rows, int D,
+    uint8_t* __restrict__ kv_fp4, uint8_t* __restrict__ kv_scale) {
+    const int b = blockIdx.y;
+    const int wave = threadIdx.x / kWave;
+    constexpr int NW = kWideThreads / kWave;
+    constexpr int PER = kWideItems / NW;
+    const long long row0 = row_off[b] + len[b];
+    const int items = n * n_layers;
+    const int first = blockIdx.x * kWideItems + wave;
+    u32x4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int i = first + u * NW;
+        v[u] = i < items ? load_chunk(x + ((size_t)i * B + b) * D, D, 0) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+        const int i = first + u * NW;
+        if (i >= items) break;
+        const int j = i / n_layers, layer = i - j * n_layers;
+        const long long dst = layer * layer_rows + row0 + j;
+        uint8_t* cr = kv_fp4 + dst * (long long)(D / 2);
+        uint8_t* sr = kv_scale + dst * (long long)(D / 32);
+        quantise_chunk(v[u], D, 0, cr, sr);
+        for (int base = 512; base < D; base += 512)
+            quantise_chunk(load_chunk(x + ((size_t)i * B + b) * D, D, base), D, base, cr, sr);
+    }
+}
+
+__global__ __launch_bounds__(256) void append_keys_len_kernel(
+    const int8_t* __restrict__ key_rows, const long long* __restrict__ row_off,
+    int* __restrict__ len, int B, int n, int8_t* __restrict__ keys) {
+    const int b = blockIdx.x;
+    const int L = len[b];
+    const long long row0 = row_off[b] + L;
+    for (int i = threadIdx.x; i < n * (kDk / 16); i += 256) {
+        const int j = i / (kDk / 16), c = i % (kDk / 16);
+        *reinterpret_cast<u32x4*>(keys + (row0 + j) * kDk + 16 * c) =
+            *reinterpret_cast<const u32x4*>(key_rows + ((size_t)j * B + b) * kDk + 16 * c);
+    }
+    __syncthreads();                                  // every thread has read len[b]
+    if (threadIdx.x == 0) len[b] = L + n;
 }
 
 }  // namespace csa2
@@ -181,25 +239,55 @@ extern "C" int csa2_kv_append_fp4(const void* x_bf16, const long long* dst_row, 
     return launch_status("csa2_kv_append_fp4 launch");
 }
 
+static int append_tokens(const char* fn, const void* x_bf16, const signed char* key_rows,
+                         const long long* row_off, int* len, int B, int n, int n_layers,
+                         long long layer_rows, int D, int Dk, unsigned char* kv_fp4,
+                         unsigned char* kv_scale, signed char* keys, void* stream) {
+    if (B < 0 || n < 0 || n_layers < 0 || layer_rows < 0)
+        return fail(CSA2_ERR_INVALID, "%s: negative size", fn);
+    if (B == 0 || n == 0) return CSA2_OK;
+    if (!key_rows || !row_off || !len || !keys || (n_layers > 0 && (!x_bf16 || !kv_fp4 || !kv_scale)))
+        return fail(CSA2_ERR_INVALID, "%s: null pointer", fn);
+    if (Dk != kDk) return fail(CSA2_ERR_UNSUPPORTED, "%s: Dk must be 64", fn);
+    if (D <= 0 || D % 32 != 0) return fail(CSA2_ERR_INVALID, "%s: D %% 32 != 0", fn);
+    if (B > 65535) return fail(CSA2_ERR_UNSUPPORTED, "%s: B > 65535", fn);
+    if ((long long)n * n_layers > (1ll << 30) || (long long)n * B > (1ll << 30))
+        return fail(CSA2_ERR_UNSUPPORTED, "%s: n too large", fn);
+    if (!aligned(x_bf16, 16) || !aligned(key_rows, 16) || !aligned(keys, 16) ||
+        !aligned(kv_fp4, 4) || !aligned(row_off, 8) || !aligned(len, 4))
+        return fail(CSA2_ERR_INVALID, "%s: misaligned pointer", fn);
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    const uint16_t* x16 = reinterpret_cast<const uint16_t*>(x_bf16);
+    const long long items = (long long)n * n_layers;
+    if (items <= 2 * kWideItems) {                    // one workgroup per sequence, one launch
+        hipLaunchKernelGGL(append_token_kernel, dim3(B), dim3(kTokenThreads), 0, s, x16,
+                           reinterpret_cast<const int8_t*>(key_rows), row_off, len, B, n,
+                           n_layers, layer_rows, D, kv_fp4, kv_scale,
+                           reinterpret_cast<int8_t*>(keys));
+        return launch_status(fn);
+    }
+    const dim3 grid((unsigned)((items + kWideItems - 1) / kWideItems), (unsigned)B);
+    hipLaunchKernelGGL(append_rows_wide_kernel, grid, dim3(kWideThreads), 0, s, x16, row_off, len,
+                       B, n, n_layers, layer_rows, D, kv_fp4, kv_scale);
+    if (int e = launch_status(fn)) return e;
+    hipLaunchKernelGGL(append_keys_len_kernel, dim3(B), dim3(256), 0, s,
+                       reinterpret_cast<const int8_t*>(key_rows), row_off, len, B, n,
+                       reinterpret_cast<int8_t*>(keys));
+    return launch_status(fn);
+}
+
 extern "C" int csa2_append_token(const void* x_bf16, const signed char* key_rows,
                                  const long long* row_off, int* len, int B, int n_layers,
                                  long long layer_rows, int D, int Dk, unsigned char* kv_fp4,
                                  unsigned char* kv_scale, signed char* keys, void* stream) {
-    if (B < 0 || n_layers < 0 || layer_rows < 0)
-        return fail(CSA2_ERR_INVALID, "csa2_append_token: negative size");
-    if (B == 0) return CSA2_OK;
-    if (!key_rows || !row_off || !len || !keys || (n_layers > 0 && (!x_bf16 || !kv_fp4 || !kv_scale)))
-        return fail(CSA2_ERR_INVALID, "csa2_append_token: null pointer");
-    if (Dk != kDk) return fail(CSA2_ERR_UNSUPPORTED, "csa2_append_token: Dk must be 64");
-    if (D <= 0 || D % 32 != 0) return fail(CSA2_ERR_INVALID, "csa2_append_token: D %% 32 != 0");
-    if (B > 65535) return fail(CSA2_ERR_UNSUPPORTED, "csa2_append_token: B > 65535");
-    if (!aligned(x_bf16, 16) || !aligned(key_rows, 16) || !aligned(keys, 16) ||
-        !aligned(kv_fp4, 4) || !aligned(row_off, 8) || !aligned(len, 4))
-        return fail(CSA2_ERR_INVALID, "csa2_append_token: misaligned pointer");
-    hipLaunchKernelGGL(append_token_kernel, dim3(B), dim3(kTokenThreads), 0,
-                       reinterpret_cast<hipStream_t>(stream),
-                       reinterpret_cast<const uint16_t*>(x_bf16),
-                       reinterpret_cast<const int8_t*>(key_rows), row_off, len, B, n_layers,
-                       layer_rows, D, kv_fp4, kv_scale, reinterpret_cast<int8_t*>(keys));
-    return launch_status("csa2_append_token launch");
+    return append_tokens("csa2_append_token", x_bf16, key_rows, row_off, len, B, 1, n_layers,
+                         layer_rows, D, Dk, kv_fp4, kv_scale, keys, stream);
+}
+
+extern "C" int csa2_append_tokens(const void* x_bf16, const signed char* key_rows,
+                                  const long long* row_off, int* len, int B, int n, int n_layers,
+                                  long long layer_rows, int D, int Dk, unsigned char* kv_fp4,
+                                  unsigned char* kv_scale, signed char* keys, void* stream) {
+    return append_tokens("csa2_append_tokens", x_bf16, key_rows, row_off, len, B, n, n_layers,
+                         layer_rows, D, Dk, kv_fp4, kv_scale, keys, stream);
 }

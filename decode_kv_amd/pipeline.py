@@ -9,7 +9,7 @@ selection.  Every layer then attends over its selection plus the window.
 With appends, one library call first writes the new token's FP4 rows (every
 layer) and index key at the device-side length and advances it, so the token
 attends to itself.  A verify block of T drafted tokens per sequence appends
-its T tokens (one call each) and runs the block variants of the calls, which
+its T tokens (one call) and runs the block variants of the calls, which
 score, select and attend for all T tokens at once.
 """
 from __future__ import annotations
@@ -140,9 +140,12 @@ class Engine:
         s = stream
         note = mark if mark is not None else (lambda name: None)
         if wl.append:
-            for j in range(wl.block):        # a block's tokens in order, each advancing len
-                csa2.append_token(inp["app_x"][j], inp["key_rows"][j], self.row_off, self.lens,
+            if wl.block == 1:
+                csa2.append_token(inp["app_x"][0], inp["key_rows"][0], self.row_off, self.lens,
                                   self.kv_fp4, self.kv_scale, self.keys, s)
+            else:                            # a block's tokens in one call
+                csa2.append_tokens(inp["app_x"], inp["key_rows"], self.row_off, self.lens,
+                                   self.kv_fp4, self.kv_scale, self.keys, s)
             note("append")
         blk = wl.block > 1
         sh = wl.block_shared

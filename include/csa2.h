@@ -135,6 +135,67 @@ int csa2_append_token(const void* x_bf16, const signed char* key_rows,
                       unsigned char* kv_scale, signed char* keys, void* stream);
 
 /*
+ * csa2_append_tokens -- csa2_append_token for n tokens per sequence at once:
+ * token j of sequence b goes to position len[b] + j (row row_off[b] + len[b]
+ * + j), and len[b] advances by n.  A verify block appends its drafted tokens
+ * with one call; a resumed session replays its dropped window with one call
+ * (csa2_session_import).
+ *   x_bf16   [n][n_layers][B][D] bf16 (token-major), 16-byte aligned.
+ *   key_rows [n][B][Dk] int8, 16-byte aligned.
+ *   row_off, len, layer_rows, D, Dk, kv_fp4, kv_scale, keys: as
+ *            csa2_append_token.
+ * A few rows per sequence are written by one workgroup per sequence; many
+ * (a replayed window) by a grid of workgroups, then a second kernel writes
+ * the index keys and advances len.  The caller guarantees that rows
+ * row_off[b] + len[b] .. + n - 1 belong to sequence b.
+ * Errors as csa2_append_token; n == 0 is a no-op.
+ */
+int csa2_append_tokens(const void* x_bf16, const signed char* key_rows,
+                       const long long* row_off, int* len, int B, int n, int n_layers,
+                       long long layer_rows, int D, int Dk, unsigned char* kv_fp4,
+                       unsigned char* kv_scale, signed char* keys, void* stream);
+
+/*
+ * Sessions: what outlives a session, and its restore (bounded replay).
+ * ("How DeepSeek V4.1 Flash Actually Works", "The three KV-cache
+ * optimizations", item 3: the local state of the newest 128 tokens is kept
+ * only during an active session and is rebuilt by replaying those tokens;
+ * "DeepSeek V4.1-Flash 552B runs like 16B (CED)", "Act 3: FP4 KV & SWA
+ * Bounded Replay".)  In this library a sequence's state is its index keys
+ * and the FP4 rows of every layer.  csa2_session_export saves positions
+ * [0, L - min(replay, L)) of each sequence; the newest min(replay, L)
+ * positions are dropped.  csa2_session_import writes a saved state into the
+ * caches (possibly at other rows) and sets len to the saved length; the
+ * caller then appends the replayed tokens with csa2_append_tokens.  The
+ * replay itself (recomputing those tokens' rows) needs the model and is not
+ * part of this library.
+ * Saved arrays (cap rows per sequence, cap >= the longest saved length):
+ *   saved_keys  [B][cap][Dk] int8;
+ *   saved_fp4   [n_layers][B][cap][D/2];  saved_scale [n_layers][B][cap][D/32];
+ *   saved_len   [B] int32: positions saved per sequence.
+ * Every array may be device memory or pinned host memory (hipHostMalloc);
+ * the copy runs in a kernel on `stream`.  All data pointers 16-byte aligned.
+ * Requires Dk == 64 and D a multiple of 512 (else UNSUPPORTED).  A sequence
+ * with more than cap positions to save keeps only its first cap (saved_len
+ * says how many).
+ */
+int csa2_session_export(const long long* row_off, const int* len, int B, int replay,
+                        long long cap, int n_layers, long long layer_rows, int D, int Dk,
+                        const unsigned char* kv_fp4, const unsigned char* kv_scale,
+                        const signed char* keys, unsigned char* saved_fp4,
+                        unsigned char* saved_scale, signed char* saved_keys, int* saved_len,
+                        void* stream);
+
+/* csa2_session_import -- inverse of csa2_session_export: rows [0,
+ * saved_len[b]) of the saved arrays go to rows row_off[b] + p of the caches,
+ * and len[b] = saved_len[b] (device).  Arguments as csa2_session_export. */
+int csa2_session_import(const long long* row_off, int* len, const int* saved_len, int B,
+                        long long cap, int n_layers, long long layer_rows, int D, int Dk,
+                        const unsigned char* saved_fp4, const unsigned char* saved_scale,
+                        const signed char* saved_keys, unsigned char* kv_fp4,
+                        unsigned char* kv_scale, signed char* keys, void* stream);
+
+/*
  * csa2_index_full -- Full mode: score every eligible position of each
  * sequence and keep the first P_eff = min(P, E_b) positions under the rank
  * order as the candidate pool.

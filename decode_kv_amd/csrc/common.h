@@ -22,6 +22,15 @@ __device__ __forceinline__ T bitcast(const auto& x) {
     return __builtin_bit_cast(T, x);
 }
 
+// a * b + c with a, b < 2^24, as one v_mad_u32_u24 (left to itself the
+// compiler forms a multiply per product and a three-input add per pair: one
+// VALU instruction more for every two products of the scoring epilogue)
+__device__ __forceinline__ uint32_t mad_u24(uint32_t a, uint32_t b, uint32_t c) {
+    uint32_t d;
+    asm("v_mad_u32_u24 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
 // Integer score of one 16-token group against up to 64 index heads, on the
 // int8 matrix cores.  One v_mfma_i32_16x16x64_i8 per block of 16 heads:
 //   A = q rows (M = head, K = key byte), B = key rows (K = key byte, N = token).
@@ -44,7 +53,7 @@ __device__ __forceinline__ uint32_t score_partial16(const i32x4 (&qa)[NB],
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int r = acc[mb][i] > 0 ? acc[mb][i] : 0;   // ReLU, < 2^21
-            part += __umul24(wr[mb][i], (uint32_t)r);         // weight <= 15
+            part = mad_u24(wr[mb][i], (uint32_t)r, part);     // weight <= 15
         }
     return part;
 }

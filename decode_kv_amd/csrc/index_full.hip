@@ -388,7 +388,7 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
     const int* __restrict__ len, int B, int H, int window, int P, FullWs w,
     int* __restrict__ score_out, long long seq_stride) {
     __shared__ uint32_t s_hist[kKeyBins];
-    __shared__ uint32_t s_w[kDk / 4];                          // head weights, byte h = head h
+    __shared__ __attribute__((aligned(16))) uint32_t s_w[kDk];   // head weights, one dword each
     const int t = blockIdx.x;
     const int l = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -434,15 +434,17 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
     }
     asm volatile("" ::: "memory");                             // keys are in flight first
     for (int i = threadIdx.x; i < kKeyBins; i += kScoreThreads) s_hist[i] = 0;
-    if (threadIdx.x < kDk) reinterpret_cast<uint8_t*>(s_w)[threadIdx.x] = (uint8_t)wv;
+    if (threadIdx.x < kDk) s_w[threadIdx.x] = (uint32_t)wv;
     __syncthreads();                                           // histogram zeroed, weights in LDS
-    // lane l weighs heads 16 mb + 4 (l >> 4) + i, i = 0..3: one LDS word per block
+    // lane l weighs heads 16 mb + 4 (l >> 4) + i, i = 0..3: one 16-byte LDS
+    // read per block, each weight a whole dword, so the epilogue is one
+    // v_max_i32 and one v_mad_u32_u24 per product (no byte selects)
     uint32_t wr[NB][4];
 #pragma unroll
     for (int mb = 0; mb < NB; ++mb) {
-        const uint32_t word = s_w[4 * mb + (l >> 4)];
+        const u32x4 w4 = *reinterpret_cast<const u32x4*>(s_w + 16 * mb + 4 * (l >> 4));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) wr[mb][i] = (word >> (8 * i)) & 0xFFu;
+        for (int i = 0; i < 4; ++i) wr[mb][i] = w4[i];
     }
     int* sc_out = score_out + (seq_stride < 0 ? (size_t)t * kTile
                                               : (size_t)b * (size_t)seq_stride + p_tile);
@@ -485,10 +487,10 @@ constexpr int kBlockChunk = 8;            // tokens whose queries sit in LDS at 
 constexpr int kBlockGroup = 32;           // per-token lists: tokens per grid row
 
 // Dynamic LDS of the block kernel: queries [kBlockChunk][16 NB][64] (heads
-// past H are zero), weights [kBlockChunk][64] bytes (zero past H),
+// past H are zero), weights [kBlockChunk][64] dwords (zero past H),
 // histograms [kBlockChunk or 1][kKeyBins].
 static size_t block_score_lds(int NB, int planes) {
-    return (size_t)kBlockChunk * NB * 16 * kDk + (size_t)kBlockChunk * 64 +
+    return (size_t)kBlockChunk * NB * 16 * kDk + (size_t)kBlockChunk * 64 * 4 +
            (size_t)(planes == 1 ? 1 : kBlockChunk) * kKeyBins * 4;
 }
 
@@ -505,7 +507,7 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_block_kernel(
     extern __shared__ __attribute__((aligned(16))) unsigned char s_dyn[];
     i32x4* s_q = reinterpret_cast<i32x4*>(s_dyn);
     uint32_t* s_w = reinterpret_cast<uint32_t*>(s_dyn + (size_t)kBlockChunk * NB * 16 * kDk);
-    uint32_t* s_hist = s_w + kBlockChunk * 16;
+    uint32_t* s_hist = s_w + kBlockChunk * 64;
     const int g = blockIdx.x;
     const int l = lane_id();
     const int wave = threadIdx.x / kWave;
@@ -548,10 +550,9 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_block_kernel(
                                                                  (i & 3) * 16)
                                : i32x4{0, 0, 0, 0};
             }
-            uint8_t* sw8 = reinterpret_cast<uint8_t*>(s_w);
             for (int i = threadIdx.x; i < nc * 64; i += kScoreThreads) {
                 const int tk = i >> 6, h = i & 63;
-                sw8[i] = h < H ? (uint8_t)wts[((size_t)b * T + c0 + tk) * H + h] : (uint8_t)0;
+                s_w[i] = h < H ? (uint32_t)(uint8_t)wts[((size_t)b * T + c0 + tk) * H + h] : 0u;
             }
             if (planes > 1 || c0 == 0)
                 for (int i = threadIdx.x; i < (planes == 1 ? 1 : nc) * kKeyBins; i += kScoreThreads)
@@ -565,9 +566,10 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_block_kernel(
 #pragma unroll
             for (int mb = 0; mb < NB; ++mb) {
                 qa[mb] = s_q[((tc * NB + mb) * 16 + (l & 15)) * 4 + (l >> 4)];
-                const uint32_t word = s_w[tc * 16 + 4 * mb + (l >> 4)];
+                const u32x4 w4 =
+                    *reinterpret_cast<const u32x4*>(s_w + tc * 64 + 16 * mb + 4 * (l >> 4));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) wr[mb][i] = (word >> (8 * i)) & 0xFFu;
+                for (int i = 0; i < 4; ++i) wr[mb][i] = w4[i];
             }
             // per-token lists: this token's plane and its own count of positions
             const int nv = planes == 1 ? nvalid : min(kTile, ti.E - (T - 1 - tk) - p_tile);

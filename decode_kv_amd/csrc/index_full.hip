@@ -99,7 +99,8 @@ struct FullWs {
     int B;                // sequences
     int tmax;             // Tmax: tiles of the layout, the slot stride of cand_head
     int k;                // size of target 1, 0 when there is none
-    int pad;
+    int plane_tiles;      // > 0: the lists are the planes of one sequence, tile t in list
+                          // t / plane_tiles (no lookup); 0: found from the lists' states
     int* scores;          // [Tmax][kTile]
     FullState* st;        // [2][B]
     uint32_t* hist2;      // [2][B][kSubBins]
@@ -166,6 +167,7 @@ static size_t full_ws_layout(int B, long long T, int ntargets, char* base, FullW
     x.B = B;
     x.tmax = (int)T;
     x.k = 0;
+    x.plane_tiles = 0;
     if (w) *w = x;
     return off;
 }
@@ -682,13 +684,20 @@ __device__ int tile_seq(const FullState* __restrict__ st, int B, int t, int* s_b
     return *s_b;
 }
 
-// Sequence of global tile t (-1 past the last tile) and its state.  With one
-// sequence that is a single load; a batch looks the tile up first.
+// List of global tile t (-1 past the list's last tile) and its state.  With
+// one list, or with the per-token lists of one sequence (each in its own
+// plane of plane_tiles tiles), that is a single load; a batch looks the tile
+// up first.
 __device__ __forceinline__ int tile_state(const FullState* __restrict__ sts, int B, int t, int* s_b,
-                                          FullState& st) {
+                                          FullState& st, int plane_tiles) {
     if (B == 1) {
         st = sts[0];                                  // tile0 == 0
         return t < st.ntiles ? 0 : -1;
+    }
+    if (plane_tiles > 0) {
+        const int b = t / plane_tiles;
+        st = sts[b];
+        return t - st.tile0 < st.ntiles ? b : -1;
     }
     const int b = tile_seq(sts, B, t, s_b);
     if (b >= 0) st = sts[b];
@@ -711,7 +720,7 @@ __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(FullWs w) {
     for (int j = 0; j < PER; ++j) v[j] = sc[i0 + j];
     const FullTarget g = target(w, blockIdx.y);
     FullState st;
-    const int b = tile_state(g.st, B, t, &s_b, st);
+    const int b = tile_state(g.st, B, t, &s_b, st, w.plane_tiles);
     if (b < 0) return;
     const int p_tile = (t - st.tile0) * kTile;
     const int nvalid = min(kTile, st.E - p_tile);
@@ -1011,7 +1020,7 @@ __global__ __launch_bounds__(kScanThreads) void full_write_kernel(FullWs w, Full
     for (int j = 0; j < PER; ++j) v[j] = sc[i0 + j];
     const int tile_gt = g.tile_off[2 * t], tile_eq = g.tile_off[2 * t + 1];
     FullState st;
-    const int b = tile_state(g.st, B, t, &s_b, st);
+    const int b = tile_state(g.st, B, t, &s_b, st, w.plane_tiles);
     // tail fill of sequence t (each block handles at most one sequence's tail)
     if (t < B) {
         const int Peff = B == 1 ? st.Peff : g.st[t].Peff;
@@ -1224,6 +1233,7 @@ extern "C" int csa2_index_full_block(const signed char* q, const signed char* w,
     FullWs fw;
     full_ws_layout(B * planes, planes * TB, k > 0 ? 2 : 1, reinterpret_cast<char*>(ws), &fw);
     fw.k = k;
+    if (B == 1 && planes > 1) fw.plane_tiles = (int)TB;     // list v owns plane v
     // per-token lists: tiles over the last token's positions (it sees the
     // most); shared list: over the first token's, the ones every token sees
     if (int e = launch_score_block(H, T, shared, (unsigned)TB, s, q, w, keys, row_off, len, B,

@@ -280,6 +280,66 @@ def session_measure(eng, case, stream, reps: int = 10) -> dict:
     }
 
 
+def measure_overheads() -> dict:
+    """The cost of a dependent kernel node in a captured graph (a chain of
+    empty kernels) and of handing split partials to a merge in a second kernel
+    versus inside one kernel (csa2_handoff), at the attention's one-sequence
+    shape (4 head groups x 20 splits) and a wider one (8 x 16)."""
+    import torch
+
+    from decode_kv_amd import csa2
+    stream = torch.cuda.Stream()
+
+    def graph_us(fn, n, reps=5):
+        with torch.cuda.stream(stream):
+            fn()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            fn()
+        best = None
+        for _ in range(reps):
+            with torch.cuda.stream(stream):
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                g.replay()
+                b.record()
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e3 / n
+            best = t if best is None else min(best, t)
+        return best
+
+    res = {}
+    for n in (55, 110):
+        res["graph_node_us_%d_nodes" % n] = round(
+            graph_us(lambda: [csa2.empty_kernel(stream) for _ in range(n)], n), 3)
+    ho = {}
+    for groups, splits in ((4, 20), (8, 16)):
+        scratch = torch.zeros(csa2.handoff_scratch_bytes(groups, splits), dtype=torch.uint8,
+                              device="cuda")
+        out = torch.zeros((groups, 8192), dtype=torch.float32, device="cuda")
+        ref = None
+        row = {}
+        for mode, name in ((0, "two_kernels"), (1, "one_kernel_write_through_counter"),
+                           (2, "one_kernel_device_fences")):
+            iters = 50
+            us = graph_us(lambda: [csa2.handoff(mode, groups, splits, 1.0 + (i % 7), scratch, out,
+                                                stream) for i in range(iters)], iters)
+            got = out.clone()
+            ok = bool(torch.isfinite(got).all())
+            if ref is None:
+                ref = got
+            row[name] = {"us_per_handoff": round(us, 3), "finite": ok,
+                         "same_as_two_kernels": bool(torch.equal(got, ref))}
+        ho["%d_groups_x_%d_splits" % (groups, splits)] = row
+    res["handoff"] = ho
+    res["note"] = ("graph of dependent empty kernels (per node), and 50 hand-offs of 32 KiB "
+                   "partials per workgroup captured in one graph (per hand-off); best of 5 "
+                   "replays, HIP events on the replay stream")
+    return res
+
+
 def say(msg: str):
     """Progress line on stderr (the JSON result is the only stdout line)."""
     print(msg, file=sys.stderr, flush=True)
@@ -297,6 +357,8 @@ def main():
     ap.add_argument("--cold-only", action="store_true", help="skip the warm-mode timing")
     ap.add_argument("--no-session", action="store_true",
                     help="skip the session save / restore / replay measurement")
+    ap.add_argument("--overheads", action="store_true",
+                    help="only measure the kernel-node and partial hand-off costs (one JSON line)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the library has no multi-GPU path "
@@ -310,6 +372,9 @@ def main():
 
     assert torch.cuda.is_available(), "no GPU"
     csa2.lib()
+    if args.overheads:
+        print(json.dumps({"overheads": measure_overheads()}), flush=True)
+        return
     dev = torch.device("cuda:0")
     wl0 = W.WORKLOADS[args.workload]
     K = args.steps if args.steps is not None else (64 if wl0.append else 50)

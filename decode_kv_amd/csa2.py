@@ -69,6 +69,12 @@ def lib():
         L.csa2_stream_read_sink_words.argtypes = [SZ]
         L.csa2_stream_read.restype = I
         L.csa2_stream_read.argtypes = [V, SZ, V, SZ, V]
+        L.csa2_empty_kernel.restype = I
+        L.csa2_empty_kernel.argtypes = [V]
+        L.csa2_handoff_scratch_bytes.restype = SZ
+        L.csa2_handoff_scratch_bytes.argtypes = [I, I]
+        L.csa2_handoff.restype = I
+        L.csa2_handoff.argtypes = [I, I, I, F, V, SZ, V, V]
         L.csa2_sparse_attn_decode_static.restype = I
         L.csa2_sparse_attn_decode_static.argtypes = [V, V, V, V, V, LL, V, V, I, I, I, I, I, F,
                                                      V, V, V]
@@ -249,6 +255,22 @@ def stream_read(src, sink, stream=None):
 
 def stream_read_sink_words(nbytes: int) -> int:
     return int(lib().csa2_stream_read_sink_words(nbytes))
+
+
+def empty_kernel(stream=None):
+    _check("csa2_empty_kernel", lib().csa2_empty_kernel(_s(stream)))
+
+
+def handoff_scratch_bytes(groups: int, splits: int) -> int:
+    return int(lib().csa2_handoff_scratch_bytes(groups, splits))
+
+
+def handoff(mode: int, groups: int, splits: int, value: float, scratch, out, stream=None):
+    """Measurement helper (include/csa2_measure.h): split partials handed to a
+    merge in a second kernel (mode 0) or in the same kernel (modes 1, 2)."""
+    nbytes = scratch.numel() * scratch.element_size()
+    _check("csa2_handoff", lib().csa2_handoff(mode, groups, splits, float(value), _p(scratch),
+                                              nbytes, _p(out), _s(stream)))
 
 
 def sparse_attn_decode(q, kv_fp4, kv_scale, row_off, lens, max_len, sel_pos, sel_len, k, window,

@@ -204,3 +204,56 @@ def test_attention_rejects_misaligned_cache_and_outputs(lib):
     ok[2] = 258                                      # scale bytes: 2-byte alignment suffices
     ok[16] = None                                    # ...so the call gets as far as the workspace
     assert a(*ok) == csa2.CSA2_ERR_WORKSPACE
+
+
+def test_block_and_session_entries_reject_bad_arguments(lib):
+    """Every call below fails its host-side checks, so nothing is launched
+    (the pointers are not real device memory)."""
+    OK, INV, UNS, WS = csa2.CSA2_OK, csa2.CSA2_ERR_INVALID, csa2.CSA2_ERR_UNSUPPORTED, \
+        csa2.CSA2_ERR_WORKSPACE
+    p = 1 << 20                                       # 16-aligned stand-in address
+    full = lib.csa2_index_full_block
+    args = lambda T, shared, B=1, H=64, Dk=64: (p, p, p, p, p, B, T, shared, 100, 100, H, Dk, 128,
+                                               64, p, p, p, 0, None, None, p, 1 << 30, None)
+    assert full(*args(0, 0)) == INV                  # T < 1
+    assert full(*args(5, 2)) == INV                  # shared not 0 / 1
+    assert full(*args(1025, 0)) == UNS               # T > 1024
+    assert full(*args(5, 0, Dk=32)) == UNS
+    assert full(*args(5, 0, B=0)) == OK              # nothing to do
+    assert full(*args(1000, 0, B=100)) == UNS        # more than 65535 lists
+    assert lib.csa2_index_score_block(p, p, p, p, p, 1, 0, 0, 100, 100, 64, 64, 128, p, p, 1 << 30,
+                                      None) == INV
+    assert lib.csa2_index_reindex_block(p, p, p, p, p, p, 1, 5, 3, 64, 64, 16, p, None) == INV
+    assert lib.csa2_index_reindex_block(p, p, p, p, p, p, 100, 1000, 0, 64, 64, 16, p, None) == UNS
+    attn = lib.csa2_sparse_attn_decode_block
+    aargs = lambda T, shared, q=p: (q, p, p, p, p, 100, p, p, 1, T, shared, 64, 512, 16, 128,
+                                   0.1, p, None, p, 1 << 30, None)
+    assert attn(*aargs(0, 0)) == INV and attn(*aargs(2, 5)) == INV
+    assert attn(*aargs(1025, 0)) == UNS
+    assert attn(*aargs(5, 0, q=p + 8)) == INV        # query rows read in 16-byte pieces
+    tok = lib.csa2_append_tokens
+    assert tok(p, p, p, p, 1, -1, 3, 100, 512, 64, p, p, p, None) == INV
+    assert tok(p, p, p, p, 1, 0, 3, 100, 512, 64, p, p, p, None) == OK   # n == 0
+    assert tok(p, p, p, p, 1, 5, 3, 100, 512, 32, p, p, p, None) == UNS   # Dk != 64
+    assert tok(p, p, p, p, 1, 5, 3, 100, 500, 64, p, p, p, None) == INV   # D % 32 != 0
+    exp = lib.csa2_session_export
+    assert exp(p, p, 1, 128, 10, 2, 100, 96, 64, p, p, p, p, p, p, p, None) == UNS   # D % 512
+    assert exp(p, p, 1, 128, 10, 2, 100, 512, 64, p + 4, p, p, p, p, p, p, None) == INV
+    assert exp(p, p, 1, -1, 10, 2, 100, 512, 64, p, p, p, p, p, p, p, None) == INV
+    imp = lib.csa2_session_import
+    assert imp(p, p, None, 1, 10, 2, 100, 512, 64, p, p, p, p, p, p, None) == INV
+    assert lib.csa2_block_workspace_bytes(csa2.OP_INDEX_FULL, 1, 0, 0, 100, 100, 64, 64, 0, 0, 0,
+                                          128) == 0
+
+
+def test_handoff_rejects_bad_arguments(lib):
+    p = 1 << 20
+    need = lib.csa2_handoff_scratch_bytes(4, 20)
+    assert need == ((4 * 20 * 8192 * 4 + 255) // 256) * 256 + 32
+    assert lib.csa2_handoff_scratch_bytes(0, 20) == 0
+    h = lib.csa2_handoff
+    assert h(3, 4, 20, 1.0, p, need, p, None) == csa2.CSA2_ERR_INVALID
+    assert h(0, 4, 20, 1.0, p + 16, need, p, None) == csa2.CSA2_ERR_INVALID   # scratch 256-aligned
+    assert h(1, 4, 20, 1.0, p, need - 1, p, None) == csa2.CSA2_ERR_WORKSPACE
+    big = lib.csa2_handoff_scratch_bytes(8, 40)
+    assert h(1, 8, 40, 1.0, p, big, p, None) == csa2.CSA2_ERR_UNSUPPORTED     # 320 workgroups

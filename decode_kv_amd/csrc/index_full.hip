@@ -383,7 +383,9 @@ __device__ __noinline__ TileInfo map_tile(const int* __restrict__ len,
 // need no lookup, so they travel together with the length), then all of the
 // wave's key loads, and only then the first barrier, so nothing waits between
 // the length arriving and the key stream starting.
-template <int NB>
+// ONE: one sequence (no tile lookup, so no call to map_tile and fewer
+// registers: three workgroups fit on a CU).
+template <int NB, bool ONE>
 __global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ wts,
     const int8_t* __restrict__ keys, const long long* __restrict__ row_off,
@@ -407,7 +409,7 @@ __global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
         if (threadIdx.x < H) wv = (uint8_t)wts[(size_t)b * H + threadIdx.x];
     };
     TileInfo ti;
-    if (B == 1) {
+    if constexpr (ONE) {
         load_query(0);
         ti = map_tile_one(len, row_off, window, P, w.k, t, w.st, w.k > 0 ? w.st + B : nullptr);
         if (ti.b < 0) return;                              // past the last tile
@@ -1101,11 +1103,16 @@ static int launch_score(int H, unsigned tiles, hipStream_t s, const signed char*
     const int8_t* w8 = reinterpret_cast<const int8_t*>(w);
     const int8_t* k8 = reinterpret_cast<const int8_t*>(keys);
     const dim3 grid(tiles), blk(kScoreThreads);
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw,
+                           out, seq_stride);
+    };
+    const bool one = B == 1;
     switch ((H + 15) / 16) {
-        case 1: hipLaunchKernelGGL(full_score_kernel<1>, grid, blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw, out, seq_stride); break;
-        case 2: hipLaunchKernelGGL(full_score_kernel<2>, grid, blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw, out, seq_stride); break;
-        case 3: hipLaunchKernelGGL(full_score_kernel<3>, grid, blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw, out, seq_stride); break;
-        default: hipLaunchKernelGGL(full_score_kernel<4>, grid, blk, 0, s, q8, w8, k8, row_off, len, B, H, window, P, fw, out, seq_stride); break;
+        case 1: one ? launch(full_score_kernel<1, true>) : launch(full_score_kernel<1, false>); break;
+        case 2: one ? launch(full_score_kernel<2, true>) : launch(full_score_kernel<2, false>); break;
+        case 3: one ? launch(full_score_kernel<3, true>) : launch(full_score_kernel<3, false>); break;
+        default: one ? launch(full_score_kernel<4, true>) : launch(full_score_kernel<4, false>); break;
     }
     return launch_status("full_score");
 }

@@ -267,7 +267,7 @@ __device__ __forceinline__ void find_bin(const H* h, int nb, int need, int* s_tm
 
 // Tile t -> sequence, from the lengths (up to kMaxBatch sequences, 8 per
 // thread).  Returns the sequence (or -1 past the last tile) and the layout of
-// that sequence.  Workgroup 0 also writes every list's state (write_states):
+// that sequence.  The lists' states are written on the way (write_states):
 // st0 gets P_eff = min(P, E) and st1 (when not null) min(k, E).
 struct TileInfo {
     int b, tile0, E;
@@ -363,7 +363,12 @@ __device__ __noinline__ TileInfo map_tile(const int* __restrict__ len,
                 s_E = Ev[i];
                 s_roff = row_off[b];
             }
-            if (t == 0 && st0) write_states(st0, st1, b, Ev[i], P, k, pre_t, planes, TB);
+            // one list per sequence: workgroup 0 writes them all; several
+            // (per-token lists) are written by the sequence's first tile,
+            // spread over its threads, and workgroup 0 covers sequences
+            // without tiles
+            if (t == 0 && st0 && (planes == 1 || nt[i] == 0))
+                write_states(st0, st1, b, Ev[i], P, k, pre_t, planes, TB);
         }
         pre_t += nt[i];
     }
@@ -372,6 +377,9 @@ __device__ __noinline__ TileInfo map_tile(const int* __restrict__ len,
     r.tile0 = s_tile0;
     r.E = s_E;
     r.roff = s_roff;
+    if (planes > 1 && st0 && r.b >= 0 && t == r.tile0)
+        for (int i = threadIdx.x; i < planes; i += NT)
+            write_state(st0, st1, r.b, r.E, P, k, r.tile0, planes, TB, i);
     return r;
 }
 

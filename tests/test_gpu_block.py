@@ -81,8 +81,10 @@ def check_full_block(keys, row_off, lens, q, w, window, P, k, shared, what=""):
 @pytest.mark.parametrize("shared", [False, True])
 def test_index_full_block_ragged(shared):
     """Lengths around tile edges (1,024 positions) and the window, one
-    sequence shorter than a tile, one whose first tokens see nothing."""
-    lens = [70000, 1024 + 128 + 2, 3 * 1024 + 128 + 4, 140, 133, 130]
+    sequence shorter than a tile, one whose first tokens see nothing, one
+    where no token ranks a position (no tiles: its lists' states come from
+    workgroup 0)."""
+    lens = [70000, 1024 + 128 + 2, 3 * 1024 + 128 + 4, 140, 133, 130, 100]
     keys, row_off, q, w = _block_case(1, lens, 5)
     check_full_block(keys, row_off, lens, q, w, 128, 2048, 100, shared, "ragged")
 
@@ -360,3 +362,12 @@ def test_workload_prefill_chunk_sampled():
         check_attention(eng.out[0, 0, t].cpu().numpy(), eng.lse[0, 0, t].cpu().numpy(), ro, rl,
                         "prefill token %d" % t)
         _say("  checked prefill token", t)
+
+
+def test_index_full_block_long_batch():
+    """600 per-token lists per sequence (the lists' states written by each
+    sequence's first tile, two per thread); the shorter sequences' first
+    tokens rank nothing (700: tokens 0-26, 600: tokens 0-127)."""
+    lens = [3000, 2500, 700, 600]
+    keys, row_off, q, w = _block_case(13, lens, 600, H=16)
+    check_full_block(keys, row_off, lens, q, w, 128, 500, 50, False, "B=3 T=600")

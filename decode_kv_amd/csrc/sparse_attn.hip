@@ -47,7 +47,7 @@ constexpr int kHeadsPerWg = 16;
 constexpr int kVjdLdMax = kAttnD + 16;  // bf16 per row-major row, at most (1,056 B)
 constexpr int kAttnMaxTilesPerWg = 4;   // tiles whose loads one workgroup keeps in flight
 constexpr int kAttnMaxRows = 16384;     // k + window
-constexpr int kAttnMinWgs = 64;         // workgroups wanted per launch
+constexpr int kAttnMinWgs = 160;        // workgroups wanted per launch
 constexpr int kAttnWideWgs = 256;       // above this many workgroups, the wide layout
 constexpr int kAttnMaxSplits = kAttnMaxRows / kAttnRows;   // one tile per split at most
 

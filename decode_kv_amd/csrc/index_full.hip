@@ -326,7 +326,7 @@ __device__ __forceinline__ TileInfo map_tile_one(const int* __restrict__ len,
 }
 
 template <int NT>
-__device__ __noinline__ TileInfo map_tile(const int* __restrict__ len,
+__device__ __forceinline__ TileInfo map_tile(const int* __restrict__ len,
                                           const long long* __restrict__ row_off, int B,
                                           int window, int P, int k, int t, FullState* st0,
                                           FullState* st1, int planes = 1, int TB = 0) {
@@ -391,10 +391,11 @@ __device__ __noinline__ TileInfo map_tile(const int* __restrict__ len,
 // need no lookup, so they travel together with the length), then all of the
 // wave's key loads, and only then the first barrier, so nothing waits between
 // the length arriving and the key stream starting.
-// ONE: one sequence (no tile lookup, so no call to map_tile and fewer
-// registers: three workgroups fit on a CU).
+// ONE: one sequence (no tile lookup).  Both instances fit six waves per SIMD
+// (three workgroups per CU; the batch instance spills one key operand to
+// fit), so 768 of a 1M context's 1,024 tiles run in the first round.
 template <int NB, bool ONE>
-__global__ __launch_bounds__(kScoreThreads) void full_score_kernel(
+__global__ __launch_bounds__(kScoreThreads, 6) void full_score_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ wts,
     const int8_t* __restrict__ keys, const long long* __restrict__ row_off,
     const int* __restrict__ len, int B, int H, int window, int P, FullWs w,

@@ -716,61 +716,76 @@ __device__ __forceinline__ int tile_state(const FullState* __restrict__ sts, int
 }
 
 // ---- 3. gather: entries above / inside bin B1 --------------------------------------
+// Workgroup x handles tiles G x .. G x + G - 1 (G > 1 when there are many
+// tiles: every tile's scores are loaded at once, and consecutive tiles of one
+// list share the bin search).
+template <int G>
 __global__ __launch_bounds__(kScanThreads) void full_gather_kernel(FullWs w) {
     const int B = w.B;
     __shared__ int s_b;
     __shared__ int s_tmp[kScanThreads / kWave];
     __shared__ int s_res[3];
-    const int t = blockIdx.x;
-    // the tile's scores sit at t * kTile whatever its sequence: load them first
-    const int* sc = w.scores + (size_t)t * kTile;
+    const int tfirst = blockIdx.x * G;
     constexpr int PER = kTile / kScanThreads;   // contiguous positions per thread
     const int i0 = threadIdx.x * PER;
-    int v[PER];
+    // the tiles' scores sit at t * kTile whatever their list: load them first
+    int v[G][PER];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) v[j] = sc[i0 + j];
+    for (int i = 0; i < G; ++i) {
+        const int* sc = w.scores + (size_t)min(tfirst + i, w.tmax - 1) * kTile;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[i][j] = sc[i0 + j];
+    }
     const FullTarget g = target(w, blockIdx.y);
-    FullState st;
-    const int b = tile_state(g.st, B, t, &s_b, st, w.plane_tiles);
-    if (b < 0) return;
-    const int p_tile = (t - st.tile0) * kTile;
-    const int nvalid = min(kTile, st.E - p_tile);
+    int bprev = -1, kb = 0, above = 0, cnt = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j)
-        if (i0 + j >= nvalid) v[j] = -1;
-    int kb, above, cnt;
-    find_bin<kScanThreads, (kKeyBins + kScanThreads - 1) / kScanThreads>(
-        w.hist + (size_t)b * kKeyBins, kKeyBins, st.Peff, s_tmp, s_res, kb, above, cnt);
-    int lo, hi, sh, nb;
-    key_interval(kb, lo, hi);
-    sub_digit(lo, hi, sh, nb);
-    // per-thread counts of entries above / inside the bin, packed in one scan
-    int n_above = 0, n_in = 0;
+    for (int i = 0; i < G; ++i) {
+        const int t = tfirst + i;
+        if (t >= w.tmax) break;                      // uniform
+        FullState st;
+        const int b = tile_state(g.st, B, t, &s_b, st, w.plane_tiles);
+        if (b < 0) continue;                         // uniform
+        const int p_tile = (t - st.tile0) * kTile;
+        const int nvalid = min(kTile, st.E - p_tile);
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        n_above += v[j] > hi;
-        n_in += v[j] >= lo && v[j] <= hi;
-    }
-    int tot;
-    int slot = block_exclusive_scan<kScanThreads>((n_in << 16) | n_above, s_tmp, tot) >> 16;
-    if (threadIdx.x == 0) {
-        g.tile_above[t] = tot & 0xFFFF;
-        g.tile_cnt[t] = tot >> 16;
-        if (t == st.tile0) {
-            g.st[b].kb = kb;
-            g.st[b].above = above;
+        for (int j = 0; j < PER; ++j)
+            if (i0 + j >= nvalid) v[i][j] = -1;
+        if (b != bprev) {                            // uniform
+            find_bin<kScanThreads, (kKeyBins + kScanThreads - 1) / kScanThreads>(
+                w.hist + (size_t)b * kKeyBins, kKeyBins, st.Peff, s_tmp, s_res, kb, above, cnt);
+            bprev = b;
         }
-    }
-    int* head = g.cand_head + t;
-    int* out = g.cand + (size_t)t * kTile;
-    uint32_t* h2 = g.hist2 + (size_t)b * kSubBins;
+        int lo, hi, sh, nb;
+        key_interval(kb, lo, hi);
+        sub_digit(lo, hi, sh, nb);
+        // per-thread counts of entries above / inside the bin, packed in one scan
+        int n_above = 0, n_in = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        if (v[j] >= lo && v[j] <= hi) {
-            if (slot < kCandHead) head[(size_t)slot * w.tmax] = v[j];
-            else out[slot] = v[j];
-            ++slot;
-            atomicAdd(&h2[(unsigned)(v[j] - lo) >> sh], 1u);
+        for (int j = 0; j < PER; ++j) {
+            n_above += v[i][j] > hi;
+            n_in += v[i][j] >= lo && v[i][j] <= hi;
+        }
+        int tot;
+        int slot = block_exclusive_scan<kScanThreads>((n_in << 16) | n_above, s_tmp, tot) >> 16;
+        if (threadIdx.x == 0) {
+            g.tile_above[t] = tot & 0xFFFF;
+            g.tile_cnt[t] = tot >> 16;
+            if (t == st.tile0) {
+                g.st[b].kb = kb;
+                g.st[b].above = above;
+            }
+        }
+        int* head = g.cand_head + t;
+        int* out = g.cand + (size_t)t * kTile;
+        uint32_t* h2 = g.hist2 + (size_t)b * kSubBins;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            if (v[i][j] >= lo && v[i][j] <= hi) {
+                if (slot < kCandHead) head[(size_t)slot * w.tmax] = v[i][j];
+                else out[slot] = v[i][j];
+                ++slot;
+                atomicAdd(&h2[(unsigned)(v[i][j] - lo) >> sh], 1u);
+            }
         }
     }
 }
@@ -1013,71 +1028,84 @@ __global__ __launch_bounds__(kThrThreads) void full_threshold_kernel(FullWs w) {
 }
 
 // ---- 5. write: ordered compaction of the pool (and of the top k) -----------------
-// blockIdx.y selects the target and its output.
+// blockIdx.y selects the target and its output.  Workgroup x handles tiles
+// G x .. G x + G - 1, and fills the tails of the lists with those indices.
+template <int G>
 __global__ __launch_bounds__(kScanThreads) void full_write_kernel(FullWs w, FullOut o0,
                                                                   FullOut o1) {
     const int B = w.B;
     __shared__ int s_b;
     __shared__ int s_tmp[kScanThreads / kWave];
-    const int t = blockIdx.x;
+    const int tfirst = blockIdx.x * G;
     const FullTarget g = target(w, blockIdx.y);
     const FullOut o = blockIdx.y ? o1 : o0;
-    // the tile's scores and output offsets sit at t whatever its sequence: load first
-    const int* sc = w.scores + (size_t)t * kTile;
     constexpr int PER = kTile / kScanThreads;   // contiguous positions per thread
     const int i0 = threadIdx.x * PER;
-    int v[PER];
+    // the tiles' scores and output offsets sit at t whatever their list: load first
+    int v[G][PER];
+    int tile_gt[G], tile_eq[G];
 #pragma unroll
-    for (int j = 0; j < PER; ++j) v[j] = sc[i0 + j];
-    const int tile_gt = g.tile_off[2 * t], tile_eq = g.tile_off[2 * t + 1];
-    FullState st;
-    const int b = tile_state(g.st, B, t, &s_b, st, w.plane_tiles);
-    // tail fill of sequence t (each block handles at most one sequence's tail)
-    if (t < B) {
-        const int Peff = B == 1 ? st.Peff : g.st[t].Peff;
-        for (int i = Peff + threadIdx.x; i < o.stride; i += kScanThreads) {
-            o.pos[(size_t)t * o.stride + i] = -1;
-            if (o.score) o.score[(size_t)t * o.stride + i] = -1;
-        }
-        if (threadIdx.x == 0) o.len[t] = Peff;
+    for (int i = 0; i < G; ++i) {
+        const int tc = min(tfirst + i, w.tmax - 1);
+        const int* sc = w.scores + (size_t)tc * kTile;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[i][j] = sc[i0 + j];
+        tile_gt[i] = g.tile_off[2 * tc];
+        tile_eq[i] = g.tile_off[2 * tc + 1];
     }
-    if (b < 0) return;
-    const int p_tile = (t - st.tile0) * kTile;
-    const int nvalid = min(kTile, st.E - p_tile);
-    int n_eq = 0;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        if (i0 + j >= nvalid) v[j] = -1;             // scores are >= 0
-        n_eq += (v[j] >= 0) & (v[j] == st.T);
-    }
-    int tot;
-    const int eq_before = block_exclusive_scan<kScanThreads>(n_eq, s_tmp, tot) + tile_eq;
-    int n_sel = 0, eq_rank = eq_before;
-    bool take[PER];
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        bool tk = false;
-        if (v[j] < 0) tk = false;
-        else if (v[j] > st.T) tk = true;
-        else if (v[j] == st.T) {
-            tk = eq_rank < st.needT;
-            ++eq_rank;
-        }
-        take[j] = tk;
-        n_sel += tk;
-    }
-    int base = tile_gt + (tile_eq < st.needT ? tile_eq : st.needT);
-    base += block_exclusive_scan<kScanThreads>(n_sel, s_tmp, tot);
-    int* out_p = o.pos + (size_t)b * o.stride;
-    int* out_s = o.score ? o.score + (size_t)b * o.stride : nullptr;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        if (take[j]) {
-            if (base < st.Peff) {            // always true for consistent inputs
-                out_p[base] = p_tile + i0 + j;
-                if (out_s) out_s[base] = v[j];
+    for (int i = 0; i < G; ++i) {
+        const int t = tfirst + i;
+        if (t >= w.tmax && t >= B) break;            // uniform
+        FullState st;
+        const int b = t < w.tmax ? tile_state(g.st, B, t, &s_b, st, w.plane_tiles) : -1;
+        // tail fill of list t (each tile index fills at most one list's tail)
+        if (t < B) {
+            const int Peff = B == 1 ? g.st[0].Peff : g.st[t].Peff;
+            for (int r = Peff + threadIdx.x; r < o.stride; r += kScanThreads) {
+                o.pos[(size_t)t * o.stride + r] = -1;
+                if (o.score) o.score[(size_t)t * o.stride + r] = -1;
             }
-            ++base;
+            if (threadIdx.x == 0) o.len[t] = Peff;
+        }
+        if (b < 0) continue;                         // uniform
+        const int p_tile = (t - st.tile0) * kTile;
+        const int nvalid = min(kTile, st.E - p_tile);
+        int n_eq = 0;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            if (i0 + j >= nvalid) v[i][j] = -1;      // scores are >= 0
+            n_eq += (v[i][j] >= 0) & (v[i][j] == st.T);
+        }
+        int tot;
+        const int eq_before = block_exclusive_scan<kScanThreads>(n_eq, s_tmp, tot) + tile_eq[i];
+        int n_sel = 0, eq_rank = eq_before;
+        bool take[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            bool tk = false;
+            if (v[i][j] < 0) tk = false;
+            else if (v[i][j] > st.T) tk = true;
+            else if (v[i][j] == st.T) {
+                tk = eq_rank < st.needT;
+                ++eq_rank;
+            }
+            take[j] = tk;
+            n_sel += tk;
+        }
+        int base = tile_gt[i] + (tile_eq[i] < st.needT ? tile_eq[i] : st.needT);
+        base += block_exclusive_scan<kScanThreads>(n_sel, s_tmp, tot);
+        int* out_p = o.pos + (size_t)b * o.stride;
+        int* out_s = o.score ? o.score + (size_t)b * o.stride : nullptr;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            if (take[j]) {
+                if (base < st.Peff) {            // always true for consistent inputs
+                    out_p[base] = p_tile + i0 + j;
+                    if (out_s) out_s[base] = v[i][j];
+                }
+                ++base;
+            }
         }
     }
 }
@@ -1169,8 +1197,16 @@ static int launch_chain(const FullWs& fw, unsigned tiles, int P, int k, int* poo
     const int ntg = k > 0 ? 2 : 1;
     const int nl = fw.B;
     const dim3 blk(kScanThreads);
+    // very many tiles (the per-token lists of a prompt chunk): four per gather
+    // and write workgroup, so each workgroup keeps four tiles' loads in flight
+    // (prefill_128k_chunk256: index call 434 -> 418 us); with a few thousand
+    // tiles one per workgroup is faster (ragged32_1m, ctx_1m_block5: 3-4 us)
+    const bool many = tiles > 16384;
     hipLaunchKernelGGL(full_reduce_kernel, dim3(kKeyBins / kRedBins, nl), blk, 0, s, fw);
-    hipLaunchKernelGGL(full_gather_kernel, dim3(tiles, ntg), blk, 0, s, fw);
+    if (many)
+        hipLaunchKernelGGL(full_gather_kernel<4>, dim3((tiles + 3) / 4, ntg), blk, 0, s, fw);
+    else
+        hipLaunchKernelGGL(full_gather_kernel<1>, dim3(tiles, ntg), blk, 0, s, fw);
     if (nl == 1)
         hipLaunchKernelGGL(full_threshold_kernel<true>, dim3(nl, ntg), dim3(kThrThreads), 0, s, fw);
     else
@@ -1178,7 +1214,10 @@ static int launch_chain(const FullWs& fw, unsigned tiles, int P, int k, int* poo
     const unsigned wgrid = tiles > (unsigned)nl ? tiles : (unsigned)nl;
     const FullOut o0 = {pool_pos, pool_score, pool_len, P};
     const FullOut o1 = {sel_pos, nullptr, sel_len, k};
-    hipLaunchKernelGGL(full_write_kernel, dim3(wgrid, ntg), blk, 0, s, fw, o0, o1);
+    if (many)
+        hipLaunchKernelGGL(full_write_kernel<4>, dim3((wgrid + 3) / 4, ntg), blk, 0, s, fw, o0, o1);
+    else
+        hipLaunchKernelGGL(full_write_kernel<1>, dim3(wgrid, ntg), blk, 0, s, fw, o0, o1);
     return launch_status(fn);
 }
 

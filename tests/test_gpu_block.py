@@ -371,3 +371,12 @@ def test_index_full_block_long_batch():
     lens = [3000, 2500, 700, 600]
     keys, row_off, q, w = _block_case(13, lens, 600, H=16)
     check_full_block(keys, row_off, lens, q, w, 128, 500, 50, False, "B=3 T=600")
+
+
+def test_index_full_block_many_tiles():
+    """200 per-token lists over a 90,000-position context: 19,200 tiles, so
+    the gather and write kernels take four tiles per workgroup; every list
+    checked in full."""
+    lens = [90000]
+    keys, row_off, q, w = _block_case(14, lens, 200, H=16)
+    check_full_block(keys, row_off, lens, q, w, 128, 3000, 100, False, "T=200 many tiles")

@@ -329,8 +329,10 @@ int csa2_sparse_attn_decode(const void* q_bf16, const unsigned char* kv_fp4,
 /*
  * Verify blocks.  A decode step may check several drafted tokens at once: the
  * T newest cached positions of a sequence (the last T tokens appended, all
- * counted in len[b]) form its block, and token t = 0 .. T-1 sits at position
- * L_t - 1 with L_t = len[b] - (T - 1 - t).  Token t sees positions 0 .. L_t - 1
+ * counted in len[b], so len[b] >= T) form its block, and token t = 0 .. T-1
+ * sits at position L_t - 1 with L_t = len[b] - (T - 1 - t).  (A sequence
+ * shorter than its block is not valid input; the kernels give its tokens
+ * with L_t <= 0 empty lists and attention output 0, lse -inf.)  Token t sees positions 0 .. L_t - 1
  * only: its window is [L_t - min(window, L_t), L_t) and its eligible positions
  * are [0, E_t), E_t = max(0, L_t - window).  Two selection modes:
  *  - per-token (shared == 0): every token has its own pool and selection,

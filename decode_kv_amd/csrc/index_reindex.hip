@@ -12,6 +12,7 @@
 namespace csa2 {
 
 constexpr int kReThreads = 256;  // 4 waves x 64 candidates
+constexpr int kSimds = 1024;     // 256 compute units x 4 SIMDs
 
 // List y of a verify block of T tokens per sequence: shared (one list per
 // sequence, scored with the best score over the block's tokens) or per token
@@ -74,6 +75,73 @@ __global__ __launch_bounds__(kReThreads) void reindex_kernel(
     if (i < P) out[i] = i < n ? mine : -1;
 }
 
+// A shared list of a block of T > 1 tokens when the lists are few: the
+// workgroup's four waves score the same 64 candidates, wave w with tokens
+// w, w + 4, ..., and the best score over the block goes through LDS (each
+// wave's chain is about a quarter of one wave scoring every token).
+template <int NB>
+__global__ __launch_bounds__(kReThreads) void reindex_shared_kernel(
+    const int8_t* __restrict__ q, const int8_t* __restrict__ wts,
+    const int8_t* __restrict__ keys, const long long* __restrict__ row_off,
+    const int* __restrict__ cand_pos, const int* __restrict__ cand_len, int H, int P,
+    int* __restrict__ score, int T) {
+    constexpr int NW = kReThreads / kWave;
+    __shared__ int s_best[NW][kWave];
+    const int b = blockIdx.y;
+    const int l = lane_id(), wave = threadIdx.x / kWave;
+    const int base = blockIdx.x * kWave;                 // this workgroup's 64 candidates
+    if (base >= P) return;                               // uniform
+    const int* cp = cand_pos + (size_t)b * P;
+    int* out = score + (size_t)b * P;
+    int pos[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) pos[u] = cp[min(base + 16 * u + (l & 15), P - 1)];
+    const int n = min(cand_len[b], P);
+    i32x4 qa[NB];
+    uint32_t wr[NB][4];
+    const bool has = wave < T;                           // uniform per wave
+    if (has) load_index_query<NB>(q + ((size_t)b * T + wave) * H * kDk,
+                                  wts + ((size_t)b * T + wave) * H, H, qa, wr);
+    const long long roff = row_off[b];
+    if (base >= n) {                                     // uniform
+        if (wave == 0 && base + l < P) out[base + l] = -1;
+        return;
+    }
+    int mine = -1;                                       // below every valid score
+    if (has) {
+        const int8_t* kb = keys + (size_t)roff * kDk + (l >> 4) * 16;
+        const int pos0 = __builtin_amdgcn_readfirstlane(pos[0]);
+        i32x4 kop[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = base + 16 * u + (l & 15);
+            const int p = (i < n && pos[u] >= 0) ? pos[u] : pos0;
+            kop[u] = *reinterpret_cast<const i32x4*>(kb + (size_t)p * kDk);
+        }
+        for (int tk = wave; tk < T; tk += NW) {
+            if (tk != wave) {
+                const size_t r = (size_t)b * T + tk;
+                load_index_query<NB>(q + r * H * kDk, wts + r * H, H, qa, wr);
+            }
+            uint32_t part[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) part[u] = score_partial16<NB>(qa, wr, kop[u]);
+            const int sc = (int)reduce_rows4(part);      // candidate base + l
+            mine = tk == wave ? sc : max(mine, sc);
+        }
+    }
+    s_best[wave][l] = mine;
+    __syncthreads();
+    if (wave == 0) {
+        int best = s_best[0][l];
+#pragma unroll
+        for (int v = 1; v < NW; ++v)
+            if (v < T) best = max(best, s_best[v][l]);
+        const int i = base + l;
+        if (i < P) out[i] = i < n ? best : -1;
+    }
+}
+
 static int reindex(const char* fn, const signed char* q, const signed char* w,
                    const signed char* keys, const long long* row_off, const int* cand_pos,
                    const int* cand_len, int B, int T, int shared, int H, int Dk, int P,
@@ -96,6 +164,20 @@ static int reindex(const char* fn, const signed char* q, const signed char* w,
     const int8_t* q8 = reinterpret_cast<const int8_t*>(q);
     const int8_t* w8 = reinterpret_cast<const int8_t*>(w);
     const int8_t* k8 = reinterpret_cast<const int8_t*>(keys);
+    // shared lists and too few plain waves to give every SIMD one (measured:
+    // one 1M sequence's five-token block scores 27% faster split, a batch of
+    // eight 15% slower, its extra key gathers outweighing the shorter chains)
+    const long long plain_waves = (long long)lists * ((P + kWave - 1) / kWave);
+    if (shared && T > 1 && plain_waves < kSimds) {
+        const dim3 g2((P + kWave - 1) / kWave, (unsigned)lists);
+        switch ((H + 15) / 16) {
+            case 1: hipLaunchKernelGGL(reindex_shared_kernel<1>, g2, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T); break;
+            case 2: hipLaunchKernelGGL(reindex_shared_kernel<2>, g2, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T); break;
+            case 3: hipLaunchKernelGGL(reindex_shared_kernel<3>, g2, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T); break;
+            default: hipLaunchKernelGGL(reindex_shared_kernel<4>, g2, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T); break;
+        }
+        return launch_status(fn);
+    }
     switch ((H + 15) / 16) {
         case 1: hipLaunchKernelGGL(reindex_kernel<1>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T, shared); break;
         case 2: hipLaunchKernelGGL(reindex_kernel<2>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T, shared); break;

@@ -147,18 +147,20 @@ def test_index_score_block(shared):
                 assert (got[b * T + t, E:] == -77).all(), (b, t)
 
 
-@pytest.mark.parametrize("shared", [False, True])
-def test_index_reindex_block(shared):
-    rng = np.random.default_rng(8)
+@pytest.mark.parametrize("shared,T", [(False, 5), (True, 2), (True, 5), (True, 9)])
+def test_index_reindex_block(shared, T):
+    """A shared list's tokens are spread over the workgroup's four waves:
+    T = 2 leaves two waves idle, T = 9 gives one wave three tokens."""
+    rng = np.random.default_rng(8 + T)
     lens = [200000, 6000]
-    keys, row_off, q, w = _block_case(8, lens, 5)
-    B, T, P = 2, 5, 16384
+    keys, row_off, q, w = _block_case(8, lens, T)
+    B, P = 2, 16384
     nl = B if shared else B * T
     cand = np.full((nl, P), -1, dtype=np.int32)
     clen = []
     for v in range(nl):
         b = v if shared else v // T
-        n = [16384, 4000, 1, 0, 9000][v % 5] if lens[b] > 100000 else min(3000, lens[b] - 200)
+        n = [16384, 4000, 1, 0, 9000][v % 5] if lens[b] > 100000 else 3000 - 7 * (v % 5)
         clen.append(n)
         if n:
             cand[v, :n] = np.sort(rng.choice(lens[b] - 128, n, replace=False))

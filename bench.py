@@ -6,7 +6,8 @@ every 4th layer, Reuse otherwise), pool P = 16,384, top-k 512, window 128,
 64 int8 index heads x 64, 64 bf16 query heads x 512, FP4 E2M1 latent KV with
 E8M0 scales per 32 elements.  Synthetic seeded inputs.  --workload picks any
 workload of decode_kv_amd/workloads.py (tiny_4k, single_64k, batch8_256k,
-ctx_1m, ragged32_1m).
+ctx_1m, ragged32_1m, their *_shared variants, verify blocks *_block5 and
+*_block5_shared, prefill_128k_chunk256).
 
 A step is the whole hot path: for workloads with appends, the new token of
 every sequence is written into every layer's FP4 cache and the index-key
@@ -27,7 +28,11 @@ its average launch duration comes from back-to-back launches through
 csa2_index_score, captured in one HIP graph, each over a key copy that is not
 in the Infinity Cache.  read_ceiling is the same measurement for a kernel that
 only reads the key bytes (csa2_stream_read) in the scoring kernel's launch
-shape.  per_call_us times one eager step call by call.
+shape.  attention_roofline prices each layer's attention call (the attention
+kernel and its combine) the same way, from cold calls timed one by one: the
+step spends most of its time there, far below HBM speed, because at these
+sizes the call is bound by launch and memory latency, not by bytes.
+per_call_us times one eager step call by call.
 
 Output: one JSON line (metric, value = steps/s, roofline, CPU-oracle
 baseline, ...).
@@ -140,6 +145,21 @@ def stale_traffic(profile_path: str):
         return rec.get("traffic_bytes_per_launch")
     except Exception:
         return None
+
+
+def attention_roofline(ab: dict, wl, call_us: float, calls: int) -> dict:
+    """The attention call (sparse_attn_kernel and attn_combine_kernel) of one
+    layer against HBM: its algorithmic bytes (selected and window FP4 rows,
+    queries, selection entries and fp32 outputs) over its measured cold call
+    time.  Its bf16 products need far less time at the matrix-core peak than
+    its bytes at the HBM peak, so HBM is the bound it is priced against."""
+    per_call = ab["attn"] / wl.n_layers
+    gbs = per_call / (call_us * 1e-6) / 1e9
+    return {"kernel": "sparse_attn_kernel + attn_combine_kernel (one attention call per layer, "
+                      "Infinity Cache evicted before each)",
+            "bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 5), "avg_call_us": round(call_us, 3),
+            "calls_timed": calls, "algorithmic_bytes_per_call": round(per_call)}
 
 
 def cpu_baseline(wl, seed: int, step: int, keys_np, seconds_target: float = 12.0) -> dict:
@@ -510,6 +530,40 @@ def main():
         rec["us"] = round(rec["us"], 2)
     say("call-by-call step done")
 
+    # ---- each layer's attention call alone (the attention kernel and its
+    # combine), cold: the Infinity Cache is evicted before every call and one
+    # event pair on the stream brackets the call; the GPU is first held busy
+    # so that the host queues every call ahead of it
+    def attn_call(l):
+        src = eng.selection_layer(l)
+        kl = wl.kv_layer(l)
+        args = (eng.kv_fp4[kl], eng.kv_scale[kl], eng.row_off, eng.lens, eng.max_len,
+                eng.sel_pos[src], eng.sel_len[src], wl.k, wl.window)
+        if blk:
+            csa2.sparse_attn_decode_block(static["attn_q"][l], *args, wl.block_shared,
+                                          wl.sm_scale, eng.out[l], eng.lse[l], eng.ws_attn,
+                                          stream)
+        else:
+            csa2.sparse_attn_decode(static["attn_q"][l], *args, wl.sm_scale, eng.out[l],
+                                    eng.lse[l], eng.ws_attn, stream)
+
+    attn_reps = 3
+    attn_ev = []
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(50_000_000)
+        for _ in range(attn_reps):
+            for l in range(wl.n_layers):
+                evict()
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                attn_call(l)
+                e1.record()
+                attn_ev.append((e0, e1))
+    torch.cuda.synchronize()
+    attn_call_us = statistics.mean(a.elapsed_time(b) for a, b in attn_ev) * 1e3
+    say("attention call %.2f us (cold)" % attn_call_us)
+
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph, stream=stream):
         eng.run_step(static)
@@ -626,6 +680,7 @@ def main():
                          "bytes_per_launch": key_bytes,
                          "avg_launch_us": round(read_avg_ms * 1e3, 3),
                          "scan_over_ceiling": round(scan_gbs / read_gbs, 4)},
+        "attention_roofline": attention_roofline(ab, wl, attn_call_us, len(attn_ev)),
         "per_call_us": per_call,
         "per_call_note": "one eager step after the GPU was held busy, HIP events between the "
                          "library calls (kernel time plus the gaps between launches)",

@@ -6,6 +6,8 @@
 // Same int8 MFMA scoring as the Full scan, with the key operand gathered:
 // each lane loads 16 bytes of the 64-byte key row of its candidate, four lanes
 // per row, so every row costs one 64-byte segment.
+#include <type_traits>
+
 #include "abi_common.h"
 #include "common.h"
 
@@ -17,17 +19,18 @@ constexpr int kSimds = 1024;     // 256 compute units x 4 SIMDs
 // List y of a verify block of T tokens per sequence: shared (one list per
 // sequence, scored with the best score over the block's tokens) or per token
 // (list y = b * T + t, scored with token t's query).  T == 1 is the plain
-// one-token step.
-template <int NB>
+// one-token step, whose instance (BLOCK false) carries none of the block's
+// bookkeeping.
+template <int NB, bool BLOCK>
 __global__ __launch_bounds__(kReThreads) void reindex_kernel(
     const int8_t* __restrict__ q, const int8_t* __restrict__ wts,
     const int8_t* __restrict__ keys, const long long* __restrict__ row_off,
     const int* __restrict__ cand_pos, const int* __restrict__ cand_len, int H, int P,
     int* __restrict__ score, int T, int shared) {
     const int y = blockIdx.y;
-    const int b = shared || T == 1 ? y : y / T;         // sequence: its keys
-    const int tk0 = shared ? 0 : y - b * T;              // tokens tk0 .. tk1 - 1 score the list
-    const int tk1 = shared ? T : tk0 + 1;
+    const int b = BLOCK && !shared ? y / T : y;          // sequence: its keys
+    const int tk0 = BLOCK && !shared ? y - b * T : 0;    // tokens tk0 .. tk1 - 1 score the list
+    const int tk1 = !BLOCK ? 1 : (shared ? T : tk0 + 1);
     const int l = lane_id();
     const int base = blockIdx.x * kReThreads + (threadIdx.x / kWave) * kWave;
     if (base >= P) return;
@@ -42,7 +45,7 @@ __global__ __launch_bounds__(kReThreads) void reindex_kernel(
     const int n = min(cand_len[y], P);
     i32x4 qa[NB];
     uint32_t wr[NB][4];
-    const size_t qrow = (size_t)b * T + tk0;             // the first token's query
+    const size_t qrow = BLOCK ? (size_t)b * T + tk0 : (size_t)b;   // the first token's query
     load_index_query<NB>(q + qrow * H * kDk, wts + qrow * H, H, qa, wr);
     const long long roff = row_off[b];
     if (base >= n) {
@@ -64,12 +67,14 @@ __global__ __launch_bounds__(kReThreads) void reindex_kernel(
 #pragma unroll
     for (int u = 0; u < 4; ++u) part[u] = score_partial16<NB>(qa, wr, kop[u]);
     int mine = (int)reduce_rows4(part);                // candidate base + l
-    for (int tk = tk0 + 1; tk < tk1; ++tk) {             // shared list: best over the block
-        const size_t r = (size_t)b * T + tk;
-        load_index_query<NB>(q + r * H * kDk, wts + r * H, H, qa, wr);
+    if constexpr (BLOCK) {
+        for (int tk = tk0 + 1; tk < tk1; ++tk) {         // shared list: best over the block
+            const size_t r = (size_t)b * T + tk;
+            load_index_query<NB>(q + r * H * kDk, wts + r * H, H, qa, wr);
 #pragma unroll
-        for (int u = 0; u < 4; ++u) part[u] = score_partial16<NB>(qa, wr, kop[u]);
-        mine = max(mine, (int)reduce_rows4(part));
+            for (int u = 0; u < 4; ++u) part[u] = score_partial16<NB>(qa, wr, kop[u]);
+            mine = max(mine, (int)reduce_rows4(part));
+        }
     }
     const int i = base + l;
     if (i < P) out[i] = i < n ? mine : -1;
@@ -178,12 +183,23 @@ static int reindex(const char* fn, const signed char* q, const signed char* w,
         }
         return launch_status(fn);
     }
-    switch ((H + 15) / 16) {
-        case 1: hipLaunchKernelGGL(reindex_kernel<1>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T, shared); break;
-        case 2: hipLaunchKernelGGL(reindex_kernel<2>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T, shared); break;
-        case 3: hipLaunchKernelGGL(reindex_kernel<3>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T, shared); break;
-        default: hipLaunchKernelGGL(reindex_kernel<4>, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos, cand_len, H, P, score, T, shared); break;
-    }
+    auto launch = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(kReThreads), 0, s, q8, w8, k8, row_off, cand_pos,
+                           cand_len, H, P, score, T, shared);
+    };
+    auto launch_nb = [&](auto blk) {
+        constexpr bool BLK = decltype(blk)::value;
+        switch ((H + 15) / 16) {
+            case 1: launch(reindex_kernel<1, BLK>); break;
+            case 2: launch(reindex_kernel<2, BLK>); break;
+            case 3: launch(reindex_kernel<3, BLK>); break;
+            default: launch(reindex_kernel<4, BLK>); break;
+        }
+    };
+    if (T > 1)
+        launch_nb(std::true_type{});
+    else
+        launch_nb(std::false_type{});
     return launch_status(fn);
 }
 

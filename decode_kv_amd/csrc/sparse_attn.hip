@@ -34,6 +34,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "abi_common.h"
 #include "common.h"
@@ -147,7 +148,9 @@ __device__ __forceinline__ bool attn_place(int flags, int B, int HG, int n_split
     return pair < B * HG;
 }
 
-template <int TPW, bool WIDE>
+// BLOCK: a verify block (T > 1 query rows per sequence); the one-token
+// instances carry none of its row bookkeeping.
+template <int TPW, bool WIDE, bool BLOCK>
 __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     int B, int Hq, int k, int window, int n_splits, float scale_log2, int flags,
     const long long* __restrict__ row_off, const int* __restrict__ len,
@@ -178,10 +181,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     const int t_begin = split * TPW;
 
     // round trip 1: sequence scalars, this thread's selection entries, q
-    const int bt = flags >> kBlockShift;
-    const int bs = bt > 1 ? b / bt : b;                        // the sequence of query row b
-    const int bsel = bt > 1 && (flags & kBlockShared) ? bs : b;   // the row of its selection
-    const int len_b = len[bs] - (bt > 1 ? bt - 1 - (b - bs * bt) : 0), sel_b = sel_len[bsel];
+    const int bt = BLOCK ? flags >> kBlockShift : 1;
+    const int bs = BLOCK ? b / bt : b;                         // the sequence of query row b
+    const int bsel = BLOCK && (flags & kBlockShared) ? bs : b;    // the row of its selection
+    const int len_b = len[bs] - (BLOCK ? bt - 1 - (b - bs * bt) : 0), sel_b = sel_len[bsel];
     const long long roff = row_off[bs];
     // loads of a tile: thread t takes the 32 bytes of codes of row crow at
     // bytes 32 c8 .. (latent elements 64 c8 ..) and their two scales; each
@@ -284,11 +287,22 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     }
     // the wave's exponent: the largest scale byte of its valid rows in all of
     // the workgroup's tiles (a wave holds the same 8 rows of every tile)
+    // When every valid scale byte of the wave lies in [2, 200], the absolute
+    // scales (exponent 127) are exact and overflow-free: the values stay
+    // within [2^-126, 6 * 2^73], every product and sum far inside fp32.
     int ew = 0;
+    bool outside = false;
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
-        if ((cok >> t) & 1u) ew = max(ew, (int)max(rsb[t] & 0xFFu, rsb[t] >> 8));
-    ew = __builtin_amdgcn_readfirstlane((int)wave_max((float)ew));
+        if ((cok >> t) & 1u) {
+            const int b0 = (int)(rsb[t] & 0xFFu), b1 = (int)(rsb[t] >> 8);
+            ew = max(ew, max(b0, b1));
+            outside |= min(b0, b1) < 2 || max(b0, b1) > 200;
+        }
+    if (__ballot(outside) == 0)                          // uniform
+        ew = 127;
+    else
+        ew = __builtin_amdgcn_readfirstlane((int)wave_max((float)ew));
     if (l == 0) s_e[wave] = ew;
 
     f32x4 o[kNb];                                        // set by the first tile's P.V
@@ -658,11 +672,18 @@ static int attn_decode(const char* fn, const void* q_bf16, const unsigned char* 
                            out, lse);
     };
     const bool wide = (long long)npairs * ns > kAttnWideWgs;
-    switch (tpw) {
-        case 1: wide ? launch(sparse_attn_kernel<1, true>) : launch(sparse_attn_kernel<1, false>); break;
-        case 2: wide ? launch(sparse_attn_kernel<2, true>) : launch(sparse_attn_kernel<2, false>); break;
-        default: wide ? launch(sparse_attn_kernel<4, true>) : launch(sparse_attn_kernel<4, false>); break;
-    }
+    auto launch_tpw = [&](auto blk) {
+        constexpr bool BLK = decltype(blk)::value;
+        switch (tpw) {
+            case 1: wide ? launch(sparse_attn_kernel<1, true, BLK>) : launch(sparse_attn_kernel<1, false, BLK>); break;
+            case 2: wide ? launch(sparse_attn_kernel<2, true, BLK>) : launch(sparse_attn_kernel<2, false, BLK>); break;
+            default: wide ? launch(sparse_attn_kernel<4, true, BLK>) : launch(sparse_attn_kernel<4, false, BLK>); break;
+        }
+    };
+    if (T > 1)
+        launch_tpw(std::true_type{});
+    else
+        launch_tpw(std::false_type{});
     if (int e = launch_status(fn)) return e;
     if (ns > 1) {
         const dim3 cg(8 * pr * kHeadsPerWg), cb(128);

@@ -53,11 +53,13 @@ constexpr int kAttnWideWgs = 256;       // above this many workgroups, the wide 
 constexpr int kAttnMaxSplits = kAttnMaxRows / kAttnRows;   // one tile per split at most
 
 // Eight E2M1 codes (one 32-bit word, element 2i in the low nibble of byte i)
-// times 2^d, d <= 0, to eight bf16 (element 2i in the low half of word i).
-// The kernel dequantises relative to the largest scale byte of the rows a wave
-// holds: d = (scale byte of the block) - (that maximum), so the values stay
-// between 2^-1 * 2^d and 6 and the absolute power of two is applied to the
-// scores and carried with the outputs.  v_cvt_scalef32_pk_bf16_fp4 converts the
+// times 2^d to eight bf16 (element 2i in the low half of word i).  The kernel
+// dequantises relative to a per-wave exponent e: d = (scale byte of the block)
+// - e.  In general e is the largest scale byte of the rows the wave holds, so
+// d <= 0, the values stay between 2^-1 * 2^d and 6, and the power of two is
+// applied to the scores and carried with the outputs; when all of the wave's
+// scale bytes lie in [2, 200], e = 127 (the absolute scales, d in [-125, 73],
+// every value a normal number far from overflow).  v_cvt_scalef32_pk_bf16_fp4 converts the
 // two codes of one byte and applies the fp32 scale 2^d, built from its bits
 // (subnormal below 2^-126, zero below 2^-149).  Exact whenever d >= -126:
 // the results have at most two significant bits.
@@ -286,10 +288,10 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
         rc1[t] = *reinterpret_cast<const u32x4*>(cp + 16);
     }
     // the wave's exponent: the largest scale byte of its valid rows in all of
-    // the workgroup's tiles (a wave holds the same 8 rows of every tile)
-    // When every valid scale byte of the wave lies in [2, 200], the absolute
-    // scales (exponent 127) are exact and overflow-free: the values stay
-    // within [2^-126, 6 * 2^73], every product and sum far inside fp32.
+    // the workgroup's tiles (a wave holds the same 8 rows of every tile), or
+    // 127 when every such byte lies in [2, 200]: the absolute scales are then
+    // exact and overflow-free (values within [2^-126, 6 * 2^73], every
+    // product and sum far inside fp32) and no cross-lane maximum is needed
     int ew = 0;
     bool outside = false;
 #pragma unroll

@@ -309,7 +309,8 @@ int csa2_select_topk(const int* score, const int* cand_pos, const int* cand_len,
  * k + window <= 16384.
  * Numeric range: every E8M0 scale byte 0..254 is read exactly (the rows are
  * dequantised relative to the largest scale byte among the rows a wave
- * holds, and that power of two is applied to the scores and outputs).  The
+ * holds, and that power of two is applied to the scores and outputs; a wave
+ * whose scale bytes all lie in [2, 200] uses the absolute scales).  The
  * results meet 1e-3 * max|out| whenever every score sm_scale * q . v is
  * finite in fp32; blocks more than 126 octaves below the largest scale of
  * their workgroup's rows are taken as zero (their contribution is below

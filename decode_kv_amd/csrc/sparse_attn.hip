@@ -178,8 +178,6 @@ __global__ __launch_bounds__(kAttnThreads, 1) void sparse_attn_kernel(
     const int tid = threadIdx.x, wave = tid / kWave, l = lane_id();
     const int g = l >> 4, c16 = l & 15;
     const int head = hz * kHeadsPerWg + c16;      // this lane's head
-    // dequantisation work split: thread owns rows 8rg..8rg+7 x elements 8dc..8dc+7
-    const int dc = tid >> 2, rg = tid & 3;
     const int t_begin = split * TPW;
 
     // round trip 1: sequence scalars, this thread's selection entries, q

@@ -23,8 +23,13 @@ step with an untimed read of a 1 GiB buffer; warm timing (reported beside it)
 does not.  Each step is timed with HIP events on the replay stream.
 
 The roofline object covers the Full scan's scoring kernel, the one kernel of
-the step that streams the whole context (64 B of index key per position):
-its average launch duration comes from back-to-back launches through
+the step that streams the whole context (64 B of index key per position),
+against the tightest of three bounds at the peaks: its key bytes at HBM
+speed, its int8 multiply-adds at the matrix-core rate and its score-rule
+vector operations (a max and a multiply-add per token, position and head) at
+the integer ALU rate; the other two are listed beside it.  One token is
+HBM-bound; a block of query tokens is ALU-bound.  The kernel's average
+launch duration comes from back-to-back launches through
 csa2_index_score, captured in one HIP graph, each over a key copy that is not
 in the Infinity Cache.  read_ceiling is the same measurement for a kernel that
 only reads the key bytes (csa2_stream_read) in the scoring kernel's launch
@@ -52,6 +57,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 INT8_PEAK_TOPS = 5000.0          # dense int8 MFMA, MI355X
+# integer vector ALU: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz, one operation per
+# lane-instruction (the fp32 vector peak, 157.3 TFLOP/s, counts a packed FMA
+# as four flops per lane-instruction)
+ALU_PEAK_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 METRIC = "decode steps/s at 1M ctx (index+sparse attn) + achieved HBM GB/s vs peak"
 
 
@@ -94,12 +103,16 @@ def algorithmic_bytes(wl, lengths, sel_union=None) -> dict:
         # the block against the positions it ranks
         scan_E = Es[0] * T if shared else sum(Es)
         tot["scan_ops"] = tot.get("scan_ops", 0) + 2 * wl.Dk * wl.H * scan_E
+        # and the vector work of the score rule per token, position and head:
+        # the ReLU (a max) and the weighted accumulate (a multiply-add)
+        tot["scan_alu_ops"] = tot.get("scan_alu_ops", 0) + 2 * wl.H * scan_E
         if wl.append:
             # per token and cache (one per layer, or one shared by all): the
             # bf16 row in, its FP4 codes and scales out; the 64-byte index key
             # in and out
             tot["append"] += T * (wl.n_kv * (2 * wl.D + wl.D // 2 + wl.D // 32) + 2 * wl.Dk)
     tot.setdefault("scan_ops", 0)
+    tot.setdefault("scan_alu_ops", 0)
     tot["step"] = tot["append"] + tot["full"] + tot["select"] + tot["reindex"] + tot["attn"]
     return tot
 
@@ -616,28 +629,38 @@ def main():
         return ms, gbs
 
     ms, step_gbs = summary(results["cold"])
-    scan_gbs = ab["scan_kernel"] / (scan_avg_ms * 1e-3) / 1e9
-    scan_tops = ab["scan_ops"] / (scan_avg_ms * 1e-3) / 1e12
-    # the scan's bound: HBM (its key bytes at 8 TB/s) or the int8 matrix cores
-    # (its multiply-adds at 5.0 POP/s), whichever takes longer at peak; a long
-    # block of query tokens (a prefill chunk) is bound by the matrix cores
-    mfma_bound = ab["scan_ops"] / (INT8_PEAK_TOPS * 1e12) > ab["scan_kernel"] / (HBM_PEAK_GBS * 1e9)
+    scan_s = scan_avg_ms * 1e-3
+    scan_gbs = ab["scan_kernel"] / scan_s / 1e9
+    # the scan's bound: whichever of its key bytes at the HBM peak, its int8
+    # multiply-adds at the matrix-core peak and its score-rule vector
+    # operations at the integer ALU peak takes longest (one token: HBM; a long
+    # block of query tokens, such as a prefill chunk: the vector ALU)
+    bounds = [
+        {"bound": "hbm", "achieved": scan_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+         "t_peak": ab["scan_kernel"] / (HBM_PEAK_GBS * 1e9)},
+        {"bound": "mfma", "achieved": ab["scan_ops"] / scan_s / 1e12, "peak": INT8_PEAK_TOPS,
+         "unit": "TOP/s (int8)", "t_peak": ab["scan_ops"] / (INT8_PEAK_TOPS * 1e12)},
+        {"bound": "alu", "achieved": ab["scan_alu_ops"] / scan_s / 1e12,
+         "peak": round(ALU_PEAK_TOPS, 2), "unit": "T lane-ops/s (integer VALU)",
+         "t_peak": ab["scan_alu_ops"] / (ALU_PEAK_TOPS * 1e12)},
+    ]
+    bounds.sort(key=lambda x: -x["t_peak"])
+    for x in bounds:
+        x["frac"] = round(x["achieved"] / x["peak"], 4)
+        x["achieved"] = round(x["achieved"], 1)
+        x["us_at_peak"] = round(x.pop("t_peak") * 1e6, 3)
+    top = bounds[0]
     scan_roofline = {
         "kernel": ("full_score_block_kernel (Full-mode index scan, %d tokens)" % wl.block)
         if blk else "full_score_kernel (Full-mode index scan)",
-        "bound": "mfma" if mfma_bound else "hbm",
-        "achieved": round(scan_tops if mfma_bound else scan_gbs, 1),
-        "peak": INT8_PEAK_TOPS if mfma_bound else HBM_PEAK_GBS,
-        "unit": "TOP/s" if mfma_bound else "GB/s",
-        "frac": round(scan_tops / INT8_PEAK_TOPS if mfma_bound else scan_gbs / HBM_PEAK_GBS, 4),
+        "bound": top["bound"], "achieved": top["achieved"], "peak": top["peak"],
+        "unit": top["unit"], "frac": top["frac"],
         "traffic": None,
         "avg_launch_us": round(scan_avg_ms * 1e3, 3), "launches_timed": n_scan,
         "algorithmic_bytes_per_launch": ab["scan_kernel"],
         "algorithmic_int8_ops_per_launch": ab["scan_ops"],
-        "other_bound": ({"unit": "GB/s", "achieved": round(scan_gbs, 1),
-                         "frac": round(scan_gbs / HBM_PEAK_GBS, 4)} if mfma_bound else
-                        {"unit": "TOP/s", "achieved": round(scan_tops, 1),
-                         "frac": round(scan_tops / INT8_PEAK_TOPS, 4)}),
+        "algorithmic_alu_ops_per_launch": ab["scan_alu_ops"],
+        "other_bounds": bounds[1:],
     }
     read_gbs = key_bytes / (read_avg_ms * 1e-3) / 1e9
     scan_roofline["traffic"] = (

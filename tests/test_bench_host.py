@@ -74,3 +74,27 @@ def test_verify_block_appends_every_token():
     one = bench.algorithmic_bytes(W.WORKLOADS["batch8_256k"], [262144])
     blk = bench.algorithmic_bytes(W.WORKLOADS["batch8_256k_block5"], [262144])
     assert blk["append"] == 5 * one["append"]
+
+
+def test_scan_bound_by_workload():
+    """The scan's tightest bound at the peaks: one token streams 67 MB of keys
+    (8.4 us at 8 TB/s) against 3.4 us of score-rule vector work; five tokens
+    need 5 x 2 x 64 operations per position (17.1 us at 39.3 T lane-ops/s)
+    and 256 prompt tokens 109 us, beyond their int8 matrix-core time."""
+    peak = {"hbm": bench.HBM_PEAK_GBS * 1e9, "mfma": bench.INT8_PEAK_TOPS * 1e12,
+            "alu": bench.ALU_PEAK_TOPS * 1e12}
+    assert abs(bench.ALU_PEAK_TOPS - 39.3216) < 1e-9
+
+    def times(name, lengths):
+        ab = bench.algorithmic_bytes(W.WORKLOADS[name], lengths)
+        return {"hbm": ab["scan_kernel"] / peak["hbm"], "mfma": ab["scan_ops"] / peak["mfma"],
+                "alu": ab["scan_alu_ops"] / peak["alu"]}
+
+    one = times("ctx_1m", [1 << 20])
+    assert max(one, key=one.get) == "hbm" and abs(one["alu"] * 1e6 - 3.41) < 0.01
+    blk = times("ctx_1m_block5", [1 << 20])
+    assert max(blk, key=blk.get) == "alu" and abs(blk["alu"] * 1e6 - 17.07) < 0.01
+    pf = times("prefill_128k_chunk256", [131072])
+    assert max(pf, key=pf.get) == "alu" and 108 < pf["alu"] * 1e6 < 110
+    # 64 int8 multiply-adds per head and position against 2 vector operations
+    assert abs(pf["mfma"] / pf["alu"] - 64 * bench.ALU_PEAK_TOPS / bench.INT8_PEAK_TOPS) < 1e-9

@@ -147,13 +147,15 @@ def test_index_score_block(shared):
                 assert (got[b * T + t, E:] == -77).all(), (b, t)
 
 
-@pytest.mark.parametrize("shared,T", [(False, 5), (True, 2), (True, 5), (True, 9)])
-def test_index_reindex_block(shared, T):
+@pytest.mark.parametrize("shared,T,H", [(False, 5, 64), (True, 2, 64), (True, 5, 64), (True, 9, 64),
+                                        (True, 5, 20), (False, 3, 40)])
+def test_index_reindex_block(shared, T, H):
     """A shared list's tokens are spread over the workgroup's four waves:
-    T = 2 leaves two waves idle, T = 9 gives one wave three tokens."""
-    rng = np.random.default_rng(8 + T)
+    T = 2 leaves two waves idle, T = 9 gives one wave three tokens; 20 and
+    40 heads take the two- and three-block instances."""
+    rng = np.random.default_rng(8 + T + H)
     lens = [200000, 6000]
-    keys, row_off, q, w = _block_case(8, lens, T)
+    keys, row_off, q, w = _block_case(8, lens, T, H=H)
     B, P = 2, 16384
     nl = B if shared else B * T
     cand = np.full((nl, P), -1, dtype=np.int32)

@@ -453,13 +453,17 @@ def test_index_full_extreme_scores():
 # csa2_index_reindex and csa2_select_topk
 # ---------------------------------------------------------------------------
 
-def test_index_reindex_matches_oracle():
-    rng = np.random.default_rng(3)
-    B, P, H = 3, 16384, 64
+@pytest.mark.parametrize("H,P", [(64, 16384), (4, 1000), (17, 3000), (33, 700), (48, 16384)])
+def test_index_reindex_matches_oracle(H, P):
+    """Every head-block count of the scoring instance (1 to 4 blocks of 16
+    heads, the last one partly padded) and pools that end inside a
+    workgroup's 256 candidates."""
+    rng = np.random.default_rng(3 + H)
+    B = 3
     lens = [200000, 5000, 130]
     row_off = [0, 200000, 205000]
     keys = rng.integers(-127, 128, size=(sum(lens), 64)).astype(np.int8)
-    cand_len = [16384, 4872, 2]
+    cand_len = [P, min(P, 4872), 2]
     cand = np.full((B, P), -1, dtype=np.int32)
     for b in range(B):
         cand[b, :cand_len[b]] = np.sort(rng.choice(max(lens[b] - 128, 2), cand_len[b], replace=False))
@@ -477,6 +481,30 @@ def test_index_reindex_matches_oracle():
         ref = oracle.index_reindex(keys, row_off[b], cand[b, :n], q[b], w[b])
         assert np.array_equal(got[b, :n], ref)
         assert (got[b, n:] == -1).all()
+
+
+def test_select_topk_short_rows():
+    """Rows of P = 1,000 candidates (fewer than the workgroup's threads), full,
+    partial, short and empty lists, k up to P."""
+    rng = np.random.default_rng(77)
+    B, P = 4, 1000
+    cand_len = [1000, 700, 37, 0]
+    score = rng.integers(0, 5000, size=(B, P)).astype(np.int32)
+    cand = np.zeros((B, P), dtype=np.int32)
+    for b in range(B):
+        cand[b] = np.sort(rng.choice(1_000_000, P, replace=False))
+    for k in [1, 37, 500, 1000]:
+        sel = torch.full((B, k), 0x3333, dtype=torch.int32, device=DEV)
+        sl = torch.full((B,), -5, dtype=torch.int32, device=DEV)
+        csa2.select_topk(torch.from_numpy(score).to(DEV), torch.from_numpy(cand).to(DEV),
+                         torch.tensor(cand_len, dtype=torch.int32, device=DEV), k, sel, sl)
+        got, gl = sel.cpu().numpy(), sl.cpu().numpy()
+        for b in range(B):
+            n = cand_len[b]
+            ref, _ = oracle.topk(score[b, :n], cand[b, :n], k)
+            assert gl[b] == len(ref), (k, b)
+            assert np.array_equal(got[b, :len(ref)], ref), (k, b)
+            assert (got[b, len(ref):] == -1).all(), (k, b)
 
 
 @pytest.mark.parametrize("span", [3, 50, 100000, 1 << 30])

@@ -99,7 +99,8 @@ def test_index_full_block_ties(shared):
 @pytest.mark.parametrize("shared", [False, True])
 def test_index_full_block_sizes(shared):
     """T = 1 (the one-token call's results), T = 8 (the largest block), few
-    heads, a pool larger than the context, k = 0."""
+    heads (one, two and three blocks of 16), a pool larger than the context,
+    k = 0."""
     lens = [9000, 300]
     keys, row_off, q, w = _block_case(3, lens, 1)
     check_full_block(keys, row_off, lens, q, w, 128, 1024, 64, shared, "T=1")
@@ -107,6 +108,8 @@ def test_index_full_block_sizes(shared):
     check_full_block(keys, row_off, lens, q, w, 128, 16384, 512, shared, "T=8 H=4")
     keys, row_off, q, w = _block_case(5, lens, 3, H=20)
     check_full_block(keys, row_off, lens, q, w, 16, 777, 0, shared, "k=0")
+    keys, row_off, q, w = _block_case(9, lens, 5, H=40)
+    check_full_block(keys, row_off, lens, q, w, 128, 3000, 100, shared, "H=40")
 
 
 def test_index_full_block_single_long_sequence():

@@ -365,7 +365,7 @@ def test_index_full_ragged_batch_and_edges():
         cur += L
     keys = rng.integers(-127, 128, size=(cur + 5, 64)).astype(np.int8)
     B = len(lens)
-    for H in [64, 4, 17]:
+    for H in [64, 4, 17, 40]:
         q = rng.integers(-127, 128, size=(B, H, 64)).astype(np.int8)
         w = rng.integers(0, 16, size=(B, H)).astype(np.int8)
         check_full(keys, row_off, lens, q, w, 128, 1024, "ragged H=%d" % H)

@@ -652,6 +652,14 @@ def test_attention_batched_shapes():
     attention_case(32, [0, 50, 129, 3000, 0, 640, 12000, 77, 4096, 1], 512, 64)
 
 
+def test_attention_uneven_window_and_head_groups():
+    """A 300-token window with k = 100 (400 rows: a partial last tile) and 80
+    query heads (five 16-head groups per sequence, an odd pair count per
+    XCD); sequences shorter than the window and one with no selection."""
+    attention_case(33, [5000, 900, 200, 120], 100, 80, window=300)
+    attention_case(34, [3000] * 9, 100, 80, window=300)    # sequence-major placement
+
+
 def test_attention_scale_ranges():
     attention_case(20, [4096, 2000], 512, 64, scale_lo=100, scale_hi=150)
     attention_case(21, [4096, 2000], 512, 64, scale_lo=1, scale_hi=1)

@@ -121,8 +121,8 @@ __global__ __launch_bounds__(kAppendThreads) void kv_append_fp4_kernel(
 // ...) and its index key go to row row_off[b] + len[b] + j; after a barrier,
 // thread 0 advances len[b] by n.  Only this workgroup reads or writes len[b],
 // so the old length is read before the new one is stored.  A wave issues the
-// loads of two rows before it quantises either, so a one-token step pays one
-// load round trip.
+// loads of its first two rows before it reads the length and quantises
+// either, so a one-token step pays one load round trip.
 constexpr int kTokenThreads = 1024;
 
 __global__ __launch_bounds__(kTokenThreads) void append_token_kernel(
@@ -132,6 +132,15 @@ __global__ __launch_bounds__(kTokenThreads) void append_token_kernel(
     int8_t* __restrict__ keys) {
     const int b = blockIdx.x;
     const int wave = threadIdx.x / kWave;
+    constexpr int NW = kTokenThreads / kWave;
+    const int items = n * n_layers;                   // (token, layer) rows of this sequence
+    auto src = [&](int i) {                           // x is [n][n_layers][B][D]
+        return x + ((size_t)i * B + b) * D;
+    };
+    // the wave's first two rows are loaded before the length arrives: their
+    // round trip overlaps the length's
+    u32x4 v0 = wave < items ? load_chunk(src(wave), D, 0) : u32x4{0u, 0u, 0u, 0u};
+    u32x4 v1 = wave + NW < items ? load_chunk(src(wave + NW), D, 0) : u32x4{0u, 0u, 0u, 0u};
     const int L = len[b];
     const long long row0 = row_off[b] + L;
     for (int i = threadIdx.x; i < n * (kDk / 16); i += kTokenThreads) {   // 16 key bytes a thread
@@ -139,11 +148,6 @@ __global__ __launch_bounds__(kTokenThreads) void append_token_kernel(
         *reinterpret_cast<u32x4*>(keys + (row0 + j) * kDk + 16 * c) =
             *reinterpret_cast<const u32x4*>(key_rows + ((size_t)j * B + b) * kDk + 16 * c);
     }
-    constexpr int NW = kTokenThreads / kWave;
-    const int items = n * n_layers;                   // (token, layer) rows of this sequence
-    auto src = [&](int i) {                           // x is [n][n_layers][B][D]
-        return x + ((size_t)i * B + b) * D;
-    };
     auto finish = [&](int i, u32x4 v) {
         const int j = i / n_layers, layer = i - j * n_layers;
         const long long dst = layer * layer_rows + row0 + j;
@@ -155,8 +159,10 @@ __global__ __launch_bounds__(kTokenThreads) void append_token_kernel(
     };
     for (int i0 = wave; i0 < items; i0 += 2 * NW) {  // two rows' loads in flight
         const int i1 = i0 + NW;
-        const u32x4 v0 = load_chunk(src(i0), D, 0);
-        const u32x4 v1 = i1 < items ? load_chunk(src(i1), D, 0) : u32x4{0u, 0u, 0u, 0u};
+        if (i0 > wave) {
+            v0 = load_chunk(src(i0), D, 0);
+            v1 = i1 < items ? load_chunk(src(i1), D, 0) : u32x4{0u, 0u, 0u, 0u};
+        }
         finish(i0, v0);
         if (i1 < items) finish(i1, v1);
     }

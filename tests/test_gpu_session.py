@@ -60,12 +60,13 @@ def _random_caches(rng, rows, nl, D=512):
     return keys, fp4, sc
 
 
-@pytest.mark.parametrize("pinned", [False, True])
-def test_session_export_import(pinned):
+@pytest.mark.parametrize("pinned,nl", [(False, 4), (True, 4), (False, 1)])
+def test_session_export_import(pinned, nl):
     """Ragged lengths (0, shorter than the window, window + 1, long), saved to
-    device or pinned host memory, restored at other row offsets."""
-    rng = np.random.default_rng(2)
-    nl, R = 4, 128
+    device or pinned host memory, restored at other row offsets; four layers'
+    caches, or the one cache of the shared-KV layout."""
+    rng = np.random.default_rng(2 + nl)
+    R = 128
     lens = [0, 50, 128, 129, 5000]
     B = len(lens)
     row_off = list(np.cumsum([0] + [L + 3 for L in lens[:-1]]))
